@@ -1,0 +1,345 @@
+"""CPU oracle for the HGA route + exact-token attention path.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module. The product path (the HIP library
+and its Python binding) never calls it, and it shares no code with them: it
+reads plain numpy arrays and computes every step with plain loops and library
+primitives (sum, matmul, sort), in the order the pages describe the method.
+
+Sources (all five pages share the title "Long-Context Fine-Tuning with Limited
+VRAM"):
+  [gist 2.1]  gist.science, Technical Summary §2.1 "Hierarchical Global
+              Attention (HGA)": chunk selection over 64-token chunk summaries,
+              group selection over 8-token group summaries inside the chosen
+              chunks, exact-token attention over the selected groups, routing
+              without gradient, no router weights.
+  [gist 2.2]  same page, §2.2 "Segment-wise Backward and Tiered Storage":
+              history K/V is detached at the segment boundary.
+  [pith F1]   pith.science review, Figure 1 caption: summaries select regions,
+              the final attention uses exact token K/V only.
+  [pith core] pith.science review, "Core claim": the router is built from the
+              model's projected keys; only exact K/V of selected groups enter
+              the working set.
+
+Readings where the pages are silent (each listed in the design notes):
+  * summary vector = arithmetic mean of the keys of the chunk / group;
+  * block query = mean of the block's 64 queries over the r query heads that
+    share one KV head (grouped-query attention, head h uses KV head h // r);
+  * score = unscaled fp32 dot product, no softmax;
+  * top-k order = score descending, then index ascending (lowest index wins a
+    tie); NaN counts as -inf, -0 equals +0;
+  * selections are emitted in ascending index order, padded with -1;
+  * every history chunk (all lie before the segment) is eligible;
+  * the local window is the whole active segment, causal; no sink window;
+  * the gathered history is detached: no gradient reaches K_hist / V_hist.
+
+Precision: the routing decisions (summaries, block queries, scores) are taken
+in float32, the precision the kernels decide them in; attention forward and
+backward run in float64.
+
+Parity pins live in tests/test_oracle.py (dense-attention equivalence through
+torch's SDPA, brute-force top-k, closed forms, finite differences). No function
+here is left unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+CHUNK = 64     # tokens per chunk [gist 2.1]
+GROUP = 8      # tokens per group [gist 2.1]
+BLOCK = 64     # queries per routed query block (one routing decision)
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# Summaries [gist 2.1 "Chunk Selection" / "Group Selection"; pith core]
+# ---------------------------------------------------------------------------
+def _segmented_mean(k_hist: np.ndarray, width: int) -> np.ndarray:
+    """Mean over consecutive runs of ``width`` tokens, summed in token order."""
+    n_kv, H, d = k_hist.shape
+    if H % width:
+        raise ValueError(f"history length {H} is not a multiple of {width}")
+    k = np.asarray(k_hist, dtype=F32).reshape(n_kv, H // width, width, d)
+    acc = np.zeros((n_kv, H // width, d), dtype=F32)
+    for u in range(width):                 # sequential sum over the run
+        acc += k[:, :, u, :]
+    return acc * F32(1.0 / width)
+
+
+def chunk_summaries(k_hist: np.ndarray) -> np.ndarray:
+    """C[j][m] = mean of K_hist[j][64m .. 64m+63]; float32 [n_kv][H/64][d]."""
+    return _segmented_mean(k_hist, CHUNK)
+
+
+def group_summaries(k_hist: np.ndarray) -> np.ndarray:
+    """G[j][n] = mean of K_hist[j][8n .. 8n+7]; float32 [n_kv][H/8][d]."""
+    return _segmented_mean(k_hist, GROUP)
+
+
+# ---------------------------------------------------------------------------
+# Block query [gist 2.1 "the current query block scores these summaries"]
+# ---------------------------------------------------------------------------
+def block_queries(q: np.ndarray, n_kv: int) -> np.ndarray:
+    """qbar[b][j] = mean of Q[h][64b .. 64b+63] over the r heads h of KV head j.
+
+    Returns float32 [S/64][n_kv][d].
+    """
+    n_q, S, d = q.shape
+    if n_q % n_kv or S % BLOCK:
+        raise ValueError("bad query shape")
+    r = n_q // n_kv
+    qq = np.asarray(q, dtype=F32).reshape(n_kv, r, S // BLOCK, BLOCK, d)
+    acc = np.zeros((n_kv, S // BLOCK, d), dtype=F32)
+    for h in range(r):
+        for i in range(BLOCK):
+            acc += qq[:, h, :, i, :]
+    acc *= F32(1.0 / (BLOCK * r))
+    return np.ascontiguousarray(acc.transpose(1, 0, 2))
+
+
+# ---------------------------------------------------------------------------
+# Top-k with lowest-index tie-break
+# ---------------------------------------------------------------------------
+def topk_lowest_index(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k best scores: score descending, index ascending on ties.
+
+    NaN ranks as -inf; -0 and +0 compare equal. Returned in ascending index
+    order (the selection is a set; ascending keeps later gathers monotone).
+    """
+    s = np.asarray(scores, dtype=F32).copy()
+    s[np.isnan(s)] = -np.inf
+    idx = np.arange(s.shape[0])
+    order = np.lexsort((idx, -s))          # primary: -score, secondary: index
+    return np.sort(order[: min(k, s.shape[0])])
+
+
+def chunk_scores(qbar: np.ndarray, C: np.ndarray) -> np.ndarray:
+    """sc[b][j][m] = qbar[b][j] . C[j][m] in float32; [n_B][n_kv][n_C]."""
+    n_B, n_kv, d = qbar.shape
+    out = np.empty((n_B, n_kv, C.shape[1]), dtype=F32)
+    for j in range(n_kv):
+        out[:, j, :] = np.asarray(qbar[:, j, :], F32) @ np.asarray(C[j], F32).T
+    return out
+
+
+def route_chunks(qbar: np.ndarray, C: np.ndarray, k_c: int):
+    """Chunk selection [gist 2.1 "Chunk Selection"].
+
+    Every history chunk precedes the active segment, so all n_C chunks are
+    candidates for every query block. Returns (sel int32 [n_B][n_kv][k_c]
+    ascending, -1 padded; scores float32 [n_B][n_kv][n_C]).
+    """
+    sc = chunk_scores(qbar, C)
+    n_B, n_kv, n_C = sc.shape
+    sel = np.full((n_B, n_kv, k_c), -1, dtype=np.int32)
+    for b in range(n_B):
+        for j in range(n_kv):
+            top = topk_lowest_index(sc[b, j], k_c)
+            sel[b, j, : top.shape[0]] = top
+    return sel, sc
+
+
+def group_candidates(chunks: np.ndarray) -> np.ndarray:
+    """Groups 8m .. 8m+7 of every selected chunk m (ascending chunks)."""
+    ch = [int(m) for m in chunks if m >= 0]
+    return np.array([8 * m + u for m in ch for u in range(CHUNK // GROUP)],
+                    dtype=np.int64)
+
+
+def route_groups_one(qbar_bj: np.ndarray, G_j: np.ndarray, chunks: np.ndarray,
+                     k_g: int):
+    """Group selection for one (query block, KV head) [gist 2.1 "Group Selection"].
+
+    Returns (selected group ids ascending, candidate ids, candidate scores).
+    """
+    cand = group_candidates(chunks)
+    if cand.shape[0] == 0:
+        return cand.astype(np.int32), cand, np.zeros(0, F32)
+    sg = np.asarray(G_j[cand], F32) @ np.asarray(qbar_bj, F32)
+    top = topk_lowest_index(sg, k_g)       # positions in cand (ascending)
+    return cand[top].astype(np.int32), cand, sg
+
+
+def route_groups(qbar: np.ndarray, G: np.ndarray, sel_chunks: np.ndarray, k_g: int):
+    """sel_groups int32 [n_B][n_kv][k_g], ascending, -1 padded."""
+    n_B, n_kv, _ = sel_chunks.shape
+    sel = np.full((n_B, n_kv, k_g), -1, dtype=np.int32)
+    for b in range(n_B):
+        for j in range(n_kv):
+            g, _, _ = route_groups_one(qbar[b, j], G[j], sel_chunks[b, j], k_g)
+            sel[b, j, : g.shape[0]] = g
+    return sel
+
+
+def route(q, k_hist, n_kv, k_c, k_g):
+    """The whole routing step from raw inputs: summaries, block queries,
+    chunk top-k, group top-k. Returns (sel_chunks, sel_groups, aux)."""
+    C = chunk_summaries(k_hist)
+    G = group_summaries(k_hist)
+    qbar = block_queries(q, n_kv)
+    sel_c, sc = route_chunks(qbar, C, k_c)
+    sel_g = route_groups(qbar, G, sel_c, k_g)
+    return sel_c, sel_g, dict(C=C, G=G, qbar=qbar, chunk_scores=sc)
+
+
+# ---------------------------------------------------------------------------
+# Exact-token attention [gist 2.1 "Exact-Token Attention"; pith F1]
+# ---------------------------------------------------------------------------
+def attended_history_tokens(sel_groups_bj: np.ndarray) -> np.ndarray:
+    """History token ids 8n .. 8n+7 of every selected group n >= 0."""
+    return np.array([GROUP * int(n) + u for n in sel_groups_bj if n >= 0
+                     for u in range(GROUP)], dtype=np.int64)
+
+
+def _block_keys(k_hist, v_hist, k_seg, v_seg, sel_groups, b, j):
+    hist = attended_history_tokens(sel_groups[b, j])
+    n_loc = BLOCK * (b + 1)                  # segment keys 0 .. 64b+63
+    Kc = np.concatenate([np.asarray(k_hist[j][hist], F64),
+                         np.asarray(k_seg[j][:n_loc], F64)], axis=0)
+    Vc = np.concatenate([np.asarray(v_hist[j][hist], F64),
+                         np.asarray(v_seg[j][:n_loc], F64)], axis=0)
+    return Kc, Vc, hist.shape[0], n_loc
+
+
+def _block_probs(Qb, Kc, n_hist, n_loc, b, scale):
+    """Softmax over [gathered history || causal segment] for 64 query rows."""
+    s = scale * (Qb @ Kc.T)                          # (64, n_hist + n_loc)
+    qpos = BLOCK * b + np.arange(BLOCK)[:, None]     # segment position of row
+    kpos = np.arange(n_loc)[None, :]
+    allowed = np.concatenate([np.ones((BLOCK, n_hist), bool), kpos <= qpos], axis=1)
+    s = np.where(allowed, s, -np.inf)
+    M = s.max(axis=1, keepdims=True)
+    e = np.exp(s - M)
+    ell = e.sum(axis=1, keepdims=True)
+    return e / ell, (M + np.log(ell))[:, 0]
+
+
+def attn_fwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale):
+    """O[h][i] = softmax(scale * Q[h][i] . K_t) weighted sum of V_t over
+    t in {selected history tokens of block i//64, KV head h//r} U {segment 0..i}.
+
+    Returns (O float64 [n_q][S][d], LSE float64 [n_q][S]).
+    """
+    n_q, S, d = q.shape
+    n_kv = k_seg.shape[0]
+    r = n_q // n_kv
+    O = np.zeros((n_q, S, d), F64)
+    LSE = np.zeros((n_q, S), F64)
+    for h in range(n_q):
+        j = h // r
+        for b in range(S // BLOCK):
+            Kc, Vc, n_hist, n_loc = _block_keys(k_hist, v_hist, k_seg, v_seg,
+                                                sel_groups, b, j)
+            Qb = np.asarray(q[h, BLOCK * b: BLOCK * (b + 1)], F64)
+            P, lse = _block_probs(Qb, Kc, n_hist, n_loc, b, scale)
+            O[h, BLOCK * b: BLOCK * (b + 1)] = P @ Vc
+            LSE[h, BLOCK * b: BLOCK * (b + 1)] = lse
+    return O, LSE
+
+
+def attn_bwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale, d_o):
+    """Gradients of sum(O * dO) w.r.t. Q, K_seg, V_seg [gist 2.1, gist 2.2].
+
+    The history K/V is detached (no gradient); routing is a stop-gradient step,
+    so the selections are constants. Uses the softmax Jacobian directly:
+    dS = P * (dP - sum_t P_t dP_t). Returns float64 (dQ, dK_seg, dV_seg).
+    """
+    n_q, S, d = q.shape
+    n_kv = k_seg.shape[0]
+    r = n_q // n_kv
+    dQ = np.zeros((n_q, S, d), F64)
+    dK = np.zeros((n_kv, S, d), F64)
+    dV = np.zeros((n_kv, S, d), F64)
+    for h in range(n_q):
+        j = h // r
+        for b in range(S // BLOCK):
+            rows = slice(BLOCK * b, BLOCK * (b + 1))
+            Kc, Vc, n_hist, n_loc = _block_keys(k_hist, v_hist, k_seg, v_seg,
+                                                sel_groups, b, j)
+            Qb = np.asarray(q[h, rows], F64)
+            dOb = np.asarray(d_o[h, rows], F64)
+            P, _ = _block_probs(Qb, Kc, n_hist, n_loc, b, scale)
+            dP = dOb @ Vc.T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dQ[h, rows] = scale * (dS @ Kc)
+            dK[j, :n_loc] += scale * (dS[:, n_hist:].T @ Qb)
+            dV[j, :n_loc] += P[:, n_hist:].T @ dOb
+    return dQ, dK, dV
+
+
+# ---------------------------------------------------------------------------
+# Parity criteria used by the tests
+# ---------------------------------------------------------------------------
+def scaled_max_error(got: np.ndarray, ref: np.ndarray):
+    """(max|got-ref|, bound scale = min(1, max|ref|))."""
+    got = np.asarray(got, F64)
+    ref = np.asarray(ref, F64)
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    scale = min(1.0, float(np.max(np.abs(ref)))) if ref.size else 1.0
+    return err, scale
+
+
+def within_tolerance(got, ref, tol: float) -> bool:
+    """Pass iff max|got - ref| <= tol * min(1, max|ref|).
+
+    Tighter than (and implying) the plain max-abs bound ``tol``; it stays
+    meaningful when the reference itself is far below ``tol`` in magnitude.
+    """
+    err, scale = scaled_max_error(got, ref)
+    return err <= tol * scale
+
+
+def check_selection(qbar, C, G, sel_chunks, sel_groups, k_c, k_g, gap=1e-5):
+    """Validate a selection against this oracle, allowing near-tie swaps.
+
+    Per (block b, KV head j):
+      chunks: the set must have min(k_c, n_C) distinct ascending valid ids,
+        -1 padded; every id in the symmetric difference with the oracle's set
+        must score within ``gap`` of the oracle's k-th best chunk score.
+      groups: the oracle's group step is re-run on the given chunk set, then
+        the same rule applies; every group must lie inside a given chunk.
+    Returns dict(ok, failures[list], chunk_exemptions, group_exemptions).
+    """
+    sc = chunk_scores(qbar, C)
+    n_B, n_kv, n_C = sc.shape
+    fails, ex_c, ex_g = [], 0, 0
+    for b in range(n_B):
+        for j in range(n_kv):
+            got_c = [int(x) for x in sel_chunks[b, j]]
+            want_n = min(k_c, n_C)
+            ids = [x for x in got_c if x >= 0]
+            if (len(ids) != want_n or got_c[len(ids):] != [-1] * (k_c - len(ids))
+                    or any(x >= n_C for x in ids)
+                    or any(ids[i] >= ids[i + 1] for i in range(len(ids) - 1))):
+                fails.append((b, j, "chunk set malformed", got_c))
+                continue
+            ref_c = topk_lowest_index(sc[b, j], k_c)
+            tau = float(np.min(sc[b, j][ref_c])) if ref_c.size else 0.0
+            diff = set(ids) ^ set(int(x) for x in ref_c)
+            bad = [m for m in diff if not abs(float(sc[b, j, m]) - tau) < gap]
+            if bad:
+                fails.append((b, j, "chunk mismatch", sorted(diff)))
+                continue
+            ex_c += len(diff) // 2
+            ref_g, cand, sg = route_groups_one(qbar[b, j], G[j], np.array(ids), k_g)
+            got_g = [int(x) for x in sel_groups[b, j]]
+            gids = [x for x in got_g if x >= 0]
+            want_g = min(k_g, cand.shape[0])
+            cset = set(ids)
+            if (len(gids) != want_g or got_g[len(gids):] != [-1] * (k_g - len(gids))
+                    or any(gids[i] >= gids[i + 1] for i in range(len(gids) - 1))
+                    or any((x // (CHUNK // GROUP)) not in cset for x in gids)):
+                fails.append((b, j, "group set malformed", got_g))
+                continue
+            score_of = {int(n): float(s) for n, s in zip(cand, sg)}
+            tau_g = min(score_of[int(n)] for n in ref_g) if ref_g.size else 0.0
+            diff_g = set(gids) ^ set(int(x) for x in ref_g)
+            bad_g = [n for n in diff_g if not abs(score_of[n] - tau_g) < gap]
+            if bad_g:
+                fails.append((b, j, "group mismatch", sorted(diff_g)))
+                continue
+            ex_g += len(diff_g) // 2
+    return dict(ok=not fails, failures=fails, chunk_exemptions=ex_c,
+                group_exemptions=ex_g)
