@@ -1,0 +1,241 @@
+"""Benchmark of the HGA hot path on one MI355X.
+
+One step = one per-layer call of the whole path on one batch of seeded
+synthetic input at Qwen3-8B layer shapes: summaries of the newest closed
+segment (incremental), routing (block queries, chunk top-k, group top-k),
+exact-token attention forward and, for the fwd+bwd workload, its backward.
+Prints one JSON line. Inputs are resident in HBM before the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "query tokens/sec HGA route+attn fwd(+bwd) per layer; achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_16k_fwdbwd")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def kernel_work(w, s):
+    """Algorithmic bytes / flops per launch of each kernel (see the design notes)."""
+    S, H, d = w.seg_len, w.hist_len, w.head_dim
+    nq, kv, kc, kg = w.n_q_heads, w.n_kv_heads, w.top_k_chunks, w.top_k_groups
+    e = 2 if w.dtype == "bf16" else 4
+    n_B, n_C = S // 64, H // 64
+    seg_tokens = min(S, H)                 # incremental summaries: newest closed segment
+    hist_tok = kg * 8                      # routed history tokens per (block, KV head)
+    pairs_hist = S * hist_tok              # per query head
+    pairs_causal = S * (S + 1) // 2
+    work = {
+        "summaries": ("hbm", kv * seg_tokens * d * e + kv * (seg_tokens // 64 + seg_tokens // 8) * d * 4),
+        "block_query": ("hbm", nq * S * d * e + n_B * kv * d * 4),
+        "chunk_score": ("hbm", kv * n_C * d * 4 + n_B * kv * d * 4 + n_B * kv * n_C * 4),
+        "select": ("hbm", n_B * kv * n_C * 4 + n_B * kv * 8 * kc * d * 4 + n_B * kv * (kc + kg) * 4),
+        "attn_fwd": ("mfma", 4 * d * nq * (pairs_hist + pairs_causal)),
+        "bwd_rowdot": ("hbm", 2 * nq * S * d * e + nq * S * 4),
+        "bwd_dq": ("mfma", 6 * d * nq * (pairs_hist + pairs_causal)),
+        "bwd_dkdv": ("mfma", 8 * d * nq * pairs_causal),
+    }
+    if w.hist_on_host:
+        work["gather"] = ("host", n_B * kv * hist_tok * d * e * 2)
+    return work
+
+
+def cpu_baseline(w, inp, budget_s):
+    """The oracle, as it stands, timed on this host for whole steps."""
+    import numpy as np
+    from oracle import hga_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+    except ImportError:                     # pragma: no cover
+        threadpool_info = None
+    a = {k: v.float().numpy() for k, v in inp.items()}
+    n_steps, t_total = 0, 0.0
+    while n_steps < 5 and (n_steps == 0 or t_total < budget_s):
+        t0 = time.perf_counter()
+        _, sel_g, _ = orc.route(a["q"], a["k_hist"], w.n_kv_heads, w.top_k_chunks, w.top_k_groups)
+        orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel_g, w.softmax_scale)
+        if w.backward:
+            orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel_g,
+                         w.softmax_scale, a["d_o"])
+        t_total += time.perf_counter() - t0
+        n_steps += 1
+    cores = 1
+    if threadpool_info is not None:
+        cores = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+    del np
+    return {"value": w.seg_len * n_steps / t_total, "unit": "query tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n_steps} whole step(s) of the same workload (route incl. full summaries, "
+                      f"attention fwd{'+bwd' if w.backward else ''} over all {w.seg_len // 64} "
+                      f"query blocks x {w.n_q_heads} heads), numpy fp32 routing / fp64 attention, "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the path would shard by KV head across GPUs, which is "
+              "not implemented here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_fine_amd import hga, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    hga.lib()
+    w = synth.WORKLOADS[args.workload]
+    s = hga.make_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.hist_len, w.seg_len,
+                       w.top_k_chunks, w.top_k_groups, w.torch_dtype, w.softmax_scale,
+                       hist_on_host=w.hist_on_host)
+    inp = synth.make_inputs(w, args.seed, with_grad_out=w.backward)
+    dev = torch.device("cuda:0")
+    g = {k: v.to(dev) for k, v in inp.items() if k not in ("k_hist", "v_hist")}
+    if w.hist_on_host:
+        for k in ("k_hist", "v_hist"):
+            t = torch.empty(inp[k].shape, dtype=inp[k].dtype, pin_memory=True)
+            t.copy_(inp[k])
+            g[k] = t
+        k_dev = inp["k_hist"].to(dev)      # summaries are built while K is still on the GPU
+    else:
+        g["k_hist"] = inp["k_hist"].to(dev)
+        g["v_hist"] = inp["v_hist"].to(dev)
+        k_dev = g["k_hist"]
+    s_dev = hga.make_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.hist_len, w.seg_len,
+                           w.top_k_chunks, w.top_k_groups, w.torch_dtype, w.softmax_scale)
+    C, G = hga.summaries(s_dev, k_dev)      # summaries of all earlier segments
+    n_B = w.seg_len // 64
+    sel_c = torch.empty((n_B, w.n_kv_heads, w.top_k_chunks), dtype=torch.int32, device=dev)
+    sel_g = torch.empty((n_B, w.n_kv_heads, w.top_k_groups), dtype=torch.int32, device=dev)
+    o = torch.empty_like(g["q"])
+    lse = torch.empty((w.n_q_heads, w.seg_len), dtype=torch.float32, device=dev)
+    ws_r = hga.alloc_workspace(s, hga.HGA_OP_ROUTE, dev)
+    ws_f = hga.alloc_workspace(s, hga.HGA_OP_ATTN_FWD, dev)
+    if w.backward:
+        dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k_seg"]), torch.empty_like(g["v_seg"])
+        ws_b = hga.alloc_workspace(s, hga.HGA_OP_ATTN_BWD, dev)
+    tok0 = max(0, w.hist_len - w.seg_len)
+
+    def step():
+        hga.hga_build_summaries(s_dev, k_dev, C, G, tok0, w.hist_len)
+        hga.hga_route(s, g["q"], C, G, sel_c, sel_g, ws_r)
+        hga.hga_attn_fwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"], sel_g, o, lse, ws_f)
+        if w.backward:
+            hga.hga_attn_bwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"], sel_g, o, lse,
+                             g["d_o"], dq, dk, dv, ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel HIP events, recorded by the library on the launch stream
+    names = list(hga.KERNELS)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for kid, (a, b) in enumerate(evs[i]):
+            hga.hga_set_kernel_events(kid, a, b)
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for kid in range(len(names)):
+        hga.hga_set_kernel_events(kid, None, None)
+
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = w.seg_len * args.steps / elapsed
+    work = kernel_work(w, s)
+    kernels = {}
+    for kid, name in enumerate(names):
+        if name not in work:
+            continue
+        kind, amount = work[name]
+        try:
+            us = sum(evs[i][kid][0].elapsed_time(evs[i][kid][1]) for i in range(args.steps)) \
+                * 1e3 / args.steps
+        except RuntimeError:               # kernel not launched in this workload
+            continue
+        ent = {"avg_us": round(us, 3)}
+        if kind == "mfma":
+            ent["tflops"] = round(amount / (us * 1e-6) / 1e12, 2)
+            ent["gflop_per_launch"] = round(amount / 1e9, 3)
+        else:
+            ent["gbs"] = round(amount / (us * 1e-6) / 1e9, 1)
+            ent["mib_per_launch"] = round(amount / 2 ** 20, 3)
+        kernels[name] = ent
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    kind, amount = work[dom]
+    dus = kernels[dom]["avg_us"]
+    if kind == "mfma":
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        ach = amount / (dus * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+    else:
+        ach = amount / (dus * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    route_us = sum(kernels[k]["avg_us"] for k in ("block_query", "chunk_score", "select") if k in kernels)
+    route_bytes = sum(work[k][1] for k in ("block_query", "chunk_score", "select"))
+    sel_cpu = sel_g.cpu()
+    density = float((sel_cpu >= 0).sum()) * 8 / (n_B * w.n_kv_heads)  # routed tokens per block
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) Q/K/V at Qwen3-8B layer shapes with per-chunk key "
+                "offsets (no weights or corpus)",
+        "config": {"workload": w.name, "context_tokens": w.hist_len + w.seg_len,
+                   "hist_len": w.hist_len, "seg_len": w.seg_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "top_k_chunks": w.top_k_chunks, "top_k_groups": w.top_k_groups,
+                   "pass": "fwd+bwd" if w.backward else "fwd",
+                   "history": "pinned host" if w.hist_on_host else "hbm"},
+        "roofline": roof,
+        "route": {"avg_us": round(route_us, 3),
+                  "gbs": round(route_bytes / (route_us * 1e-6) / 1e9, 1) if route_us else None,
+                  "frac_hbm": round(route_bytes / (route_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                  if route_us else None},
+        "kernels": kernels,
+        "routed_history_tokens_per_block": density,
+    }
+    if args.cpu_baseline == "on":
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * hga.h - C ABI of the MI355X (gfx950) Hierarchical Global Attention hot path.
+ *
+ * HGA is two-level, content-routed attention for one query block (all five
+ * pages titled "Long-Context Fine-Tuning with Limited VRAM"; the method detail
+ * is on gist.science, Technical Summary §2.1 "Hierarchical Global Attention"):
+ *   1. a summary vector per closed 64-token chunk is scored against the query
+ *      block and the best chunks are kept ("Chunk Selection");
+ *   2. inside those chunks, summaries of 8-token groups are scored and the best
+ *      groups are kept ("Group Selection");
+ *   3. attention runs over the exact K/V of the selected groups plus the local
+ *      window, here the whole active segment, causal ("Exact-Token Attention").
+ * Routing has no gradient and no learned weights (same section); history K/V
+ * is detached at the segment boundary (§2.2 "Segment-wise Backward and Tiered
+ * Storage"), so the backward produces dQ for every query and dK/dV only for the
+ * active segment.
+ *
+ * Readings where the pages are silent:
+ *   - summary = mean of the chunk's / group's keys (fp32);
+ *   - block query = mean of the block's 64 queries over the r = n_q/n_kv query
+ *     heads that share one KV head; query head h uses KV head h / r;
+ *   - score = unscaled fp32 dot product; top-k keeps the highest scores and the
+ *     lowest index on ties (NaN ranks lowest, -0 == +0);
+ *   - one routing decision per (query block, KV head), shared by its r heads
+ *     and 64 queries;
+ *   - selections are written in ascending index order, padded with -1;
+ *   - no sink window.
+ *
+ * Layouts (contiguous, head-major, batch 1; "dtype" = hga_shape.dtype, i.e.
+ * fp32 or bf16 stored as raw 16-bit words):
+ *   q, o, d_o, dq                [n_q_heads][seg_len][head_dim]   dtype
+ *   k_hist, v_hist               [n_kv_heads][hist_len][head_dim] dtype
+ *   k_seg, v_seg, dk_seg, dv_seg [n_kv_heads][seg_len][head_dim]  dtype
+ *   chunk_sum                    [n_kv_heads][hist_len/64][head_dim] fp32
+ *   group_sum                    [n_kv_heads][hist_len/8][head_dim]  fp32
+ *   lse                          [n_q_heads][seg_len] fp32 (natural log)
+ *   sel_chunks                   [seg_len/64][n_kv_heads][top_k_chunks] int32
+ *   sel_groups                   [seg_len/64][n_kv_heads][top_k_groups] int32
+ *
+ * Ownership: the caller allocates every buffer and the workspace; the library
+ * allocates no device memory and keeps no state between calls except, for the
+ * pinned-host history tier, one side stream and two events per device, created
+ * on first use. Every pointer is a device pointer except k_hist / v_hist under
+ * HGA_HIST_HOST_PINNED, which must come from hipHostMalloc (page-locked,
+ * mapped) memory.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the null stream). All work is
+ * enqueued asynchronously on it; calls return before the GPU finishes.
+ *
+ * Errors: every argument is checked on the host before anything is launched;
+ * on failure nothing is enqueued and a status code is returned (never an abort
+ * or exception). A failed launch returns HGA_ERR_HIP. Faults that occur while
+ * kernels run surface at the caller's next synchronisation. hga_last_error()
+ * gives a human-readable detail of the last failure on the calling thread.
+ */
+#ifndef HGA_H
+#define HGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HGA_ABI_VERSION 1
+
+typedef enum {
+  HGA_OK = 0,
+  HGA_ERR_INVALID_ARG = 1,   /* bad shape, null pointer, bad range */
+  HGA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim 96) */
+  HGA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  HGA_ERR_HIP = 4            /* a HIP runtime call or launch failed */
+} hga_status;
+
+typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
+typedef enum { HGA_HIST_DEVICE = 0, HGA_HIST_HOST_PINNED = 1 } hga_hist_loc;
+typedef enum { HGA_OP_ROUTE = 0, HGA_OP_ATTN_FWD = 1, HGA_OP_ATTN_BWD = 2 } hga_op;
+
+/* Problem description shared by every call. */
+typedef struct {
+  int32_t n_q_heads;      /* query heads; a multiple of n_kv_heads (GQA) */
+  int32_t n_kv_heads;     /* key/value heads */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t chunk;          /* tokens per chunk; must be 64 */
+  int32_t group;          /* tokens per group; must be 8 */
+  int32_t block_q;        /* queries per routed block; must be 64 */
+  int32_t top_k_chunks;   /* chunks kept per (block, KV head); 1..64 */
+  int32_t top_k_groups;   /* groups kept per (block, KV head); 1..512 */
+  int64_t hist_len;       /* H: history tokens, a multiple of 64, may be 0 */
+  int32_t seg_len;        /* S: active-segment tokens, a positive multiple of 64 */
+  float softmax_scale;    /* multiplies Q.K before the softmax, > 0 */
+  int32_t dtype;          /* hga_dtype of Q/K/V/O/dO/dQ/dK/dV */
+  int32_t hist_loc;       /* hga_hist_loc of k_hist / v_hist */
+} hga_shape;
+
+/* Chunk and group summaries (gist.science Technical Summary §2.1, "Chunk
+ * Selection" and "Group Selection"; pith.science review, "What carries the
+ * argument": summaries are built from the model's projected keys).
+ * For every chunk m with 64m in [tok_begin, tok_end):
+ *   chunk_sum[j][m] = mean of k_hist[j][64m .. 64m+63]
+ *   group_sum[j][n] = mean of k_hist[j][8n .. 8n+7] for its 8 groups n.
+ * tok_begin, tok_end: multiples of 64 with 0 <= tok_begin <= tok_end <= hist_len
+ * (incremental use: summarise only the tokens of a newly closed segment).
+ * k_hist must be in device memory. Summaries outside the range are untouched. */
+hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist,
+                               int64_t tok_begin, int64_t tok_end,
+                               float* chunk_sum, float* group_sum, void* stream);
+
+/* Two-level routing (gist.science Technical Summary §2.1, "Chunk Selection",
+ * "Group Selection"; routing runs without gradient). For each query block b
+ * and KV head j: qbar = block query; chunk scores qbar . chunk_sum[j][m] over
+ * all hist_len/64 history chunks; keep top_k_chunks; group scores over the 8
+ * groups of each kept chunk; keep top_k_groups. Both lists are ascending and
+ * padded with -1 when fewer candidates exist (e.g. hist_len == 0).
+ * ws: device workspace of at least hga_workspace_size(shape, HGA_OP_ROUTE)
+ * bytes, 256-byte aligned; its contents are scratch. */
+hga_status hga_route(const hga_shape* shape, const void* q, const float* chunk_sum,
+                     const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Exact-token attention forward (gist.science Technical Summary §2.1,
+ * "Exact-Token Attention"; pith.science review, Figure 1: summaries select
+ * regions, attention uses exact K/V only). For query i of head h (block
+ * b = i/64, KV head j = h/r) the keys are the 8 tokens of every group
+ * n >= 0 in sel_groups[b][j] (history) and segment tokens 0..i (causal):
+ *   o[h][i] = sum_t softmax_t(scale * q[h][i] . k_t) v_t
+ *   lse[h][i] = log sum_t exp(scale * q[h][i] . k_t)
+ * sel_groups entries must be -1 or in [0, hist_len/8); the library does not
+ * re-check them on the device. ws: hga_workspace_size(shape, HGA_OP_ATTN_FWD)
+ * bytes (zero for device-resident history; staging for the pinned-host tier,
+ * whose gathers run on an internal side stream fenced back to `stream`). */
+hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_hist,
+                        const void* v_hist, const void* k_seg, const void* v_seg,
+                        const int32_t* sel_groups, void* o, float* lse,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of hga_attn_fwd for the loss sum(o * d_o) (gist.science Technical
+ * Summary §2.1: gradients flow through exact-token attention; §2.2: history
+ * is detached at the segment boundary). Writes dq for every query, dk_seg and
+ * dv_seg for the active segment; history K/V, summaries and selections get no
+ * gradient. o and lse are the forward's outputs. Deterministic: no atomics.
+ * ws: hga_workspace_size(shape, HGA_OP_ATTN_BWD) bytes. k_hist / v_hist must
+ * be in device memory (HGA_HIST_DEVICE). */
+hga_status hga_attn_bwd(const hga_shape* shape, const void* q, const void* k_hist,
+                        const void* v_hist, const void* k_seg, const void* v_seg,
+                        const int32_t* sel_groups, const void* o, const float* lse,
+                        const void* d_o, void* dq, void* dk_seg, void* dv_seg,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Exact-token gather on its own (gist.science Technical Summary §2.1 and
+ * §2.2 "Tiered Memory Hierarchy": only the selected groups' exact K/V are
+ * brought into the working set). Copies the 8 tokens of every selected group
+ * into k_out / v_out [seg_len/64][n_kv_heads][top_k_groups*8][head_dim]
+ * (dtype), zero-filling the rows of -1 entries. k_hist / v_hist live where
+ * shape->hist_loc says (device or pinned host); outputs are device memory. */
+hga_status hga_gather_groups(const hga_shape* shape, const void* k_hist,
+                             const void* v_hist, const int32_t* sel_groups,
+                             void* k_out, void* v_out, void* stream);
+
+/* Internal kernels, for hga_set_kernel_events. */
+typedef enum {
+  HGA_KERNEL_SUMMARIES = 0,    /* hga_build_summaries */
+  HGA_KERNEL_BLOCK_QUERY = 1,  /* hga_route: block queries */
+  HGA_KERNEL_CHUNK_SCORE = 2,  /* hga_route: chunk scores */
+  HGA_KERNEL_SELECT = 3,       /* hga_route: chunk + group top-k */
+  HGA_KERNEL_GATHER = 4,       /* hga_gather_groups, pinned-host tier gathers */
+  HGA_KERNEL_ATTN_FWD = 5,     /* hga_attn_fwd */
+  HGA_KERNEL_BWD_ROWDOT = 6,   /* hga_attn_bwd: rowsum(dO * O) */
+  HGA_KERNEL_BWD_DQ = 7,       /* hga_attn_bwd: dQ */
+  HGA_KERNEL_BWD_DKDV = 8,     /* hga_attn_bwd: dK, dV of the segment */
+  HGA_KERNEL_COUNT = 9
+} hga_kernel;
+
+/* Instrumentation: while set, every launch of `kernel` is bracketed by
+ * hipEventRecord(ev_start) / hipEventRecord(ev_stop) on the stream it is
+ * launched on, so hipEventElapsedTime gives that kernel's duration (of its
+ * most recent launch). Both NULL turns it off. The setting is process-wide and
+ * not synchronised between threads; the caller owns the hipEvent_t handles. */
+hga_status hga_set_kernel_events(int32_t kernel, void* ev_start, void* ev_stop);
+
+/* Bytes of workspace `op` (an hga_op) needs for this shape; 0 if the shape is
+ * invalid or the op needs none. */
+size_t hga_workspace_size(const hga_shape* shape, int32_t op);
+
+/* Static string for a status code. */
+const char* hga_status_string(hga_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none). The pointer stays valid until the next call on that thread. */
+const char* hga_last_error(void);
+
+/* HGA_ABI_VERSION of the loaded library. */
+int32_t hga_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H */

@@ -1,0 +1,349 @@
+// C ABI entry points: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before anything is enqueued; failures return a
+// status code and record a message for hga_last_error().
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "hga.h"
+#include "hga_common.hpp"
+
+namespace hga {
+size_t route_workspace_bytes(const hga_shape& s);
+size_t bwd_workspace_bytes(const hga_shape& s);
+}  // namespace hga
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hga_status fail(hga_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hga_status fail(hga_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hga_status ok() {
+  g_last_error.clear();
+  return HGA_OK;
+}
+
+hga_status hip_fail(hipError_t e, const char* what) {
+  return fail(HGA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elem_bytes(const hga_shape& s) { return s.dtype == HGA_BF16 ? 2 : 4; }
+
+hga_status check_shape(const hga_shape* s) {
+  if (!s) return fail(HGA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(HGA_ERR_INVALID_ARG, "head counts must be positive (n_q=%d, n_kv=%d)", s->n_q_heads,
+                s->n_kv_heads);
+  if (s->n_q_heads % s->n_kv_heads)
+    return fail(HGA_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->dtype != HGA_F32 && s->dtype != HGA_BF16)
+    return fail(HGA_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
+  if (s->hist_loc != HGA_HIST_DEVICE && s->hist_loc != HGA_HIST_HOST_PINNED)
+    return fail(HGA_ERR_INVALID_ARG, "unknown hist_loc %d", s->hist_loc);
+  if (s->head_dim <= 0) return fail(HGA_ERR_INVALID_ARG, "head_dim must be positive");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(HGA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", s->head_dim);
+  if (s->chunk <= 0 || s->group <= 0 || s->block_q <= 0)
+    return fail(HGA_ERR_INVALID_ARG, "chunk, group and block_q must be positive");
+  if (s->chunk != hga::kChunk || s->group != hga::kGroup || s->block_q != hga::kBlockQ)
+    return fail(HGA_ERR_UNSUPPORTED, "chunk/group/block_q = %d/%d/%d (supported: 64/8/64)", s->chunk,
+                s->group, s->block_q);
+  if (s->top_k_chunks < 1 || s->top_k_groups < 1)
+    return fail(HGA_ERR_INVALID_ARG, "top_k_chunks and top_k_groups must be >= 1");
+  if (s->top_k_chunks > hga::kMaxTopKChunks || s->top_k_groups > hga::kMaxTopKGroups)
+    return fail(HGA_ERR_UNSUPPORTED, "top_k_chunks %d / top_k_groups %d exceed 64 / 512",
+                s->top_k_chunks, s->top_k_groups);
+  if (s->hist_len < 0 || s->hist_len % hga::kChunk)
+    return fail(HGA_ERR_INVALID_ARG, "hist_len %lld is not a non-negative multiple of 64",
+                static_cast<long long>(s->hist_len));
+  if (s->hist_len / hga::kGroup > INT32_MAX / 2)
+    return fail(HGA_ERR_UNSUPPORTED, "hist_len %lld too large for int32 group ids",
+                static_cast<long long>(s->hist_len));
+  if (s->seg_len <= 0 || s->seg_len % hga::kBlockQ)
+    return fail(HGA_ERR_INVALID_ARG, "seg_len %d is not a positive multiple of 64", s->seg_len);
+  if (!(std::isfinite(s->softmax_scale) && s->softmax_scale > 0.f))
+    return fail(HGA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  return HGA_OK;
+}
+
+#define HGA_REQUIRE(cond, ...)                                   \
+  do {                                                           \
+    if (!(cond)) return fail(HGA_ERR_INVALID_ARG, __VA_ARGS__);  \
+  } while (0)
+
+#define HGA_TRY(stmt)                     \
+  do {                                    \
+    const hga_status st__ = (stmt);       \
+    if (st__ != HGA_OK) return st__;      \
+  } while (0)
+
+// Device-side address of a page-locked host allocation.
+hga_status host_to_device_ptr(const void* host, const void** dev, const char* name) {
+  void* d = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&d, const_cast<void*>(host), 0);
+  if (e != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return fail(HGA_ERR_INVALID_ARG, "%s is not page-locked host memory from hipHostMalloc (%s)", name,
+                hipGetErrorString(e));
+  }
+  *dev = d;
+  return HGA_OK;
+}
+
+// Staging for the pinned-host tier: 2 buffers x kPhaseBlocks blocks, K and V.
+constexpr int kPhaseBlocks = 4;
+
+size_t staging_bytes_per_buffer(const hga_shape& s) {
+  return static_cast<size_t>(kPhaseBlocks) * s.n_kv_heads * s.top_k_groups * hga::kGroup *
+         s.head_dim * elem_bytes(s);
+}
+
+size_t fwd_workspace_bytes(const hga_shape& s) {
+  if (s.hist_loc != HGA_HIST_HOST_PINNED) return 0;
+  return 4 * align256(staging_bytes_per_buffer(s));  // {K, V} x 2 buffers
+}
+
+struct SideResources {
+  hipStream_t side = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t gathered[2] = {nullptr, nullptr};
+  hipEvent_t consumed[2] = {nullptr, nullptr};
+};
+
+std::mutex g_side_mu;
+std::unordered_map<int, SideResources> g_side;
+
+hga_status side_resources(SideResources** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  auto it = g_side.find(dev);
+  if (it == g_side.end()) {
+    SideResources r;
+    if ((e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking)) != hipSuccess)
+      return hip_fail(e, "hipStreamCreateWithFlags");
+    hipEvent_t* evs[5] = {&r.start, &r.gathered[0], &r.gathered[1], &r.consumed[0], &r.consumed[1]};
+    for (hipEvent_t* ev : evs)
+      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "hipEventCreateWithFlags");
+    it = g_side.emplace(dev, r).first;
+  }
+  *out = &it->second;
+  return HGA_OK;
+}
+
+std::atomic<hipEvent_t> g_timer_ev[HGA_KERNEL_COUNT][2];
+
+}  // namespace
+
+namespace hga {
+void timer_begin(int id, hipStream_t stream) {
+  hipEvent_t e = g_timer_ev[id][0].load(std::memory_order_relaxed);
+  if (e) (void)hipEventRecord(e, stream);
+}
+void timer_end(int id, hipStream_t stream) {
+  hipEvent_t e = g_timer_ev[id][1].load(std::memory_order_relaxed);
+  if (e) (void)hipEventRecord(e, stream);
+}
+}  // namespace hga
+
+extern "C" {
+
+hga_status hga_set_kernel_events(int32_t kernel, void* ev_start, void* ev_stop) {
+  if (kernel < 0 || kernel >= HGA_KERNEL_COUNT)
+    return fail(HGA_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+  if ((ev_start == nullptr) != (ev_stop == nullptr))
+    return fail(HGA_ERR_INVALID_ARG, "give both events or neither");
+  g_timer_ev[kernel][0].store(static_cast<hipEvent_t>(ev_start));
+  g_timer_ev[kernel][1].store(static_cast<hipEvent_t>(ev_stop));
+  return ok();
+}
+
+int32_t hga_abi_version(void) { return HGA_ABI_VERSION; }
+
+const char* hga_status_string(hga_status status) {
+  switch (status) {
+    case HGA_OK: return "HGA_OK";
+    case HGA_ERR_INVALID_ARG: return "HGA_ERR_INVALID_ARG";
+    case HGA_ERR_UNSUPPORTED: return "HGA_ERR_UNSUPPORTED";
+    case HGA_ERR_WORKSPACE: return "HGA_ERR_WORKSPACE";
+    case HGA_ERR_HIP: return "HGA_ERR_HIP";
+  }
+  return "HGA_ERR_UNKNOWN";
+}
+
+const char* hga_last_error(void) { return g_last_error.c_str(); }
+
+size_t hga_workspace_size(const hga_shape* shape, int32_t op) {
+  const std::string saved = g_last_error;
+  const hga_status st = check_shape(shape);
+  g_last_error = saved;
+  if (st != HGA_OK) return 0;
+  switch (op) {
+    case HGA_OP_ROUTE: return hga::route_workspace_bytes(*shape);
+    case HGA_OP_ATTN_FWD: return fwd_workspace_bytes(*shape);
+    case HGA_OP_ATTN_BWD: return hga::bwd_workspace_bytes(*shape);
+  }
+  return 0;
+}
+
+hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist, int64_t tok_begin,
+                               int64_t tok_end, float* chunk_sum, float* group_sum, void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_REQUIRE(tok_begin >= 0 && tok_begin <= tok_end && tok_end <= s.hist_len,
+              "token range [%lld, %lld) outside [0, %lld]", static_cast<long long>(tok_begin),
+              static_cast<long long>(tok_end), static_cast<long long>(s.hist_len));
+  HGA_REQUIRE(tok_begin % hga::kChunk == 0 && tok_end % hga::kChunk == 0,
+              "token range bounds must be multiples of 64");
+  if (tok_end == tok_begin) return ok();
+  HGA_REQUIRE(k_hist && chunk_sum && group_sum, "k_hist, chunk_sum and group_sum must be non-NULL");
+  const void* kd = k_hist;
+  if (s.hist_loc == HGA_HIST_HOST_PINNED) HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
+  const hipError_t e = hga::launch_build_summaries(s, kd, tok_begin, tok_end, chunk_sum, group_sum,
+                                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "build_summaries launch");
+  return ok();
+}
+
+hga_status hga_route(const hga_shape* shape, const void* q, const float* chunk_sum,
+                     const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups, void* ws,
+                     size_t ws_bytes, void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_REQUIRE(q && sel_chunks && sel_groups, "q, sel_chunks and sel_groups must be non-NULL");
+  HGA_REQUIRE(s.hist_len == 0 || (chunk_sum && group_sum),
+              "chunk_sum and group_sum must be non-NULL when hist_len > 0");
+  const size_t need = hga::route_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const hipError_t e = hga::launch_route(s, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+  return ok();
+}
+
+hga_status hga_gather_groups(const hga_shape* shape, const void* k_hist, const void* v_hist,
+                             const int32_t* sel_groups, void* k_out, void* v_out, void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_REQUIRE(sel_groups && k_out && v_out, "sel_groups, k_out and v_out must be non-NULL");
+  HGA_REQUIRE(s.hist_len == 0 || (k_hist && v_hist), "k_hist and v_hist must be non-NULL");
+  const void* kd = k_hist;
+  const void* vd = v_hist;
+  if (s.hist_loc == HGA_HIST_HOST_PINNED && s.hist_len > 0) {
+    HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
+    HGA_TRY(host_to_device_ptr(v_hist, &vd, "v_hist"));
+  }
+  const hipError_t e = hga::launch_gather(s, kd, vd, sel_groups, k_out, v_out, 0,
+                                          s.seg_len / hga::kBlockQ, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_hist,
+                        const void* v_hist, const void* k_seg, const void* v_seg,
+                        const int32_t* sel_groups, void* o, float* lse, void* ws, size_t ws_bytes,
+                        void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_REQUIRE(q && k_seg && v_seg && sel_groups && o && lse,
+              "q, k_seg, v_seg, sel_groups, o and lse must be non-NULL");
+  HGA_REQUIRE(s.hist_len == 0 || (k_hist && v_hist), "k_hist and v_hist must be non-NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n_blocks = s.seg_len / hga::kBlockQ;
+  if (s.hist_loc == HGA_HIST_DEVICE || s.hist_len == 0) {
+    const hipError_t e = hga::launch_attn_fwd(s, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse,
+                                              nullptr, nullptr, 0, n_blocks, st);
+    if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+    return ok();
+  }
+
+  // Pinned-host history: gather phase p (kPhaseBlocks query blocks) over the
+  // host link on the side stream into staging buffer p % 2, while the main
+  // stream runs attention on phase p-1 from the other buffer.
+  const size_t need = fwd_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "attn_fwd (pinned-host history) needs %zu workspace bytes, got %zu",
+                need, ws ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const void* kd = nullptr;
+  const void* vd = nullptr;
+  HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
+  HGA_TRY(host_to_device_ptr(v_hist, &vd, "v_hist"));
+  SideResources* r = nullptr;
+  HGA_TRY(side_resources(&r));
+  const size_t buf = align256(staging_bytes_per_buffer(s));
+  char* base = static_cast<char*>(ws);
+  void* kbuf[2] = {base, base + buf};
+  void* vbuf[2] = {base + 2 * buf, base + 3 * buf};
+  hipError_t e;
+  // the side stream must see everything already enqueued on `stream` (sel_groups)
+  if ((e = hipEventRecord(r->start, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(r->side, r->start, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  const int n_phases = (n_blocks + kPhaseBlocks - 1) / kPhaseBlocks;
+  for (int ph = 0; ph < n_phases; ++ph) {
+    const int b0 = ph * kPhaseBlocks;
+    const int b1 = b0 + kPhaseBlocks < n_blocks ? b0 + kPhaseBlocks : n_blocks;
+    const int x = ph % 2;
+    if (ph >= 2 && (e = hipStreamWaitEvent(r->side, r->consumed[x], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+    if ((e = hga::launch_gather(s, kd, vd, sel_groups, kbuf[x], vbuf[x], b0, b1, r->side)) != hipSuccess)
+      return hip_fail(e, "gather launch");
+    if ((e = hipEventRecord(r->gathered[x], r->side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(st, r->gathered[x], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if ((e = hga::launch_attn_fwd(s, q, kd, vd, k_seg, v_seg, sel_groups, o, lse, kbuf[x], vbuf[x], b0,
+                                  b1, st)) != hipSuccess)
+      return hip_fail(e, "attn_fwd launch");
+    if ((e = hipEventRecord(r->consumed[x], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return ok();
+}
+
+hga_status hga_attn_bwd(const hga_shape* shape, const void* q, const void* k_hist,
+                        const void* v_hist, const void* k_seg, const void* v_seg,
+                        const int32_t* sel_groups, const void* o, const float* lse, const void* d_o,
+                        void* dq, void* dk_seg, void* dv_seg, void* ws, size_t ws_bytes,
+                        void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  if (s.hist_loc != HGA_HIST_DEVICE)
+    return fail(HGA_ERR_UNSUPPORTED, "attn_bwd needs device-resident history (hist_loc = HGA_HIST_DEVICE)");
+  HGA_REQUIRE(q && k_seg && v_seg && sel_groups && o && lse && d_o && dq && dk_seg && dv_seg,
+              "q, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk_seg and dv_seg must be non-NULL");
+  HGA_REQUIRE(s.hist_len == 0 || (k_hist && v_hist), "k_hist and v_hist must be non-NULL");
+  const size_t need = hga::bwd_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const hipError_t e = hga::launch_attn_bwd(s, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, d_o,
+                                            dq, dk_seg, dv_seg, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Shared device helpers for the HGA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hga.h"
+
+namespace hga {
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kGroup = 8;    // tokens per group
+constexpr int kBlockQ = 64;  // queries per routed block
+constexpr int kWave = 64;
+constexpr int kMaxTopKChunks = 64;
+constexpr int kMaxTopKGroups = 512;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 is carried as raw 16-bit words in memory.
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+// Round-to-nearest-even fp32 -> bf16 (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Loads 8 consecutive elements as fp32 from fp32 or bf16 storage.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static void load8(const float* p, float* out) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+  __device__ __forceinline__ static float to_f32(float x) { return x; }
+  __device__ __forceinline__ static float from_f32(float x) { return x; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static void load8(const uint16_t* p, float* out) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static float to_f32(uint16_t x) { return bf16_to_f32(x); }
+  __device__ __forceinline__ static uint16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Order-preserving map of an fp32 score to uint32: larger score -> larger key.
+// NaN maps to the key of -inf and -0 to the key of +0.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
+  if (u == 0x80000000u) u = 0u;                          // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// 64-bit ranking key: score first, then the LOWER index wins.
+__device__ __forceinline__ uint64_t rank_key(float s, uint32_t idx) {
+  return (static_cast<uint64_t>(score_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
+}
+__device__ __forceinline__ uint32_t rank_key_index(uint64_t k) {
+  return 0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), mask, kWave);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), mask, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Optional event pair recorded around each launch of kernel `id` (hga_kernel).
+void timer_begin(int id, hipStream_t stream);
+void timer_end(int id, hipStream_t stream);
+
+// Kernel launchers (defined in the .hip files).
+hipError_t launch_build_summaries(const hga_shape& s, const void* k_hist, int64_t tok_begin,
+                                  int64_t tok_end, float* chunk_sum, float* group_sum,
+                                  hipStream_t stream);
+hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,
+                        const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
+                        void* ws, hipStream_t stream);
+hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_hist,
+                         const int32_t* sel_groups, void* k_out, void* v_out,
+                         int32_t block_begin, int32_t block_end, hipStream_t stream);
+// staged != nullptr: history rows come from gathered buffers laid out as
+// [n_blocks][n_kv][top_k_groups*8][head_dim] for blocks [block_begin, block_end).
+hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist,
+                           const void* v_hist, const void* k_seg, const void* v_seg,
+                           const int32_t* sel_groups, void* o, float* lse,
+                           const void* k_staged, const void* v_staged, int32_t block_begin,
+                           int32_t block_end, hipStream_t stream);
+hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist,
+                           const void* v_hist, const void* k_seg, const void* v_seg,
+                           const int32_t* sel_groups, const void* o, const float* lse,
+                           const void* d_o, void* dq, void* dk_seg, void* dv_seg, void* ws,
+                           hipStream_t stream);
+
+}  // namespace hga

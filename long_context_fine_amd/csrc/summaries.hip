@@ -1,0 +1,91 @@
+// Chunk and group summaries: segmented means of the history keys.
+//
+// One workgroup summarises one 64-token chunk of one KV head: it streams the
+// chunk's keys once (coalesced 16-byte loads, 256 B per token row), forms the
+// eight 8-token group sums in LDS, and derives the chunk sum from them. HBM
+// bound: per chunk it reads 64*d elements and writes 9*d floats.
+#include "hga_common.hpp"
+
+namespace hga {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void build_summaries_kernel(
+    const T* __restrict__ k_hist, int64_t hist_len, int64_t chunk_begin,
+    float* __restrict__ chunk_sum, float* __restrict__ group_sum) {
+  constexpr int TPR = D / 8;                  // threads per token row
+  constexpr int RG = kThreads / TPR;          // row groups
+  constexpr int TOK_PER_RG = kChunk / RG;     // consecutive tokens per row group
+  constexpr int RG_PER_GROUP = kGroup / TOK_PER_RG;
+  static_assert(TOK_PER_RG * RG == kChunk && RG_PER_GROUP * TOK_PER_RG == kGroup, "tiling");
+
+  __shared__ float part[RG][D + 1];
+  __shared__ float gsum[kChunk / kGroup][D + 1];
+
+  const int t = threadIdx.x;
+  const int dc = t % TPR;
+  const int rg = t / TPR;
+  const int64_t m = chunk_begin + blockIdx.x;  // chunk index
+  const int j = blockIdx.y;                    // KV head
+
+  const T* src = k_hist + (static_cast<int64_t>(j) * hist_len + m * kChunk + rg * TOK_PER_RG) * D + dc * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < TOK_PER_RG; ++u) {
+    float v[8];
+    Elem<T>::load8(src + static_cast<int64_t>(u) * D, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][dc * 8 + e] = acc[e];
+  __syncthreads();
+
+  const int64_t n_groups_total = hist_len / kGroup;
+  for (int idx = t; idx < (kChunk / kGroup) * D; idx += kThreads) {
+    const int g = idx / D, e = idx % D;
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < RG_PER_GROUP; ++q) s += part[g * RG_PER_GROUP + q][e];
+    gsum[g][e] = s;
+    group_sum[(static_cast<int64_t>(j) * n_groups_total + m * (kChunk / kGroup) + g) * D + e] =
+        s * (1.0f / kGroup);
+  }
+  __syncthreads();
+  if (t < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < kChunk / kGroup; ++g) s += gsum[g][t];
+    chunk_sum[(static_cast<int64_t>(j) * (hist_len / kChunk) + m) * D + t] = s * (1.0f / kChunk);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_t(const hga_shape& s, const void* k, int64_t c0, int64_t c1, float* cs,
+                    float* gs, hipStream_t st) {
+  dim3 grid(static_cast<unsigned>(c1 - c0), static_cast<unsigned>(s.n_kv_heads));
+  timer_begin(HGA_KERNEL_SUMMARIES, st);
+  hipLaunchKernelGGL((build_summaries_kernel<T, D>), grid, dim3(kThreads), 0, st,
+                     static_cast<const T*>(k), s.hist_len, c0, cs, gs);
+  timer_end(HGA_KERNEL_SUMMARIES, st);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_build_summaries(const hga_shape& s, const void* k_hist, int64_t tok_begin,
+                                  int64_t tok_end, float* chunk_sum, float* group_sum,
+                                  hipStream_t stream) {
+  const int64_t c0 = tok_begin / kChunk, c1 = tok_end / kChunk;
+  if (c1 <= c0) return hipSuccess;
+  const bool bf = s.dtype == HGA_BF16;
+  if (s.head_dim == 128)
+    return bf ? launch_t<uint16_t, 128>(s, k_hist, c0, c1, chunk_sum, group_sum, stream)
+              : launch_t<float, 128>(s, k_hist, c0, c1, chunk_sum, group_sum, stream);
+  return bf ? launch_t<uint16_t, 64>(s, k_hist, c0, c1, chunk_sum, group_sum, stream)
+            : launch_t<float, 64>(s, k_hist, c0, c1, chunk_sum, group_sum, stream);
+}
+
+}  // namespace hga

@@ -1,0 +1,284 @@
+"""Python binding of libhga.so (the C ABI in include/hga.h).
+
+Argument marshalling only: every function checks tensor shapes, dtypes and
+devices, then hands raw pointers and the current HIP stream to the library.
+All computation happens in the library's HIP kernels; there is no fallback.
+If libhga.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
+
+HGA_OK, HGA_ERR_INVALID_ARG, HGA_ERR_UNSUPPORTED, HGA_ERR_WORKSPACE, HGA_ERR_HIP = range(5)
+HGA_F32, HGA_BF16 = 0, 1
+HGA_HIST_DEVICE, HGA_HIST_HOST_PINNED = 0, 1
+HGA_OP_ROUTE, HGA_OP_ATTN_FWD, HGA_OP_ATTN_BWD = 0, 1, 2
+
+EXPORTS = ("hga_build_summaries", "hga_route", "hga_attn_fwd", "hga_attn_bwd",
+           "hga_gather_groups", "hga_workspace_size", "hga_status_string",
+           "hga_last_error", "hga_abi_version", "hga_set_kernel_events")
+
+KERNELS = ("summaries", "block_query", "chunk_score", "select", "gather", "attn_fwd",
+           "bwd_rowdot", "bwd_dq", "bwd_dkdv")
+
+
+class HGAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("group", ctypes.c_int32), ("block_q", ctypes.c_int32),
+        ("top_k_chunks", ctypes.c_int32), ("top_k_groups", ctypes.c_int32),
+        ("hist_len", ctypes.c_int64), ("seg_len", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("hist_loc", ctypes.c_int32),
+    ]
+
+    @property
+    def n_blocks(self) -> int:
+        return self.seg_len // self.block_q
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == HGA_BF16 else torch.float32
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhga.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m long_context_fine_amd.build` (needs hipcc)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, SZ, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    SP = ctypes.POINTER(Shape)
+    sig = {
+        "hga_build_summaries": [SP, P, I64, I64, P, P, P],
+        "hga_route": [SP, P, P, P, P, P, P, SZ, P],
+        "hga_attn_fwd": [SP, P, P, P, P, P, P, P, P, P, SZ, P],
+        "hga_attn_bwd": [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "hga_gather_groups": [SP, P, P, P, P, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.hga_workspace_size.argtypes = [SP, I32]
+    L.hga_workspace_size.restype = SZ
+    L.hga_status_string.argtypes = [ctypes.c_int]
+    L.hga_status_string.restype = ctypes.c_char_p
+    L.hga_last_error.argtypes = []
+    L.hga_last_error.restype = ctypes.c_char_p
+    L.hga_set_kernel_events.argtypes = [I32, P, P]
+    L.hga_set_kernel_events.restype = ctypes.c_int
+    L.hga_abi_version.argtypes = []
+    L.hga_abi_version.restype = I32
+    _lib = L
+    return L
+
+
+def make_shape(n_q_heads: int, n_kv_heads: int, head_dim: int, hist_len: int, seg_len: int,
+               top_k_chunks: int, top_k_groups: int, dtype=torch.bfloat16,
+               softmax_scale: float | None = None, hist_on_host: bool = False) -> Shape:
+    return Shape(n_q_heads, n_kv_heads, head_dim, 64, 8, 64, top_k_chunks, top_k_groups,
+                 hist_len, seg_len,
+                 softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(head_dim),
+                 HGA_BF16 if dtype == torch.bfloat16 else HGA_F32,
+                 HGA_HIST_HOST_PINNED if hist_on_host else HGA_HIST_DEVICE)
+
+
+def _check(status: int) -> None:
+    if status != HGA_OK:
+        L = lib()
+        raise HGAError(status, f"{L.hga_status_string(status).decode()}: "
+                               f"{L.hga_last_error().decode()}")
+
+
+def _ptr(t: torch.Tensor | None, shape=None, dtype=None, name="", device=True) -> int | None:
+    if t is None:
+        return None
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not device and (t.is_cuda or not t.is_pinned()):
+        raise ValueError(f"{name}: must be a pinned host tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def hga_set_kernel_events(kernel: int | str, ev_start=None, ev_stop=None) -> None:
+    """Bracket every launch of `kernel` with two caller-owned HIP events
+    (torch.cuda.Event objects or raw hipEvent_t handles); None turns it off."""
+    kid = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+
+    def h(e):
+        if e is None:
+            return None
+        return e.cuda_event if hasattr(e, "cuda_event") else int(e)
+
+    _check(lib().hga_set_kernel_events(kid, h(ev_start), h(ev_stop)))
+
+
+def hga_workspace_size(shape: Shape, op: int) -> int:
+    return int(lib().hga_workspace_size(ctypes.byref(shape), op))
+
+
+def alloc_workspace(shape: Shape, op: int, device="cuda") -> torch.Tensor:
+    n = hga_workspace_size(shape, op)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def hga_build_summaries(shape: Shape, k_hist, chunk_sum, group_sum, tok_begin=0, tok_end=None,
+                        stream=None) -> None:
+    H, kv, d = shape.hist_len, shape.n_kv_heads, shape.head_dim
+    tok_end = H if tok_end is None else tok_end
+    host = shape.hist_loc == HGA_HIST_HOST_PINNED
+    _check(lib().hga_build_summaries(
+        ctypes.byref(shape), _ptr(k_hist, (kv, H, d), shape.torch_dtype, "k_hist", not host),
+        tok_begin, tok_end,
+        _ptr(chunk_sum, (kv, H // 64, d), torch.float32, "chunk_sum"),
+        _ptr(group_sum, (kv, H // 8, d), torch.float32, "group_sum"), _stream(stream)))
+
+
+def hga_route(shape: Shape, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws=None,
+              stream=None) -> None:
+    H, kv, d, S = shape.hist_len, shape.n_kv_heads, shape.head_dim, shape.seg_len
+    if ws is None:
+        ws = alloc_workspace(shape, HGA_OP_ROUTE, q.device)
+    _check(lib().hga_route(
+        ctypes.byref(shape), _ptr(q, (shape.n_q_heads, S, d), shape.torch_dtype, "q"),
+        _ptr(chunk_sum, (kv, H // 64, d), torch.float32, "chunk_sum"),
+        _ptr(group_sum, (kv, H // 8, d), torch.float32, "group_sum"),
+        _ptr(sel_chunks, (shape.n_blocks, kv, shape.top_k_chunks), torch.int32, "sel_chunks"),
+        _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hga_attn_fwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, ws=None,
+                 stream=None) -> None:
+    H, kv, d, S, nq = shape.hist_len, shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
+    dt = shape.torch_dtype
+    host = shape.hist_loc == HGA_HIST_HOST_PINNED
+    if ws is None and hga_workspace_size(shape, HGA_OP_ATTN_FWD) > 0:
+        ws = alloc_workspace(shape, HGA_OP_ATTN_FWD, q.device)
+    _check(lib().hga_attn_fwd(
+        ctypes.byref(shape), _ptr(q, (nq, S, d), dt, "q"),
+        _ptr(k_hist, (kv, H, d), dt, "k_hist", not host),
+        _ptr(v_hist, (kv, H, d), dt, "v_hist", not host),
+        _ptr(k_seg, (kv, S, d), dt, "k_seg"), _ptr(v_seg, (kv, S, d), dt, "v_seg"),
+        _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        _ptr(o, (nq, S, d), dt, "o"), _ptr(lse, (nq, S), torch.float32, "lse"),
+        None if ws is None else ws.data_ptr(),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hga_attn_bwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, d_o,
+                 dq, dk_seg, dv_seg, ws=None, stream=None) -> None:
+    H, kv, d, S, nq = shape.hist_len, shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
+    dt = shape.torch_dtype
+    if ws is None:
+        ws = alloc_workspace(shape, HGA_OP_ATTN_BWD, q.device)
+    _check(lib().hga_attn_bwd(
+        ctypes.byref(shape), _ptr(q, (nq, S, d), dt, "q"),
+        _ptr(k_hist, (kv, H, d), dt, "k_hist"), _ptr(v_hist, (kv, H, d), dt, "v_hist"),
+        _ptr(k_seg, (kv, S, d), dt, "k_seg"), _ptr(v_seg, (kv, S, d), dt, "v_seg"),
+        _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        _ptr(o, (nq, S, d), dt, "o"), _ptr(lse, (nq, S), torch.float32, "lse"),
+        _ptr(d_o, (nq, S, d), dt, "d_o"), _ptr(dq, (nq, S, d), dt, "dq"),
+        _ptr(dk_seg, (kv, S, d), dt, "dk_seg"), _ptr(dv_seg, (kv, S, d), dt, "dv_seg"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hga_gather_groups(shape: Shape, k_hist, v_hist, sel_groups, k_out, v_out, stream=None) -> None:
+    H, kv, d = shape.hist_len, shape.n_kv_heads, shape.head_dim
+    dt = shape.torch_dtype
+    host = shape.hist_loc == HGA_HIST_HOST_PINNED
+    out_shape = (shape.n_blocks, kv, shape.top_k_groups * 8, d)
+    _check(lib().hga_gather_groups(
+        ctypes.byref(shape), _ptr(k_hist, (kv, H, d), dt, "k_hist", not host),
+        _ptr(v_hist, (kv, H, d), dt, "v_hist", not host),
+        _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        _ptr(k_out, out_shape, dt, "k_out"), _ptr(v_out, out_shape, dt, "v_out"), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# conveniences built from the calls above (allocation + call order only)
+# ---------------------------------------------------------------------------
+def summaries(shape: Shape, k_hist, device="cuda"):
+    """Allocate and build the chunk / group summaries of the whole history."""
+    H, kv, d = shape.hist_len, shape.n_kv_heads, shape.head_dim
+    C = torch.empty((kv, H // 64, d), dtype=torch.float32, device=device)
+    G = torch.empty((kv, H // 8, d), dtype=torch.float32, device=device)
+    hga_build_summaries(shape, k_hist, C, G)
+    return C, G
+
+
+def route(shape: Shape, q, chunk_sum, group_sum, ws=None):
+    """Allocate the selection lists and route every query block."""
+    dev = q.device
+    sc = torch.empty((shape.n_blocks, shape.n_kv_heads, shape.top_k_chunks), dtype=torch.int32, device=dev)
+    sg = torch.empty((shape.n_blocks, shape.n_kv_heads, shape.top_k_groups), dtype=torch.int32, device=dev)
+    hga_route(shape, q, chunk_sum, group_sum, sc, sg, ws)
+    return sc, sg
+
+
+def attn_fwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, ws=None):
+    o = torch.empty_like(q)
+    lse = torch.empty((shape.n_q_heads, shape.seg_len), dtype=torch.float32, device=q.device)
+    hga_attn_fwd(shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, ws)
+    return o, lse
+
+
+def attn_bwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, d_o, ws=None):
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k_seg)
+    dv = torch.empty_like(v_seg)
+    hga_attn_bwd(shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+class HGAAttention(torch.autograd.Function):
+    """Routed exact-token attention as an autograd op: forward routes with the
+    given summaries and attends; backward returns grads for q, k_seg, v_seg
+    only (history, summaries and routing get none)."""
+
+    @staticmethod
+    def forward(ctx, shape, q, k_seg, v_seg, k_hist, v_hist, chunk_sum, group_sum):
+        _, sel_g = route(shape, q, chunk_sum, group_sum)
+        o, lse = attn_fwd(shape, q, k_hist, v_hist, k_seg, v_seg, sel_g)
+        ctx.shape = shape
+        ctx.save_for_backward(q, k_seg, v_seg, k_hist, v_hist, sel_g, o, lse)
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k_seg, v_seg, k_hist, v_hist, sel_g, o, lse = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(ctx.shape, q, k_hist, v_hist, k_seg, v_seg, sel_g, o, lse,
+                              d_o.contiguous())
+        return None, dq, dk, dv, None, None, None, None

@@ -272,23 +272,29 @@ def attn_bwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale, d_o):
 # ---------------------------------------------------------------------------
 # Parity criteria used by the tests
 # ---------------------------------------------------------------------------
-def scaled_max_error(got: np.ndarray, ref: np.ndarray):
-    """(max|got-ref|, bound scale = min(1, max|ref|))."""
+def error_stats(got: np.ndarray, ref: np.ndarray):
+    """(max|got-ref|, ||got-ref||_2 / ||ref||_2)."""
     got = np.asarray(got, F64)
     ref = np.asarray(ref, F64)
-    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
-    scale = min(1.0, float(np.max(np.abs(ref)))) if ref.size else 1.0
-    return err, scale
+    if ref.size == 0:
+        return 0.0, 0.0
+    diff = got - ref
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff)) / den if den > 0 else float(np.linalg.norm(diff))
+    return float(np.max(np.abs(diff))), rel
 
 
 def within_tolerance(got, ref, tol: float) -> bool:
-    """Pass iff max|got - ref| <= tol * min(1, max|ref|).
+    """Pass iff max|got - ref| <= tol (the stated bar: 2e-2 for bf16 outputs,
+    1e-4 for fp32) and ||got - ref||_2 <= tol * ||ref||_2.
 
-    Tighter than (and implying) the plain max-abs bound ``tol``; it stays
-    meaningful when the reference itself is far below ``tol`` in magnitude.
+    The second, relative part keeps the check meaningful when |ref| is itself
+    of the order of tol (attention outputs at these shapes are ~1e-2): an
+    all-zero output, dense attention, local-only attention or a selection
+    shifted by one chunk all fail it.
     """
-    err, scale = scaled_max_error(got, ref)
-    return err <= tol * scale
+    err, rel = error_stats(got, ref)
+    return err <= tol and rel <= tol
 
 
 def check_selection(qbar, C, G, sel_chunks, sel_groups, k_c, k_g, gap=1e-5):

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every symbol include/hga.h declares, and
+rejects bad arguments on the host with status codes (no GPU needed: every
+path exercised here returns before anything is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_fine_amd import hga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "hga.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hga_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hga._LIB_PATH):
+        from long_context_fine_amd import build
+        build.build()
+    return hga.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert set(names) == set(hga.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.hga_abi_version() == 1
+    assert L.hga_status_string(0) == b"HGA_OK"
+    assert L.hga_status_string(3) == b"HGA_ERR_WORKSPACE"
+    assert L.hga_status_string(99) == b"HGA_ERR_UNKNOWN"
+
+
+def _shape(**kw):
+    s = hga.make_shape(32, 8, 128, 14336, 2048, 16, 32)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_q_heads", 0, hga.HGA_ERR_INVALID_ARG),
+    ("n_q_heads", 30, hga.HGA_ERR_INVALID_ARG),          # not a multiple of n_kv
+    ("head_dim", 96, hga.HGA_ERR_UNSUPPORTED),
+    ("head_dim", -1, hga.HGA_ERR_INVALID_ARG),
+    ("chunk", 32, hga.HGA_ERR_UNSUPPORTED),
+    ("group", 16, hga.HGA_ERR_UNSUPPORTED),
+    ("block_q", 128, hga.HGA_ERR_UNSUPPORTED),
+    ("top_k_chunks", 0, hga.HGA_ERR_INVALID_ARG),
+    ("top_k_groups", 513, hga.HGA_ERR_UNSUPPORTED),
+    ("hist_len", 100, hga.HGA_ERR_INVALID_ARG),          # H % 64 != 0
+    ("hist_len", -64, hga.HGA_ERR_INVALID_ARG),
+    ("seg_len", 100, hga.HGA_ERR_INVALID_ARG),           # S % 64 != 0
+    ("seg_len", 0, hga.HGA_ERR_INVALID_ARG),
+    ("softmax_scale", float("nan"), hga.HGA_ERR_INVALID_ARG),
+    ("softmax_scale", 0.0, hga.HGA_ERR_INVALID_ARG),
+    ("dtype", 7, hga.HGA_ERR_INVALID_ARG),
+    ("hist_loc", 5, hga.HGA_ERR_INVALID_ARG),
+])
+def test_invalid_shapes_are_rejected(L, field, value, status):
+    s = _shape(**{field: value})
+    st = L.hga_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == status
+    assert L.hga_last_error() != b""
+    assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ROUTE) == 0
+
+
+def test_null_shape_and_null_pointers(L):
+    assert L.hga_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) \
+        == hga.HGA_ERR_INVALID_ARG
+    s = _shape()
+    assert L.hga_route(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) \
+        == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0,
+                          None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_attn_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          FAKE, None, FAKE, FAKE, 1 << 30, None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_gather_groups(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, None) \
+        == hga.HGA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_and_undersized_workspace(L):
+    s = _shape()
+    n_route = L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ROUTE)
+    # block queries [32][8][128] f32 + chunk scores [32][8][224] f32
+    assert n_route == 32 * 8 * 128 * 4 + 32 * 8 * 224 * 4
+    assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_FWD) == 0
+    assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_BWD) == 32 * 2048 * 4
+    assert L.hga_workspace_size(ctypes.byref(s), 9) == 0
+    st = L.hga_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_route - 1, None)
+    assert st == hga.HGA_ERR_WORKSPACE
+    st = L.hga_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, n_route, None)
+    assert st == hga.HGA_ERR_WORKSPACE                    # misaligned
+    st = L.hga_attn_bwd(ctypes.byref(s), *([FAKE] * 13), 16, None)
+    assert st == hga.HGA_ERR_WORKSPACE
+    host = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED)
+    n_fwd = L.hga_workspace_size(ctypes.byref(host), hga.HGA_OP_ATTN_FWD)
+    assert n_fwd == 4 * (4 * 8 * 32 * 8 * 128 * 2)        # {K,V} x 2 buffers x 4 blocks
+    st = L.hga_attn_fwd(ctypes.byref(host), *([FAKE] * 8), FAKE, n_fwd - 1, None)
+    assert st == hga.HGA_ERR_WORKSPACE
+    assert L.hga_attn_bwd(ctypes.byref(host), *([FAKE] * 13), 1 << 30, None) == hga.HGA_ERR_UNSUPPORTED
+
+
+def test_summary_range_checks(L):
+    s = _shape()
+    assert L.hga_build_summaries(ctypes.byref(s), FAKE, 64, 32, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_build_summaries(ctypes.byref(s), FAKE, 0, 14336 + 64, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_build_summaries(ctypes.byref(s), FAKE, 0, 100, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
+    # an empty range is a no-op that touches nothing
+    assert L.hga_build_summaries(ctypes.byref(s), None, 128, 128, None, None, None) == hga.HGA_OK
+    assert L.hga_last_error() == b""
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(hga, "_lib", None)
+    monkeypatch.setattr(hga, "_LIB_PATH", str(tmp_path / "libhga.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        hga.lib()

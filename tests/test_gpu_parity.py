@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs. Index parity: exact, except near-ties (oracle score gap
+< 1e-5), judged by the oracle's checker. Output parity: max|got-ref| <= tol
+and ||got-ref||_2 <= tol * ||ref||_2 with tol = 2e-2 (bf16) / 1e-4 (fp32),
+computed with the oracle's attention fed the GPU's own selections."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_fine_amd import hga, synth
+from oracle import hga_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hga.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _shape(w: synth.Workload):
+    return hga.make_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.hist_len, w.seg_len,
+                          w.top_k_chunks, w.top_k_groups, w.torch_dtype, w.softmax_scale,
+                          hist_on_host=w.hist_on_host)
+
+
+def _f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _dev(inp):
+    return {k: v.cuda() for k, v in inp.items()}
+
+
+def _assert_close(name, got, ref, tol):
+    err, rel = orc.error_stats(got, ref)
+    _say(f"  {name}: max|d|={err:.3e} rel_l2={rel:.3e} (tol {tol:g}) max|ref|={np.abs(ref).max():.3e}")
+    assert orc.within_tolerance(got, ref, tol), f"{name}: max {err}, rel {rel} vs {tol}"
+
+
+def run_case(w: synth.Workload, seed: int, check_bwd: bool):
+    _say(f"[case] {w.name} seed={seed} H={w.hist_len} S={w.seg_len} nq={w.n_q_heads} "
+         f"nkv={w.n_kv_heads} d={w.head_dim} kc={w.top_k_chunks} kg={w.top_k_groups} {w.dtype}")
+    inp = synth.make_inputs(w, seed, with_grad_out=check_bwd)
+    a = {k: _f32(v) for k, v in inp.items()}
+    g = _dev(inp)
+    s = _shape(w)
+    C, G = hga.summaries(s, g["k_hist"])
+    sel_c, sel_g = hga.route(s, g["q"], C, G)
+    o, lse = hga.attn_fwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"], sel_g)
+    torch.cuda.synchronize()
+
+    C_ref = orc.chunk_summaries(a["k_hist"])
+    G_ref = orc.group_summaries(a["k_hist"])
+    if w.hist_len:
+        kmax = float(np.abs(a["k_hist"]).max())
+        assert np.max(np.abs(_f32(C) - C_ref)) <= 2e-6 * kmax
+        assert np.max(np.abs(_f32(G) - G_ref)) <= 2e-6 * kmax
+    qbar = orc.block_queries(a["q"], w.n_kv_heads)
+    sc_np, sg_np = sel_c.cpu().numpy(), sel_g.cpu().numpy()
+    rep = orc.check_selection(qbar, C_ref, G_ref, sc_np, sg_np, w.top_k_chunks, w.top_k_groups)
+    _say(f"  route: ok={rep['ok']} chunk_exemptions={rep['chunk_exemptions']} "
+         f"group_exemptions={rep['group_exemptions']} failures={rep['failures'][:3]}")
+    assert rep["ok"]
+
+    O_ref, LSE_ref = orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"],
+                                  sg_np, w.softmax_scale)
+    tol = TOL[w.dtype]
+    _assert_close("O", _f32(o), O_ref, tol)
+    _assert_close("LSE", _f32(lse), LSE_ref, tol)
+    out = dict(inp=inp, g=g, s=s, C=C, G=G, sel_c=sel_c, sel_g=sel_g, o=o, lse=lse)
+    if check_bwd:
+        dq, dk, dv = hga.attn_bwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"],
+                                  sel_g, o, lse, g["d_o"])
+        torch.cuda.synchronize()
+        dQ, dK, dV = orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"],
+                                  sg_np, w.softmax_scale, a["d_o"])
+        _assert_close("dQ", _f32(dq), dQ, tol)
+        _assert_close("dK_seg", _f32(dk), dK, tol)
+        _assert_close("dV_seg", _f32(dv), dV, tol)
+        out.update(dq=dq, dk=dk, dv=dv)
+    return out
+
+
+def _w(name, n_q, n_kv, d, H, S, kc, kg, dtype, bwd=True):
+    return synth.Workload(name, n_q, n_kv, d, H, S, kc, kg, dtype,
+                          1.0 if dtype == "f32" else 1.0 / math.sqrt(d), backward=bwd)
+
+
+SMALL = [
+    synth.WORKLOADS["tiny_f32"],
+    _w("f32_gqa_d128", 4, 2, 128, 512, 192, 3, 10, "f32"),
+    _w("bf16_gqa_ragged", 8, 2, 128, 1536, 320, 5, 13, "bf16"),       # k_g % 8 != 0, 5 blocks
+    _w("bf16_r3_d64", 6, 2, 64, 1024, 192, 3, 20, "bf16"),            # odd GQA ratio, d = 64
+    _w("bf16_budget_exceeds_candidates", 4, 1, 128, 512, 128, 2, 20, "bf16"),  # 16 cands, 4 pads
+    _w("bf16_no_history", 4, 2, 128, 0, 256, 4, 8, "bf16"),
+    _w("bf16_single_chunk", 2, 1, 128, 64, 64, 4, 32, "bf16"),        # k_c, k_g > candidates
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_small_cases_match_oracle(w, seed):
+    run_case(w, seed, check_bwd=True)
+
+
+def test_full_budget_is_dense_attention():
+    """Router disabled (every group selected) = dense causal attention."""
+    w = _w("bf16_full_budget", 8, 2, 128, 1024, 256, 16, 128, "bf16")
+    r = run_case(w, 3, check_bwd=True)
+    assert (r["sel_g"].cpu().numpy() == np.arange(128)).all()
+
+
+def test_exact_arithmetic_route_is_bit_exact():
+    """Small-integer inputs make every fp32 score exact in any summation order:
+    the GPU's selections must equal the oracle's with no exemption."""
+    w = _w("bf16_int_ties", 8, 2, 128, 2048, 256, 6, 12, "bf16", bwd=False)
+    rng = np.random.default_rng(5)
+    q = torch.from_numpy(rng.integers(0, 2, (8, 256, 128)).astype(np.float32)).bfloat16()
+    k = torch.from_numpy(rng.integers(0, 3, (2, 2048, 128)).astype(np.float32)).bfloat16()
+    k[:, 64 * 7:64 * 8] = 1.0      # ties between whole chunks
+    k[:, 64 * 20:64 * 21] = 1.0
+    s = _shape(w)
+    C, G = hga.summaries(s, k.cuda())
+    sel_c, sel_g = hga.route(s, q.cuda(), C, G)
+    torch.cuda.synchronize()
+    ref_c, ref_g, _ = orc.route(q.float().numpy(), k.float().numpy(), 2, 6, 12)
+    assert np.array_equal(sel_c.cpu().numpy(), ref_c)
+    assert np.array_equal(sel_g.cpu().numpy(), ref_g)
+
+
+def test_arbitrary_selection_with_holes():
+    """Selections with -1 holes anywhere (not only at the end) are masked."""
+    w = _w("bf16_holes", 8, 2, 128, 1024, 192, 4, 24, "bf16")
+    inp = synth.make_inputs(w, 7, with_grad_out=True)
+    a = {k: _f32(v) for k, v in inp.items()}
+    g = _dev(inp)
+    s = _shape(w)
+    rng = np.random.default_rng(8)
+    sel = np.sort(rng.choice(128, (3, 2, 24)), axis=-1).astype(np.int32)
+    sel[rng.random(sel.shape) < 0.3] = -1
+    sel[0, 0, :] = -1                                   # a block with no history at all
+    sel_t = torch.from_numpy(sel).cuda()
+    o, lse = hga.attn_fwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"], sel_t)
+    dq, dk, dv = hga.attn_bwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"], sel_t,
+                              o, lse, g["d_o"])
+    torch.cuda.synchronize()
+    O_ref, L_ref = orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel,
+                                w.softmax_scale)
+    dQ, dK, dV = orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel,
+                              w.softmax_scale, a["d_o"])
+    for n, x, y in (("O", o, O_ref), ("LSE", lse, L_ref), ("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
+        _assert_close(n, _f32(x), y, 2e-2)
+
+
+def test_gather_groups_is_exact():
+    w = _w("bf16_gather", 8, 2, 128, 2048, 256, 4, 13, "bf16", bwd=False)
+    inp = synth.make_inputs(w, 9)
+    s = _shape(w)
+    g = _dev(inp)
+    C, G = hga.summaries(s, g["k_hist"])
+    _, sel = hga.route(s, g["q"], C, G)
+    sel[1, 1, 3] = -1
+    out_shape = (4, 2, 13 * 8, 128)
+    ko = torch.full(out_shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    vo = torch.full(out_shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    hga.hga_gather_groups(s, g["k_hist"], g["v_hist"], sel, ko, vo)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    for b in range(4):
+        for j in range(2):
+            tok = np.array([8 * n + u for n in sel_np[b, j] for u in range(8)])
+            valid = np.repeat(sel_np[b, j] >= 0, 8)
+            want_k = inp["k_hist"][j][np.where(valid, tok, 0)].clone()
+            want_v = inp["v_hist"][j][np.where(valid, tok, 0)].clone()
+            want_k[~torch.from_numpy(valid)] = 0
+            want_v[~torch.from_numpy(valid)] = 0
+            assert torch.equal(ko[b, j].cpu(), want_k)
+            assert torch.equal(vo[b, j].cpu(), want_v)
+
+
+def test_runs_are_bitwise_repeatable():
+    w = _w("bf16_repeat", 8, 2, 128, 1024, 256, 4, 16, "bf16")
+    inp = _dev(synth.make_inputs(w, 11, with_grad_out=True))
+    s = _shape(w)
+    outs = []
+    for _ in range(2):
+        C, G = hga.summaries(s, inp["k_hist"])
+        sc, sg = hga.route(s, inp["q"], C, G)
+        o, lse = hga.attn_fwd(s, inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"], sg)
+        grads = hga.attn_bwd(s, inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"],
+                             sg, o, lse, inp["d_o"])
+        outs.append([C, G, sc, sg, o, lse, *grads])
+    torch.cuda.synchronize()
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# full-size Qwen3-8B layer workloads
+# ---------------------------------------------------------------------------
+def test_qwen3_8b_16k_forward():
+    run_case(synth.WORKLOADS["qwen3_8b_16k_fwd"], 0, check_bwd=False)
+
+
+def test_qwen3_8b_16k_forward_backward():
+    run_case(synth.WORKLOADS["qwen3_8b_16k_fwdbwd"], 1, check_bwd=True)
+
+
+def test_qwen3_8b_131k_forward_and_pinned_host_tier():
+    w = synth.WORKLOADS["qwen3_8b_131k_fwd"]
+    r = run_case(w, 2, check_bwd=False)
+    # the same call with history in page-locked host memory (gathered over the
+    # host link on a side stream) must give bit-identical results
+    wh = synth.WORKLOADS["qwen3_8b_131k_fwd_host"]
+    sh = _shape(wh)
+    kh = torch.empty(r["inp"]["k_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty(r["inp"]["v_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
+    kh.copy_(r["inp"]["k_hist"])
+    vh.copy_(r["inp"]["v_hist"])
+    _say("[case] 131k pinned-host history")
+    g = r["g"]
+    C2, G2 = hga.summaries(sh, kh)
+    o2, lse2 = hga.attn_fwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"])
+    torch.cuda.synchronize()
+    assert torch.equal(C2, r["C"]) and torch.equal(G2, r["G"])
+    assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
+
+
+def test_autograd_function_matches_explicit_calls():
+    w = _w("bf16_autograd", 8, 2, 128, 1024, 128, 4, 16, "bf16")
+    inp = _dev(synth.make_inputs(w, 12, with_grad_out=True))
+    s = _shape(w)
+    C, G = hga.summaries(s, inp["k_hist"])
+    q = inp["q"].clone().requires_grad_(True)
+    ks = inp["k_seg"].clone().requires_grad_(True)
+    vs = inp["v_seg"].clone().requires_grad_(True)
+    o = hga.HGAAttention.apply(s, q, ks, vs, inp["k_hist"], inp["v_hist"], C, G)
+    o.backward(inp["d_o"])
+    _, sg = hga.route(s, inp["q"], C, G)
+    o_ref, lse = hga.attn_fwd(s, inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"], sg)
+    dq, dk, dv = hga.attn_bwd(s, inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"],
+                              sg, o_ref, lse, inp["d_o"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    assert torch.equal(q.grad, dq) and torch.equal(ks.grad, dk) and torch.equal(vs.grad, dv)

@@ -381,25 +381,33 @@ def test_selection_checker_accepts_an_exact_tie_swap():
 
 def test_output_tolerance_is_not_vacuous():
     """At Qwen3-8B-like magnitudes |O| is ~2e-2, the size of the plain 2e-2
-    max-abs bound itself, so that bound barely separates a correct output from
-    an all-zero one. The scaled criterion must reject the zero output, dense
-    attention, local-only attention and selections shifted by one chunk, and
-    accept the reference rounded to bf16."""
-    w = synth.Workload("neg", 8, 2, 128, 2048, 256, 8, 16, "bf16", 1 / math.sqrt(128))
+    max-abs bar itself, so that bar alone barely separates a correct output
+    from an all-zero one. The relative part of the criterion must reject the
+    zero output, dense attention, local-only attention and selections shifted
+    by one chunk (forward, and dQ / dK of the backward), and accept the
+    reference rounded to bf16."""
+    w = synth.Workload("neg", 8, 2, 128, 2048, 256, 8, 16, "bf16", 1 / math.sqrt(128),
+                       backward=True)
     inp = _np(synth.make_inputs(w, seed=17))
     sel_c, sel_g, _ = orc.route(inp["q"], inp["k_hist"], 2, 8, 16)
     args = (inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"])
     ref, _ = orc.attn_fwd(*args, sel_g, w.softmax_scale)
     tol = 2e-2
-    assert np.abs(ref).max() < 0.05                      # scaled bound ~40x tighter
+    assert np.abs(ref).max() < 0.05
     rounded = torch.from_numpy(ref).bfloat16().double().numpy()
     assert orc.within_tolerance(rounded, ref, tol)
     assert not orc.within_tolerance(np.zeros_like(ref), ref, tol)
-    all_groups = np.broadcast_to(np.arange(w.hist_len // 8), sel_g.shape[:2] + (w.hist_len // 8,))
-    dense, _ = orc.attn_fwd(*args, np.ascontiguousarray(all_groups), w.softmax_scale)
-    assert not orc.within_tolerance(dense, ref, tol)
-    local, _ = orc.attn_fwd(*args, np.full_like(sel_g, -1), w.softmax_scale)
-    assert not orc.within_tolerance(local, ref, tol)
-    shifted = (sel_g + 8) % (w.hist_len // 8)
-    shifted_o, _ = orc.attn_fwd(*args, np.sort(shifted, axis=-1), w.softmax_scale)
-    assert not orc.within_tolerance(shifted_o, ref, tol)
+    all_groups = np.ascontiguousarray(
+        np.broadcast_to(np.arange(w.hist_len // 8), sel_g.shape[:2] + (w.hist_len // 8,)))
+    shifted = np.sort((sel_g + 8) % (w.hist_len // 8), axis=-1)
+    none = np.full_like(sel_g, -1)
+    for sel in (all_groups, none, shifted):
+        wrong, _ = orc.attn_fwd(*args, sel, w.softmax_scale)
+        assert not orc.within_tolerance(wrong, ref, tol)
+    g_ref = orc.attn_bwd(*args, sel_g, w.softmax_scale, inp["d_o"])
+    for sel in (all_groups, shifted):
+        g_bad = orc.attn_bwd(*args, sel, w.softmax_scale, inp["d_o"])
+        for i in (0, 1):                                 # dQ, dK
+            assert not orc.within_tolerance(g_bad[i], g_ref[i], tol)
+        assert orc.within_tolerance(torch.from_numpy(g_ref[i]).bfloat16().double().numpy(),
+                                    g_ref[i], tol)
