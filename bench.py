@@ -51,10 +51,11 @@ def kernel_work(w, s):
         "chunk_score": ("hbm", kv * n_C * d * 4 + n_B * kv * d * 4 + n_B * kv * n_C * 4),
         "select": ("hbm", n_B * kv * n_C * 4 + n_B * kv * 8 * kc * d * 4 + n_B * kv * (kc + kg) * 4),
         "attn_fwd": ("mfma", 4 * d * nq * (pairs_hist + pairs_causal)),
-        "bwd_rowdot": ("hbm", 2 * nq * S * d * e + nq * S * 4),
-        "bwd_dq": ("mfma", 6 * d * nq * (pairs_hist + pairs_causal)),
-        "bwd_dkdv": ("mfma", 8 * d * nq * pairs_causal),
     }
+    if w.backward:
+        work["bwd_rowdot"] = ("hbm", 2 * nq * S * d * e + nq * S * 4)
+        work["bwd_dq"] = ("mfma", 6 * d * nq * (pairs_hist + pairs_causal))
+        work["bwd_dkdv"] = ("mfma", 8 * d * nq * pairs_causal)
     if w.hist_on_host:
         work["gather"] = ("host", n_B * kv * hist_tok * d * e * 2)
     return work
@@ -155,6 +156,10 @@ def main():
     names = list(hga.KERNELS)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in names] for _ in range(args.steps)]
+    for per_step in evs:                   # torch creates the HIP event on first record
+        for a, b in per_step:
+            a.record()
+            b.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -175,10 +180,9 @@ def main():
         if name not in work:
             continue
         kind, amount = work[name]
-        try:
-            us = sum(evs[i][kid][0].elapsed_time(evs[i][kid][1]) for i in range(args.steps)) \
-                * 1e3 / args.steps
-        except RuntimeError:               # kernel not launched in this workload
+        us = sum(evs[i][kid][0].elapsed_time(evs[i][kid][1]) for i in range(args.steps)) \
+            * 1e3 / args.steps
+        if us <= 0.0:                      # not launched in this workload
             continue
         ent = {"avg_us": round(us, 3)}
         if kind == "mfma":
