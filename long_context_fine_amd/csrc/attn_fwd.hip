@@ -12,14 +12,13 @@
 // pinned-host tier); segment tiles 0..b follow, the last one causally masked.
 //
 // fp32 path: a plain VALU kernel, one thread per query row.
-#include "hga_common.hpp"
+#include "attn_tile.hpp"
 
 namespace hga {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTile = 64;  // keys per tile
 
 struct FwdParams {
   const void* q;
@@ -63,35 +62,52 @@ __device__ __forceinline__ const T* hist_row(const FwdParams& p, const T* base, 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
+// Workgroup = (KV head j, group of HPW query heads, pair of query blocks). The
+// pair is {b, n-1-b}: block b attends to b+1 segment tiles, so pairing the
+// i-th latest with the i-th earliest block gives every workgroup the same
+// amount of work. 4*HPW waves: wave (g, h, q) owns 32 query rows (half q) of
+// head h for the key tiles of parity g, so two waves share each SIMD and one
+// wave's softmax overlaps the other's MFMAs. The two parity groups keep their
+// own online-softmax state; the states are merged exactly through LDS at the
+// end of each block. Per iteration each group stages its next 64-key tile in
+// registers while the current pair of tiles (double-buffered in LDS) is used.
+// K and V both sit row-major in LDS; V^T reaches the MFMA through transposed
+// LDS reads (ds_read_b64_tr_b16).
 template <int D, int HPW>
-__global__ __launch_bounds__(128 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
-  constexpr int NT = 128 * HPW;       // threads
-  constexpr int KS = D + 8;           // Ks row stride (elements)
-  constexpr int VS = kTile + 4;       // Vt row stride (elements)
+__global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
+  constexpr int NT = 256 * HPW;       // threads
+  constexpr int GT = NT / 2;          // threads per parity group
+  constexpr int KS = D + 8;           // K row stride (elements): conflict-free row reads
+  constexpr int VS = D + 32;          // V row stride: conflict-free transposed reads
   constexpr int NDT = D / 32;         // 32-wide d tiles of O^T
   constexpr int NKS = D / 16;         // k-steps of S^T
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+  constexpr int STAGE = kTile * (KS + VS);  // K + V of one tile (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][STAGE];  // [buffer][parity]
   __shared__ int32_t sel_s[kMaxTopKGroups];
+  __shared__ int32_t hlist[kMaxTopKGroups / 8];
+  __shared__ int32_t n_hist_s;
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int l32 = lane % 32;
-  const int hh = lane / 32;  // lane half
+  const int hh = lane / 32;            // lane half
+  const int grp = wave / (2 * HPW);    // tile parity group
+  const int gw = wave % (2 * HPW);     // wave within the group
+  const int gtid = tid % GT;           // thread within the group
 
-  // workgroup -> (b, j, head group); KV head fastest so that with 8 KV heads
-  // every workgroup of head j lands on the same XCD (round-robin dispatch);
-  // heaviest (latest) query blocks first.
+  // KV head fastest: with 8 KV heads every workgroup of head j lands on the
+  // same XCD under round-robin dispatch and shares that XCD's L2.
   const int n_hg = p.r / HPW;
   int w = blockIdx.x;
   const int j = w % p.n_kv;
   w /= p.n_kv;
   const int hg = w % n_hg;
-  const int b = p.block_begin + p.n_blocks_here - 1 - w / n_hg;
-  const int head = j * p.r + hg * HPW + wave / 2;
-  const int qrow0 = (wave % 2) * 32;  // first query row (within the block) of this wave
-  const int q_tok = b * kBlockQ + qrow0 + l32;
+  const int pair = w / n_hg;
+  const int b_hi = p.block_begin + p.n_blocks_here - 1 - pair;
+  const int b_lo = p.block_begin + pair;
+  const int head = j * p.r + hg * HPW + gw / 2;
+  const int qrow0 = (gw % 2) * 32;  // first query row (within the block) of this wave
 
   const uint16_t* q = static_cast<const uint16_t*>(p.q);
   const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist);
@@ -100,168 +116,197 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
   const uint16_t* vs_g = static_cast<const uint16_t*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const uint16_t* kst = static_cast<const uint16_t*>(p.k_staged);
   const uint16_t* vst = static_cast<const uint16_t*>(p.v_staged);
-  const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
+  const float c2 = p.scale_log2;
 
-  for (int i = tid; i < p.k_g; i += NT) sel_s[i] = sel_bj[i];
-
-  // Q^T operand: lane column = query, slots = 8 consecutive d
-  bf16x8 qreg[NKS];
-  {
-    const uint16_t* qp = q + (static_cast<int64_t>(head) * p.seg_len + q_tok) * D + hh * 8;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16);
-  }
-
-  f32x16 oacc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-  float m_run = -INFINITY;  // running max (log2 domain), shared by both lane halves
-  float l_run = 0.f;        // partial row sum over this lane's keys
-
-  const int n_hist_tiles = (p.k_g + 7) / 8;
-  const int n_tiles = n_hist_tiles + b + 1;
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const bool is_hist = tile < n_hist_tiles;
-    const int st = tile - n_hist_tiles;  // segment tile index when !is_hist
-    uint32_t gmask = 0xffu;              // valid 8-token groups of the tile
-    if (is_hist) {
-      gmask = 0;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const int slot = tile * 8 + g;
-        gmask |= (slot < p.k_g && sel_s[slot] >= 0) ? (1u << g) : 0u;
-      }
-      if (gmask == 0) continue;  // uniform across the workgroup
-    }
-
-    // ---- stage K (row-major) and V (transposed) tiles in LDS -------------
-    {
-      constexpr int CPR = D / 8;  // 16-byte chunks per row
-      for (int idx = tid; idx < kTile * CPR; idx += NT) {
-        const int kk = idx / CPR, c = idx % CPR;
-        const uint16_t* src = is_hist ? hist_row(p, kh, kst, sel_s, b, j, tile, kk, D)
-                                      : ks_g + static_cast<int64_t>(st * kTile + kk) * D;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (src) v = *reinterpret_cast<const uint4*>(src + c * 8);
-        *reinterpret_cast<uint4*>(&Ks[kk * KS + c * 8]) = v;
-      }
-      for (int idx = tid; idx < (kTile / 4) * CPR; idx += NT) {
-        const int kq = idx / CPR, c = idx % CPR;
-        uint4 rows[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int kk = kq * 4 + u;
-          const uint16_t* src = is_hist ? hist_row(p, vh, vst, sel_s, b, j, tile, kk, D)
-                                        : vs_g + static_cast<int64_t>(st * kTile + kk) * D;
-          rows[u] = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
-        }
-        const uint16_t* r16[4] = {reinterpret_cast<const uint16_t*>(&rows[0]),
-                                  reinterpret_cast<const uint16_t*>(&rows[1]),
-                                  reinterpret_cast<const uint16_t*>(&rows[2]),
-                                  reinterpret_cast<const uint16_t*>(&rows[3])};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint2 col;
-          col.x = static_cast<uint32_t>(r16[0][e]) | (static_cast<uint32_t>(r16[1][e]) << 16);
-          col.y = static_cast<uint32_t>(r16[2][e]) | (static_cast<uint32_t>(r16[3][e]) << 16);
-          *reinterpret_cast<uint2*>(&Vt[(c * 8 + e) * VS + kq * 4]) = col;
-        }
-      }
-    }
+  for (int half = 0; half < 2; ++half) {
+    const int b = half == 0 ? b_hi : b_lo;
+    if (half == 1 && b_lo >= b_hi) break;  // odd count: the middle block runs once
+    const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
     __syncthreads();
+    for (int i = tid; i < p.k_g; i += NT) sel_s[i] = sel_bj[i];
+    __syncthreads();
+    build_hist_tile_list(sel_s, p.k_g, hlist, &n_hist_s);
+    __syncthreads();
+    const int n_hist = n_hist_s;
+    const int n_tiles = n_hist + b + 1;
+    const int n_iter = (n_tiles + 1) / 2;
+    const int q_tok = b * kBlockQ + qrow0 + l32;
+    const int64_t staged_row0 =
+        (static_cast<int64_t>(b - p.block_begin) * p.n_kv + j) * static_cast<int64_t>(p.k_g) * kGroup;
 
-    // ---- S^T = K . Q^T for two 32-key subtiles ---------------------------
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kt * 32 + l32) * KS + s * 16 + hh * 8]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kt], 0, 0, 0);
+    // rows 4kq..4kq+3 of tile t, for K (which=0) or V (which=1); nullptr = zeros
+    auto rowptr = [&](int t, int kq, int which) -> const uint16_t* {
+      if (t >= n_tiles) return nullptr;
+      if (t < n_hist) {
+        const int slot = hlist[t] * 8 + kq / 2;
+        if (slot >= p.k_g) return nullptr;
+        const int n = sel_s[slot];
+        if (n < 0) return nullptr;
+        if (kst) return (which ? vst : kst) + (staged_row0 + slot * kGroup + (kq % 2) * 4) * D;
+        return (which ? vh : kh) +
+               (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup + (kq % 2) * 4) * D;
       }
-    }
+      return (which ? vs_g : ks_g) + static_cast<int64_t>((t - n_hist) * kTile + kq * 4) * D;
+    };
 
-    // ---- scale, mask, online softmax --------------------------------------
-    const bool diag = !is_hist && st == b;
-    float tmax = -INFINITY;
+    bf16x8 qreg[NKS];
+    {
+      const uint16_t* qp = q + (static_cast<int64_t>(head) * p.seg_len + q_tok) * D + hh * 8;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = kt * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
-        float x = sacc[kt][v] * p.scale_log2;
-        const bool masked = is_hist ? !((gmask >> (kk / 8)) & 1u) : (diag && kk > qrow0 + l32);
-        x = masked ? -INFINITY : x;
-        sacc[kt][v] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int s = 0; s < NKS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_base = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_base);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = exp2f(sacc[kt][v] - m_base);
-        psum += e;
-        pb[kt][v / 8][v % 8] = static_cast<__bf16>(e);
-      }
-    }
-    l_run = l_run * alpha + psum;
+    f32x16 oacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
+    float m_run = -INFINITY;  // running max (scaled, log2 domain), same in both lane halves
+    float l_run = 0.f;        // partial row sum over this lane's keys
 
-    // ---- O^T += V^T . P^T ------------------------------------------------
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t* vrow = &Vt[(dt * 32 + l32) * VS];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int ksi = 0; ksi < 2; ++ksi) {
-          const int k0 = kt * 32 + ksi * 16 + 4 * hh;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + k0);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + k0 + 8);
-          const uint4 packed = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, packed);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][ksi], oacc[dt], 0, 0, 0);
-        }
+    TileRegs<D, GT> kr, vr;
+    kr.load(gtid, [&](int kq) { return rowptr(grp, kq, 0); });
+    vr.load(gtid, [&](int kq) { return rowptr(grp, kq, 1); });
+    kr.store_rows(gtid, smem[0][grp], KS);
+    vr.store_rows(gtid, smem[0][grp] + kTile * KS, VS);
+    __syncthreads();
+
+    for (int it = 0; it < n_iter; ++it) {
+      const int cur = it & 1;
+      const int t = 2 * it + grp;          // this group's tile
+      const bool more = it + 1 < n_iter;
+      if (more) {
+        kr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 0); });
+        vr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 1); });
       }
+      if (t < n_tiles) {
+        // mask mode: 0 none, 1 history groups, 2 causal diagonal
+        uint32_t gmask = 0xffu;
+        int mode = 0;
+        if (t < n_hist) {
+          gmask = hist_group_mask(sel_s, p.k_g, hlist[t]);
+          mode = gmask == 0xffu ? 0 : 1;
+        } else if (t - n_hist == b) {
+          mode = 2;
+        }
+        const uint16_t* kbuf = smem[cur][grp];
+        const uint16_t* vbuf = kbuf + kTile * KS;
+
+        // ---- S^T = K . Q^T for two 32-key subtiles -----------------------
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kbuf[(kt * 32 + l32) * KS + s * 16 + hh * 8]);
+            sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
+          }
+        }
+
+        // ---- mask, online softmax (raw scores; scale folded into exp2) ------
+        if (mode == 1) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (!((gmask >> (kt * 4 + v / 4)) & 1u)) sacc[kt][v] = -INFINITY;
+        } else if (mode == 2) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int kk = kt * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
+              sacc[kt][v] = kk > qrow0 + l32 ? -INFINITY : sacc[kt][v];
+            }
+        }
+        float tmax = sacc[0][0];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[kt][v]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        const float m_new = fmaxf(m_run, tmax * c2);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.f;
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float e = fast_exp2(fmaf(sacc[kt][v], c2, -m_new));
+            psum += e;
+            sacc[kt][v] = e;
+          }
+          pb[kt][0] = acc_to_bf16x8(sacc[kt], 0);
+          pb[kt][1] = acc_to_bf16x8(sacc[kt], 8);
+        }
+        l_run = l_run * alpha + psum;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+        }
+
+        // ---- O^T += V^T . P^T --------------------------------------------
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ksi = 0; ksi < 2; ++ksi)
+              oacc[dt] = mfma32(lds_a_tr(vbuf, VS, kt * 32 + ksi * 16, dt * 32, lane), pb[kt][ksi], oacc[dt]);
+      }
+      if (more) {
+        kr.store_rows(gtid, smem[cur ^ 1][grp], KS);
+        vr.store_rows(gtid, smem[cur ^ 1][grp] + kTile * KS, VS);
+      }
+      __syncthreads();
+    }
+
+    // ---- merge the two parity states, normalise, write O (bf16) and LSE -----
+    float* xch = reinterpret_cast<float*>(&smem[0][0][0]);  // free after the last barrier
+    constexpr int XW = NDT * 16 + 2;                          // floats per lane
+    float* mine = xch + (static_cast<int64_t>(gw) * kWave + lane) * XW;
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[dt * 16 + v] = oacc[dt][v];
+      mine[NDT * 16] = m_run;
+      mine[NDT * 16 + 1] = l_run;
     }
     __syncthreads();
-  }
-
-  // ---- normalise and write O (bf16) and LSE --------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  const float inv = 1.0f / l_tot;
-  uint16_t* o = static_cast<uint16_t*>(p.o) + (static_cast<int64_t>(head) * p.seg_len + q_tok) * D;
+    if (grp == 0) {
+      const float m1 = mine[NDT * 16], l1 = mine[NDT * 16 + 1];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = fast_exp2(m_run - m), a1 = fast_exp2(m1 - m);
+      const float l_lane = l_run * a0 + l1 * a1;
+      const float l_tot = l_lane + __shfl_xor(l_lane, 32, kWave);
+      const float inv = 1.0f / l_tot;
+      const float s0 = a0 * inv, s1 = a1 * inv;
+      uint16_t* o = static_cast<uint16_t*>(p.o) + (static_cast<int64_t>(head) * p.seg_len + q_tok) * D;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = dt * 32 + 8 * g + 4 * hh;
-      uint2 w2;
-      w2.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-      w2.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-      *reinterpret_cast<uint2*>(o + d0) = w2;
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = dt * 32 + 8 * g + 4 * hh;
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[dt][4 * g + e] * s0 + mine[dt * 16 + 4 * g + e] * s1;
+          uint2 w2;
+          w2.x = cvt_pk_bf16(x[0], x[1]);
+          w2.y = cvt_pk_bf16(x[2], x[3]);
+          *reinterpret_cast<uint2*>(o + d0) = w2;
+        }
+      }
+      if (hh == 0) p.lse[static_cast<int64_t>(head) * p.seg_len + q_tok] = (m + __log2f(l_tot)) * kLn2;
     }
   }
-  if (hh == 0) p.lse[static_cast<int64_t>(head) * p.seg_len + q_tok] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -350,12 +395,14 @@ hipError_t launch_d(const hga_shape& s, FwdParams& p, hipStream_t st) {
   if (s.dtype == HGA_F32) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(p.n_blocks_here * s.n_q_heads), dim3(kWave),
                        0, st, p);
-  } else if (p.r % 2 == 0) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>),
-                       dim3(p.n_blocks_here * s.n_kv_heads * (p.r / 2)), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(p.n_blocks_here * s.n_kv_heads * p.r),
-                       dim3(128), 0, st, p);
+    const int n_pairs = (p.n_blocks_here + 1) / 2;
+    if (p.r % 2 == 0)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3(n_pairs * s.n_kv_heads * (p.r / 2)),
+                         dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(n_pairs * s.n_kv_heads * p.r), dim3(256),
+                         0, st, p);
   }
   timer_end(HGA_KERNEL_ATTN_FWD, st);
   return hipGetLastError();

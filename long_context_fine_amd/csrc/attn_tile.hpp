@@ -1,0 +1,170 @@
+// Shared pieces of the MFMA attention kernels: register-staged 64-key tiles and
+// small MFMA / softmax helpers (gfx950, wave64, v_mfma_f32_32x32x16_bf16).
+//
+// MFMA 32x32x16 operand layout used throughout: A[i][k] comes from lane
+// (i % 32) + 32*h with k = 8h .. 8h+7 in its 8 slots; B[k][j] from lane
+// (j % 32) + 32*h likewise; the 16 accumulator registers v of lane l hold
+// D[8*(v/4) + 4*(l/32) + v%4][l % 32]. The k <-> (lane half, slot) pairing only
+// has to agree between A and B, which lets an accumulator tile be fed back as a
+// B operand with the contraction index permuted the same way on the A side.
+#pragma once
+
+#include "hga_common.hpp"
+
+namespace hga {
+
+constexpr int kTile = 64;  // keys (or queries) per tile
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 8 accumulator registers [v0, v0+8) of a 32x32 tile as a bf16 B operand
+// (contraction slots = rows 8*(v/4) + 4*half + v%4 of the tile).
+__device__ __forceinline__ bf16x8 acc_to_bf16x8(const f32x16& acc, int v0) {
+  uint4 u;
+  u.x = cvt_pk_bf16(acc[v0 + 0], acc[v0 + 1]);
+  u.y = cvt_pk_bf16(acc[v0 + 2], acc[v0 + 3]);
+  u.z = cvt_pk_bf16(acc[v0 + 4], acc[v0 + 5]);
+  u.w = cvt_pk_bf16(acc[v0 + 6], acc[v0 + 7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// A operand from a transposed LDS tile T[row][col] (row stride `ts` elements):
+// row = this lane's row, columns {c0..c0+3} and {c0+8..c0+11} -- the column
+// permutation that matches acc_to_bf16x8 on the B side when c0 = base + 4*half.
+__device__ __forceinline__ bf16x8 lds_a_permuted(const uint16_t* row, int c0) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(row + c0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(row + c0 + 8);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+// element (i % 4) of the 8-byte chunks read by lanes 4k + i/4, k = 0..3.
+__device__ __forceinline__ i16x4 ds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+
+// A operand read transposed from a row-major LDS tile T[row][col] (row stride
+// `stride` elements): the lane's M index is column cbase + lane % 32, and its 8
+// contraction slots are rows rbase + 8*(i/4) + 4*(lane/32) + i%4 -- the row
+// permutation acc_to_bf16x8 produces on the B side. Each 16-lane group reads 4
+// rows x 16 columns per instruction.
+__device__ __forceinline__ bf16x8 lds_a_tr(const uint16_t* T, int stride, int rbase, int cbase,
+                                           int lane) {
+  const int g16 = lane >> 4, gl = lane & 15;
+  const int col = cbase + 16 * (g16 & 1) + 4 * (gl & 3);
+  const int row = rbase + 4 * (g16 >> 1) + (gl >> 2);
+  const i16x4 lo = ds_read_tr16(T + row * stride + col);
+  const i16x4 hi = ds_read_tr16(T + (row + 8) * stride + col);
+  const uint2 l2 = __builtin_bit_cast(uint2, lo);
+  const uint2 h2 = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One 64-row x D tile held in registers between its global load and its LDS
+// store. A task is 4 consecutive rows x 8 columns (one 16-byte chunk per row);
+// the 4 rows are contiguous in memory for every tile kind used here.
+template <int D, int NT>
+struct TileRegs {
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int NTASK = (kTile / 4) * CPR;
+  static constexpr int TPT = (NTASK + NT - 1) / NT;
+  uint4 a[TPT][4];
+
+  // rowptr(kq) -> pointer to row 4*kq of the tile (nullptr: rows are zero)
+  template <class F>
+  __device__ __forceinline__ void load(int tid, F rowptr) {
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int task = tid + t * NT;
+      if (NTASK % NT == 0 || task < NTASK) {
+        const int kq = task / CPR, c = task % CPR;
+        const uint16_t* src = rowptr(kq);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          a[t][u] = src ? *reinterpret_cast<const uint4*>(src + u * D + c * 8) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  // row-major: dst[row * stride + col]
+  __device__ __forceinline__ void store_rows(int tid, uint16_t* dst, int stride) const {
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int task = tid + t * NT;
+      if (NTASK % NT == 0 || task < NTASK) {
+        const int kq = task / CPR, c = task % CPR;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(dst + (kq * 4 + u) * stride + c * 8) = a[t][u];
+      }
+    }
+  }
+  // transposed: dst[col * stride + row], 4 rows packed per 8-byte store
+  __device__ __forceinline__ void store_transposed(int tid, uint16_t* dst, int stride) const {
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int task = tid + t * NT;
+      if (NTASK % NT == 0 || task < NTASK) {
+        const int kq = task / CPR, c = task % CPR;
+        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&a[t][0]);
+        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&a[t][1]);
+        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&a[t][2]);
+        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&a[t][3]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // column pair (2w, 2w+1) of the chunk
+          uint2 lo, hi;
+          lo.x = (r0[w] & 0xffffu) | (r1[w] << 16);
+          lo.y = (r2[w] & 0xffffu) | (r3[w] << 16);
+          hi.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
+          hi.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
+          *reinterpret_cast<uint2*>(dst + (c * 8 + 2 * w) * stride + kq * 4) = lo;
+          *reinterpret_cast<uint2*>(dst + (c * 8 + 2 * w + 1) * stride + kq * 4) = hi;
+        }
+      }
+    }
+  }
+};
+
+// Builds, in LDS, the list of history tiles (8 selected groups each) that hold
+// at least one valid group; returns nothing, the count lands in *n_out.
+__device__ __forceinline__ void build_hist_tile_list(const int32_t* sel_s, int k_g, int32_t* list,
+                                                     int32_t* n_out) {
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int ht = 0; ht < (k_g + 7) / 8; ++ht) {
+      bool any = false;
+      for (int g = 0; g < 8; ++g) {
+        const int slot = ht * 8 + g;
+        any |= slot < k_g && sel_s[slot] >= 0;
+      }
+      if (any) list[n++] = ht;
+    }
+    *n_out = n;
+  }
+}
+
+__device__ __forceinline__ uint32_t hist_group_mask(const int32_t* sel_s, int k_g, int ht) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int slot = ht * 8 + g;
+    m |= (slot < k_g && sel_s[slot] >= 0) ? (1u << g) : 0u;
+  }
+  return m;
+}
+
+}  // namespace hga
