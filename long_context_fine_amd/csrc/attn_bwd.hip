@@ -14,13 +14,12 @@
 // accumulators. Transposed copies of the streamed operand (K^T for dQ; Q^T and
 // dO^T for dK/dV) are written to LDS while staging.
 // fp32 path: plain VALU kernels.
-#include "hga_common.hpp"
+#include "attn_tile.hpp"
 
 namespace hga {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTile = 64;
 
 struct BwdParams {
   const void* q;
@@ -36,6 +35,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* dvec;
+  float* dkdv_part;  // [n_hg][2][n_kv][S][D] fp32 partials (dK, dV) when n_hg > 1
   int n_q, n_kv, r;
   int seg_len;
   int64_t hist_len;
@@ -77,290 +77,415 @@ __global__ __launch_bounds__(256) void row_dot_kernel(const T* __restrict__ o,
 // ---------------------------------------------------------------------------
 // bf16: dQ
 // ---------------------------------------------------------------------------
+// Same decomposition as the forward: workgroup = (KV head j, HPW query heads,
+// pair of query blocks {b, n-1-b}); 4*HPW waves in two tile-parity groups,
+// each wave owning 32 query rows of one head (Q^T and dO^T stay in registers
+// as B operands). Per 64-key tile: S^T = K.Q^T, dP^T = V.dO^T, dS^T = P^T o
+// (dP^T - Dvec), dQ^T += K^T.dS^T with K^T read transposed from the row-major
+// K tile. The two parity groups' dQ partials are summed in a fixed order.
 template <int D, int HPW>
-__global__ __launch_bounds__(128 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p) {
-  constexpr int NT = 128 * HPW;
-  constexpr int KS = D + 8;
-  constexpr int TS = kTile + 4;
+__global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p) {
+  constexpr int NT = 256 * HPW;
+  constexpr int GT = NT / 2;
+  constexpr int KS = D + 16;          // K: read by rows and transposed
+  constexpr int VS = D + 8;           // V: read by rows
   constexpr int NDT = D / 32;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kTile * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
+  constexpr int STAGE = kTile * (KS + VS);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][STAGE];  // [buffer][parity]
   __shared__ int32_t sel_s[kMaxTopKGroups];
+  __shared__ int32_t hlist[kMaxTopKGroups / 8];
+  __shared__ int32_t n_hist_s;
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int l32 = lane % 32, hh = lane / 32;
-  const int n_hg = p.r / HPW;
+  const int grp = wave / (2 * HPW);
+  const int gw = wave % (2 * HPW);
+  const int gtid = tid % GT;
   const int n_blocks = p.seg_len / kBlockQ;
+  const int n_hg = p.r / HPW;
   int w = blockIdx.x;
   const int j = w % p.n_kv;
   w /= p.n_kv;
   const int hg = w % n_hg;
-  const int b = n_blocks - 1 - w / n_hg;
-  const int head = j * p.r + hg * HPW + wave / 2;
-  const int qrow0 = (wave % 2) * 32;
-  const int q_tok = b * kBlockQ + qrow0 + l32;
+  const int pair = w / n_hg;
+  const int b_hi = n_blocks - 1 - pair;
+  const int b_lo = pair;
+  const int head = j * p.r + hg * HPW + gw / 2;
+  const int qrow0 = (gw % 2) * 32;
 
   const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist);
   const uint16_t* vh = static_cast<const uint16_t*>(p.v_hist);
   const uint16_t* ks_g = static_cast<const uint16_t*>(p.k_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const uint16_t* vs_g = static_cast<const uint16_t*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
-  const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
-  for (int i = tid; i < p.k_g; i += NT) sel_s[i] = sel_bj[i];
+  const float c2 = p.scale_log2;
 
-  const int64_t row_off = static_cast<int64_t>(head) * p.seg_len + q_tok;
-  bf16x8 qreg[NKS], goreg[NKS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + row_off * D + hh * 8;
-    const uint16_t* gp = static_cast<const uint16_t*>(p.d_o) + row_off * D + hh * 8;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16);
-      goreg[s] = *reinterpret_cast<const bf16x8*>(gp + s * 16);
-    }
-  }
-  const float lse2 = p.lse[row_off] * kLog2e;
-  const float dq_row = p.dvec[row_off];
+  for (int half = 0; half < 2; ++half) {
+    const int b = half == 0 ? b_hi : b_lo;
+    if (half == 1 && b_lo >= b_hi) break;
+    const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
+    __syncthreads();
+    for (int i = tid; i < p.k_g; i += NT) sel_s[i] = sel_bj[i];
+    __syncthreads();
+    build_hist_tile_list(sel_s, p.k_g, hlist, &n_hist_s);
+    __syncthreads();
+    const int n_hist = n_hist_s;
+    const int n_tiles = n_hist + b + 1;
+    const int n_iter = (n_tiles + 1) / 2;
+    const int q_tok = b * kBlockQ + qrow0 + l32;
+    const int64_t row_off = static_cast<int64_t>(head) * p.seg_len + q_tok;
 
-  f32x16 acc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
-
-  const int n_hist_tiles = (p.k_g + 7) / 8;
-  const int n_tiles = n_hist_tiles + b + 1;
-  __syncthreads();
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const bool is_hist = tile < n_hist_tiles;
-    const int st = tile - n_hist_tiles;
-    uint32_t gmask = 0xffu;
-    if (is_hist) {
-      gmask = 0;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const int slot = tile * 8 + g;
-        gmask |= (slot < p.k_g && sel_s[slot] >= 0) ? (1u << g) : 0u;
+    auto rowptr = [&](int t, int kq, int which) -> const uint16_t* {
+      if (t >= n_tiles) return nullptr;
+      if (t < n_hist) {
+        const int slot = hlist[t] * 8 + kq / 2;
+        if (slot >= p.k_g) return nullptr;
+        const int n = sel_s[slot];
+        if (n < 0) return nullptr;
+        return (which ? vh : kh) +
+               (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup + (kq % 2) * 4) * D;
       }
-      if (gmask == 0) continue;
-    }
+      return (which ? vs_g : ks_g) + static_cast<int64_t>((t - n_hist) * kTile + kq * 4) * D;
+    };
+
+    bf16x8 qreg[NKS], goreg[NKS];
     {
-      constexpr int CPR = D / 8;
-      for (int idx = tid; idx < kTile * CPR; idx += NT) {
-        const int kk = idx / CPR, c = idx % CPR;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (is_hist) {
-          const int64_t off = hist_offset(p, sel_s, j, tile, kk, D);
-          if (off >= 0) {
-            kv = *reinterpret_cast<const uint4*>(kh + off + c * 8);
-            vv = *reinterpret_cast<const uint4*>(vh + off + c * 8);
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + row_off * D + hh * 8;
+      const uint16_t* gp = static_cast<const uint16_t*>(p.d_o) + row_off * D + hh * 8;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16);
+        goreg[s] = *reinterpret_cast<const bf16x8*>(gp + s * 16);
+      }
+    }
+    const float lse2 = p.lse[row_off] * kLog2e;
+    const float drow = p.dvec[row_off];
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
+
+    TileRegs<D, GT> kr, vr;
+    kr.load(gtid, [&](int kq) { return rowptr(grp, kq, 0); });
+    vr.load(gtid, [&](int kq) { return rowptr(grp, kq, 1); });
+    kr.store_rows(gtid, smem[0][grp], KS);
+    vr.store_rows(gtid, smem[0][grp] + kTile * KS, VS);
+    __syncthreads();
+
+    for (int it = 0; it < n_iter; ++it) {
+      const int cur = it & 1;
+      const int t = 2 * it + grp;
+      const bool more = it + 1 < n_iter;
+      if (more) {
+        kr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 0); });
+        vr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 1); });
+      }
+      if (t < n_tiles) {
+        uint32_t gmask = 0xffu;
+        int mode = 0;
+        if (t < n_hist) {
+          gmask = hist_group_mask(sel_s, p.k_g, hlist[t]);
+          mode = gmask == 0xffu ? 0 : 1;
+        } else if (t - n_hist == b) {
+          mode = 2;
+        }
+        const uint16_t* kbuf = smem[cur][grp];
+        const uint16_t* vbuf = kbuf + kTile * KS;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {   // one 32-key subtile at a time
+          f32x16 sacc, pacc;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kbuf[(kt * 32 + l32) * KS + s * 16 + hh * 8]);
+            sacc = mfma32(ka, qreg[s], sacc);
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(&vbuf[(kt * 32 + l32) * VS + s * 16 + hh * 8]);
+            pacc = mfma32(va, goreg[s], pacc);
           }
-        } else {
-          const int64_t off = static_cast<int64_t>(st * kTile + kk) * D + c * 8;
-          kv = *reinterpret_cast<const uint4*>(ks_g + off);
-          vv = *reinterpret_cast<const uint4*>(vs_g + off);
-        }
-        *reinterpret_cast<uint4*>(&Ks[kk * KS + c * 8]) = kv;
-        *reinterpret_cast<uint4*>(&Vs[kk * KS + c * 8]) = vv;
-        const uint16_t* k16 = reinterpret_cast<const uint16_t*>(&kv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Kt[(c * 8 + e) * TS + kk] = k16[e];
-      }
-    }
-    __syncthreads();
-
-    f32x16 sacc[2], pacc[2];
+          for (int v = 0; v < 16; ++v) {
+            float pr = fast_exp2(fmaf(sacc[v], c2, -lse2));
+            if (mode == 1) {
+              if (!((gmask >> (kt * 4 + v / 4)) & 1u)) pr = 0.f;
+            } else if (mode == 2) {
+              const int kk = kt * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
+              pr = kk > qrow0 + l32 ? 0.f : pr;
+            }
+            sacc[v] = pr * (pacc[v] - drow);
+          }
+          const bf16x8 ds0 = acc_to_bf16x8(sacc, 0);
+          const bf16x8 ds1 = acc_to_bf16x8(sacc, 8);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) { sacc[kt][v] = 0.f; pacc[kt][v] = 0.f; }
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[(kt * 32 + l32) * KS + s * 16 + hh * 8]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[kt], 0, 0, 0);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[(kt * 32 + l32) * KS + s * 16 + hh * 8]);
-        pacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, goreg[s], pacc[kt], 0, 0, 0);
-      }
-    }
-    const bool diag = !is_hist && st == b;
-    bf16x8 dsb[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = kt * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
-        const bool masked = is_hist ? !((gmask >> (kk / 8)) & 1u) : (diag && kk > qrow0 + l32);
-        const float pr = masked ? 0.f : exp2f(sacc[kt][v] * p.scale_log2 - lse2);
-        const float ds = pr * (pacc[kt][v] - dq_row);
-        dsb[kt][v / 8][v % 8] = static_cast<__bf16>(ds);
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t* krow = &Kt[(dt * 32 + l32) * TS];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int ksi = 0; ksi < 2; ++ksi) {
-          const int k0 = kt * 32 + ksi * 16 + 4 * hh;
-          const uint2 lo = *reinterpret_cast<const uint2*>(krow + k0);
-          const uint2 hi = *reinterpret_cast<const uint2*>(krow + k0 + 8);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[kt][ksi], acc[dt], 0, 0, 0);
+          for (int dt = 0; dt < NDT; ++dt) {
+            acc[dt] = mfma32(lds_a_tr(kbuf, KS, kt * 32, dt * 32, lane), ds0, acc[dt]);
+            acc[dt] = mfma32(lds_a_tr(kbuf, KS, kt * 32 + 16, dt * 32, lane), ds1, acc[dt]);
+          }
         }
       }
+      if (more) {
+        kr.store_rows(gtid, smem[cur ^ 1][grp], KS);
+        vr.store_rows(gtid, smem[cur ^ 1][grp] + kTile * KS, VS);
+      }
+      __syncthreads();
+    }
+
+    // ---- sum the two parity partials (group 0 + group 1), write dQ ----------
+    float* xch = reinterpret_cast<float*>(&smem[0][0][0]);
+    constexpr int XW = NDT * 16;
+    float* mine = xch + (static_cast<int64_t>(gw) * kWave + lane) * XW;
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[dt * 16 + v] = acc[dt][v];
     }
     __syncthreads();
-  }
-
-  uint16_t* dq = static_cast<uint16_t*>(p.dq) + row_off * D;
+    if (grp == 0) {
+      uint16_t* dq = static_cast<uint16_t*>(p.dq) + row_off * D;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = dt * 32 + 8 * g + 4 * hh;
-      uint2 w2;
-      w2.x = pack_bf16x2(acc[dt][4 * g + 0] * p.scale, acc[dt][4 * g + 1] * p.scale);
-      w2.y = pack_bf16x2(acc[dt][4 * g + 2] * p.scale, acc[dt][4 * g + 3] * p.scale);
-      *reinterpret_cast<uint2*>(dq + d0) = w2;
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = dt * 32 + 8 * g + 4 * hh;
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (acc[dt][4 * g + e] + mine[dt * 16 + 4 * g + e]) * p.scale;
+          uint2 w2;
+          w2.x = cvt_pk_bf16(x[0], x[1]);
+          w2.y = cvt_pk_bf16(x[2], x[3]);
+          *reinterpret_cast<uint2*>(dq + d0) = w2;
+        }
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// bf16: dK, dV for one 64-key segment tile of one KV head, over every query
-// block at or after it and every query head of the group.
+// bf16: dK, dV of the active segment
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(128) void attn_bwd_dkdv_bf16_kernel(BwdParams p) {
-  constexpr int KS = D + 8;
-  constexpr int TS = kTile + 4;
+// Workgroup = (KV head j, pair of 64-key segment tiles {kt, n-1-kt}, group of
+// HPW query heads). Key tile kt receives gradient from query blocks kt..n-1,
+// so the pair gives every workgroup the same work. 2*HPW waves: wave (g, ks)
+// keeps K^T and V^T of its 32 keys (subtile ks) in registers as B operands and
+// streams the 64-query tiles of head g: S = Q.K^T, dP = dO.V^T, then
+// dV^T += dO^T.P and dK^T += Q^T.dS with Q^T / dO^T read transposed from the
+// row-major tiles. The next query block's Q/dO tiles are loaded into registers
+// while the current ones (double-buffered in LDS) are used. Head partials are
+// summed in LDS; with more than one head group per KV head each workgroup
+// writes an fp32 partial that dkdv_reduce_kernel sums in a fixed order.
+template <int D, int HPW>
+__global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams p) {
+  constexpr int NT = 128 * HPW;
+  constexpr int QS = D + 8;
   constexpr int NDT = D / 32;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kTile * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[kTile * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Gt[D * TS];
-  __shared__ float lse_s[kTile];
-  __shared__ float dvec_s[kTile];
+  constexpr int TILE = kTile * QS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][HPW][2][TILE];  // [buf][head][Q, dO]
+  __shared__ __attribute__((aligned(16))) float lse_s[2][HPW][kTile];
+  __shared__ __attribute__((aligned(16))) float dvec_s[2][HPW][kTile];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int l32 = lane % 32, hh = lane / 32;
+  const int ks = wave % 2;       // 32-key subtile
+  const int g = wave / 2;        // head within the group
   const int n_blocks = p.seg_len / kBlockQ;
-  const int j = blockIdx.x % p.n_kv;
-  const int kt_blk = blockIdx.x / p.n_kv;  // key tile, heaviest (earliest) first
-  const int key_local = wave * 32 + l32;   // key within the tile (lane column)
-  const int key_tok = kt_blk * kTile + key_local;
+  const int n_hg = p.r / HPW;
+  int w = blockIdx.x;
+  const int j = w % p.n_kv;
+  w /= p.n_kv;
+  const int hg = w % n_hg;
+  const int pair = w / n_hg;
+  const float c2 = p.scale_log2;
 
   const uint16_t* kseg = static_cast<const uint16_t*>(p.k_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const uint16_t* vseg = static_cast<const uint16_t*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
-  bf16x8 kreg[NKS], vreg[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    kreg[s] = *reinterpret_cast<const bf16x8*>(kseg + static_cast<int64_t>(key_tok) * D + s * 16 + hh * 8);
-    vreg[s] = *reinterpret_cast<const bf16x8*>(vseg + static_cast<int64_t>(key_tok) * D + s * 16 + hh * 8);
-  }
-  f32x16 dk[NDT], dv[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { dk[dt][v] = 0.f; dv[dt][v] = 0.f; }
-
   const uint16_t* qg = static_cast<const uint16_t*>(p.q);
   const uint16_t* gg = static_cast<const uint16_t*>(p.d_o);
-  for (int qb = kt_blk; qb < n_blocks; ++qb) {
-    for (int hi = 0; hi < p.r; ++hi) {
-      const int head = j * p.r + hi;
-      const int64_t row0 = static_cast<int64_t>(head) * p.seg_len + qb * kBlockQ;
-      __syncthreads();
-      constexpr int CPR = D / 8;
-      for (int idx = tid; idx < kTile * CPR; idx += 128) {
-        const int qq = idx / CPR, c = idx % CPR;
-        const uint4 qv = *reinterpret_cast<const uint4*>(qg + (row0 + qq) * D + c * 8);
-        const uint4 gv = *reinterpret_cast<const uint4*>(gg + (row0 + qq) * D + c * 8);
-        *reinterpret_cast<uint4*>(&Qs[qq * KS + c * 8]) = qv;
-        *reinterpret_cast<uint4*>(&Gs[qq * KS + c * 8]) = gv;
-        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(&qv);
-        const uint16_t* g16 = reinterpret_cast<const uint16_t*>(&gv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          Qt[(c * 8 + e) * TS + qq] = q16[e];
-          Gt[(c * 8 + e) * TS + qq] = g16[e];
-        }
-      }
-      if (tid < kTile) {
-        lse_s[tid] = p.lse[row0 + tid] * kLog2e;
-        dvec_s[tid] = p.dvec[row0 + tid];
-      }
-      __syncthreads();
 
-      const bool diag = qb == kt_blk;
-      bf16x8 pb[2][2], dsb[2][2];
+  for (int half = 0; half < 2; ++half) {
+    const int kt = half == 0 ? pair : n_blocks - 1 - pair;
+    if (half == 1 && kt <= pair) break;  // odd count: the middle tile runs once
+    const int key_local = ks * 32 + l32;
+    const int key_tok = kt * kTile + key_local;
+    bf16x8 kreg[NKS], vreg[NKS];
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
+    for (int s = 0; s < NKS; ++s) {
+      kreg[s] = *reinterpret_cast<const bf16x8*>(kseg + static_cast<int64_t>(key_tok) * D + s * 16 + hh * 8);
+      vreg[s] = *reinterpret_cast<const bf16x8*>(vseg + static_cast<int64_t>(key_tok) * D + s * 16 + hh * 8);
+    }
+    f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { dk[dt][v] = 0.f; dv[dt][v] = 0.f; }
+
+    // staging of query block qb: Q and dO tiles of the HPW heads, plus LSE / Dvec
+    TileRegs<D, NT> tq[HPW], tg[HPW];
+    float lse_r = 0.f, dvec_r = 0.f;
+    auto load_block = [&](int qb) {
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        const int64_t row0 = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ;
+        tq[h].load(tid, [&](int kq) { return qg + (row0 + kq * 4) * D; });
+        tg[h].load(tid, [&](int kq) { return gg + (row0 + kq * 4) * D; });
+      }
+      if (tid < HPW * kTile) {
+        const int h = tid / kTile, qq = tid % kTile;
+        const int64_t row = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ + qq;
+        lse_r = p.lse[row] * kLog2e;
+        dvec_r = p.dvec[row];
+      }
+    };
+    auto store_block = [&](int buf) {
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        tq[h].store_rows(tid, smem[buf][h][0], QS);
+        tg[h].store_rows(tid, smem[buf][h][1], QS);
+      }
+      if (tid < HPW * kTile) {
+        lse_s[buf][tid / kTile][tid % kTile] = lse_r;
+        dvec_s[buf][tid / kTile][tid % kTile] = dvec_r;
+      }
+    };
+
+    __syncthreads();  // previous key tile's readers of smem are done
+    load_block(kt);
+    store_block(0);
+    __syncthreads();
+    for (int qb = kt; qb < n_blocks; ++qb) {
+      const int cur = (qb - kt) & 1;
+      const bool more = qb + 1 < n_blocks;
+      if (more) load_block(qb + 1);
+      const uint16_t* Qs = smem[cur][g][0];
+      const uint16_t* Gs = smem[cur][g][1];
+      const float* lse_b = lse_s[cur][g];
+      const float* dvec_b = dvec_s[cur][g];
+      const bool diag = qb == kt;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {  // 32-query halves of the tile
         f32x16 sacc, pacc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[(qs * 32 + l32) * KS + s * 16 + hh * 8]);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[s], sacc, 0, 0, 0);
-          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gs[(qs * 32 + l32) * KS + s * 16 + hh * 8]);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vreg[s], pacc, 0, 0, 0);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[(qs * 32 + l32) * QS + s * 16 + hh * 8]);
+          sacc = mfma32(qa, kreg[s], sacc);
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gs[(qs * 32 + l32) * QS + s * 16 + hh * 8]);
+          pacc = mfma32(ga, vreg[s], pacc);
         }
+        // rows of the accumulators: queries qs*32 + 8*(v/4) + 4*hh + v%4
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int qi = qs * 32 + 8 * (v / 4) + 4 * hh + (v % 4);  // query row in block
-          const bool masked = diag && key_local > qi;
-          const float pr = masked ? 0.f : exp2f(sacc[v] * p.scale_log2 - lse_s[qi]);
-          const float ds = pr * (pacc[v] - dvec_s[qi]);
-          pb[qs][v / 8][v % 8] = static_cast<__bf16>(pr);
-          dsb[qs][v / 8][v % 8] = static_cast<__bf16>(ds);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int q0 = qs * 32 + 8 * r4 + 4 * hh;
+          const float4 l4 = *reinterpret_cast<const float4*>(&lse_b[q0]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dvec_b[q0]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * r4 + e;
+            float pr = fast_exp2(fmaf(sacc[v], c2, -lv[e]));
+            if (diag && key_local > q0 + e) pr = 0.f;
+            sacc[v] = pr;
+            pacc[v] = pr * (pacc[v] - dvv[e]);
+          }
+        }
+        const bf16x8 p0 = acc_to_bf16x8(sacc, 0), p1 = acc_to_bf16x8(sacc, 8);
+        const bf16x8 d0 = acc_to_bf16x8(pacc, 0), d1 = acc_to_bf16x8(pacc, 8);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          dv[dt] = mfma32(lds_a_tr(Gs, QS, qs * 32, dt * 32, lane), p0, dv[dt]);
+          dv[dt] = mfma32(lds_a_tr(Gs, QS, qs * 32 + 16, dt * 32, lane), p1, dv[dt]);
+          dk[dt] = mfma32(lds_a_tr(Qs, QS, qs * 32, dt * 32, lane), d0, dk[dt]);
+          dk[dt] = mfma32(lds_a_tr(Qs, QS, qs * 32 + 16, dt * 32, lane), d1, dk[dt]);
         }
       }
-      // dV^T += dO^T . P ; dK^T += Q^T . dS   (contraction over the 64 queries)
+      if (more) store_block(cur ^ 1);
+      __syncthreads();
+    }
+
+    // ---- sum over the heads of the group (fixed order), then write ----------
+    float* xch = reinterpret_cast<float*>(&smem[0][0][0][0]);
+    constexpr int XW = NDT * 32;
+    if (HPW > 1) {
+      if (g > 0) {
+        float* mine = xch + ((static_cast<int64_t>(g - 1) * 2 + ks) * kWave + lane) * XW;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint16_t* grow = &Gt[(dt * 32 + l32) * TS];
-        const uint16_t* qrow = &Qt[(dt * 32 + l32) * TS];
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
+          for (int v = 0; v < 16; ++v) { mine[dt * 32 + v] = dk[dt][v]; mine[dt * 32 + 16 + v] = dv[dt][v]; }
+      }
+      __syncthreads();
+      if (g == 0) {
+        for (int h = 1; h < HPW; ++h) {
+          const float* other = xch + ((static_cast<int64_t>(h - 1) * 2 + ks) * kWave + lane) * XW;
 #pragma unroll
-          for (int ksi = 0; ksi < 2; ++ksi) {
-            const int k0 = qs * 32 + ksi * 16 + 4 * hh;
-            const uint2 glo = *reinterpret_cast<const uint2*>(grow + k0);
-            const uint2 ghi = *reinterpret_cast<const uint2*>(grow + k0 + 8);
-            const bf16x8 ga = __builtin_bit_cast(bf16x8, make_uint4(glo.x, glo.y, ghi.x, ghi.y));
-            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb[qs][ksi], dv[dt], 0, 0, 0);
-            const uint2 qlo = *reinterpret_cast<const uint2*>(qrow + k0);
-            const uint2 qhi = *reinterpret_cast<const uint2*>(qrow + k0 + 8);
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
-            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsb[qs][ksi], dk[dt], 0, 0, 0);
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { dk[dt][v] += other[dt * 32 + v]; dv[dt][v] += other[dt * 32 + 16 + v]; }
+        }
+      }
+    }
+    if (g == 0) {
+      // accumulator rows: d = dt*32 + 8*(v/4) + 4*hh + v%4 ; column: this lane's key
+      if (n_hg == 1) {
+        uint16_t* dkp = static_cast<uint16_t*>(p.dk) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
+        uint16_t* dvp = static_cast<uint16_t*>(p.dv) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = dt * 32 + 8 * r4 + 4 * hh;
+            uint2 a, c;
+            a.x = cvt_pk_bf16(dk[dt][4 * r4 + 0] * p.scale, dk[dt][4 * r4 + 1] * p.scale);
+            a.y = cvt_pk_bf16(dk[dt][4 * r4 + 2] * p.scale, dk[dt][4 * r4 + 3] * p.scale);
+            c.x = cvt_pk_bf16(dv[dt][4 * r4 + 0], dv[dt][4 * r4 + 1]);
+            c.y = cvt_pk_bf16(dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3]);
+            *reinterpret_cast<uint2*>(dkp + d0) = a;
+            *reinterpret_cast<uint2*>(dvp + d0) = c;
+          }
+        }
+      } else {
+        const int64_t slot = static_cast<int64_t>(p.n_kv) * p.seg_len * D;
+        float* pk = p.dkdv_part + (static_cast<int64_t>(hg) * 2) * slot +
+                    (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
+        float* pv = pk + slot;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = dt * 32 + 8 * r4 + 4 * hh;
+            *reinterpret_cast<float4*>(pk + d0) =
+                make_float4(dk[dt][4 * r4], dk[dt][4 * r4 + 1], dk[dt][4 * r4 + 2], dk[dt][4 * r4 + 3]);
+            *reinterpret_cast<float4*>(pv + d0) =
+                make_float4(dv[dt][4 * r4], dv[dt][4 * r4 + 1], dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3]);
           }
         }
       }
     }
   }
+}
 
-  uint16_t* dkp = static_cast<uint16_t*>(p.dk) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
-  uint16_t* dvp = static_cast<uint16_t*>(p.dv) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = dt * 32 + 8 * g + 4 * hh;
-      uint2 a, c;
-      a.x = pack_bf16x2(dk[dt][4 * g + 0] * p.scale, dk[dt][4 * g + 1] * p.scale);
-      a.y = pack_bf16x2(dk[dt][4 * g + 2] * p.scale, dk[dt][4 * g + 3] * p.scale);
-      c.x = pack_bf16x2(dv[dt][4 * g + 0], dv[dt][4 * g + 1]);
-      c.y = pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]);
-      *reinterpret_cast<uint2*>(dkp + d0) = a;
-      *reinterpret_cast<uint2*>(dvp + d0) = c;
-    }
+// dK = scale * sum_h partial_h, dV = sum_h partial_h, summed in head-group order.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part, int n_hg,
+                                                          int64_t n_elem, float scale,
+                                                          uint16_t* __restrict__ dk,
+                                                          uint16_t* __restrict__ dv) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n_elem) return;
+  float4 sk = *reinterpret_cast<const float4*>(part + i);
+  float4 sv = *reinterpret_cast<const float4*>(part + n_elem + i);
+  for (int h = 1; h < n_hg; ++h) {
+    const float4 a = *reinterpret_cast<const float4*>(part + (2 * h) * n_elem + i);
+    const float4 b = *reinterpret_cast<const float4*>(part + (2 * h + 1) * n_elem + i);
+    sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
+    sv.x += b.x; sv.y += b.y; sv.z += b.z; sv.w += b.w;
   }
+  *reinterpret_cast<uint2*>(dk + i) = make_uint2(cvt_pk_bf16(sk.x * scale, sk.y * scale),
+                                                 cvt_pk_bf16(sk.z * scale, sk.w * scale));
+  *reinterpret_cast<uint2*>(dv + i) = make_uint2(cvt_pk_bf16(sv.x, sv.y), cvt_pk_bf16(sv.z, sv.w));
 }
 
 // ---------------------------------------------------------------------------
@@ -504,15 +629,28 @@ hipError_t launch_d(const hga_shape& s, BwdParams& p, hipStream_t st) {
                        n_rows);
     timer_end(HGA_KERNEL_BWD_ROWDOT, st);
     timer_begin(HGA_KERNEL_BWD_DQ, st);
+    const int n_pairs = (n_blocks + 1) / 2;
     if (p.r % 2 == 0)
-      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 2>), dim3(n_blocks * s.n_kv_heads * (p.r / 2)),
-                         dim3(256), 0, st, p);
+      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 2>), dim3(n_pairs * s.n_kv_heads * (p.r / 2)),
+                         dim3(512), 0, st, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 1>), dim3(n_blocks * s.n_kv_heads * p.r),
-                         dim3(128), 0, st, p);
+      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 1>), dim3(n_pairs * s.n_kv_heads * p.r),
+                         dim3(256), 0, st, p);
     timer_end(HGA_KERNEL_BWD_DQ, st);
     timer_begin(HGA_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D>), dim3(n_blocks * s.n_kv_heads), dim3(128), 0, st, p);
+    const int hpw = p.r % 2 == 0 ? 2 : 1;
+    const int n_hg = p.r / hpw;
+    const unsigned grid = static_cast<unsigned>(n_pairs * s.n_kv_heads * n_hg);
+    if (hpw == 2)
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, 2>), dim3(grid), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, 1>), dim3(grid), dim3(128), 0, st, p);
+    if (n_hg > 1) {
+      const int64_t n_elem = static_cast<int64_t>(s.n_kv_heads) * s.seg_len * D;
+      hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(static_cast<unsigned>((n_elem / 4 + 255) / 256)), dim3(256),
+                         0, st, p.dkdv_part, n_hg, n_elem, p.scale, static_cast<uint16_t*>(p.dk),
+                         static_cast<uint16_t*>(p.dv));
+    }
     timer_end(HGA_KERNEL_BWD_DKDV, st);
   }
   return hipGetLastError();
@@ -520,8 +658,14 @@ hipError_t launch_d(const hga_shape& s, BwdParams& p, hipStream_t st) {
 
 }  // namespace
 
+// Dvec [n_q][S] fp32, then (bf16, more than one head group per KV head) the
+// dK/dV partials [n_hg][2][n_kv][S][D] fp32.
 size_t bwd_workspace_bytes(const hga_shape& s) {
-  return ((sizeof(float) * static_cast<size_t>(s.n_q_heads) * s.seg_len) + 255) & ~size_t(255);
+  const size_t dvec = ((sizeof(float) * static_cast<size_t>(s.n_q_heads) * s.seg_len) + 255) & ~size_t(255);
+  const int r = s.n_q_heads / s.n_kv_heads;
+  const int n_hg = r / (r % 2 == 0 ? 2 : 1);
+  if (s.dtype != HGA_BF16 || n_hg <= 1) return dvec;
+  return dvec + sizeof(float) * static_cast<size_t>(n_hg) * 2 * s.n_kv_heads * s.seg_len * s.head_dim;
 }
 
 hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist,
@@ -534,6 +678,8 @@ hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist
   p.sel = sel_groups; p.o = o; p.lse = lse; p.d_o = d_o;
   p.dq = dq; p.dk = dk_seg; p.dv = dv_seg;
   p.dvec = static_cast<float*>(ws);
+  p.dkdv_part = reinterpret_cast<float*>(
+      static_cast<char*>(ws) + (((sizeof(float) * static_cast<size_t>(s.n_q_heads) * s.seg_len) + 255) & ~size_t(255)));
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads;
   p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.k_g = s.top_k_groups;
   p.scale = s.softmax_scale;
