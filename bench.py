@@ -47,13 +47,13 @@ def kernel_work(w, s):
     pairs_causal = S * (S + 1) // 2
     work = {
         "summaries": ("hbm", kv * seg_tokens * d * e + kv * (seg_tokens // 64 + seg_tokens // 8) * d * 4),
-        "block_query": ("hbm", nq * S * d * e + n_B * kv * d * 4),
-        "chunk_score": ("hbm", kv * n_C * d * 4 + n_B * kv * d * 4 + n_B * kv * n_C * 4),
-        "select": ("hbm", n_B * kv * n_C * 4 + n_B * kv * 8 * kc * d * 4 + n_B * kv * (kc + kg) * 4),
+        # Q once, the chunk summaries once, the 8*k_c candidate group summaries per
+        # (block, KV head), the selections written
+        "route": ("hbm", nq * S * d * e + kv * n_C * d * 4 + n_B * kv * 8 * kc * d * 4
+                  + n_B * kv * (kc + kg) * 4),
         "attn_fwd": ("mfma", 4 * d * nq * (pairs_hist + pairs_causal)),
     }
     if w.backward:
-        work["bwd_rowdot"] = ("hbm", 2 * nq * S * d * e + nq * S * 4)
         work["bwd_dq"] = ("mfma", 6 * d * nq * (pairs_hist + pairs_causal))
         work["bwd_dkdv"] = ("mfma", 8 * d * nq * pairs_causal)
     if w.hist_on_host:
@@ -204,8 +204,8 @@ def main():
         ach = amount / (dus * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
-    route_us = sum(kernels[k]["avg_us"] for k in ("block_query", "chunk_score", "select") if k in kernels)
-    route_bytes = sum(work[k][1] for k in ("block_query", "chunk_score", "select"))
+    route_us = kernels["route"]["avg_us"]
+    route_bytes = work["route"][1]
     sel_cpu = sel_g.cpu()
     density = float((sel_cpu >= 0).sum()) * 8 / (n_B * w.n_kv_heads)  # routed tokens per block
     out = {

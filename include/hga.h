@@ -161,15 +161,12 @@ hga_status hga_gather_groups(const hga_shape* shape, const void* k_hist,
 /* Internal kernels, for hga_set_kernel_events. */
 typedef enum {
   HGA_KERNEL_SUMMARIES = 0,    /* hga_build_summaries */
-  HGA_KERNEL_BLOCK_QUERY = 1,  /* hga_route: block queries */
-  HGA_KERNEL_CHUNK_SCORE = 2,  /* hga_route: chunk scores */
-  HGA_KERNEL_SELECT = 3,       /* hga_route: chunk + group top-k */
-  HGA_KERNEL_GATHER = 4,       /* hga_gather_groups, pinned-host tier gathers */
-  HGA_KERNEL_ATTN_FWD = 5,     /* hga_attn_fwd */
-  HGA_KERNEL_BWD_ROWDOT = 6,   /* hga_attn_bwd: rowsum(dO * O) */
-  HGA_KERNEL_BWD_DQ = 7,       /* hga_attn_bwd: dQ */
-  HGA_KERNEL_BWD_DKDV = 8,     /* hga_attn_bwd: dK, dV of the segment */
-  HGA_KERNEL_COUNT = 9
+  HGA_KERNEL_ROUTE = 1,        /* hga_route */
+  HGA_KERNEL_GATHER = 2,       /* hga_gather_groups, pinned-host tier gathers */
+  HGA_KERNEL_ATTN_FWD = 3,     /* hga_attn_fwd */
+  HGA_KERNEL_BWD_DQ = 4,       /* hga_attn_bwd: dQ (and rowsum(dO * O)) */
+  HGA_KERNEL_BWD_DKDV = 5,     /* hga_attn_bwd: dK, dV of the segment (+ partial sum) */
+  HGA_KERNEL_COUNT = 6
 } hga_kernel;
 
 /* Instrumentation: while set, every launch of `kernel` is bracketed by

@@ -1,6 +1,6 @@
 // Backward of exact-token attention with detached history.
 //
-//   Dvec[h][i] = dO[h][i] . O[h][i]                      (row_dot_kernel)
+//   Dvec[h][i] = dO[h][i] . O[h][i]                      (in the dQ kernel)
 //   dQ[h][i]   = scale * sum_t P_t (dO.v_t - Dvec) k_t   over history + segment
 //   dK_seg[j][t], dV_seg[j][t]                           over segment keys only
 // with P_t = exp(scale q.k_t - LSE). The history K/V of the selected groups is
@@ -53,7 +53,8 @@ __device__ __forceinline__ int64_t hist_offset(const BwdParams& p, const int32_t
   return (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup + kk % kGroup) * D;
 }
 
-// Dvec = rowsum(dO * O), fp32 accumulation; 16 threads per row (bf16 d=128).
+// Dvec = rowsum(dO * O), fp32 accumulation (fp32 path; the bf16 dQ kernel
+// computes it for its own rows).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void row_dot_kernel(const T* __restrict__ o,
                                                       const T* __restrict__ d_o,
@@ -159,7 +160,20 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
       }
     }
     const float lse2 = p.lse[row_off] * kLog2e;
-    const float drow = p.dvec[row_off];
+    // Dvec = dO . O for this row (O is the forward's bf16 output); the dK/dV
+    // kernel, launched next on the same stream, reads it back.
+    float drow = 0.f;
+    {
+      const uint16_t* op = static_cast<const uint16_t*>(p.o) + row_off * D + hh * 8;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(op + s * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) drow += static_cast<float>(goreg[s][e]) * static_cast<float>(ov[e]);
+      }
+      drow += __shfl_xor(drow, 32, kWave);
+      if (grp == 0 && hh == 0) p.dvec[row_off] = drow;
+    }
     f32x16 acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -612,22 +626,15 @@ hipError_t launch_d(const hga_shape& s, BwdParams& p, hipStream_t st) {
   constexpr int RPB = 256 / (D / 8);
   const unsigned dot_grid = static_cast<unsigned>((n_rows + RPB - 1) / RPB);
   if (s.dtype == HGA_F32) {
-    timer_begin(HGA_KERNEL_BWD_ROWDOT, st);
+    timer_begin(HGA_KERNEL_BWD_DQ, st);
     hipLaunchKernelGGL((row_dot_kernel<float, D>), dim3(dot_grid), dim3(256), 0, st,
                        static_cast<const float*>(p.o), static_cast<const float*>(p.d_o), p.dvec, n_rows);
-    timer_end(HGA_KERNEL_BWD_ROWDOT, st);
-    timer_begin(HGA_KERNEL_BWD_DQ, st);
     hipLaunchKernelGGL((attn_bwd_dq_f32_kernel<D>), dim3(n_blocks * s.n_q_heads), dim3(kWave), 0, st, p);
     timer_end(HGA_KERNEL_BWD_DQ, st);
     timer_begin(HGA_KERNEL_BWD_DKDV, st);
     hipLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<D>), dim3(n_blocks * s.n_kv_heads), dim3(kWave), 0, st, p);
     timer_end(HGA_KERNEL_BWD_DKDV, st);
   } else {
-    timer_begin(HGA_KERNEL_BWD_ROWDOT, st);
-    hipLaunchKernelGGL((row_dot_kernel<uint16_t, D>), dim3(dot_grid), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(p.o), static_cast<const uint16_t*>(p.d_o), p.dvec,
-                       n_rows);
-    timer_end(HGA_KERNEL_BWD_ROWDOT, st);
     timer_begin(HGA_KERNEL_BWD_DQ, st);
     const int n_pairs = (n_blocks + 1) / 2;
     if (p.r % 2 == 0)

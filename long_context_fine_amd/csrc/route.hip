@@ -1,192 +1,182 @@
-// Two-level content routing: block queries, chunk scores, chunk top-k, group
-// scores inside the kept chunks, group top-k. Three launches:
-//   block_query_kernel  (n_B x n_kv WGs)  Q -> qbar            reads Q once
-//   chunk_score_kernel  (n_C/64 x n_kv)   qbar, C -> scores    reads C once
-//   select_kernel       (n_B x n_kv)      scores, G -> lists   reads 8*k_c rows of G
-// All three are HBM/latency bound. Ranking uses a 64-bit key (order-preserving
-// fp32 bits, then the complemented index) so the max of keys is the best score
-// with the lowest index on ties; the whole route is deterministic.
+// Two-level content routing, one workgroup per (query block b, KV head j):
+//   1. block query qbar = mean of the block's 64 queries over the r heads of j
+//      (reads its 64 KiB of Q once, 16-byte loads);
+//   2. chunk scores qbar . C[j][m] for every history chunk (16 lanes per chunk,
+//      coalesced 512-byte rows; C[j] stays in L2 across the 32 blocks);
+//   3. chunk top-k: each wave takes the k_c best of its strided share in k_c
+//      rounds of a wave-wide max over 64-bit keys strictly below the previous
+//      one (key = order-preserving fp32 bits, then the complemented index, so
+//      the maximum is the best score with the lowest index); the 4*k_c wave
+//      candidates are merged by rank counting;
+//   4. scores of the 8 groups of every kept chunk (reads 8*k_c rows of G);
+//   5. group top-k by rank counting; candidates are enumerated in ascending
+//      group id, so ballot prefix counts place the output in ascending order.
+// HBM/latency bound. Deterministic.
 #include "hga_common.hpp"
 
 namespace hga {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunkTile = 64;  // chunks per chunk_score workgroup
-constexpr int kBlockTile = 32;  // query blocks held in LDS at once
+constexpr int kLdsScores = 4096;  // chunk scores kept in LDS up to this many chunks
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// qbar[b][j][:] = mean of q[h][64b .. 64b+63][:] over h in [j*r, j*r + r).
+// Dot products of qv with `n` rows of `base` (row length D floats), 8 lanes per
+// row, 8 rows per wave pass, UNROLL passes in flight; results to out[row].
+template <int D, int UNROLL, class RowPtr>
+__device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_ptr, float* out) {
+  constexpr int LPR = 8;                 // lanes per row
+  constexpr int EPL = D / LPR;           // elements per lane (16 or 8)
+  constexpr int RPP = kWave / LPR;       // rows per wave pass
+  constexpr int NW = kThreads / kWave;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int sub = lane % LPR;
+  float qr[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qr[e] = qv[sub * EPL + e];
+  for (int r0 = wave * RPP; r0 < n; r0 += NW * RPP * UNROLL) {
+    float4 v[UNROLL][EPL / 4];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int row = r0 + u * NW * RPP + lane / LPR;
+      const float* src = row < n ? row_ptr(row) + sub * EPL : nullptr;
+#pragma unroll
+      for (int c = 0; c < EPL / 4; ++c)
+        v[u][c] = src ? reinterpret_cast<const float4*>(src)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < EPL / 4; ++c)
+        s += v[u][c].x * qr[4 * c] + v[u][c].y * qr[4 * c + 1] + v[u][c].z * qr[4 * c + 2] +
+             v[u][c].w * qr[4 * c + 3];
+#pragma unroll
+      for (int msk = LPR / 2; msk >= 1; msk >>= 1) s += __shfl_xor(s, msk, kWave);
+      const int row = r0 + u * NW * RPP + lane / LPR;
+      if (row < n && sub == 0) out[row] = s;
+    }
+  }
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void block_query_kernel(const T* __restrict__ q, int seg_len,
-                                                               int n_kv, int r,
-                                                               float* __restrict__ qbar) {
-  constexpr int TPR = D / 8;
-  constexpr int RG = kThreads / TPR;
-  __shared__ float part[RG][D + 1];
-  const int t = threadIdx.x, dc = t % TPR, rg = t / TPR;
-  const int b = blockIdx.x, j = blockIdx.y;
-  const int rows = kBlockQ * r;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int row = rg; row < rows; row += RG) {
-    const int h = j * r + row / kBlockQ, i = b * kBlockQ + row % kBlockQ;
-    float v[8];
-    Elem<T>::load8(q + (static_cast<int64_t>(h) * seg_len + i) * D + dc * 8, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += v[e];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg][dc * 8 + e] = acc[e];
-  __syncthreads();
-  if (t < D) {
-    float s = 0.f;
-    for (int g = 0; g < RG; ++g) s += part[g][t];
-    qbar[(static_cast<int64_t>(b) * n_kv + j) * D + t] = s * (1.0f / static_cast<float>(rows));
-  }
-}
-
-// scores[b][j][m] = qbar[b][j] . C[j][m] for a tile of 64 chunks, all blocks.
-template <int D>
-__global__ __launch_bounds__(kThreads) void chunk_score_kernel(const float* __restrict__ qbar,
-                                                               const float* __restrict__ csum,
-                                                               int n_blocks, int n_kv, int n_chunks,
-                                                               float* __restrict__ scores) {
-  __shared__ float ct[kChunkTile][D + 1];
-  __shared__ float qb[kBlockTile][D];
-  const int t = threadIdx.x;
-  const int j = blockIdx.y;
-  const int m0 = blockIdx.x * kChunkTile;
-  const int n_here = min(kChunkTile, n_chunks - m0);
-  for (int idx = t; idx < kChunkTile * D; idx += kThreads) {
-    const int c = idx / D, e = idx % D;
-    ct[c][e] = c < n_here ? csum[(static_cast<int64_t>(j) * n_chunks + m0 + c) * D + e] : 0.f;
-  }
-  const int c = t % kChunkTile;
-  const int bq = t / kChunkTile;  // 0..3 (one per wave: broadcast reads of qb)
-  for (int b0 = 0; b0 < n_blocks; b0 += kBlockTile) {
-    const int nb = min(kBlockTile, n_blocks - b0);
-    __syncthreads();
-    for (int idx = t; idx < kBlockTile * D; idx += kThreads) {
-      const int bb = idx / D, e = idx % D;
-      qb[bb][e] = bb < nb ? qbar[(static_cast<int64_t>(b0 + bb) * n_kv + j) * D + e] : 0.f;
-    }
-    __syncthreads();
-    float acc[kBlockTile / 4];
-#pragma unroll
-    for (int k = 0; k < kBlockTile / 4; ++k) acc[k] = 0.f;
-    for (int e = 0; e < D; ++e) {
-      const float cv = ct[c][e];
-#pragma unroll
-      for (int k = 0; k < kBlockTile / 4; ++k) acc[k] += qb[bq + 4 * k][e] * cv;
-    }
-    if (c < n_here) {
-#pragma unroll
-      for (int k = 0; k < kBlockTile / 4; ++k) {
-        const int bb = bq + 4 * k;
-        if (bb < nb)
-          scores[(static_cast<int64_t>(b0 + bb) * n_kv + j) * n_chunks + m0 + c] = acc[k];
-      }
-    }
-  }
-}
-
-__device__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
-  v = wave_max_u64(v);
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if ((threadIdx.x % kWave) == 0) red[w] = v;
-  __syncthreads();
-  uint64_t best = red[0];
-#pragma unroll
-  for (int i = 1; i < kThreads / kWave; ++i) best = red[i] > best ? red[i] : best;
-  return best;
-}
-
-// Per (block, KV head): chunk top-k from the scores, then group scoring over the
-// 8 groups of each kept chunk and group top-k. Outputs ascending, -1 padded.
-template <int D>
-__global__ __launch_bounds__(kThreads) void select_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ scores,
-    const float* __restrict__ gsum, int n_kv, int n_chunks, int k_c, int k_g,
+__global__ __launch_bounds__(kThreads) void route_kernel(
+    const T* __restrict__ q, const float* __restrict__ csum, const float* __restrict__ gsum,
+    int seg_len, int n_kv, int r, int n_chunks, int k_c, int k_g, float* __restrict__ ws_scores,
     int32_t* __restrict__ sel_chunks, int32_t* __restrict__ sel_groups) {
-  constexpr int TPC = D / 8;  // threads per group candidate
+  constexpr int TPR = D / 8;            // threads per Q row (8 elements each)
+  constexpr int RG = kThreads / TPR;    // row groups
+  constexpr int NW = kThreads / kWave;
   constexpr int kMaxCand = kMaxTopKChunks * (kChunk / kGroup);
-  __shared__ uint64_t red[kThreads / kWave];
-  __shared__ int32_t chosen[kMaxTopKChunks];
-  __shared__ int32_t sorted[kMaxTopKChunks];
+  __shared__ float part[RG][D + 1];
   __shared__ float qv[D];
+  __shared__ float sc_lds[kLdsScores];
+  __shared__ uint64_t wcand[NW][kMaxTopKChunks];
+  __shared__ int32_t sorted[kMaxTopKChunks];
   __shared__ float gsc[kMaxCand];
-  __shared__ uint8_t flag[kMaxCand];
+  __shared__ uint64_t gkey[kMaxCand];
+  __shared__ uint64_t wmask[kMaxCand / kWave];
 
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int b = blockIdx.x, j = blockIdx.y;
   const int64_t bj = static_cast<int64_t>(b) * n_kv + j;
-  const float* sc = scores + bj * n_chunks;
+
+  // ---- 1. block query ----------------------------------------------------
+  {
+    const int dc = t % TPR, rg = t / TPR;
+    const int rows = kBlockQ * r;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 8
+    for (int row = rg; row < rows; row += RG) {
+      const int h = j * r + row / kBlockQ, i = b * kBlockQ + row % kBlockQ;
+      float v[8];
+      Elem<T>::load8(q + (static_cast<int64_t>(h) * seg_len + i) * D + dc * 8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg][dc * 8 + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+      float s = 0.f;
+      for (int g = 0; g < RG; ++g) s += part[g][t];
+      qv[t] = s * (1.0f / static_cast<float>(rows));
+    }
+    __syncthreads();
+  }
+
+  // ---- 2. chunk scores ----------------------------------------------------
+  float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
+  const float* cbase = csum + static_cast<int64_t>(j) * n_chunks * D;
+  score_rows<D, 2>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
+  __syncthreads();
+
+  // ---- 3. chunk top-k: per-wave top-k over strided elements, then merge ---
   const int kc_eff = min(k_c, n_chunks);
-
-  if (t < D) qv[t] = qbar[bj * D + t];
-
-  // chunk top-k: each round takes the best key strictly below the previous one
-  uint64_t prev = ~0ull;
-  for (int round = 0; round < kc_eff; ++round) {
-    uint64_t local = 0;
-    for (int m = t; m < n_chunks; m += kThreads) {
-      const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(m));
-      if (k < prev && k > local) local = k;
+  {
+    uint64_t prev = ~0ull;
+    for (int round = 0; round < kc_eff; ++round) {
+      uint64_t local = 0;
+      for (int m = wave * kWave + lane; m < n_chunks; m += kThreads) {
+        const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(m));
+        if (k < prev && k > local) local = k;
+      }
+      prev = wave_max_u64(local);      // 0 once this wave has no element left
+      if (lane == 0) wcand[wave][round] = prev;
     }
-    prev = block_max_u64(local, red);
-    if (t == 0) chosen[round] = static_cast<int32_t>(rank_key_index(prev));
   }
   __syncthreads();
-  if (t < kc_eff) {
-    const int id = chosen[t];
-    int pos = 0;
-    for (int u = 0; u < kc_eff; ++u) pos += chosen[u] < id;
-    sorted[pos] = id;
-  }
-  __syncthreads();
-  if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
-
-  // group scores for the 8 groups of every kept chunk
-  const int n_cand = kc_eff * (kChunk / kGroup);
-  const int64_t n_groups_total = static_cast<int64_t>(n_chunks) * (kChunk / kGroup);
-  const int lane_in = t % TPC;
-  for (int c0 = 0; c0 < n_cand; c0 += kThreads / TPC) {
-    const int c = c0 + t / TPC;
-    float part = 0.f;
-    if (c < n_cand) {
-      const int64_t gid = static_cast<int64_t>(sorted[c / 8]) * 8 + (c % 8);
-      float g[8];
-      Elem<float>::load8(gsum + (static_cast<int64_t>(j) * n_groups_total + gid) * D + lane_in * 8, g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += g[e] * qv[lane_in * 8 + e];
+  {
+    // t < NW*kc_eff: candidate (wave t / kc_eff, round t % kc_eff)
+    if (t < NW * kc_eff) {
+      const uint64_t mine = wcand[t / kc_eff][t % kc_eff];
+      int rank = 0;
+      for (int o = 0; o < NW * kc_eff; ++o) rank += wcand[o / kc_eff][o % kc_eff] > mine;
+      // keys are unique (index in the low bits); the kc_eff best are all valid
+      if (rank < kc_eff) part[0][rank] = __uint_as_float(rank_key_index(mine));
     }
-#pragma unroll
-    for (int m = TPC / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
-    if (c < n_cand && lane_in == 0) gsc[c] = part;
-  }
-  __syncthreads();
-
-  // group top-k by rank counting: selected iff fewer than k_g candidates beat it
-  for (int c = t; c < n_cand; c += kThreads) {
-    const uint32_t gid = static_cast<uint32_t>(sorted[c / 8] * 8 + (c % 8));
-    const uint64_t kc = rank_key(gsc[c], gid);
-    int beaten = 0;
-    for (int o = 0; o < n_cand; ++o) {
-      const uint32_t gido = static_cast<uint32_t>(sorted[o / 8] * 8 + (o % 8));
-      beaten += rank_key(gsc[o], gido) > kc;
-    }
-    flag[c] = beaten < k_g;
-  }
-  __syncthreads();
-  // candidates are enumerated in ascending group id, so the output position
-  // of a selected candidate is the number of selected candidates before it
-  for (int c = t; c < n_cand; c += kThreads) {
-    if (flag[c]) {
+    __syncthreads();
+    if (t < kc_eff) {
+      const int id = static_cast<int>(__float_as_uint(part[0][t]));
       int pos = 0;
-      for (int o = 0; o < c; ++o) pos += flag[o];
+      for (int u = 0; u < kc_eff; ++u) pos += static_cast<int>(__float_as_uint(part[0][u])) < id;
+      sorted[pos] = id;
+    }
+    __syncthreads();
+    if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
+  }
+
+  // ---- 4. group scores for the 8 groups of every kept chunk ----------------
+  const int n_cand = kc_eff * (kChunk / kGroup);
+  const float* gbase = gsum + static_cast<int64_t>(j) * n_chunks * (kChunk / kGroup) * D;
+  score_rows<D, 2>(qv, n_cand, [&](int c) {
+    return gbase + (static_cast<int64_t>(sorted[c / 8]) * 8 + (c % 8)) * D;
+  }, gsc);
+  __syncthreads();
+  for (int c = t; c < n_cand; c += kThreads)
+    gkey[c] = rank_key(gsc[c], static_cast<uint32_t>(sorted[c / 8] * 8 + (c % 8)));
+  __syncthreads();
+
+  // ---- 5. group top-k by rank counting, ascending output via ballots ------
+  for (int c0 = 0; c0 < n_cand; c0 += kThreads) {
+    const int c = c0 + t;
+    bool take = false;
+    if (c < n_cand) {
+      const uint64_t kc = gkey[c];
+      int beaten = 0;
+      for (int o = 0; o < n_cand; ++o) beaten += gkey[o] > kc;
+      take = beaten < k_g;
+    }
+    const uint64_t m = __ballot(take);
+    if (lane == 0) wmask[(c0 / kWave) + wave] = m;
+  }
+  __syncthreads();
+  for (int c = t; c < n_cand; c += kThreads) {
+    const uint64_t m = wmask[c / kWave];
+    if ((m >> (c % kWave)) & 1ull) {
+      int pos = __popcll(m & ((1ull << (c % kWave)) - 1ull));
+      for (int w2 = 0; w2 < c / kWave; ++w2) pos += __popcll(wmask[w2]);
       sel_groups[bj * k_g + pos] = sorted[c / 8] * 8 + (c % 8);
     }
   }
@@ -200,35 +190,23 @@ hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const fl
   const int n_blocks = s.seg_len / kBlockQ;
   const int n_chunks = static_cast<int>(s.hist_len / kChunk);
   const int r = s.n_q_heads / s.n_kv_heads;
-  float* qbar = static_cast<float*>(ws);
-  float* scores = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                           align256(sizeof(float) * n_blocks * s.n_kv_heads * D));
-  timer_begin(HGA_KERNEL_BLOCK_QUERY, st);
-  hipLaunchKernelGGL((block_query_kernel<T, D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0,
-                     st, static_cast<const T*>(q), s.seg_len, s.n_kv_heads, r, qbar);
-  timer_end(HGA_KERNEL_BLOCK_QUERY, st);
-  if (n_chunks > 0) {
-    timer_begin(HGA_KERNEL_CHUNK_SCORE, st);
-    hipLaunchKernelGGL((chunk_score_kernel<D>),
-                       dim3((n_chunks + kChunkTile - 1) / kChunkTile, s.n_kv_heads),
-                       dim3(kThreads), 0, st, qbar, cs, n_blocks, s.n_kv_heads, n_chunks, scores);
-    timer_end(HGA_KERNEL_CHUNK_SCORE, st);
-  }
-  timer_begin(HGA_KERNEL_SELECT, st);
-  hipLaunchKernelGGL((select_kernel<D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
-                     qbar, scores, gs, s.n_kv_heads, n_chunks, s.top_k_chunks, s.top_k_groups,
-                     sc_out, sg_out);
-  timer_end(HGA_KERNEL_SELECT, st);
+  float* scores = static_cast<float*>(ws);
+  timer_begin(HGA_KERNEL_ROUTE, st);
+  hipLaunchKernelGGL((route_kernel<T, D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
+                     static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, n_chunks,
+                     s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out);
+  timer_end(HGA_KERNEL_ROUTE, st);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Chunk scores spill to the workspace only when a KV head has more than
+// kLdsScores history chunks; the size is reported for every shape anyway.
 size_t route_workspace_bytes(const hga_shape& s) {
   const size_t n_blocks = s.seg_len / kBlockQ;
   const size_t n_chunks = static_cast<size_t>(s.hist_len / kChunk);
-  return align256(sizeof(float) * n_blocks * s.n_kv_heads * s.head_dim) +
-         align256(sizeof(float) * n_blocks * s.n_kv_heads * (n_chunks ? n_chunks : 1));
+  return align256(sizeof(float) * n_blocks * s.n_kv_heads * (n_chunks ? n_chunks : 1));
 }
 
 hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,

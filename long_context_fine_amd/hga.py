@@ -24,8 +24,7 @@ EXPORTS = ("hga_build_summaries", "hga_route", "hga_attn_fwd", "hga_attn_bwd",
            "hga_gather_groups", "hga_workspace_size", "hga_status_string",
            "hga_last_error", "hga_abi_version", "hga_set_kernel_events")
 
-KERNELS = ("summaries", "block_query", "chunk_score", "select", "gather", "attn_fwd",
-           "bwd_rowdot", "bwd_dq", "bwd_dkdv")
+KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv")
 
 
 class HGAError(RuntimeError):

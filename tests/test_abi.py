@@ -94,8 +94,8 @@ def test_null_shape_and_null_pointers(L):
 def test_workspace_sizes_and_undersized_workspace(L):
     s = _shape()
     n_route = L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ROUTE)
-    # block queries [32][8][128] f32 + chunk scores [32][8][224] f32
-    assert n_route == 32 * 8 * 128 * 4 + 32 * 8 * 224 * 4
+    # chunk scores [32][8][224] f32
+    assert n_route == 32 * 8 * 224 * 4
     assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_FWD) == 0
     # Dvec [32][2048] f32 + dK/dV partials of the 2 head groups [2][2][8][2048][128] f32
     assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_BWD) == 32 * 2048 * 4 + 2 * 2 * 8 * 2048 * 128 * 4
