@@ -73,6 +73,41 @@ __device__ __forceinline__ bf16x8 lds_a_tr(const uint16_t* T, int stride, int rb
   return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
 
+// Unpadded 64 x D bf16 LDS tile whose 16-byte chunks are XOR-permuted by row,
+// so that both row reads (b128, 16 lanes on 16 rows at one column) and
+// transposed reads (ds_read_b64_tr_b16, 4 rows x 16 columns per 16 lanes) hit
+// 64 distinct banks (checked with a bank model of both access patterns).
+template <int D>
+struct Swz {
+  static constexpr int NCH = D / 8;  // chunks per row
+  __device__ __forceinline__ static int f(int row) {
+    return NCH == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : (((row & 3) << 1) | ((row >> 2) & 1));
+  }
+  __device__ __forceinline__ static int off(int row, int col) {
+    return row * D + ((((col >> 3) ^ f(row)) & (NCH - 1)) << 3) + (col & 7);
+  }
+};
+
+// A operand (rows of the tile = M index) from a swizzled tile: lane row
+// rbase + lane % 32, slots = 8 columns starting at k0 + 8 * (lane / 32).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_a_row_swz(const uint16_t* T, int rbase, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(T + Swz<D>::off(rbase + (lane & 31), k0 + 8 * (lane >> 5)));
+}
+
+// lds_a_tr for a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_a_tr_swz(const uint16_t* T, int rbase, int cbase, int lane) {
+  const int g16 = lane >> 4, gl = lane & 15;
+  const int col = cbase + 16 * (g16 & 1) + 4 * (gl & 3);
+  const int row = rbase + 4 * (g16 >> 1) + (gl >> 2);
+  const i16x4 lo = ds_read_tr16(T + Swz<D>::off(row, col));
+  const i16x4 hi = ds_read_tr16(T + Swz<D>::off(row + 8, col));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo);
+  const uint2 h2 = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // One 64-row x D tile held in registers between its global load and its LDS
@@ -112,6 +147,19 @@ struct TileRegs {
       }
     }
   }
+  // swizzled row-major (Swz<D>)
+  __device__ __forceinline__ void store_swz(int tid, uint16_t* dst) const {
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const int task = tid + t * NT;
+      if (NTASK % NT == 0 || task < NTASK) {
+        const int kq = task / CPR, c = task % CPR;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          *reinterpret_cast<uint4*>(dst + Swz<D>::off(kq * 4 + u, c * 8)) = a[t][u];
+      }
+    }
+  }
   // transposed: dst[col * stride + row], 4 rows packed per 8-byte store
   __device__ __forceinline__ void store_transposed(int tid, uint16_t* dst, int stride) const {
 #pragma unroll
@@ -138,6 +186,36 @@ struct TileRegs {
     }
   }
 };
+
+// Loads one 64 x D bf16 tile straight from global memory into a swizzled LDS
+// tile (Swz<D>) with global_load_lds_dwordx4: each wave instruction fills 1 KiB
+// of LDS (lane i -> 16-byte position i), so lane i fetches the global chunk
+// that the swizzle places at its position. No registers, no LDS store
+// instructions; completion is tracked by vmcnt (wait before the barrier).
+// rowptr(r) must return a readable row for every r in 0..63 (masked rows may
+// point anywhere valid: their values are never used unmasked).
+template <int D, int NT, class RowPtr>
+__device__ __forceinline__ void tile_load_lds(uint16_t* lds_tile, int tid, RowPtr rowptr) {
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int CHUNKS = kTile * CPR;
+  const int wave = tid / kWave, lane = tid % kWave;
+#pragma unroll
+  for (int i0 = 0; i0 < CHUNKS; i0 += NT) {
+    const int i = i0 + wave * kWave;      // first chunk position of this wave instruction
+    if (CHUNKS % NT == 0 || i < CHUNKS) {
+      const int pos = i + lane;
+      const int row = pos / CPR, pc = pos % CPR;
+      const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
+      const uint16_t* src = rowptr(row) + lc * 8;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(src),
+          (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(lds_tile + i * 8)), 16,
+          0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Builds, in LDS, the list of history tiles (8 selected groups each) that hold
 // at least one valid group; returns nothing, the count lands in *n_out.
