@@ -32,6 +32,9 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB (one plain copy "
+                         "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -59,6 +62,38 @@ def kernel_work(w, s):
     if w.hist_on_host:
         work["gather"] = ("host", n_B * kv * hist_tok * d * e * 2)
     return work
+
+
+KERNEL_SOURCES = {
+    "summaries": ["summaries.hip"], "route": ["route.hip"], "gather": ["gather.hip"],
+    "attn_fwd": ["attn_fwd.hip", "attn_tile.hpp"], "bwd_dq": ["attn_bwd.hip", "attn_tile.hpp"],
+    "bwd_dkdv": ["attn_bwd.hip", "attn_tile.hpp"],
+}
+
+
+def source_digest(kernel):
+    """sha256 over the sources a kernel is built from (plus the shared header)."""
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_fine_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["hga_common.hpp"]:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record
+    of this workload, or None if absent or taken on different kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 3 and parts[0] == kernel and parts[1] == source_digest(kernel):
+            return int(parts[2])
+    return None
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -199,11 +234,13 @@ def main():
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         ach = amount / (dus * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": recorded_traffic(w.name, dom)}
     else:
         ach = amount / (dus * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": recorded_traffic(w.name, dom)}
     route_us = kernels["route"]["avg_us"]
     route_bytes = work["route"][1]
     sel_cpu = sel_g.cpu()
@@ -236,6 +273,14 @@ def main():
         "kernels": kernels,
         "routed_history_tokens_per_block": density,
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_mib"] = args.copy_calibration_mib
     if args.cpu_baseline == "on":
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
