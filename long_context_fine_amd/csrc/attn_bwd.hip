@@ -284,18 +284,20 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
 // so the pair gives every workgroup the same work. 2*HPW waves: wave (g, ks)
 // keeps K^T and V^T of its 32 keys (subtile ks) in registers as B operands and
 // streams the 64-query tiles of head g: S = Q.K^T, dP = dO.V^T, then
-// dV^T += dO^T.P and dK^T += Q^T.dS with Q^T / dO^T read transposed from the
-// row-major tiles. The next query block's Q/dO tiles are loaded into registers
-// while the current ones (double-buffered in LDS) are used. Head partials are
-// summed in LDS; with more than one head group per KV head each workgroup
-// writes an fp32 partial that dkdv_reduce_kernel sums in a fixed order.
+// dV^T += dO^T.P and dK^T += Q^T.dS with Q^T / dO^T read transposed
+// (ds_read_b64_tr_b16). Q/dO tiles (XOR-swizzled, so row reads and transposed
+// reads are both conflict-free) and LSE/Dvec go straight from global memory
+// into the other half of a double-buffered LDS stage (global_load_lds) while
+// the current one is used; LDS operands are read one k-step ahead of their
+// MFMAs. Head partials are summed in LDS; with more than one head group per
+// KV head each workgroup writes an fp32 partial that dkdv_reduce_kernel sums
+// in a fixed order.
 template <int D, int HPW>
 __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams p) {
   constexpr int NT = 128 * HPW;
-  constexpr int QS = D + 8;
   constexpr int NDT = D / 32;
   constexpr int NKS = D / 16;
-  constexpr int TILE = kTile * QS;
+  constexpr int TILE = kTile * D;     // swizzled Q / dO tile (Swz<D>)
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][HPW][2][TILE];  // [buf][head][Q, dO]
   __shared__ __attribute__((aligned(16))) float lse_s[2][HPW][kTile];
   __shared__ __attribute__((aligned(16))) float dvec_s[2][HPW][kTile];
@@ -318,6 +320,18 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
   const uint16_t* qg = static_cast<const uint16_t*>(p.q);
   const uint16_t* gg = static_cast<const uint16_t*>(p.d_o);
 
+  // issue the loads of query block qb (all HPW heads) into LDS stage buf
+  auto issue_block = [&](int qb, int buf) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      const int64_t row0 = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ;
+      tile_load_lds_rows<D, NT>(smem[buf][h][0], tid, qg + row0 * D);
+      tile_load_lds_rows<D, NT>(smem[buf][h][1], tid, gg + row0 * D);
+      if (wave == 0) row64_load_lds(lse_s[buf][h], p.lse + row0, lane);
+      if (wave == 1) row64_load_lds(dvec_s[buf][h], p.dvec + row0, lane);
+    }
+  };
+
   for (int half = 0; half < 2; ++half) {
     const int kt = half == 0 ? pair : n_blocks - 1 - pair;
     if (half == 1 && kt <= pair) break;  // odd count: the middle tile runs once
@@ -335,43 +349,13 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
 #pragma unroll
       for (int v = 0; v < 16; ++v) { dk[dt][v] = 0.f; dv[dt][v] = 0.f; }
 
-    // staging of query block qb: Q and dO tiles of the HPW heads, plus LSE / Dvec
-    TileRegs<D, NT> tq[HPW], tg[HPW];
-    float lse_r = 0.f, dvec_r = 0.f;
-    auto load_block = [&](int qb) {
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) {
-        const int64_t row0 = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ;
-        tq[h].load(tid, [&](int kq) { return qg + (row0 + kq * 4) * D; });
-        tg[h].load(tid, [&](int kq) { return gg + (row0 + kq * 4) * D; });
-      }
-      if (tid < HPW * kTile) {
-        const int h = tid / kTile, qq = tid % kTile;
-        const int64_t row = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ + qq;
-        lse_r = p.lse[row] * kLog2e;
-        dvec_r = p.dvec[row];
-      }
-    };
-    auto store_block = [&](int buf) {
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) {
-        tq[h].store_rows(tid, smem[buf][h][0], QS);
-        tg[h].store_rows(tid, smem[buf][h][1], QS);
-      }
-      if (tid < HPW * kTile) {
-        lse_s[buf][tid / kTile][tid % kTile] = lse_r;
-        dvec_s[buf][tid / kTile][tid % kTile] = dvec_r;
-      }
-    };
-
     __syncthreads();  // previous key tile's readers of smem are done
-    load_block(kt);
-    store_block(0);
+    issue_block(kt, 0);
+    wait_vmem();
     __syncthreads();
     for (int qb = kt; qb < n_blocks; ++qb) {
       const int cur = (qb - kt) & 1;
-      const bool more = qb + 1 < n_blocks;
-      if (more) load_block(qb + 1);
+      if (qb + 1 < n_blocks) issue_block(qb + 1, cur ^ 1);
       const uint16_t* Qs = smem[cur][g][0];
       const uint16_t* Gs = smem[cur][g][1];
       const float* lse_b = lse_s[cur][g];
@@ -382,12 +366,20 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
         f32x16 sacc, pacc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
+        bf16x8 qa = lds_a_row_swz<D>(Qs, qs * 32, 0, lane);
+        bf16x8 ga = lds_a_row_swz<D>(Gs, qs * 32, 0, lane);
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[(qs * 32 + l32) * QS + s * 16 + hh * 8]);
+          bf16x8 qn = qa, gn = ga;
+          if (s + 1 < NKS) {
+            qn = lds_a_row_swz<D>(Qs, qs * 32, (s + 1) * 16, lane);
+            gn = lds_a_row_swz<D>(Gs, qs * 32, (s + 1) * 16, lane);
+          }
           sacc = mfma32(qa, kreg[s], sacc);
-          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gs[(qs * 32 + l32) * QS + s * 16 + hh * 8]);
           pacc = mfma32(ga, vreg[s], pacc);
+          qa = qn;
+          ga = gn;
+          __builtin_amdgcn_sched_barrier(0);
         }
         // rows of the accumulators: queries qs*32 + 8*(v/4) + 4*hh + v%4
 #pragma unroll
@@ -400,7 +392,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * r4 + e;
-            float pr = fast_exp2(fmaf(sacc[v], c2, -lv[e]));
+            float pr = fast_exp2(fmaf(sacc[v], c2, -lv[e] * kLog2e));
             if (diag && key_local > q0 + e) pr = 0.f;
             sacc[v] = pr;
             pacc[v] = pr * (pacc[v] - dvv[e]);
@@ -408,15 +400,31 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
         }
         const bf16x8 p0 = acc_to_bf16x8(sacc, 0), p1 = acc_to_bf16x8(sacc, 8);
         const bf16x8 d0 = acc_to_bf16x8(pacc, 0), d1 = acc_to_bf16x8(pacc, 8);
+        bf16x8 a[4], an[4];
+        a[0] = lds_a_tr_swz<D>(Gs, qs * 32, 0, lane);
+        a[1] = lds_a_tr_swz<D>(Gs, qs * 32 + 16, 0, lane);
+        a[2] = lds_a_tr_swz<D>(Qs, qs * 32, 0, lane);
+        a[3] = lds_a_tr_swz<D>(Qs, qs * 32 + 16, 0, lane);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          dv[dt] = mfma32(lds_a_tr(Gs, QS, qs * 32, dt * 32, lane), p0, dv[dt]);
-          dv[dt] = mfma32(lds_a_tr(Gs, QS, qs * 32 + 16, dt * 32, lane), p1, dv[dt]);
-          dk[dt] = mfma32(lds_a_tr(Qs, QS, qs * 32, dt * 32, lane), d0, dk[dt]);
-          dk[dt] = mfma32(lds_a_tr(Qs, QS, qs * 32 + 16, dt * 32, lane), d1, dk[dt]);
+          if (dt + 1 < NDT) {
+            an[0] = lds_a_tr_swz<D>(Gs, qs * 32, (dt + 1) * 32, lane);
+            an[1] = lds_a_tr_swz<D>(Gs, qs * 32 + 16, (dt + 1) * 32, lane);
+            an[2] = lds_a_tr_swz<D>(Qs, qs * 32, (dt + 1) * 32, lane);
+            an[3] = lds_a_tr_swz<D>(Qs, qs * 32 + 16, (dt + 1) * 32, lane);
+          }
+          dv[dt] = mfma32(a[0], p0, dv[dt]);
+          dv[dt] = mfma32(a[1], p1, dv[dt]);
+          dk[dt] = mfma32(a[2], d0, dk[dt]);
+          dk[dt] = mfma32(a[3], d1, dk[dt]);
+          if (dt + 1 < NDT) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a[u] = an[u];
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (more) store_block(cur ^ 1);
+      wait_vmem();
       __syncthreads();
     }
 

@@ -217,6 +217,38 @@ __device__ __forceinline__ void tile_load_lds(uint16_t* lds_tile, int tid, RowPt
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// tile_load_lds for a tile whose 64 rows are contiguous in global memory
+// (row stride D): the per-lane source offset takes only 4 distinct values, so
+// every instruction is a scalar base plus a precomputed lane offset.
+template <int D, int NT>
+__device__ __forceinline__ void tile_load_lds_rows(uint16_t* lds_tile, int tid, const uint16_t* src) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = kWave / CPR;          // rows per wave instruction (4 for D = 128)
+  constexpr int CHUNKS = kTile * CPR;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int lrow = lane / CPR, pc = lane % CPR;
+#pragma unroll
+  for (int i0 = 0; i0 < CHUNKS; i0 += NT) {
+    const int i = i0 + wave * kWave;        // first chunk position of this wave instruction
+    if (CHUNKS % NT == 0 || i < CHUNKS) {
+      const int row = i / CPR + lrow;
+      const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(src + row * D + lc * 8),
+          (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(lds_tile + i * 8)), 16,
+          0, 0);
+    }
+  }
+  (void)RPI;
+}
+
+// 64 consecutive floats from global memory into LDS (one wave instruction).
+__device__ __forceinline__ void row64_load_lds(float* lds_dst, const float* src, int lane) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + lane),
+                                   (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(lds_dst)),
+                                   4, 0, 0);
+}
+
 // Builds, in LDS, the list of history tiles (8 selected groups each) that hold
 // at least one valid group; returns nothing, the count lands in *n_out.
 __device__ __forceinline__ void build_hist_tile_list(const int32_t* sel_s, int k_g, int32_t* list,
