@@ -82,18 +82,21 @@ __global__ __launch_bounds__(256) void row_dot_kernel(const T* __restrict__ o,
 // pair of query blocks {b, n-1-b}); 4*HPW waves in two tile-parity groups,
 // each wave owning 32 query rows of one head (Q^T and dO^T stay in registers
 // as B operands). Per 64-key tile: S^T = K.Q^T, dP^T = V.dO^T, dS^T = P^T o
-// (dP^T - Dvec), dQ^T += K^T.dS^T with K^T read transposed from the row-major
-// K tile. The two parity groups' dQ partials are summed in a fixed order.
+// (dP^T - Dvec), dQ^T += K^T.dS^T with K^T read transposed from the K tile.
+// Each parity group loads its K/V tiles straight from global memory into a
+// double-buffered, XOR-swizzled LDS stage (global_load_lds; history tiles are
+// runs of whole selected groups) while it works on the current one; LDS
+// operands are read one k-step ahead of their MFMAs. The two parity groups'
+// dQ partials are summed in a fixed order.
 template <int D, int HPW>
 __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p) {
   constexpr int NT = 256 * HPW;
   constexpr int GT = NT / 2;
-  constexpr int KS = D + 16;          // K: read by rows and transposed
-  constexpr int VS = D + 8;           // V: read by rows
   constexpr int NDT = D / 32;
   constexpr int NKS = D / 16;
-  constexpr int STAGE = kTile * (KS + VS);
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][STAGE];  // [buffer][parity]
+  constexpr int TILE = kTile * D;
+  constexpr int RPI = kWave / (D / 8);   // rows per global_load_lds run
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][2][TILE];  // [buffer][parity][K, V]
   __shared__ int32_t sel_s[kMaxTopKGroups];
   __shared__ int32_t hlist[kMaxTopKGroups / 8];
   __shared__ int32_t n_hist_s;
@@ -115,8 +118,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   const int head = j * p.r + hg * HPW + gw / 2;
   const int qrow0 = (gw % 2) * 32;
 
-  const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist);
-  const uint16_t* vh = static_cast<const uint16_t*>(p.v_hist);
+  const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist) + static_cast<int64_t>(j) * p.hist_len * D;
+  const uint16_t* vh = static_cast<const uint16_t*>(p.v_hist) + static_cast<int64_t>(j) * p.hist_len * D;
   const uint16_t* ks_g = static_cast<const uint16_t*>(p.k_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const uint16_t* vs_g = static_cast<const uint16_t*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const float c2 = p.scale_log2;
@@ -136,18 +139,32 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
     const int q_tok = b * kBlockQ + qrow0 + l32;
     const int64_t row_off = static_cast<int64_t>(head) * p.seg_len + q_tok;
 
-    auto rowptr = [&](int t, int kq, int which) -> const uint16_t* {
-      if (t >= n_tiles) return nullptr;
+    // K and V of tile t (history tiles first, then segment tiles 0..b) into
+    // LDS buffer buf of this parity group. A history slot without a group
+    // (-1 or past k_g) loads the segment's first rows instead: finite values
+    // whose probabilities are forced to zero.
+    auto issue_tile = [&](int t, int buf) {
+      if (t >= n_tiles) return;
+      int gt = gtid;
+      asm volatile("" : "+v"(gt));
       if (t < n_hist) {
-        const int slot = hlist[t] * 8 + kq / 2;
-        if (slot >= p.k_g) return nullptr;
-        const int n = sel_s[slot];
-        if (n < 0) return nullptr;
-        return (which ? vh : kh) +
-               (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup + (kq % 2) * 4) * D;
+        const int ht = hlist[t];
+        auto run = [&](int kq, const uint16_t* base, const uint16_t* seg) -> const uint16_t* {
+          const int slot = ht * 8 + (kq * RPI) / kGroup;
+          const int n = slot < p.k_g ? sel_s[slot] : -1;
+          const int sub = (kq * RPI) % kGroup;
+          return n >= 0 ? base + (static_cast<int64_t>(n) * kGroup + sub) * D : seg + sub * D;
+        };
+        tile_load_lds_runs<D, GT>(smem[buf][grp][0], gt, [&](int kq) { return run(kq, kh, ks_g); });
+        tile_load_lds_runs<D, GT>(smem[buf][grp][1], gt, [&](int kq) { return run(kq, vh, vs_g); });
+      } else {
+        const int64_t r0 = static_cast<int64_t>(t - n_hist) * kTile * D;
+        tile_load_lds_rows<D, GT>(smem[buf][grp][0], gt, ks_g + r0);
+        tile_load_lds_rows<D, GT>(smem[buf][grp][1], gt, vs_g + r0);
       }
-      return (which ? vs_g : ks_g) + static_cast<int64_t>((t - n_hist) * kTile + kq * 4) * D;
     };
+
+    issue_tile(grp, 0);
 
     bf16x8 qreg[NKS], goreg[NKS];
     {
@@ -180,21 +197,13 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
 
-    TileRegs<D, GT> kr, vr;
-    kr.load(gtid, [&](int kq) { return rowptr(grp, kq, 0); });
-    vr.load(gtid, [&](int kq) { return rowptr(grp, kq, 1); });
-    kr.store_rows(gtid, smem[0][grp], KS);
-    vr.store_rows(gtid, smem[0][grp] + kTile * KS, VS);
+    wait_vmem();
     __syncthreads();
 
     for (int it = 0; it < n_iter; ++it) {
       const int cur = it & 1;
       const int t = 2 * it + grp;
-      const bool more = it + 1 < n_iter;
-      if (more) {
-        kr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 0); });
-        vr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 1); });
-      }
+      if (it + 1 < n_iter) issue_tile(t + 2, cur ^ 1);
       if (t < n_tiles) {
         uint32_t gmask = 0xffu;
         int mode = 0;
@@ -204,20 +213,34 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
         } else if (t - n_hist == b) {
           mode = 2;
         }
-        const uint16_t* kbuf = smem[cur][grp];
-        const uint16_t* vbuf = kbuf + kTile * KS;
+        const uint16_t* kbuf = smem[cur][grp][0];
+        const uint16_t* vbuf = smem[cur][grp][1];
+        // the swizzled LDS offsets derive from the lane id; an opaque copy per
+        // tile keeps the compiler from hoisting all of them into live registers
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {   // one 32-key subtile at a time
           f32x16 sacc, pacc;
 #pragma unroll
           for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
+          bf16x8 ka = lds_a_row_swz<D>(kbuf, kt * 32, 0, ln);
+          bf16x8 va = lds_a_row_swz<D>(vbuf, kt * 32, 0, ln);
 #pragma unroll
           for (int s = 0; s < NKS; ++s) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kbuf[(kt * 32 + l32) * KS + s * 16 + hh * 8]);
+            bf16x8 kn = ka, vn = va;
+            if (s + 1 < NKS) {
+              kn = lds_a_row_swz<D>(kbuf, kt * 32, (s + 1) * 16, ln);
+              vn = lds_a_row_swz<D>(vbuf, kt * 32, (s + 1) * 16, ln);
+            }
             sacc = mfma32(ka, qreg[s], sacc);
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(&vbuf[(kt * 32 + l32) * VS + s * 16 + hh * 8]);
             pacc = mfma32(va, goreg[s], pacc);
+            ka = kn;
+            va = vn;
+            __builtin_amdgcn_sched_barrier(0);
           }
+          bf16x8 a0 = lds_a_tr_swz<D>(kbuf, kt * 32, 0, ln);
+          bf16x8 a1 = lds_a_tr_swz<D>(kbuf, kt * 32 + 16, 0, ln);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             float pr = fast_exp2(fmaf(sacc[v], c2, -lse2));
@@ -233,27 +256,38 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
           const bf16x8 ds1 = acc_to_bf16x8(sacc, 8);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            acc[dt] = mfma32(lds_a_tr(kbuf, KS, kt * 32, dt * 32, lane), ds0, acc[dt]);
-            acc[dt] = mfma32(lds_a_tr(kbuf, KS, kt * 32 + 16, dt * 32, lane), ds1, acc[dt]);
+            bf16x8 n0 = a0, n1 = a1;
+            if (dt + 1 < NDT) {
+              n0 = lds_a_tr_swz<D>(kbuf, kt * 32, (dt + 1) * 32, ln);
+              n1 = lds_a_tr_swz<D>(kbuf, kt * 32 + 16, (dt + 1) * 32, ln);
+            }
+            acc[dt] = mfma32(a0, ds0, acc[dt]);
+            acc[dt] = mfma32(a1, ds1, acc[dt]);
+            a0 = n0;
+            a1 = n1;
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
-      if (more) {
-        kr.store_rows(gtid, smem[cur ^ 1][grp], KS);
-        vr.store_rows(gtid, smem[cur ^ 1][grp] + kTile * KS, VS);
-      }
+      wait_vmem();
       __syncthreads();
     }
 
     // ---- sum the two parity partials (group 0 + group 1), write dQ ----------
-    float* xch = reinterpret_cast<float*>(&smem[0][0][0]);
+    // exchange layout [wave][4-float column][lane][4]: a wave's b128 accesses
+    // cover 1 KiB contiguously (no bank conflicts)
+    float* xch = reinterpret_cast<float*>(&smem[0][0][0][0]);
     constexpr int XW = NDT * 16;
-    float* mine = xch + (static_cast<int64_t>(gw) * kWave + lane) * XW;
+    auto xaddr = [&](int idx) -> float* {
+      return xch + ((static_cast<int64_t>(gw) * (XW / 4) + idx / 4) * kWave + lane) * 4;
+    };
     if (grp == 1) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mine[dt * 16 + v] = acc[dt][v];
+        for (int v = 0; v < 16; v += 4)
+          *reinterpret_cast<float4*>(xaddr(dt * 16 + v)) =
+              make_float4(acc[dt][v], acc[dt][v + 1], acc[dt][v + 2], acc[dt][v + 3]);
     }
     __syncthreads();
     if (grp == 0) {
@@ -263,9 +297,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = dt * 32 + 8 * g + 4 * hh;
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = (acc[dt][4 * g + e] + mine[dt * 16 + 4 * g + e]) * p.scale;
+          const float4 o = *reinterpret_cast<const float4*>(xaddr(dt * 16 + 4 * g));
+          const float x[4] = {(acc[dt][4 * g] + o.x) * p.scale, (acc[dt][4 * g + 1] + o.y) * p.scale,
+                              (acc[dt][4 * g + 2] + o.z) * p.scale, (acc[dt][4 * g + 3] + o.w) * p.scale};
           uint2 w2;
           w2.x = cvt_pk_bf16(x[0], x[1]);
           w2.y = cvt_pk_bf16(x[2], x[3]);
@@ -429,24 +463,39 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
     }
 
     // ---- sum over the heads of the group (fixed order), then write ----------
+    // exchange layout [slot][4-float column][lane][4]: b128 accesses of a wave
+    // cover 1 KiB contiguously (no bank conflicts)
     float* xch = reinterpret_cast<float*>(&smem[0][0][0][0]);
-    constexpr int XW = NDT * 32;
+    constexpr int XW = NDT * 32;            // floats per lane: dK then dV
+    auto xaddr = [&](int slot, int idx) -> float* {
+      return xch + ((static_cast<int64_t>(slot) * (XW / 4) + idx / 4) * kWave + lane) * 4;
+    };
     if (HPW > 1) {
       if (g > 0) {
-        float* mine = xch + ((static_cast<int64_t>(g - 1) * 2 + ks) * kWave + lane) * XW;
+        const int slot = (g - 1) * 2 + ks;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) { mine[dt * 32 + v] = dk[dt][v]; mine[dt * 32 + 16 + v] = dv[dt][v]; }
+          for (int v = 0; v < 16; v += 4) {
+            *reinterpret_cast<float4*>(xaddr(slot, dt * 32 + v)) =
+                make_float4(dk[dt][v], dk[dt][v + 1], dk[dt][v + 2], dk[dt][v + 3]);
+            *reinterpret_cast<float4*>(xaddr(slot, dt * 32 + 16 + v)) =
+                make_float4(dv[dt][v], dv[dt][v + 1], dv[dt][v + 2], dv[dt][v + 3]);
+          }
       }
       __syncthreads();
       if (g == 0) {
         for (int h = 1; h < HPW; ++h) {
-          const float* other = xch + ((static_cast<int64_t>(h - 1) * 2 + ks) * kWave + lane) * XW;
+          const int slot = (h - 1) * 2 + ks;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) { dk[dt][v] += other[dt * 32 + v]; dv[dt][v] += other[dt * 32 + 16 + v]; }
+            for (int v = 0; v < 16; v += 4) {
+              const float4 a = *reinterpret_cast<const float4*>(xaddr(slot, dt * 32 + v));
+              const float4 c = *reinterpret_cast<const float4*>(xaddr(slot, dt * 32 + 16 + v));
+              dk[dt][v] += a.x; dk[dt][v + 1] += a.y; dk[dt][v + 2] += a.z; dk[dt][v + 3] += a.w;
+              dv[dt][v] += c.x; dv[dt][v + 1] += c.y; dv[dt][v + 2] += c.z; dv[dt][v + 3] += c.w;
+            }
         }
       }
     }

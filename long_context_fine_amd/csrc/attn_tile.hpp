@@ -187,66 +187,76 @@ struct TileRegs {
   }
 };
 
-// Loads one 64 x D bf16 tile straight from global memory into a swizzled LDS
-// tile (Swz<D>) with global_load_lds_dwordx4: each wave instruction fills 1 KiB
-// of LDS (lane i -> 16-byte position i), so lane i fetches the global chunk
-// that the swizzle places at its position. No registers, no LDS store
-// instructions; completion is tracked by vmcnt (wait before the barrier).
-// rowptr(r) must return a readable row for every r in 0..63 (masked rows may
-// point anywhere valid: their values are never used unmasked).
-template <int D, int NT, class RowPtr>
-__device__ __forceinline__ void tile_load_lds(uint16_t* lds_tile, int tid, RowPtr rowptr) {
-  constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int CHUNKS = kTile * CPR;
-  const int wave = tid / kWave, lane = tid % kWave;
-#pragma unroll
-  for (int i0 = 0; i0 < CHUNKS; i0 += NT) {
-    const int i = i0 + wave * kWave;      // first chunk position of this wave instruction
-    if (CHUNKS % NT == 0 || i < CHUNKS) {
-      const int pos = i + lane;
-      const int row = pos / CPR, pc = pos % CPR;
-      const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
-      const uint16_t* src = rowptr(row) + lc * 8;
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(src),
-          (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(lds_tile + i * 8)), 16,
-          0, 0);
-    }
-  }
+// Global-to-LDS copies (global_load_lds): lane i of the wave copies `size`
+// bytes from sbase + voff to LDS address M0 + size * i. They are issued from
+// inline asm because the compiler, when it sees such a copy pending, waits for
+// every outstanding LDS read (lgkmcnt(0)) and for the copy itself (vmcnt(0))
+// before later LDS reads it cannot prove disjoint, which serializes the
+// pipeline. The instructions have no register outputs; M0 is used by nothing
+// else in these kernels. Callers wait with wait_vmem() and a workgroup
+// barrier before any wave reads the LDS they fill, and issue them only into a
+// buffer no wave is reading.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+// The base address must be the same on every lane; it is moved to SGPRs.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ void dma_b128(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
+               "s"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory");
+}
+__device__ __forceinline__ void dma_b32(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
+               "s"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory");
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// tile_load_lds for a tile whose 64 rows are contiguous in global memory
-// (row stride D): the per-lane source offset takes only 4 distinct values, so
-// every instruction is a scalar base plus a precomputed lane offset.
-template <int D, int NT>
-__device__ __forceinline__ void tile_load_lds_rows(uint16_t* lds_tile, int tid, const uint16_t* src) {
+
+// Loads a 64 x D bf16 tile straight from global memory into the swizzled LDS
+// layout of Swz<D>, 16 bytes per lane, no registers held. The tile is made of
+// runs of RPI = 64 / (D / 8) rows that are contiguous in global memory (one
+// wave instruction per run); run(kq) returns the first row of rows
+// RPI*kq .. RPI*kq + RPI - 1 and must be the same on every lane. The lane
+// offsets inside a run take at most 4 distinct values.
+template <int D, int NT, class RunPtr>
+__device__ __forceinline__ void tile_load_lds_runs(uint16_t* lds_tile, int tid, RunPtr run) {
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;          // rows per wave instruction (4 for D = 128)
   constexpr int CHUNKS = kTile * CPR;
   const int wave = tid / kWave, lane = tid % kWave;
   const int lrow = lane / CPR, pc = lane % CPR;
+  const uint32_t base = lds_addr(lds_tile);
 #pragma unroll
   for (int i0 = 0; i0 < CHUNKS; i0 += NT) {
     const int i = i0 + wave * kWave;        // first chunk position of this wave instruction
     if (CHUNKS % NT == 0 || i < CHUNKS) {
-      const int row = i / CPR + lrow;
+      const int kq = i / kWave;
+      const int row = kq * RPI + lrow;
       const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(src + row * D + lc * 8),
-          (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(lds_tile + i * 8)), 16,
-          0, 0);
+      const uint32_t voff = static_cast<uint32_t>((lrow * D + lc * 8) * 2);
+      dma_b128(voff, run(kq), base + i * 16);
     }
   }
-  (void)RPI;
+}
+
+// tile_load_lds_runs for a tile whose 64 rows are contiguous (row stride D).
+template <int D, int NT>
+__device__ __forceinline__ void tile_load_lds_rows(uint16_t* lds_tile, int tid, const uint16_t* src) {
+  constexpr int RPI = kWave / (D / 8);
+  tile_load_lds_runs<D, NT>(lds_tile, tid, [&](int kq) { return src + kq * RPI * D; });
 }
 
 // 64 consecutive floats from global memory into LDS (one wave instruction).
 __device__ __forceinline__ void row64_load_lds(float* lds_dst, const float* src, int lane) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + lane),
-                                   (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(lds_dst)),
-                                   4, 0, 0);
+  dma_b32(static_cast<uint32_t>(lane * 4), src, lds_addr(lds_dst));
 }
 
 // Builds, in LDS, the list of history tiles (8 selected groups each) that hold
