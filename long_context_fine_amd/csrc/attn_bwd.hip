@@ -322,8 +322,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
 // (ds_read_b64_tr_b16). Q/dO tiles (XOR-swizzled, so row reads and transposed
 // reads are both conflict-free) and LSE/Dvec go straight from global memory
 // into the other half of a double-buffered LDS stage (global_load_lds) while
-// the current one is used; LDS operands are read one k-step ahead of their
-// MFMAs. Head partials are summed in LDS; with more than one head group per
+// the current one is used, one copy instruction per S/dP k-step; LDS operands
+// are read one k-step ahead of their MFMAs. Head partials are summed in LDS; with more than one head group per
 // KV head each workgroup writes an fp32 partial that dkdv_reduce_kernel sums
 // in a fixed order.
 template <int D, int HPW>
@@ -354,16 +354,29 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
   const uint16_t* qg = static_cast<const uint16_t*>(p.q);
   const uint16_t* gg = static_cast<const uint16_t*>(p.d_o);
 
-  // issue the loads of query block qb (all HPW heads) into LDS stage buf
+  // Copies of query block qb (Q and dO tiles of the HPW heads, LSE, Dvec) into
+  // LDS stage buf, as NDMA single wave instructions: copy k (0 <= k < NDMA)
+  // is instruction k % IPT of tile k / IPT (tile = head * 2 + {Q, dO}); LSE
+  // and Dvec ride with copy 0.
+  constexpr int IPT = tile_lds_instrs<D, NT>();
+  constexpr int NDMA = 2 * HPW * IPT;
+  static_assert(NDMA <= 2 * NKS, "one copy per S/dP k-step");
+  auto issue_copy = [&](int qb, int buf, int k) {
+    const int tile = k / IPT, h = tile / 2;
+    const int64_t row0 = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ;
+    tile_load_lds_rows_part<D, NT>(smem[buf][h][tile % 2], tid, (tile % 2 ? gg : qg) + row0 * D, k % IPT);
+    if (k == 0) {
+#pragma unroll
+      for (int hh2 = 0; hh2 < HPW; ++hh2) {
+        const int64_t r0 = static_cast<int64_t>(j * p.r + hg * HPW + hh2) * p.seg_len + qb * kBlockQ;
+        if (wave == 0) row64_load_lds(lse_s[buf][hh2], p.lse + r0, lane);
+        if (wave == 1) row64_load_lds(dvec_s[buf][hh2], p.dvec + r0, lane);
+      }
+    }
+  };
   auto issue_block = [&](int qb, int buf) {
 #pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      const int64_t row0 = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ;
-      tile_load_lds_rows<D, NT>(smem[buf][h][0], tid, qg + row0 * D);
-      tile_load_lds_rows<D, NT>(smem[buf][h][1], tid, gg + row0 * D);
-      if (wave == 0) row64_load_lds(lse_s[buf][h], p.lse + row0, lane);
-      if (wave == 1) row64_load_lds(dvec_s[buf][h], p.dvec + row0, lane);
-    }
+    for (int k = 0; k < NDMA; ++k) issue_copy(qb, buf, k);
   };
 
   for (int half = 0; half < 2; ++half) {
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
     __syncthreads();
     for (int qb = kt; qb < n_blocks; ++qb) {
       const int cur = (qb - kt) & 1;
-      if (qb + 1 < n_blocks) issue_block(qb + 1, cur ^ 1);
+      const bool more = qb + 1 < n_blocks;
       const uint16_t* Qs = smem[cur][g][0];
       const uint16_t* Gs = smem[cur][g][1];
       const float* lse_b = lse_s[cur][g];
@@ -409,6 +422,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
             qn = lds_a_row_swz<D>(Qs, qs * 32, (s + 1) * 16, lane);
             gn = lds_a_row_swz<D>(Gs, qs * 32, (s + 1) * 16, lane);
           }
+          if (more && qs * NKS + s < NDMA) issue_copy(qb + 1, cur ^ 1, qs * NKS + s);
           sacc = mfma32(qa, kreg[s], sacc);
           pacc = mfma32(ga, vreg[s], pacc);
           qa = qn;

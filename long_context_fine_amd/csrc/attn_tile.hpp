@@ -254,6 +254,30 @@ __device__ __forceinline__ void tile_load_lds_rows(uint16_t* lds_tile, int tid, 
   tile_load_lds_runs<D, NT>(lds_tile, tid, [&](int kq) { return src + kq * RPI * D; });
 }
 
+// Number of wave instructions one workgroup of NT threads needs per tile.
+template <int D, int NT>
+constexpr int tile_lds_instrs() { return (kTile * (D / 8) + NT - 1) / NT; }
+
+// Instruction `part` (0 .. tile_lds_instrs - 1) of tile_load_lds_rows alone, so
+// that a tile's copies can be spread between MFMAs: a wave that issues many
+// global_load_lds back to back stalls once the memory pipeline's queue fills.
+template <int D, int NT>
+__device__ __forceinline__ void tile_load_lds_rows_part(uint16_t* lds_tile, int tid, const uint16_t* src,
+                                                        int part) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = kWave / CPR;
+  constexpr int CHUNKS = kTile * CPR;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int lrow = lane / CPR, pc = lane % CPR;
+  const int i = part * NT + wave * kWave;
+  if (CHUNKS % NT == 0 || i < CHUNKS) {
+    const int kq = i / kWave;
+    const int row = kq * RPI + lrow;
+    const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
+    dma_b128(static_cast<uint32_t>((lrow * D + lc * 8) * 2), src + kq * RPI * D, lds_addr(lds_tile) + i * 16);
+  }
+}
+
 // 64 consecutive floats from global memory into LDS (one wave instruction).
 __device__ __forceinline__ void row64_load_lds(float* lds_dst, const float* src, int lane) {
   dma_b32(static_cast<uint32_t>(lane * 4), src, lds_addr(lds_dst));
