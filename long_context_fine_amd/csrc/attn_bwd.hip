@@ -96,6 +96,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   constexpr int NKS = D / 16;
   constexpr int TILE = kTile * D;
   constexpr int RPI = kWave / (D / 8);   // rows per global_load_lds run
+  constexpr int IPT = tile_lds_instrs<D, GT>();
+  constexpr int NDMA = 2 * IPT;          // copy instructions per K/V tile pair
+  static_assert(NDMA <= 2 * (D / 16), "one copy per S/dP k-step");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][2][TILE];  // [buffer][parity][K, V]
   __shared__ int32_t sel_s[kMaxTopKGroups];
   __shared__ int32_t hlist[kMaxTopKGroups / 8];
@@ -140,28 +143,33 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
     const int64_t row_off = static_cast<int64_t>(head) * p.seg_len + q_tok;
 
     // K and V of tile t (history tiles first, then segment tiles 0..b) into
-    // LDS buffer buf of this parity group. A history slot without a group
-    // (-1 or past k_g) loads the segment's first rows instead: finite values
-    // whose probabilities are forced to zero.
-    auto issue_tile = [&](int t, int buf) {
-      if (t >= n_tiles) return;
-      int gt = gtid;
+    // LDS buffer buf of this parity group, as NDMA single wave instructions
+    // (copy k: instruction k % IPT of the K (k < IPT) or V tile). A history
+    // slot without a group (-1 or past k_g) loads the segment's first rows
+    // instead: finite values whose probabilities are forced to zero.
+    auto issue_copy = [&](int t, int buf, int k) {
+      int gt = gtid;                 // opaque: keeps lane offsets out of live registers
       asm volatile("" : "+v"(gt));
+      const int which = k / IPT, part = k % IPT;
+      const uint16_t* seg = which ? vs_g : ks_g;
       if (t < n_hist) {
         const int ht = hlist[t];
-        auto run = [&](int kq, const uint16_t* base, const uint16_t* seg) -> const uint16_t* {
+        const uint16_t* base = which ? vh : kh;
+        tile_load_lds_runs_part<D, GT>(smem[buf][grp][which], gt, [&](int kq) -> const uint16_t* {
           const int slot = ht * 8 + (kq * RPI) / kGroup;
           const int n = slot < p.k_g ? sel_s[slot] : -1;
           const int sub = (kq * RPI) % kGroup;
           return n >= 0 ? base + (static_cast<int64_t>(n) * kGroup + sub) * D : seg + sub * D;
-        };
-        tile_load_lds_runs<D, GT>(smem[buf][grp][0], gt, [&](int kq) { return run(kq, kh, ks_g); });
-        tile_load_lds_runs<D, GT>(smem[buf][grp][1], gt, [&](int kq) { return run(kq, vh, vs_g); });
+        }, part);
       } else {
-        const int64_t r0 = static_cast<int64_t>(t - n_hist) * kTile * D;
-        tile_load_lds_rows<D, GT>(smem[buf][grp][0], gt, ks_g + r0);
-        tile_load_lds_rows<D, GT>(smem[buf][grp][1], gt, vs_g + r0);
+        tile_load_lds_rows_part<D, GT>(smem[buf][grp][which], gt,
+                                       seg + static_cast<int64_t>(t - n_hist) * kTile * D, part);
       }
+    };
+    auto issue_tile = [&](int t, int buf) {
+      if (t >= n_tiles) return;
+#pragma unroll
+      for (int k = 0; k < NDMA; ++k) issue_copy(t, buf, k);
     };
 
     issue_tile(grp, 0);
@@ -203,16 +211,32 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
     for (int it = 0; it < n_iter; ++it) {
       const int cur = it & 1;
       const int t = 2 * it + grp;
-      if (it + 1 < n_iter) issue_tile(t + 2, cur ^ 1);
+      const bool more = it + 1 < n_iter && t + 2 < n_tiles;
       if (t < n_tiles) {
-        uint32_t gmask = 0xffu;
-        int mode = 0;
+        // keep: bit kt*16 + v set if accumulator element v of subtile kt (key
+        // kt*32 + 8*(v/4) + 4*hh + v%4 of the tile) takes part; all ones
+        // except on a history tile with empty slots or the diagonal tile
+        uint32_t keep = 0xffffffffu;
         if (t < n_hist) {
-          gmask = hist_group_mask(sel_s, p.k_g, hlist[t]);
-          mode = gmask == 0xffu ? 0 : 1;
+          const uint32_t gm = hist_group_mask(sel_s, p.k_g, hlist[t]);
+#pragma unroll
+          for (int gi = 0; gi < 8; ++gi)
+            if (!((gm >> gi) & 1u)) keep &= ~(0xfu << (4 * gi));
         } else if (t - n_hist == b) {
-          mode = 2;
+          // causal: key <= query row r; per subtile the kept elements are a
+          // prefix of v (keys rise with v): n = sum_g clamp(x - 8g + 1, 0, 4)
+          keep = 0u;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const int x = qrow0 + l32 - kt * 32 - 4 * hh;
+            int n = 0;
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) n += min(max(x - 8 * gi + 1, 0), 4);
+            keep |= static_cast<uint32_t>((1ull << n) - 1ull) << (16 * kt);
+          }
         }
+        const bool masked = __builtin_amdgcn_readfirstlane(keep == 0xffffffffu ? 0 : 1) != 0 ||
+                            t - n_hist == b;
         const uint16_t* kbuf = smem[cur][grp][0];
         const uint16_t* vbuf = smem[cur][grp][1];
         // the swizzled LDS offsets derive from the lane id; an opaque copy per
@@ -233,6 +257,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
               kn = lds_a_row_swz<D>(kbuf, kt * 32, (s + 1) * 16, ln);
               vn = lds_a_row_swz<D>(vbuf, kt * 32, (s + 1) * 16, ln);
             }
+            if (more && kt * NKS + s < NDMA) issue_copy(t + 2, cur ^ 1, kt * NKS + s);
             sacc = mfma32(ka, qreg[s], sacc);
             pacc = mfma32(va, goreg[s], pacc);
             ka = kn;
@@ -241,16 +266,16 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
           }
           bf16x8 a0 = lds_a_tr_swz<D>(kbuf, kt * 32, 0, ln);
           bf16x8 a1 = lds_a_tr_swz<D>(kbuf, kt * 32 + 16, 0, ln);
+          if (masked) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            float pr = fast_exp2(fmaf(sacc[v], c2, -lse2));
-            if (mode == 1) {
-              if (!((gmask >> (kt * 4 + v / 4)) & 1u)) pr = 0.f;
-            } else if (mode == 2) {
-              const int kk = kt * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
-              pr = kk > qrow0 + l32 ? 0.f : pr;
+            for (int v = 0; v < 16; ++v) {
+              float pr = fast_exp2(fmaf(sacc[v], c2, -lse2));
+              pr = (keep >> (kt * 16 + v)) & 1u ? pr : 0.f;
+              sacc[v] = pr * (pacc[v] - drow);
             }
-            sacc[v] = pr * (pacc[v] - drow);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[v] = fast_exp2(fmaf(sacc[v], c2, -lse2)) * (pacc[v] - drow);
           }
           const bf16x8 ds0 = acc_to_bf16x8(sacc, 0);
           const bf16x8 ds1 = acc_to_bf16x8(sacc, 8);
@@ -310,7 +335,6 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   }
 }
 
-// ---------------------------------------------------------------------------
 // bf16: dK, dV of the active segment
 // ---------------------------------------------------------------------------
 // Workgroup = (KV head j, pair of 64-key segment tiles {kt, n-1-kt}, group of

@@ -193,7 +193,8 @@ struct TileRegs {
 // every outstanding LDS read (lgkmcnt(0)) and for the copy itself (vmcnt(0))
 // before later LDS reads it cannot prove disjoint, which serializes the
 // pipeline. The instructions have no register outputs; M0 is used by nothing
-// else in these kernels. Callers wait with wait_vmem() and a workgroup
+// else in these kernels; one wait state separates the M0 write from the copy
+// that reads it. Callers wait with wait_vmem() and a workgroup
 // barrier before any wave reads the LDS they fill, and issue them only into a
 // buffer no wave is reading.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -207,12 +208,12 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 __device__ __forceinline__ void dma_b128(uint32_t voff, const void* sbase, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
                "s"(__builtin_amdgcn_readfirstlane(m0))
                : "memory");
 }
 __device__ __forceinline__ void dma_b32(uint32_t voff, const void* sbase, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
                "s"(__builtin_amdgcn_readfirstlane(m0))
                : "memory");
 }
@@ -244,6 +245,23 @@ __device__ __forceinline__ void tile_load_lds_runs(uint16_t* lds_tile, int tid, 
       const uint32_t voff = static_cast<uint32_t>((lrow * D + lc * 8) * 2);
       dma_b128(voff, run(kq), base + i * 16);
     }
+  }
+}
+
+// Instruction `part` of tile_load_lds_runs alone (see tile_load_lds_rows_part).
+template <int D, int NT, class RunPtr>
+__device__ __forceinline__ void tile_load_lds_runs_part(uint16_t* lds_tile, int tid, RunPtr run, int part) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = kWave / CPR;
+  constexpr int CHUNKS = kTile * CPR;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int lrow = lane / CPR, pc = lane % CPR;
+  const int i = part * NT + wave * kWave;
+  if (CHUNKS % NT == 0 || i < CHUNKS) {
+    const int kq = i / kWave;
+    const int row = kq * RPI + lrow;
+    const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
+    dma_b128(static_cast<uint32_t>((lrow * D + lc * 8) * 2), run(kq), lds_addr(lds_tile) + i * 16);
   }
 }
 
