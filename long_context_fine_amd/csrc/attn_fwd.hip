@@ -19,6 +19,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;
 
 struct FwdParams {
   const void* q;
@@ -134,19 +135,20 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
     const int64_t staged_row0 =
         (static_cast<int64_t>(b - p.block_begin) * p.n_kv + j) * static_cast<int64_t>(p.k_g) * kGroup;
 
-    // rows 4kq..4kq+3 of tile t, for K (which=0) or V (which=1); nullptr = zeros
+    // rows 4kq..4kq+3 of tile t < n_tiles, for K (which=0) or V (which=1). A
+    // history slot without a group (-1 or past k_g) reads the segment's first
+    // rows instead: finite values whose scores are masked to -inf.
     auto rowptr = [&](int t, int kq, int which) -> const uint16_t* {
-      if (t >= n_tiles) return nullptr;
+      const uint16_t* seg = which ? vs_g : ks_g;
       if (t < n_hist) {
         const int slot = hlist[t] * 8 + kq / 2;
-        if (slot >= p.k_g) return nullptr;
-        const int n = sel_s[slot];
-        if (n < 0) return nullptr;
+        const int n = slot < p.k_g ? sel_s[slot] : -1;
+        if (n < 0) return seg + (kq % 2) * 4 * D;
         if (kst) return (which ? vst : kst) + (staged_row0 + slot * kGroup + (kq % 2) * 4) * D;
         return (which ? vh : kh) +
                (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup + (kq % 2) * 4) * D;
       }
-      return (which ? vs_g : ks_g) + static_cast<int64_t>((t - n_hist) * kTile + kq * 4) * D;
+      return seg + static_cast<int64_t>((t - n_hist) * kTile + kq * 4) * D;
     };
 
     bf16x8 qreg[NKS];
@@ -164,30 +166,47 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
     float l_run = 0.f;        // partial row sum over this lane's keys
 
     TileRegs<D, GT> kr, vr;
-    kr.load(gtid, [&](int kq) { return rowptr(grp, kq, 0); });
-    vr.load(gtid, [&](int kq) { return rowptr(grp, kq, 1); });
-    kr.store_rows(gtid, smem[0][grp], KS);
-    vr.store_rows(gtid, smem[0][grp] + kTile * KS, VS);
+    if (grp < n_tiles) {
+      kr.load(gtid, [&](int kq) { return rowptr(grp, kq, 0); });
+      vr.load(gtid, [&](int kq) { return rowptr(grp, kq, 1); });
+      kr.store_rows(gtid, smem[0][grp], KS);
+      vr.store_rows(gtid, smem[0][grp] + kTile * KS, VS);
+    }
     __syncthreads();
 
     for (int it = 0; it < n_iter; ++it) {
       const int cur = it & 1;
       const int t = 2 * it + grp;          // this group's tile
-      const bool more = it + 1 < n_iter;
+      const bool more = it + 1 < n_iter && t + 2 < n_tiles;
       if (more) {
         kr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 0); });
         vr.load(gtid, [&](int kq) { return rowptr(t + 2, kq, 1); });
       }
       if (t < n_tiles) {
-        // mask mode: 0 none, 1 history groups, 2 causal diagonal
-        uint32_t gmask = 0xffu;
-        int mode = 0;
+        // keep: bit kt*16 + v set if accumulator element v of subtile kt (key
+        // kt*32 + 8*(v/4) + 4*hh + v%4 of the tile) takes part; all ones
+        // except on a history tile with empty slots or the diagonal tile
+        uint32_t keep = 0xffffffffu;
+        const bool diag = t - n_hist == b;
         if (t < n_hist) {
-          gmask = hist_group_mask(sel_s, p.k_g, hlist[t]);
-          mode = gmask == 0xffu ? 0 : 1;
-        } else if (t - n_hist == b) {
-          mode = 2;
+          const uint32_t gm = hist_group_mask(sel_s, p.k_g, hlist[t]);
+#pragma unroll
+          for (int gi = 0; gi < 8; ++gi)
+            if (!((gm >> gi) & 1u)) keep &= ~(0xfu << (4 * gi));
+        } else if (diag) {
+          // causal: key <= query row; per subtile the kept elements are a
+          // prefix of v (keys rise with v): n = sum_g clamp(x - 8g + 1, 0, 4)
+          keep = 0u;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const int x = qrow0 + l32 - kt * 32 - 4 * hh;
+            int n = 0;
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) n += min(max(x - 8 * gi + 1, 0), 4);
+            keep |= static_cast<uint32_t>((1ull << n) - 1ull) << (16 * kt);
+          }
         }
+        const bool masked = diag || __builtin_amdgcn_readfirstlane(keep == 0xffffffffu ? 0 : 1) != 0;
         const uint16_t* kbuf = smem[cur][grp];
         const uint16_t* vbuf = kbuf + kTile * KS;
 
@@ -207,20 +226,12 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
         }
 
         // ---- mask, online softmax (raw scores; scale folded into exp2) ------
-        if (mode == 1) {
+        if (masked) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              if (!((gmask >> (kt * 4 + v / 4)) & 1u)) sacc[kt][v] = -INFINITY;
-        } else if (mode == 2) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int kk = kt * 32 + 8 * (v / 4) + 4 * hh + (v % 4);
-              sacc[kt][v] = kk > qrow0 + l32 ? -INFINITY : sacc[kt][v];
-            }
+              sacc[kt][v] = (keep >> (kt * 16 + v)) & 1u ? sacc[kt][v] : -INFINITY;
         }
         float tmax = sacc[0][0];
 #pragma unroll
@@ -228,9 +239,22 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[kt][v]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        const float m_new = fmaxf(m_run, tmax * c2);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
+        // lazy rescale: the reference max only moves when some row's max
+        // exceeds it by more than kRescaleSlack (log2 units), so most tiles
+        // skip rescaling O; probabilities relative to a stale max stay below
+        // 2^kRescaleSlack and the final division by the row sum is exact
+        const float mt = tmax * c2;
+        if (__any(mt > m_run + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run, mt);
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+        }
+        const float m_new = m_run;
         float psum = 0.f;
         bf16x8 pb[2][2];
 #pragma unroll
@@ -244,13 +268,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
           pb[kt][0] = acc_to_bf16x8(sacc[kt], 0);
           pb[kt][1] = acc_to_bf16x8(sacc[kt], 8);
         }
-        l_run = l_run * alpha + psum;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
-        }
+        l_run += psum;
 
         // ---- O^T += V^T . P^T --------------------------------------------
 #pragma unroll
@@ -269,20 +287,27 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
     }
 
     // ---- merge the two parity states, normalise, write O (bf16) and LSE -----
+    // exchange layout [wave][4-float column][lane][4] (b128 accesses of a wave
+    // cover 1 KiB contiguously, no bank conflicts), then m and l per lane
     float* xch = reinterpret_cast<float*>(&smem[0][0][0]);  // free after the last barrier
-    constexpr int XW = NDT * 16 + 2;                          // floats per lane
-    float* mine = xch + (static_cast<int64_t>(gw) * kWave + lane) * XW;
+    constexpr int XW = NDT * 16;
+    auto xaddr = [&](int idx) -> float* {
+      return xch + ((static_cast<int64_t>(gw) * (XW / 4) + idx / 4) * kWave + lane) * 4;
+    };
+    float* xml = xch + static_cast<int64_t>(2 * HPW) * XW * kWave + (gw * kWave + lane) * 2;
     if (grp == 1) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mine[dt * 16 + v] = oacc[dt][v];
-      mine[NDT * 16] = m_run;
-      mine[NDT * 16 + 1] = l_run;
+        for (int v = 0; v < 16; v += 4)
+          *reinterpret_cast<float4*>(xaddr(dt * 16 + v)) =
+              make_float4(oacc[dt][v], oacc[dt][v + 1], oacc[dt][v + 2], oacc[dt][v + 3]);
+      *reinterpret_cast<float2*>(xml) = make_float2(m_run, l_run);
     }
     __syncthreads();
     if (grp == 0) {
-      const float m1 = mine[NDT * 16], l1 = mine[NDT * 16 + 1];
+      const float2 ml = *reinterpret_cast<const float2*>(xml);
+      const float m1 = ml.x, l1 = ml.y;
       const float m = fmaxf(m_run, m1);
       const float a0 = fast_exp2(m_run - m), a1 = fast_exp2(m1 - m);
       const float l_lane = l_run * a0 + l1 * a1;
@@ -295,9 +320,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = dt * 32 + 8 * g + 4 * hh;
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = oacc[dt][4 * g + e] * s0 + mine[dt * 16 + 4 * g + e] * s1;
+          const float4 x1 = *reinterpret_cast<const float4*>(xaddr(dt * 16 + 4 * g));
+          const float x[4] = {oacc[dt][4 * g] * s0 + x1.x * s1, oacc[dt][4 * g + 1] * s0 + x1.y * s1,
+                              oacc[dt][4 * g + 2] * s0 + x1.z * s1, oacc[dt][4 * g + 3] * s0 + x1.w * s1};
           uint2 w2;
           w2.x = cvt_pk_bf16(x[0], x[1]);
           w2.y = cvt_pk_bf16(x[2], x[3]);
