@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[kt][v]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        tmax = max_xor32(tmax);
         // lazy rescale: the reference max only moves when some row's max
         // exceeds it by more than kRescaleSlack (log2 units), so most tiles
         // skip rescaling O; probabilities relative to a stale max stay below

@@ -110,6 +110,14 @@ __device__ __forceinline__ bf16x8 lds_a_tr_swz(const uint16_t* T, int rbase, int
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(x[i], x[i ^ 32]) on every lane i: v_permlane32_swap exchanges the upper
+// 32 lanes of its first operand with the lower 32 lanes of its second, so with
+// both operands x the two results hold x's lower and upper halves.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // One 64-row x D tile held in registers between its global load and its LDS
 // store. A task is 4 consecutive rows x 8 columns (one 16-byte chunk per row);
 // the 4 rows are contiguous in memory for every tile kind used here.

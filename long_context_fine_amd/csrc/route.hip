@@ -31,6 +31,7 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
   constexpr int RPP = kWave / LPR;       // rows per wave pass
   constexpr int NW = kThreads / kWave;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  static_assert(LPR == 8, "sum8_f32 reduces groups of 8 lanes");
   const int sub = lane % LPR;
   float qr[EPL];
 #pragma unroll
@@ -52,8 +53,7 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
       for (int c = 0; c < EPL / 4; ++c)
         s += v[u][c].x * qr[4 * c] + v[u][c].y * qr[4 * c + 1] + v[u][c].z * qr[4 * c + 2] +
              v[u][c].w * qr[4 * c + 3];
-#pragma unroll
-      for (int msk = LPR / 2; msk >= 1; msk >>= 1) s += __shfl_xor(s, msk, kWave);
+      s = sum8_f32(s);
       const int row = r0 + u * NW * RPP + lane / LPR;
       if (row < n && sub == 0) out[row] = s;
     }
@@ -72,10 +72,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ float part[RG][D + 1];
   __shared__ float qv[D];
   __shared__ float sc_lds[kLdsScores];
-  __shared__ uint64_t wcand[NW][kMaxTopKChunks];
+  __shared__ __attribute__((aligned(16))) uint64_t wcand[NW][kMaxTopKChunks];
   __shared__ int32_t sorted[kMaxTopKChunks];
   __shared__ float gsc[kMaxCand];
-  __shared__ uint64_t gkey[kMaxCand];
+  __shared__ __attribute__((aligned(16))) uint64_t gkey[kMaxCand];
   __shared__ uint64_t wmask[kMaxCand / kWave];
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   // ---- 2. chunk scores ----------------------------------------------------
   float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
   const float* cbase = csum + static_cast<int64_t>(j) * n_chunks * D;
-  score_rows<D, 2>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
+  score_rows<D, 4>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
   __syncthreads();
 
   // ---- 3. chunk top-k: per-wave top-k over strided elements, then merge ---
@@ -131,8 +131,18 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     // t < NW*kc_eff: candidate (wave t / kc_eff, round t % kc_eff)
     if (t < NW * kc_eff) {
       const uint64_t mine = wcand[t / kc_eff][t % kc_eff];
+      // candidates are the first kc_eff slots of each wave's row, read two
+      // keys at a time
       int rank = 0;
-      for (int o = 0; o < NW * kc_eff; ++o) rank += wcand[o / kc_eff][o % kc_eff] > mine;
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const ulonglong2* row = reinterpret_cast<const ulonglong2*>(wcand[w2]);
+#pragma unroll 4
+        for (int o2 = 0; o2 < (kc_eff + 1) / 2; ++o2) {
+          const ulonglong2 c = row[o2];
+          rank += c.x > mine;
+          rank += (2 * o2 + 1 < kc_eff) && c.y > mine;
+        }
+      }
       // keys are unique (index in the low bits); the kc_eff best are all valid
       if (rank < kc_eff) part[0][rank] = __uint_as_float(rank_key_index(mine));
     }
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   // ---- 4. group scores for the 8 groups of every kept chunk ----------------
   const int n_cand = kc_eff * (kChunk / kGroup);
   const float* gbase = gsum + static_cast<int64_t>(j) * n_chunks * (kChunk / kGroup) * D;
-  score_rows<D, 2>(qv, n_cand, [&](int c) {
+  score_rows<D, 4>(qv, n_cand, [&](int c) {
     return gbase + (static_cast<int64_t>(sorted[c / 8]) * 8 + (c % 8)) * D;
   }, gsc);
   __syncthreads();
@@ -165,7 +175,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     if (c < n_cand) {
       const uint64_t kc = gkey[c];
       int beaten = 0;
-      for (int o = 0; o < n_cand; ++o) beaten += gkey[o] > kc;
+      const ulonglong2* g2 = reinterpret_cast<const ulonglong2*>(gkey);
+#pragma unroll 4
+      for (int o2 = 0; o2 < n_cand / 2; ++o2) {   // n_cand = 8 * kc_eff is even
+        const ulonglong2 x = g2[o2];
+        beaten += (x.x > kc) + (x.y > kc);
+      }
       take = beaten < k_g;
     }
     const uint64_t m = __ballot(take);
