@@ -77,6 +77,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ float gsc[kMaxCand];
   __shared__ __attribute__((aligned(16))) uint64_t gkey[kMaxCand];
   __shared__ uint64_t wmask[kMaxCand / kWave];
+  __shared__ int32_t cnt_s[kThreads / 2];
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int b = blockIdx.x, j = blockIdx.y;
@@ -109,18 +110,34 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   // ---- 2. chunk scores ----------------------------------------------------
   float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
   const float* cbase = csum + static_cast<int64_t>(j) * n_chunks * D;
-  score_rows<D, 4>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
+  score_rows<D, 8>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
   __syncthreads();
 
   // ---- 3. chunk top-k: per-wave top-k over strided elements, then merge ---
   const int kc_eff = min(k_c, n_chunks);
   {
+    // keys of this lane's strided share kept in registers across the rounds
+    // when the share is small (the common case), else re-read each round
+    constexpr int kRegKeys = 4;
+    uint64_t keys[kRegKeys];
+#pragma unroll
+    for (int e = 0; e < kRegKeys; ++e) {
+      const int m = wave * kWave + lane + e * kThreads;
+      keys[e] = m < n_chunks ? rank_key(sc[m], static_cast<uint32_t>(m)) : 0ull;
+    }
+    const bool in_regs = n_chunks <= kRegKeys * kThreads;
     uint64_t prev = ~0ull;
     for (int round = 0; round < kc_eff; ++round) {
       uint64_t local = 0;
-      for (int m = wave * kWave + lane; m < n_chunks; m += kThreads) {
-        const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(m));
-        if (k < prev && k > local) local = k;
+      if (in_regs) {
+#pragma unroll
+        for (int e = 0; e < kRegKeys; ++e)
+          if (keys[e] < prev && keys[e] > local) local = keys[e];
+      } else {
+        for (int m = wave * kWave + lane; m < n_chunks; m += kThreads) {
+          const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(m));
+          if (k < prev && k > local) local = k;
+        }
       }
       prev = wave_max_u64(local);      // 0 once this wave has no element left
       if (lane == 0) wcand[wave][round] = prev;
@@ -169,22 +186,46 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __syncthreads();
 
   // ---- 5. group top-k by rank counting, ascending output via ballots ------
-  for (int c0 = 0; c0 < n_cand; c0 += kThreads) {
-    const int c = c0 + t;
-    bool take = false;
+  // rank counts: with at most kThreads/2 candidates two threads share one
+  // candidate, each counting half of the keys
+  const ulonglong2* g2 = reinterpret_cast<const ulonglong2*>(gkey);
+  const int n_pairs = n_cand / 2;           // n_cand = 8 * kc_eff is even
+  if (n_cand <= kThreads / 2) {
+    const int c = t % (kThreads / 2), hlf = t / (kThreads / 2);
+    int beaten = 0;
     if (c < n_cand) {
       const uint64_t kc = gkey[c];
-      int beaten = 0;
-      const ulonglong2* g2 = reinterpret_cast<const ulonglong2*>(gkey);
+      const int o_end = hlf == 0 ? n_pairs / 2 : n_pairs;
 #pragma unroll 4
-      for (int o2 = 0; o2 < n_cand / 2; ++o2) {   // n_cand = 8 * kc_eff is even
+      for (int o2 = hlf == 0 ? 0 : n_pairs / 2; o2 < o_end; ++o2) {
         const ulonglong2 x = g2[o2];
         beaten += (x.x > kc) + (x.y > kc);
       }
-      take = beaten < k_g;
     }
-    const uint64_t m = __ballot(take);
-    if (lane == 0) wmask[(c0 / kWave) + wave] = m;
+    if (hlf == 1) cnt_s[c] = beaten;
+    __syncthreads();
+    if (hlf == 0) {
+      const bool take = c < n_cand && beaten + cnt_s[c] < k_g;
+      const uint64_t m = __ballot(take);
+      if (lane == 0) wmask[wave] = m;
+    }
+  } else {
+    for (int c0 = 0; c0 < n_cand; c0 += kThreads) {
+      const int c = c0 + t;
+      bool take = false;
+      if (c < n_cand) {
+        const uint64_t kc = gkey[c];
+        int beaten = 0;
+#pragma unroll 4
+        for (int o2 = 0; o2 < n_pairs; ++o2) {
+          const ulonglong2 x = g2[o2];
+          beaten += (x.x > kc) + (x.y > kc);
+        }
+        take = beaten < k_g;
+      }
+      const uint64_t m = __ballot(take);
+      if (lane == 0) wmask[(c0 / kWave) + wave] = m;
+    }
   }
   __syncthreads();
   for (int c = t; c < n_cand; c += kThreads) {
