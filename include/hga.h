@@ -172,8 +172,13 @@ typedef enum {
 /* Instrumentation: while set, every launch of `kernel` is bracketed by
  * hipEventRecord(ev_start) / hipEventRecord(ev_stop) on the stream it is
  * launched on, so hipEventElapsedTime gives that kernel's duration (of its
- * most recent launch). Both NULL turns it off. The setting is process-wide and
- * not synchronised between threads; the caller owns the hipEvent_t handles. */
+ * most recent launch). With pinned-host history (HGA_HIST_HOST_PINNED),
+ * hga_attn_fwd runs its gathers and attention in phases and records each pair
+ * once per call instead: GATHER from the first gather to the last on the
+ * library's side stream, ATTN_FWD around the whole forward on the caller's
+ * stream, waits for gathered phases included. Both NULL turns it off. The
+ * setting is process-wide and not synchronised between threads; the caller
+ * owns the hipEvent_t handles. */
 hga_status hga_set_kernel_events(int32_t kernel, void* ev_start, void* ev_stop);
 
 /* Bytes of workspace `op` (an hga_op) needs for this shape; 0 if the shape is

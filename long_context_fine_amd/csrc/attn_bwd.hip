@@ -257,8 +257,11 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
               kn = lds_a_row_swz<D>(kbuf, kt * 32, (s + 1) * 16, ln);
               vn = lds_a_row_swz<D>(vbuf, kt * 32, (s + 1) * 16, ln);
             }
-            if (more && (kt * NKS + s) % 2 == 0 && (kt * NKS + s) / 2 < NDMA)
-              issue_copy(t + 2, cur ^ 1, (kt * NKS + s) / 2);
+            {  // NDMA copies spread evenly over the 2*NKS k-steps, at most one each
+              const int st = kt * NKS + s;
+              const int k_lo = st * NDMA / (2 * NKS), k_hi = (st + 1) * NDMA / (2 * NKS);
+              if (more && k_hi > k_lo) issue_copy(t + 2, cur ^ 1, k_lo);
+            }
             sacc = mfma32(ka, qreg[s], sacc);
             pacc = mfma32(va, goreg[s], pacc);
             ka = kn;

@@ -304,6 +304,11 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   // the side stream must see everything already enqueued on `stream` (sel_groups)
   if ((e = hipEventRecord(r->start, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(r->side, r->start, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  // timers (hga_set_kernel_events) span the whole call: GATHER from the first
+  // gather to the last on the side stream, ATTN_FWD the whole forward on
+  // `stream`, waits for gathered phases included
+  hga::timer_begin(HGA_KERNEL_GATHER, r->side);
+  hga::timer_begin(HGA_KERNEL_ATTN_FWD, st);
   const int n_phases = (n_blocks + kPhaseBlocks - 1) / kPhaseBlocks;
   for (int ph = 0; ph < n_phases; ++ph) {
     const int b0 = ph * kPhaseBlocks;
@@ -311,15 +316,17 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
     const int x = ph % 2;
     if (ph >= 2 && (e = hipStreamWaitEvent(r->side, r->consumed[x], 0)) != hipSuccess)
       return hip_fail(e, "hipStreamWaitEvent");
-    if ((e = hga::launch_gather(s, kd, vd, sel_groups, kbuf[x], vbuf[x], b0, b1, r->side)) != hipSuccess)
+    if ((e = hga::launch_gather(s, kd, vd, sel_groups, kbuf[x], vbuf[x], b0, b1, r->side, false)) != hipSuccess)
       return hip_fail(e, "gather launch");
     if ((e = hipEventRecord(r->gathered[x], r->side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(st, r->gathered[x], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
     if ((e = hga::launch_attn_fwd(s, q, kd, vd, k_seg, v_seg, sel_groups, o, lse, kbuf[x], vbuf[x], b0,
-                                  b1, st)) != hipSuccess)
+                                  b1, st, false)) != hipSuccess)
       return hip_fail(e, "attn_fwd launch");
     if ((e = hipEventRecord(r->consumed[x], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
+  hga::timer_end(HGA_KERNEL_GATHER, r->side);
+  hga::timer_end(HGA_KERNEL_ATTN_FWD, st);
   return ok();
 }
 

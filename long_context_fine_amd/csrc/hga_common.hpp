@@ -131,16 +131,19 @@ hipError_t launch_build_summaries(const hga_shape& s, const void* k_hist, int64_
 hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,
                         const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
                         void* ws, hipStream_t stream);
+// timed = false: the caller records the kernel's timer events itself (around
+// several launches).
 hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_hist,
                          const int32_t* sel_groups, void* k_out, void* v_out,
-                         int32_t block_begin, int32_t block_end, hipStream_t stream);
+                         int32_t block_begin, int32_t block_end, hipStream_t stream,
+                         bool timed = true);
 // staged != nullptr: history rows come from gathered buffers laid out as
 // [n_blocks][n_kv][top_k_groups*8][head_dim] for blocks [block_begin, block_end).
 hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist,
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, void* o, float* lse,
                            const void* k_staged, const void* v_staged, int32_t block_begin,
-                           int32_t block_end, hipStream_t stream);
+                           int32_t block_end, hipStream_t stream, bool timed = true);
 hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist,
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, const void* o, const float* lse,

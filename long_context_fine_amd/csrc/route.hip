@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   {
     // keys of this lane's strided share kept in registers across the rounds
     // when the share is small (the common case), else re-read each round
-    constexpr int kRegKeys = 4;
+    constexpr int kRegKeys = 8;
     uint64_t keys[kRegKeys];
 #pragma unroll
     for (int e = 0; e < kRegKeys; ++e) {
