@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   constexpr int NDT = D / 32;
   constexpr int NKS = D / 16;
   constexpr int TILE = kTile * D;
-  constexpr int RPI = kWave / (D / 8);   // rows per global_load_lds run
+  constexpr uint32_t RPI = kWave / (D / 8);  // rows per global_load_lds run
   constexpr int IPT = tile_lds_instrs<D, GT>();
   constexpr int NDMA = 2 * IPT;          // copy instructions per K/V tile pair
   static_assert(NDMA <= 2 * (D / 16), "one copy per S/dP k-step");
@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   const int grp = wave / (2 * HPW);
   const int gw = wave % (2 * HPW);
   const int gtid = tid % GT;
+  const uint32_t gwave = __builtin_amdgcn_readfirstlane(gtid / kWave);  // wave within the group
   const int n_blocks = p.seg_len / kBlockQ;
   const int n_hg = p.r / HPW;
   int w = blockIdx.x;
@@ -148,22 +149,20 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
     // slot without a group (-1 or past k_g) loads the segment's first rows
     // instead: finite values whose probabilities are forced to zero.
     auto issue_copy = [&](int t, int buf, int k) {
-      int gt = gtid;                 // opaque: keeps lane offsets out of live registers
-      asm volatile("" : "+v"(gt));
       const int which = k / IPT, part = k % IPT;
       const uint16_t* seg = which ? vs_g : ks_g;
       if (t < n_hist) {
-        const int ht = hlist[t];
+        const int ht = __builtin_amdgcn_readfirstlane(hlist[t]);
         const uint16_t* base = which ? vh : kh;
-        tile_load_lds_runs_part<D, GT>(smem[buf][grp][which], gt, [&](int kq) -> const uint16_t* {
-          const int slot = ht * 8 + (kq * RPI) / kGroup;
-          const int n = slot < p.k_g ? sel_s[slot] : -1;
-          const int sub = (kq * RPI) % kGroup;
+        tile_copy_part<D, GT>(smem[buf][grp][which], gwave, lane, [&](uint32_t kq) -> const uint16_t* {
+          const uint32_t slot = static_cast<uint32_t>(ht) * 8u + (kq * RPI) / kGroup;
+          const int n = slot < static_cast<uint32_t>(p.k_g) ? __builtin_amdgcn_readfirstlane(sel_s[slot]) : -1;
+          const uint32_t sub = (kq * RPI) % kGroup;
           return n >= 0 ? base + (static_cast<int64_t>(n) * kGroup + sub) * D : seg + sub * D;
         }, part);
       } else {
-        tile_load_lds_rows_part<D, GT>(smem[buf][grp][which], gt,
-                                       seg + static_cast<int64_t>(t - n_hist) * kTile * D, part);
+        tile_copy_rows_part<D, GT>(smem[buf][grp][which], gwave, lane,
+                                   seg + static_cast<int64_t>(t - n_hist) * kTile * D, part);
       }
     };
     auto issue_tile = [&](int t, int buf) {
@@ -367,6 +366,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int l32 = lane % 32, hh = lane / 32;
   const int ks = wave % 2;       // 32-key subtile
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int g = wave / 2;        // head within the group
   const int n_blocks = p.seg_len / kBlockQ;
   const int n_hg = p.r / HPW;
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
   auto issue_copy = [&](int qb, int buf, int k) {
     const int tile = k / IPT, h = tile / 2;
     const int64_t row0 = static_cast<int64_t>(j * p.r + hg * HPW + h) * p.seg_len + qb * kBlockQ;
-    tile_load_lds_rows_part<D, NT>(smem[buf][h][tile % 2], tid, (tile % 2 ? gg : qg) + row0 * D, k % IPT);
+    tile_copy_rows_part<D, NT>(smem[buf][h][tile % 2], wave_u, lane, (tile % 2 ? gg : qg) + row0 * D, k % IPT);
     if (k == 0) {
 #pragma unroll
       for (int hh2 = 0; hh2 < HPW; ++hh2) {

@@ -79,12 +79,12 @@ __device__ __forceinline__ bf16x8 lds_a_tr(const uint16_t* T, int stride, int rb
 // 64 distinct banks (checked with a bank model of both access patterns).
 template <int D>
 struct Swz {
-  static constexpr int NCH = D / 8;  // chunks per row
-  __device__ __forceinline__ static int f(int row) {
-    return NCH == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : (((row & 3) << 1) | ((row >> 2) & 1));
+  static constexpr uint32_t NCH = D / 8;  // chunks per row
+  __device__ __forceinline__ static uint32_t f(uint32_t row) {
+    return NCH == 16 ? (((row & 3u) << 2) | ((row >> 2) & 3u)) : (((row & 3u) << 1) | ((row >> 2) & 1u));
   }
-  __device__ __forceinline__ static int off(int row, int col) {
-    return row * D + ((((col >> 3) ^ f(row)) & (NCH - 1)) << 3) + (col & 7);
+  __device__ __forceinline__ static uint32_t off(uint32_t row, uint32_t col) {
+    return row * D + ((((col >> 3) ^ f(row)) & (NCH - 1)) << 3) + (col & 7u);
   }
 };
 
@@ -92,15 +92,17 @@ struct Swz {
 // rbase + lane % 32, slots = 8 columns starting at k0 + 8 * (lane / 32).
 template <int D>
 __device__ __forceinline__ bf16x8 lds_a_row_swz(const uint16_t* T, int rbase, int k0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(T + Swz<D>::off(rbase + (lane & 31), k0 + 8 * (lane >> 5)));
+  const uint32_t l = static_cast<uint32_t>(lane);
+  return *reinterpret_cast<const bf16x8*>(
+      T + Swz<D>::off(static_cast<uint32_t>(rbase) + (l & 31u), static_cast<uint32_t>(k0) + 8u * (l >> 5)));
 }
 
 // lds_a_tr for a swizzled tile.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_a_tr_swz(const uint16_t* T, int rbase, int cbase, int lane) {
-  const int g16 = lane >> 4, gl = lane & 15;
-  const int col = cbase + 16 * (g16 & 1) + 4 * (gl & 3);
-  const int row = rbase + 4 * (g16 >> 1) + (gl >> 2);
+  const uint32_t g16 = static_cast<uint32_t>(lane) >> 4, gl = static_cast<uint32_t>(lane) & 15u;
+  const uint32_t col = static_cast<uint32_t>(cbase) + 16u * (g16 & 1u) + 4u * (gl & 3u);
+  const uint32_t row = static_cast<uint32_t>(rbase) + 4u * (g16 >> 1) + (gl >> 2);
   const i16x4 lo = ds_read_tr16(T + Swz<D>::off(row, col));
   const i16x4 hi = ds_read_tr16(T + Swz<D>::off(row + 8, col));
   const uint2 l2 = __builtin_bit_cast(uint2, lo);
@@ -229,79 +231,42 @@ __device__ __forceinline__ void dma_b32(uint32_t voff, const void* sbase, uint32
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 
-// Loads a 64 x D bf16 tile straight from global memory into the swizzled LDS
-// layout of Swz<D>, 16 bytes per lane, no registers held. The tile is made of
-// runs of RPI = 64 / (D / 8) rows that are contiguous in global memory (one
-// wave instruction per run); run(kq) returns the first row of rows
-// RPI*kq .. RPI*kq + RPI - 1 and must be the same on every lane. The lane
-// offsets inside a run take at most 4 distinct values.
-template <int D, int NT, class RunPtr>
-__device__ __forceinline__ void tile_load_lds_runs(uint16_t* lds_tile, int tid, RunPtr run) {
-  constexpr int CPR = D / 8;
-  constexpr int RPI = kWave / CPR;          // rows per wave instruction (4 for D = 128)
-  constexpr int CHUNKS = kTile * CPR;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int lrow = lane / CPR, pc = lane % CPR;
-  const uint32_t base = lds_addr(lds_tile);
-#pragma unroll
-  for (int i0 = 0; i0 < CHUNKS; i0 += NT) {
-    const int i = i0 + wave * kWave;        // first chunk position of this wave instruction
-    if (CHUNKS % NT == 0 || i < CHUNKS) {
-      const int kq = i / kWave;
-      const int row = kq * RPI + lrow;
-      const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
-      const uint32_t voff = static_cast<uint32_t>((lrow * D + lc * 8) * 2);
-      dma_b128(voff, run(kq), base + i * 16);
-    }
-  }
-}
-
-// Instruction `part` of tile_load_lds_runs alone (see tile_load_lds_rows_part).
-template <int D, int NT, class RunPtr>
-__device__ __forceinline__ void tile_load_lds_runs_part(uint16_t* lds_tile, int tid, RunPtr run, int part) {
-  constexpr int CPR = D / 8;
-  constexpr int RPI = kWave / CPR;
-  constexpr int CHUNKS = kTile * CPR;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int lrow = lane / CPR, pc = lane % CPR;
-  const int i = part * NT + wave * kWave;
-  if (CHUNKS % NT == 0 || i < CHUNKS) {
-    const int kq = i / kWave;
-    const int row = kq * RPI + lrow;
-    const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
-    dma_b128(static_cast<uint32_t>((lrow * D + lc * 8) * 2), run(kq), lds_addr(lds_tile) + i * 16);
-  }
-}
-
-// tile_load_lds_runs for a tile whose 64 rows are contiguous (row stride D).
-template <int D, int NT>
-__device__ __forceinline__ void tile_load_lds_rows(uint16_t* lds_tile, int tid, const uint16_t* src) {
-  constexpr int RPI = kWave / (D / 8);
-  tile_load_lds_runs<D, NT>(lds_tile, tid, [&](int kq) { return src + kq * RPI * D; });
-}
-
-// Number of wave instructions one workgroup of NT threads needs per tile.
+// Number of wave instructions a group of NT threads needs to copy one 64 x D
+// bf16 tile (16 bytes per lane per instruction).
 template <int D, int NT>
 constexpr int tile_lds_instrs() { return (kTile * (D / 8) + NT - 1) / NT; }
 
-// Instruction `part` (0 .. tile_lds_instrs - 1) of tile_load_lds_rows alone, so
-// that a tile's copies can be spread between MFMAs: a wave that issues many
-// global_load_lds back to back stalls once the memory pipeline's queue fills.
-template <int D, int NT>
-__device__ __forceinline__ void tile_load_lds_rows_part(uint16_t* lds_tile, int tid, const uint16_t* src,
-                                                        int part) {
-  constexpr int CPR = D / 8;
-  constexpr int RPI = kWave / CPR;
-  constexpr int CHUNKS = kTile * CPR;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int lrow = lane / CPR, pc = lane % CPR;
-  const int i = part * NT + wave * kWave;
+// One wave instruction (`part`, 0 .. tile_lds_instrs - 1) of a copy of a
+// 64 x D bf16 tile straight from global memory into the swizzled LDS layout
+// of Swz<D>, 16 bytes per lane, no registers held. Copies are issued one
+// instruction at a time so they can be spread between MFMAs: a wave that
+// issues many back to back stalls once the memory pipeline's queue fills.
+// The tile is made of runs of RPI = 64 / (D / 8) rows that are contiguous in
+// global memory, one run per instruction; run(kq) returns the first row of
+// rows RPI*kq .. RPI*kq + RPI - 1. `wave` (index within the NT threads) and
+// everything run() returns must be wave-uniform: the source base and LDS
+// address go to SGPRs, only the lane offset (4 distinct values) is per lane.
+template <int D, int NT, class RunPtr>
+__device__ __forceinline__ void tile_copy_part(uint16_t* lds_tile, uint32_t wave, uint32_t lane, RunPtr run,
+                                               int part) {
+  constexpr uint32_t CPR = D / 8;
+  constexpr uint32_t RPI = kWave / CPR;
+  constexpr uint32_t CHUNKS = kTile * CPR;
+  const uint32_t i = static_cast<uint32_t>(part) * NT + wave * kWave;  // first chunk of the instruction
   if (CHUNKS % NT == 0 || i < CHUNKS) {
-    const int kq = i / kWave;
-    const int row = kq * RPI + lrow;
-    const int lc = (pc ^ Swz<D>::f(row)) & (CPR - 1);
-    dma_b128(static_cast<uint32_t>((lrow * D + lc * 8) * 2), src + kq * RPI * D, lds_addr(lds_tile) + i * 16);
+    const uint32_t kq = i / kWave;
+    const uint32_t lrow = lane / CPR, pc = lane % CPR;
+    const uint32_t lc = (pc ^ Swz<D>::f(kq * RPI + lrow)) & (CPR - 1);
+    dma_b128((lrow * D + lc * 8) * 2, run(kq), lds_addr(lds_tile) + i * 16);
   }
+}
+
+// tile_copy_part for a tile whose 64 rows are contiguous (row stride D).
+template <int D, int NT>
+__device__ __forceinline__ void tile_copy_rows_part(uint16_t* lds_tile, uint32_t wave, uint32_t lane,
+                                                    const uint16_t* src, int part) {
+  constexpr uint32_t RPI = kWave / (D / 8);
+  tile_copy_part<D, NT>(lds_tile, wave, lane, [&](uint32_t kq) { return src + kq * RPI * D; }, part);
 }
 
 // 64 consecutive floats from global memory into LDS (one wave instruction).
