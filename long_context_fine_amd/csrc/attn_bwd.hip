@@ -104,12 +104,13 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   __shared__ int32_t hlist[kMaxTopKGroups / 8];
   __shared__ int32_t n_hist_s;
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int l32 = lane % 32, hh = lane / 32;
   const int grp = wave / (2 * HPW);
   const int gw = wave % (2 * HPW);
   const int gtid = tid % GT;
-  const uint32_t gwave = __builtin_amdgcn_readfirstlane(gtid / kWave);  // wave within the group
+  const uint32_t gwave = static_cast<uint32_t>(wave % (2 * HPW));  // wave within the group
   const int n_blocks = p.seg_len / kBlockQ;
   const int n_hg = p.r / HPW;
   int w = blockIdx.x;
@@ -363,10 +364,11 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
   __shared__ __attribute__((aligned(16))) float lse_s[2][HPW][kTile];
   __shared__ __attribute__((aligned(16))) float dvec_s[2][HPW][kTile];
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int l32 = lane % 32, hh = lane / 32;
   const int ks = wave % 2;       // 32-key subtile
-  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t wave_u = static_cast<uint32_t>(wave);
   const int g = wave / 2;        // head within the group
   const int n_blocks = p.seg_len / kBlockQ;
   const int n_hg = p.r / HPW;

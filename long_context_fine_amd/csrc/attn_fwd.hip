@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int l32 = lane % 32;
   const int hh = lane / 32;            // lane half
   const int grp = wave / (2 * HPW);    // tile parity group
