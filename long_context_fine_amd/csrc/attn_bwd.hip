@@ -35,6 +35,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* dvec;
+  float* lse2;       // [n_q][S] LSE * log2(e), written by the bf16 dQ kernel for dK/dV
   float* dkdv_part;  // [n_hg][2][n_kv][S][D] fp32 partials (dK, dV) when n_hg > 1
   int n_q, n_kv, r;
   int seg_len;
@@ -197,7 +198,10 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
         for (int e = 0; e < 8; ++e) drow += static_cast<float>(goreg[s][e]) * static_cast<float>(ov[e]);
       }
       drow += __shfl_xor(drow, 32, kWave);
-      if (grp == 0 && hh == 0) p.dvec[row_off] = drow;
+      if (grp == 0 && hh == 0) {
+        p.dvec[row_off] = drow;
+        p.lse2[row_off] = lse2;
+      }
     }
     f32x16 acc[NDT];
 #pragma unroll
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
   constexpr int NKS = D / 16;
   constexpr int TILE = kTile * D;     // swizzled Q / dO tile (Swz<D>)
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][HPW][2][TILE];  // [buf][head][Q, dO]
-  __shared__ __attribute__((aligned(16))) float lse_s[2][HPW][kTile];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][HPW][kTile];       // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float dvec_s[2][HPW][kTile];
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
 #pragma unroll
       for (int hh2 = 0; hh2 < HPW; ++hh2) {
         const int64_t r0 = static_cast<int64_t>(j * p.r + hg * HPW + hh2) * p.seg_len + qb * kBlockQ;
-        if (wave == 0) row64_load_lds(lse_s[buf][hh2], p.lse + r0, lane);
+        if (wave == 0) row64_load_lds(lse_s[buf][hh2], p.lse2 + r0, lane);
         if (wave == 1) row64_load_lds(dvec_s[buf][hh2], p.dvec + r0, lane);
       }
     }
@@ -467,13 +471,22 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
           const float4 d4 = *reinterpret_cast<const float4*>(&dvec_b[q0]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+          if (diag) {  // causal mask, only on the block that holds the diagonal
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = 4 * r4 + e;
-            float pr = fast_exp2(fmaf(sacc[v], c2, -lv[e] * kLog2e));
-            if (diag && key_local > q0 + e) pr = 0.f;
-            sacc[v] = pr;
-            pacc[v] = pr * (pacc[v] - dvv[e]);
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * r4 + e;
+              const float pr = key_local > q0 + e ? 0.f : fast_exp2(fmaf(sacc[v], c2, -lv[e]));
+              sacc[v] = pr;
+              pacc[v] = pr * (pacc[v] - dvv[e]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * r4 + e;
+              const float pr = fast_exp2(fmaf(sacc[v], c2, -lv[e]));
+              sacc[v] = pr;
+              pacc[v] = pr * (pacc[v] - dvv[e]);
+            }
           }
         }
         const bf16x8 p0 = acc_to_bf16x8(sacc, 0), p1 = acc_to_bf16x8(sacc, 8);
@@ -509,7 +522,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
     // ---- sum over the heads of the group (fixed order), then write ----------
     // exchange layout [slot][4-float column][lane][4]: b128 accesses of a wave
     // cover 1 KiB contiguously (no bank conflicts)
-    float* xch = reinterpret_cast<float*>(&smem[0][0][0][0]);
+    float* xch = reinterpret_cast<float*>(&smem[0][0][0][0]);  // free after the last barrier
     constexpr int XW = NDT * 32;            // floats per lane: dK then dV
     auto xaddr = [&](int slot, int idx) -> float* {
       return xch + ((static_cast<int64_t>(slot) * (XW / 4) + idx / 4) * kWave + lane) * 4;
@@ -766,14 +779,14 @@ hipError_t launch_d(const hga_shape& s, BwdParams& p, hipStream_t st) {
 
 }  // namespace
 
-// Dvec [n_q][S] fp32, then (bf16, more than one head group per KV head) the
-// dK/dV partials [n_hg][2][n_kv][S][D] fp32.
+// Dvec [n_q][S] fp32, LSE*log2(e) [n_q][S] fp32, then (bf16, more than one
+// head group per KV head) the dK/dV partials [n_hg][2][n_kv][S][D] fp32.
 size_t bwd_workspace_bytes(const hga_shape& s) {
-  const size_t dvec = ((sizeof(float) * static_cast<size_t>(s.n_q_heads) * s.seg_len) + 255) & ~size_t(255);
+  const size_t row = ((sizeof(float) * static_cast<size_t>(s.n_q_heads) * s.seg_len) + 255) & ~size_t(255);
   const int r = s.n_q_heads / s.n_kv_heads;
   const int n_hg = r / (r % 2 == 0 ? 2 : 1);
-  if (s.dtype != HGA_BF16 || n_hg <= 1) return dvec;
-  return dvec + sizeof(float) * static_cast<size_t>(n_hg) * 2 * s.n_kv_heads * s.seg_len * s.head_dim;
+  if (s.dtype != HGA_BF16 || n_hg <= 1) return 2 * row;
+  return 2 * row + sizeof(float) * static_cast<size_t>(n_hg) * 2 * s.n_kv_heads * s.seg_len * s.head_dim;
 }
 
 hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist,
@@ -785,9 +798,10 @@ hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist
   p.q = q; p.k_hist = k_hist; p.v_hist = v_hist; p.k_seg = k_seg; p.v_seg = v_seg;
   p.sel = sel_groups; p.o = o; p.lse = lse; p.d_o = d_o;
   p.dq = dq; p.dk = dk_seg; p.dv = dv_seg;
+  const size_t row = ((sizeof(float) * static_cast<size_t>(s.n_q_heads) * s.seg_len) + 255) & ~size_t(255);
   p.dvec = static_cast<float*>(ws);
-  p.dkdv_part = reinterpret_cast<float*>(
-      static_cast<char*>(ws) + (((sizeof(float) * static_cast<size_t>(s.n_q_heads) * s.seg_len) + 255) & ~size_t(255)));
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + row);
+  p.dkdv_part = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row);
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads;
   p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.k_g = s.top_k_groups;
   p.scale = s.softmax_scale;

@@ -97,8 +97,10 @@ def test_workspace_sizes_and_undersized_workspace(L):
     # chunk scores [32][8][224] f32
     assert n_route == 32 * 8 * 224 * 4
     assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_FWD) == 0
-    # Dvec [32][2048] f32 + dK/dV partials of the 2 head groups [2][2][8][2048][128] f32
-    assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_BWD) == 32 * 2048 * 4 + 2 * 2 * 8 * 2048 * 128 * 4
+    # Dvec and LSE*log2(e) [32][2048] f32 each + dK/dV partials of the 2 head groups
+    # [2][2][8][2048][128] f32
+    assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_BWD) == \
+        2 * 32 * 2048 * 4 + 2 * 2 * 8 * 2048 * 128 * 4
     assert L.hga_workspace_size(ctypes.byref(s), 9) == 0
     st = L.hga_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_route - 1, None)
     assert st == hga.HGA_ERR_WORKSPACE
