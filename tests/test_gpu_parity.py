@@ -108,6 +108,9 @@ SMALL = [
     _w("bf16_budget_exceeds_candidates", 4, 1, 128, 512, 128, 2, 20, "bf16"),  # 16 cands, 4 pads
     _w("bf16_no_history", 4, 2, 128, 0, 256, 4, 8, "bf16"),
     _w("bf16_single_chunk", 2, 1, 128, 64, 64, 4, 32, "bf16"),        # k_c, k_g > candidates
+    _w("bf16_gqa_d64", 8, 2, 64, 1024, 256, 4, 16, "bf16"),           # two heads per workgroup, d = 64
+    _w("bf16_mha_d128", 4, 4, 128, 1024, 192, 4, 16, "bf16"),         # one head per workgroup, d = 128
+    _w("bf16_max_budget", 4, 1, 128, 8192, 128, 64, 512, "bf16"),     # largest k_c, k_g: 64 history tiles
 ]
 
 
@@ -115,6 +118,14 @@ SMALL = [
 @pytest.mark.parametrize("seed", [0, 1])
 def test_small_cases_match_oracle(w, seed):
     run_case(w, seed, check_bwd=True)
+
+
+def test_route_with_scores_in_workspace():
+    """More than 4,096 chunks per KV head: chunk scores go to the workspace and
+    the chunk top-k re-reads them each round instead of holding them in
+    registers."""
+    w = _w("bf16_long_history", 2, 1, 64, 4160 * 64, 64, 8, 16, "bf16")
+    run_case(w, 4, check_bwd=True)
 
 
 def test_full_budget_is_dense_attention():
