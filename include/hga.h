@@ -169,16 +169,17 @@ typedef enum {
   HGA_KERNEL_COUNT = 6
 } hga_kernel;
 
-/* Instrumentation: while set, every launch of `kernel` is bracketed by
- * hipEventRecord(ev_start) / hipEventRecord(ev_stop) on the stream it is
- * launched on, so hipEventElapsedTime gives that kernel's duration (of its
- * most recent launch). With pinned-host history (HGA_HIST_HOST_PINNED),
- * hga_attn_fwd runs its gathers and attention in phases and records each pair
- * once per call instead: GATHER from the first gather to the last on the
- * library's side stream, ATTN_FWD around the whole forward on the caller's
- * stream, waits for gathered phases included. Both NULL turns it off. The
+/* Instrumentation: while set, the launches of `kernel` stamp ev_start with
+ * the start of the entry point's first launch of it and ev_stop with the end
+ * of its last (hipExtLaunchKernel timestamps: no extra packets on the
+ * stream), so hipEventElapsedTime gives the duration of the most recent call;
+ * BWD_DKDV includes the fixed-order partial sum. With pinned-host history
+ * (HGA_HIST_HOST_PINNED) hga_attn_fwd runs its gathers and attention in
+ * phases: GATHER then spans the first gather to the last on the library's
+ * side stream and ATTN_FWD the first attention phase to the last on the
+ * caller's stream, waits in between included. Both NULL turns it off. The
  * setting is process-wide and not synchronised between threads; the caller
- * owns the hipEvent_t handles. */
+ * owns the hipEvent_t handles, created with timing enabled. */
 hga_status hga_set_kernel_events(int32_t kernel, void* ev_start, void* ev_stop);
 
 /* Bytes of workspace `op` (an hga_op) needs for this shape; 0 if the shape is

@@ -739,40 +739,38 @@ hipError_t launch_d(const hga_shape& s, BwdParams& p, hipStream_t st) {
   const int64_t n_rows = static_cast<int64_t>(s.n_q_heads) * s.seg_len;
   constexpr int RPB = 256 / (D / 8);
   const unsigned dot_grid = static_cast<unsigned>((n_rows + RPB - 1) / RPB);
+  hipEvent_t dq0 = timer_event(HGA_KERNEL_BWD_DQ, 0), dq1 = timer_event(HGA_KERNEL_BWD_DQ, 1);
+  hipEvent_t kv0 = timer_event(HGA_KERNEL_BWD_DKDV, 0), kv1 = timer_event(HGA_KERNEL_BWD_DKDV, 1);
   if (s.dtype == HGA_F32) {
-    timer_begin(HGA_KERNEL_BWD_DQ, st);
-    hipLaunchKernelGGL((row_dot_kernel<float, D>), dim3(dot_grid), dim3(256), 0, st,
-                       static_cast<const float*>(p.o), static_cast<const float*>(p.d_o), p.dvec, n_rows);
-    hipLaunchKernelGGL((attn_bwd_dq_f32_kernel<D>), dim3(n_blocks * s.n_q_heads), dim3(kWave), 0, st, p);
-    timer_end(HGA_KERNEL_BWD_DQ, st);
-    timer_begin(HGA_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<D>), dim3(n_blocks * s.n_kv_heads), dim3(kWave), 0, st, p);
-    timer_end(HGA_KERNEL_BWD_DKDV, st);
+    hipExtLaunchKernelGGL((row_dot_kernel<float, D>), dim3(dot_grid), dim3(256), 0, st, dq0, nullptr, 0,
+                          static_cast<const float*>(p.o), static_cast<const float*>(p.d_o), p.dvec, n_rows);
+    hipExtLaunchKernelGGL((attn_bwd_dq_f32_kernel<D>), dim3(n_blocks * s.n_q_heads), dim3(kWave), 0, st,
+                          nullptr, dq1, 0, p);
+    hipExtLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<D>), dim3(n_blocks * s.n_kv_heads), dim3(kWave), 0, st,
+                          kv0, kv1, 0, p);
   } else {
-    timer_begin(HGA_KERNEL_BWD_DQ, st);
     const int n_pairs = (n_blocks + 1) / 2;
     if (p.r % 2 == 0)
-      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 2>), dim3(n_pairs * s.n_kv_heads * (p.r / 2)),
-                         dim3(512), 0, st, p);
+      hipExtLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 2>), dim3(n_pairs * s.n_kv_heads * (p.r / 2)),
+                            dim3(512), 0, st, dq0, dq1, 0, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 1>), dim3(n_pairs * s.n_kv_heads * p.r),
-                         dim3(256), 0, st, p);
-    timer_end(HGA_KERNEL_BWD_DQ, st);
-    timer_begin(HGA_KERNEL_BWD_DKDV, st);
+      hipExtLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, 1>), dim3(n_pairs * s.n_kv_heads * p.r),
+                            dim3(256), 0, st, dq0, dq1, 0, p);
     const int hpw = p.r % 2 == 0 ? 2 : 1;
     const int n_hg = p.r / hpw;
     const unsigned grid = static_cast<unsigned>(n_pairs * s.n_kv_heads * n_hg);
+    // the fixed-order partial sum, when there is one, ends the dK/dV span
+    hipEvent_t kv_end = n_hg > 1 ? nullptr : kv1;
     if (hpw == 2)
-      hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, 2>), dim3(grid), dim3(256), 0, st, p);
+      hipExtLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, 2>), dim3(grid), dim3(256), 0, st, kv0, kv_end, 0, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, 1>), dim3(grid), dim3(128), 0, st, p);
+      hipExtLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, 1>), dim3(grid), dim3(128), 0, st, kv0, kv_end, 0, p);
     if (n_hg > 1) {
       const int64_t n_elem = static_cast<int64_t>(s.n_kv_heads) * s.seg_len * D;
-      hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(static_cast<unsigned>((n_elem / 4 + 255) / 256)), dim3(256),
-                         0, st, p.dkdv_part, n_hg, n_elem, p.scale, static_cast<uint16_t*>(p.dk),
-                         static_cast<uint16_t*>(p.dv));
+      hipExtLaunchKernelGGL(dkdv_reduce_kernel, dim3(static_cast<unsigned>((n_elem / 4 + 255) / 256)),
+                            dim3(256), 0, st, nullptr, kv1, 0, p.dkdv_part, n_hg, n_elem, p.scale,
+                            static_cast<uint16_t*>(p.dk), static_cast<uint16_t*>(p.dv));
     }
-    timer_end(HGA_KERNEL_BWD_DKDV, st);
   }
   return hipGetLastError();
 }

@@ -415,21 +415,19 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
 }
 
 template <int D>
-hipError_t launch_d(const hga_shape& s, FwdParams& p, hipStream_t st, bool timed) {
-  if (timed) timer_begin(HGA_KERNEL_ATTN_FWD, st);
+hipError_t launch_d(const hga_shape& s, FwdParams& p, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (s.dtype == HGA_F32) {
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(p.n_blocks_here * s.n_q_heads), dim3(kWave),
-                       0, st, p);
+    hipExtLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3(p.n_blocks_here * s.n_q_heads), dim3(kWave), 0,
+                          st, ev0, ev1, 0, p);
   } else {
     const int n_pairs = (p.n_blocks_here + 1) / 2;
     if (p.r % 2 == 0)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3(n_pairs * s.n_kv_heads * (p.r / 2)),
-                         dim3(512), 0, st, p);
+      hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3(n_pairs * s.n_kv_heads * (p.r / 2)),
+                            dim3(512), 0, st, ev0, ev1, 0, p);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(n_pairs * s.n_kv_heads * p.r), dim3(256),
-                         0, st, p);
+      hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(n_pairs * s.n_kv_heads * p.r), dim3(256),
+                            0, st, ev0, ev1, 0, p);
   }
-  if (timed) timer_end(HGA_KERNEL_ATTN_FWD, st);
   return hipGetLastError();
 }
 
@@ -439,7 +437,8 @@ hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, void* o, float* lse,
                            const void* k_staged, const void* v_staged, int32_t block_begin,
-                           int32_t block_end, hipStream_t stream, bool timed) {
+                           int32_t block_end, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop) {
   if (block_end <= block_begin) return hipSuccess;
   FwdParams p;
   p.q = q; p.k_hist = k_hist; p.v_hist = v_hist; p.k_seg = k_seg; p.v_seg = v_seg;
@@ -450,7 +449,7 @@ hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads;
   p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.k_g = s.top_k_groups;
   p.scale_log2 = s.softmax_scale * kLog2e;
-  return s.head_dim == 128 ? launch_d<128>(s, p, stream, timed) : launch_d<64>(s, p, stream, timed);
+  return s.head_dim == 128 ? launch_d<128>(s, p, stream, ev_start, ev_stop) : launch_d<64>(s, p, stream, ev_start, ev_stop);
 }
 
 }  // namespace hga

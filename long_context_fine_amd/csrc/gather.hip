@@ -68,23 +68,22 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 
 hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_hist,
                          const int32_t* sel_groups, void* k_out, void* v_out,
-                         int32_t block_begin, int32_t block_end, hipStream_t stream, bool timed) {
+                         int32_t block_begin, int32_t block_end, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (block_end <= block_begin) return hipSuccess;
   const int elem = s.dtype == HGA_BF16 ? 2 : 4;
   const int n_tiles = (s.top_k_groups + 7) / 8;
   dim3 grid(static_cast<unsigned>((block_end - block_begin) * s.n_kv_heads * n_tiles));
-  if (timed) timer_begin(HGA_KERNEL_GATHER, stream);
   if (s.head_dim == 128)
-    hipLaunchKernelGGL((gather_kernel<128>), grid, dim3(kThreads), 0, stream,
+    hipExtLaunchKernelGGL((gather_kernel<128>), grid, dim3(kThreads), 0, stream, ev_start, ev_stop, 0,
                        static_cast<const uint8_t*>(k_hist), static_cast<const uint8_t*>(v_hist),
                        sel_groups, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), elem,
                        s.hist_len, s.n_kv_heads, s.top_k_groups, block_begin);
   else
-    hipLaunchKernelGGL((gather_kernel<64>), grid, dim3(kThreads), 0, stream,
+    hipExtLaunchKernelGGL((gather_kernel<64>), grid, dim3(kThreads), 0, stream, ev_start, ev_stop, 0,
                        static_cast<const uint8_t*>(k_hist), static_cast<const uint8_t*>(v_hist),
                        sel_groups, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), elem,
                        s.hist_len, s.n_kv_heads, s.top_k_groups, block_begin);
-  if (timed) timer_end(HGA_KERNEL_GATHER, stream);
   return hipGetLastError();
 }
 

@@ -157,14 +157,7 @@ std::atomic<hipEvent_t> g_timer_ev[HGA_KERNEL_COUNT][2];
 }  // namespace
 
 namespace hga {
-void timer_begin(int id, hipStream_t stream) {
-  hipEvent_t e = g_timer_ev[id][0].load(std::memory_order_relaxed);
-  if (e) (void)hipEventRecord(e, stream);
-}
-void timer_end(int id, hipStream_t stream) {
-  hipEvent_t e = g_timer_ev[id][1].load(std::memory_order_relaxed);
-  if (e) (void)hipEventRecord(e, stream);
-}
+hipEvent_t timer_event(int id, int which) { return g_timer_ev[id][which].load(std::memory_order_relaxed); }
 }  // namespace hga
 
 extern "C" {
@@ -258,7 +251,9 @@ hga_status hga_gather_groups(const hga_shape* shape, const void* k_hist, const v
     HGA_TRY(host_to_device_ptr(v_hist, &vd, "v_hist"));
   }
   const hipError_t e = hga::launch_gather(s, kd, vd, sel_groups, k_out, v_out, 0,
-                                          s.seg_len / hga::kBlockQ, static_cast<hipStream_t>(stream));
+                                          s.seg_len / hga::kBlockQ, static_cast<hipStream_t>(stream),
+                                          hga::timer_event(HGA_KERNEL_GATHER, 0),
+                                          hga::timer_event(HGA_KERNEL_GATHER, 1));
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   return ok();
 }
@@ -276,7 +271,9 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   const int n_blocks = s.seg_len / hga::kBlockQ;
   if (s.hist_loc == HGA_HIST_DEVICE || s.hist_len == 0) {
     const hipError_t e = hga::launch_attn_fwd(s, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse,
-                                              nullptr, nullptr, 0, n_blocks, st);
+                                              nullptr, nullptr, 0, n_blocks, st,
+                                              hga::timer_event(HGA_KERNEL_ATTN_FWD, 0),
+                                              hga::timer_event(HGA_KERNEL_ATTN_FWD, 1));
     if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
     return ok();
   }
@@ -304,11 +301,9 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   // the side stream must see everything already enqueued on `stream` (sel_groups)
   if ((e = hipEventRecord(r->start, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(r->side, r->start, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-  // timers (hga_set_kernel_events) span the whole call: GATHER from the first
-  // gather to the last on the side stream, ATTN_FWD the whole forward on
-  // `stream`, waits for gathered phases included
-  hga::timer_begin(HGA_KERNEL_GATHER, r->side);
-  hga::timer_begin(HGA_KERNEL_ATTN_FWD, st);
+  // timers (hga_set_kernel_events) span the whole call: GATHER from the start
+  // of the first gather to the end of the last, ATTN_FWD from the start of the
+  // first attention phase to the end of the last (waits in between included)
   const int n_phases = (n_blocks + kPhaseBlocks - 1) / kPhaseBlocks;
   for (int ph = 0; ph < n_phases; ++ph) {
     const int b0 = ph * kPhaseBlocks;
@@ -316,17 +311,19 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
     const int x = ph % 2;
     if (ph >= 2 && (e = hipStreamWaitEvent(r->side, r->consumed[x], 0)) != hipSuccess)
       return hip_fail(e, "hipStreamWaitEvent");
-    if ((e = hga::launch_gather(s, kd, vd, sel_groups, kbuf[x], vbuf[x], b0, b1, r->side, false)) != hipSuccess)
+    const bool first = ph == 0, last = ph == n_phases - 1;
+    if ((e = hga::launch_gather(s, kd, vd, sel_groups, kbuf[x], vbuf[x], b0, b1, r->side,
+                                first ? hga::timer_event(HGA_KERNEL_GATHER, 0) : nullptr,
+                                last ? hga::timer_event(HGA_KERNEL_GATHER, 1) : nullptr)) != hipSuccess)
       return hip_fail(e, "gather launch");
     if ((e = hipEventRecord(r->gathered[x], r->side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(st, r->gathered[x], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
     if ((e = hga::launch_attn_fwd(s, q, kd, vd, k_seg, v_seg, sel_groups, o, lse, kbuf[x], vbuf[x], b0,
-                                  b1, st, false)) != hipSuccess)
+                                  b1, st, first ? hga::timer_event(HGA_KERNEL_ATTN_FWD, 0) : nullptr,
+                                  last ? hga::timer_event(HGA_KERNEL_ATTN_FWD, 1) : nullptr)) != hipSuccess)
       return hip_fail(e, "attn_fwd launch");
     if ((e = hipEventRecord(r->consumed[x], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
-  hga::timer_end(HGA_KERNEL_GATHER, r->side);
-  hga::timer_end(HGA_KERNEL_ATTN_FWD, st);
   return ok();
 }
 

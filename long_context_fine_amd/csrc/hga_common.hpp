@@ -1,6 +1,7 @@
 // Shared device helpers for the HGA kernels (gfx950 / CDNA4, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -120,9 +121,11 @@ __device__ __forceinline__ float sum8_f32(float x) {
   return x;
 }
 
-// Optional event pair recorded around each launch of kernel `id` (hga_kernel).
-void timer_begin(int id, hipStream_t stream);
-void timer_end(int id, hipStream_t stream);
+// Timing events of kernel `id` (hga_kernel) set by hga_set_kernel_events, or
+// nullptr: which = 0 is stamped with the start of the entry point's first
+// launch, which = 1 with the end of its last (hipExtLaunchKernelGGL records
+// them from the dispatch itself, so timing adds no marker packets).
+hipEvent_t timer_event(int id, int which);
 
 // Kernel launchers (defined in the .hip files).
 hipError_t launch_build_summaries(const hga_shape& s, const void* k_hist, int64_t tok_begin,
@@ -131,19 +134,18 @@ hipError_t launch_build_summaries(const hga_shape& s, const void* k_hist, int64_
 hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,
                         const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
                         void* ws, hipStream_t stream);
-// timed = false: the caller records the kernel's timer events itself (around
-// several launches).
 hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_hist,
                          const int32_t* sel_groups, void* k_out, void* v_out,
                          int32_t block_begin, int32_t block_end, hipStream_t stream,
-                         bool timed = true);
+                         hipEvent_t ev_start, hipEvent_t ev_stop);
 // staged != nullptr: history rows come from gathered buffers laid out as
 // [n_blocks][n_kv][top_k_groups*8][head_dim] for blocks [block_begin, block_end).
 hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist,
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, void* o, float* lse,
                            const void* k_staged, const void* v_staged, int32_t block_begin,
-                           int32_t block_end, hipStream_t stream, bool timed = true);
+                           int32_t block_end, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop);
 hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist,
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, const void* o, const float* lse,

@@ -247,11 +247,10 @@ hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const fl
   const int n_chunks = static_cast<int>(s.hist_len / kChunk);
   const int r = s.n_q_heads / s.n_kv_heads;
   float* scores = static_cast<float*>(ws);
-  timer_begin(HGA_KERNEL_ROUTE, st);
-  hipLaunchKernelGGL((route_kernel<T, D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
-                     static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, n_chunks,
-                     s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out);
-  timer_end(HGA_KERNEL_ROUTE, st);
+  hipExtLaunchKernelGGL((route_kernel<T, D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
+                        timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
+                        static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, n_chunks,
+                        s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out);
   return hipGetLastError();
 }
 

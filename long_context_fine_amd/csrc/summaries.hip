@@ -66,10 +66,9 @@ template <typename T, int D>
 hipError_t launch_t(const hga_shape& s, const void* k, int64_t c0, int64_t c1, float* cs,
                     float* gs, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(c1 - c0), static_cast<unsigned>(s.n_kv_heads));
-  timer_begin(HGA_KERNEL_SUMMARIES, st);
-  hipLaunchKernelGGL((build_summaries_kernel<T, D>), grid, dim3(kThreads), 0, st,
-                     static_cast<const T*>(k), s.hist_len, c0, cs, gs);
-  timer_end(HGA_KERNEL_SUMMARIES, st);
+  hipExtLaunchKernelGGL((build_summaries_kernel<T, D>), grid, dim3(kThreads), 0, st,
+                        timer_event(HGA_KERNEL_SUMMARIES, 0), timer_event(HGA_KERNEL_SUMMARIES, 1), 0,
+                        static_cast<const T*>(k), s.hist_len, c0, cs, gs);
   return hipGetLastError();
 }
 
