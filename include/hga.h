@@ -29,10 +29,11 @@
  * Layouts (contiguous, head-major, batch 1; "dtype" = hga_shape.dtype, i.e.
  * fp32 or bf16 stored as raw 16-bit words):
  *   q, o, d_o, dq                [n_q_heads][seg_len][head_dim]   dtype
- *   k_hist, v_hist               [n_kv_heads][hist_len][head_dim] dtype
+ *   k_hist, v_hist               [n_kv_heads][P][head_dim] dtype, first hist_len
+ *                                rows of each head used, P = hist_stride or hist_len
  *   k_seg, v_seg, dk_seg, dv_seg [n_kv_heads][seg_len][head_dim]  dtype
- *   chunk_sum                    [n_kv_heads][hist_len/64][head_dim] fp32
- *   group_sum                    [n_kv_heads][hist_len/8][head_dim]  fp32
+ *   chunk_sum                    [n_kv_heads][P/64][head_dim] fp32
+ *   group_sum                    [n_kv_heads][P/8][head_dim]  fp32
  *   lse                          [n_q_heads][seg_len] fp32 (natural log)
  *   sel_chunks                   [seg_len/64][n_kv_heads][top_k_chunks] int32
  *   sel_groups                   [seg_len/64][n_kv_heads][top_k_groups] int32
@@ -63,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 1
+#define HGA_ABI_VERSION 2
 
 typedef enum {
   HGA_OK = 0,
@@ -92,6 +93,10 @@ typedef struct {
   float softmax_scale;    /* multiplies Q.K before the softmax, > 0 */
   int32_t dtype;          /* hga_dtype of Q/K/V/O/dO/dQ/dK/dV */
   int32_t hist_loc;       /* hga_hist_loc of k_hist / v_hist */
+  int64_t hist_stride;    /* rows per KV head in k_hist / v_hist, 0 = hist_len; a
+                             multiple of 64, >= hist_len. Summaries then hold
+                             hist_stride/64 chunk and hist_stride/8 group rows
+                             per KV head, so a history can grow in place */
 } hga_shape;
 
 /* Chunk and group summaries (gist.science Technical Summary §2.1, "Chunk

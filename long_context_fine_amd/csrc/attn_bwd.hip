@@ -40,6 +40,7 @@ struct BwdParams {
   int n_q, n_kv, r;
   int seg_len;
   int64_t hist_len;
+  int64_t hist_rows;  // rows per KV head in k_hist / v_hist
   int k_g;
   float scale;
   float scale_log2;
@@ -51,7 +52,7 @@ __device__ __forceinline__ int64_t hist_offset(const BwdParams& p, const int32_t
   if (slot >= p.k_g) return -1;
   const int n = sel_s[slot];
   if (n < 0) return -1;
-  return (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup + kk % kGroup) * D;
+  return (static_cast<int64_t>(j) * p.hist_rows + static_cast<int64_t>(n) * kGroup + kk % kGroup) * D;
 }
 
 // Dvec = rowsum(dO * O), fp32 accumulation (fp32 path; the bf16 dQ kernel
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   const int head = j * p.r + hg * HPW + gw / 2;
   const int qrow0 = (gw % 2) * 32;
 
-  const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist) + static_cast<int64_t>(j) * p.hist_len * D;
-  const uint16_t* vh = static_cast<const uint16_t*>(p.v_hist) + static_cast<int64_t>(j) * p.hist_len * D;
+  const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist) + static_cast<int64_t>(j) * p.hist_rows * D;
+  const uint16_t* vh = static_cast<const uint16_t*>(p.v_hist) + static_cast<int64_t>(j) * p.hist_rows * D;
   const uint16_t* ks_g = static_cast<const uint16_t*>(p.k_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const uint16_t* vs_g = static_cast<const uint16_t*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const float c2 = p.scale_log2;
@@ -801,7 +802,7 @@ hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist
   p.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + row);
   p.dkdv_part = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row);
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads;
-  p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.k_g = s.top_k_groups;
+  p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.hist_rows = hist_rows(s); p.k_g = s.top_k_groups;
   p.scale = s.softmax_scale;
   p.scale_log2 = s.softmax_scale * kLog2e;
   return s.head_dim == 128 ? launch_d<128>(s, p, stream) : launch_d<64>(s, p, stream);

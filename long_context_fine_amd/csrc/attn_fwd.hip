@@ -37,6 +37,7 @@ struct FwdParams {
   int n_q, n_kv, r;
   int seg_len;
   int64_t hist_len;
+  int64_t hist_rows;  // rows per KV head in k_hist / v_hist
   int k_g;
   float scale_log2;  // softmax_scale * log2(e)
 };
@@ -56,7 +57,7 @@ __device__ __forceinline__ const T* hist_row(const FwdParams& p, const T* base, 
     return staged + ((bl * p.n_kv + j) * static_cast<int64_t>(p.k_g) * kGroup +
                      static_cast<int64_t>(slot) * kGroup + kk % kGroup) * D;
   }
-  return base + (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup +
+  return base + (static_cast<int64_t>(j) * p.hist_rows + static_cast<int64_t>(n) * kGroup +
                  kk % kGroup) * D;
 }
 
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
         if (n < 0) return seg + (kq % 2) * 4 * D;
         if (kst) return (which ? vst : kst) + (staged_row0 + slot * kGroup + (kq % 2) * 4) * D;
         return (which ? vh : kh) +
-               (static_cast<int64_t>(j) * p.hist_len + static_cast<int64_t>(n) * kGroup + (kq % 2) * 4) * D;
+               (static_cast<int64_t>(j) * p.hist_rows + static_cast<int64_t>(n) * kGroup + (kq % 2) * 4) * D;
       }
       return seg + static_cast<int64_t>((t - n_hist) * kTile + kq * 4) * D;
     };
@@ -447,7 +448,7 @@ hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist
   p.block_begin = block_begin;
   p.n_blocks_here = block_end - block_begin;
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads;
-  p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.k_g = s.top_k_groups;
+  p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.hist_rows = hist_rows(s); p.k_g = s.top_k_groups;
   p.scale_log2 = s.softmax_scale * kLog2e;
   return s.head_dim == 128 ? launch_d<128>(s, p, stream, ev_start, ev_stop) : launch_d<64>(s, p, stream, ev_start, ev_stop);
 }

@@ -17,7 +17,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint8_t* __restrict__ k_hist, const uint8_t* __restrict__ v_hist,
     const int32_t* __restrict__ sel, uint8_t* __restrict__ k_out, uint8_t* __restrict__ v_out,
-    int elem_bytes, int64_t hist_len, int n_kv, int k_g, int block_begin) {
+    int elem_bytes, int64_t hist_rows, int n_kv, int k_g, int block_begin) {
   const int row_bytes = D * elem_bytes;
   const int cpr = row_bytes / 16;            // 16-byte chunks per row
   const int rows_per_pass = kThreads / cpr;  // 16 or 8 (bf16) / 8 or 4 (fp32)
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
         dst[u] = (out_base + static_cast<int64_t>(slot) * kGroup + row % kGroup) * row_bytes + c * 16;
         const int n = sel_bj[slot];
         if (n >= 0) {
-          const int64_t src = (static_cast<int64_t>(j) * hist_len + static_cast<int64_t>(n) * kGroup +
+          const int64_t src = (static_cast<int64_t>(j) * hist_rows + static_cast<int64_t>(n) * kGroup +
                                row % kGroup) * row_bytes + c * 16;
           kv[u] = *reinterpret_cast<const uint4*>(k_hist + src);
           vv[u] = *reinterpret_cast<const uint4*>(v_hist + src);
@@ -78,12 +78,12 @@ hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_h
     hipExtLaunchKernelGGL((gather_kernel<128>), grid, dim3(kThreads), 0, stream, ev_start, ev_stop, 0,
                        static_cast<const uint8_t*>(k_hist), static_cast<const uint8_t*>(v_hist),
                        sel_groups, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), elem,
-                       s.hist_len, s.n_kv_heads, s.top_k_groups, block_begin);
+                       hist_rows(s), s.n_kv_heads, s.top_k_groups, block_begin);
   else
     hipExtLaunchKernelGGL((gather_kernel<64>), grid, dim3(kThreads), 0, stream, ev_start, ev_stop, 0,
                        static_cast<const uint8_t*>(k_hist), static_cast<const uint8_t*>(v_hist),
                        sel_groups, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), elem,
-                       s.hist_len, s.n_kv_heads, s.top_k_groups, block_begin);
+                       hist_rows(s), s.n_kv_heads, s.top_k_groups, block_begin);
   return hipGetLastError();
 }
 

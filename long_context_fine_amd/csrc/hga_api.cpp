@@ -78,6 +78,10 @@ hga_status check_shape(const hga_shape* s) {
   if (s->hist_len / hga::kGroup > INT32_MAX / 2)
     return fail(HGA_ERR_UNSUPPORTED, "hist_len %lld too large for int32 group ids",
                 static_cast<long long>(s->hist_len));
+  if (s->hist_stride != 0 &&
+      (s->hist_stride < s->hist_len || s->hist_stride % hga::kChunk || s->hist_stride / hga::kGroup > INT32_MAX / 2))
+    return fail(HGA_ERR_INVALID_ARG, "hist_stride %lld must be 0 or a multiple of 64 >= hist_len %lld",
+                static_cast<long long>(s->hist_stride), static_cast<long long>(s->hist_len));
   if (s->seg_len <= 0 || s->seg_len % hga::kBlockQ)
     return fail(HGA_ERR_INVALID_ARG, "seg_len %d is not a positive multiple of 64", s->seg_len);
   if (!(std::isfinite(s->softmax_scale) && s->softmax_scale > 0.f))

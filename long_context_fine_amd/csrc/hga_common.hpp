@@ -121,6 +121,10 @@ __device__ __forceinline__ float sum8_f32(float x) {
   return x;
 }
 
+// Rows per KV head in k_hist / v_hist (and x64 / x8 in the chunk / group
+// summaries): hist_stride when set, else hist_len.
+inline int64_t hist_rows(const hga_shape& s) { return s.hist_stride ? s.hist_stride : s.hist_len; }
+
 // Timing events of kernel `id` (hga_kernel) set by hga_set_kernel_events, or
 // nullptr: which = 0 is stamped with the start of the entry point's first
 // launch, which = 1 with the end of its last (hipExtLaunchKernelGGL records

@@ -63,7 +63,8 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const T* __restrict__ q, const float* __restrict__ csum, const float* __restrict__ gsum,
-    int seg_len, int n_kv, int r, int n_chunks, int k_c, int k_g, float* __restrict__ ws_scores,
+    int seg_len, int n_kv, int r, int n_chunks, int chunk_rows, int k_c, int k_g,
+    float* __restrict__ ws_scores,
     int32_t* __restrict__ sel_chunks, int32_t* __restrict__ sel_groups) {
   constexpr int TPR = D / 8;            // threads per Q row (8 elements each)
   constexpr int RG = kThreads / TPR;    // row groups
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
   // ---- 2. chunk scores ----------------------------------------------------
   float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
-  const float* cbase = csum + static_cast<int64_t>(j) * n_chunks * D;
+  const float* cbase = csum + static_cast<int64_t>(j) * chunk_rows * D;
   score_rows<D, 8>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
   __syncthreads();
 
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
   // ---- 4. group scores for the 8 groups of every kept chunk ----------------
   const int n_cand = kc_eff * (kChunk / kGroup);
-  const float* gbase = gsum + static_cast<int64_t>(j) * n_chunks * (kChunk / kGroup) * D;
+  const float* gbase = gsum + static_cast<int64_t>(j) * chunk_rows * (kChunk / kGroup) * D;
   score_rows<D, 4>(qv, n_cand, [&](int c) {
     return gbase + (static_cast<int64_t>(sorted[c / 8]) * 8 + (c % 8)) * D;
   }, gsc);
@@ -250,6 +251,7 @@ hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const fl
   hipExtLaunchKernelGGL((route_kernel<T, D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
                         timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
                         static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, n_chunks,
+                        static_cast<int>(hist_rows(s) / kChunk),
                         s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out);
   return hipGetLastError();
 }

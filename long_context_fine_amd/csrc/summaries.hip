@@ -13,7 +13,7 @@ constexpr int kThreads = 256;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void build_summaries_kernel(
-    const T* __restrict__ k_hist, int64_t hist_len, int64_t chunk_begin,
+    const T* __restrict__ k_hist, int64_t hist_rows, int64_t chunk_begin,
     float* __restrict__ chunk_sum, float* __restrict__ group_sum) {
   constexpr int TPR = D / 8;                  // threads per token row
   constexpr int RG = kThreads / TPR;          // row groups
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void build_summaries_kernel(
   const int64_t m = chunk_begin + blockIdx.x;  // chunk index
   const int j = blockIdx.y;                    // KV head
 
-  const T* src = k_hist + (static_cast<int64_t>(j) * hist_len + m * kChunk + rg * TOK_PER_RG) * D + dc * 8;
+  const T* src = k_hist + (static_cast<int64_t>(j) * hist_rows + m * kChunk + rg * TOK_PER_RG) * D + dc * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < TOK_PER_RG; ++u) {
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void build_summaries_kernel(
   for (int e = 0; e < 8; ++e) part[rg][dc * 8 + e] = acc[e];
   __syncthreads();
 
-  const int64_t n_groups_total = hist_len / kGroup;
+  const int64_t n_groups_total = hist_rows / kGroup;   // group rows per KV head
   for (int idx = t; idx < (kChunk / kGroup) * D; idx += kThreads) {
     const int g = idx / D, e = idx % D;
     float s = 0.f;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void build_summaries_kernel(
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < kChunk / kGroup; ++g) s += gsum[g][t];
-    chunk_sum[(static_cast<int64_t>(j) * (hist_len / kChunk) + m) * D + t] = s * (1.0f / kChunk);
+    chunk_sum[(static_cast<int64_t>(j) * (hist_rows / kChunk) + m) * D + t] = s * (1.0f / kChunk);
   }
 }
 
@@ -68,7 +68,7 @@ hipError_t launch_t(const hga_shape& s, const void* k, int64_t c0, int64_t c1, f
   dim3 grid(static_cast<unsigned>(c1 - c0), static_cast<unsigned>(s.n_kv_heads));
   hipExtLaunchKernelGGL((build_summaries_kernel<T, D>), grid, dim3(kThreads), 0, st,
                         timer_event(HGA_KERNEL_SUMMARIES, 0), timer_event(HGA_KERNEL_SUMMARIES, 1), 0,
-                        static_cast<const T*>(k), s.hist_len, c0, cs, gs);
+                        static_cast<const T*>(k), hist_rows(s), c0, cs, gs);
   return hipGetLastError();
 }
 

@@ -41,8 +41,13 @@ class Shape(ctypes.Structure):
         ("top_k_chunks", ctypes.c_int32), ("top_k_groups", ctypes.c_int32),
         ("hist_len", ctypes.c_int64), ("seg_len", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("hist_loc", ctypes.c_int32),
+        ("hist_loc", ctypes.c_int32), ("hist_stride", ctypes.c_int64),
     ]
+
+    @property
+    def hist_rows(self) -> int:
+        """Rows per KV head of the history buffers (hist_stride, else hist_len)."""
+        return self.hist_stride or self.hist_len
 
     @property
     def n_blocks(self) -> int:
@@ -94,12 +99,13 @@ def lib() -> ctypes.CDLL:
 
 def make_shape(n_q_heads: int, n_kv_heads: int, head_dim: int, hist_len: int, seg_len: int,
                top_k_chunks: int, top_k_groups: int, dtype=torch.bfloat16,
-               softmax_scale: float | None = None, hist_on_host: bool = False) -> Shape:
+               softmax_scale: float | None = None, hist_on_host: bool = False,
+               hist_stride: int = 0) -> Shape:
     return Shape(n_q_heads, n_kv_heads, head_dim, 64, 8, 64, top_k_chunks, top_k_groups,
                  hist_len, seg_len,
                  softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(head_dim),
                  HGA_BF16 if dtype == torch.bfloat16 else HGA_F32,
-                 HGA_HIST_HOST_PINNED if hist_on_host else HGA_HIST_DEVICE)
+                 HGA_HIST_HOST_PINNED if hist_on_host else HGA_HIST_DEVICE, hist_stride)
 
 
 def _check(status: int) -> None:
@@ -155,8 +161,8 @@ def alloc_workspace(shape: Shape, op: int, device="cuda") -> torch.Tensor:
 
 def hga_build_summaries(shape: Shape, k_hist, chunk_sum, group_sum, tok_begin=0, tok_end=None,
                         stream=None) -> None:
-    H, kv, d = shape.hist_len, shape.n_kv_heads, shape.head_dim
-    tok_end = H if tok_end is None else tok_end
+    H, kv, d = shape.hist_rows, shape.n_kv_heads, shape.head_dim
+    tok_end = shape.hist_len if tok_end is None else tok_end
     host = shape.hist_loc == HGA_HIST_HOST_PINNED
     _check(lib().hga_build_summaries(
         ctypes.byref(shape), _ptr(k_hist, (kv, H, d), shape.torch_dtype, "k_hist", not host),
@@ -167,7 +173,7 @@ def hga_build_summaries(shape: Shape, k_hist, chunk_sum, group_sum, tok_begin=0,
 
 def hga_route(shape: Shape, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws=None,
               stream=None) -> None:
-    H, kv, d, S = shape.hist_len, shape.n_kv_heads, shape.head_dim, shape.seg_len
+    H, kv, d, S = shape.hist_rows, shape.n_kv_heads, shape.head_dim, shape.seg_len
     if ws is None:
         ws = alloc_workspace(shape, HGA_OP_ROUTE, q.device)
     _check(lib().hga_route(
@@ -181,7 +187,7 @@ def hga_route(shape: Shape, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws=
 
 def hga_attn_fwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, ws=None,
                  stream=None) -> None:
-    H, kv, d, S, nq = shape.hist_len, shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
+    H, kv, d, S, nq = shape.hist_rows, shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
     dt = shape.torch_dtype
     host = shape.hist_loc == HGA_HIST_HOST_PINNED
     if ws is None and hga_workspace_size(shape, HGA_OP_ATTN_FWD) > 0:
@@ -199,7 +205,7 @@ def hga_attn_fwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, l
 
 def hga_attn_bwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, d_o,
                  dq, dk_seg, dv_seg, ws=None, stream=None) -> None:
-    H, kv, d, S, nq = shape.hist_len, shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
+    H, kv, d, S, nq = shape.hist_rows, shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
     dt = shape.torch_dtype
     if ws is None:
         ws = alloc_workspace(shape, HGA_OP_ATTN_BWD, q.device)
@@ -215,7 +221,7 @@ def hga_attn_bwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, l
 
 
 def hga_gather_groups(shape: Shape, k_hist, v_hist, sel_groups, k_out, v_out, stream=None) -> None:
-    H, kv, d = shape.hist_len, shape.n_kv_heads, shape.head_dim
+    H, kv, d = shape.hist_rows, shape.n_kv_heads, shape.head_dim
     dt = shape.torch_dtype
     host = shape.hist_loc == HGA_HIST_HOST_PINNED
     out_shape = (shape.n_blocks, kv, shape.top_k_groups * 8, d)
@@ -231,7 +237,7 @@ def hga_gather_groups(shape: Shape, k_hist, v_hist, sel_groups, k_out, v_out, st
 # ---------------------------------------------------------------------------
 def summaries(shape: Shape, k_hist, device="cuda"):
     """Allocate and build the chunk / group summaries of the whole history."""
-    H, kv, d = shape.hist_len, shape.n_kv_heads, shape.head_dim
+    H, kv, d = shape.hist_rows, shape.n_kv_heads, shape.head_dim
     C = torch.empty((kv, H // 64, d), dtype=torch.float32, device=device)
     G = torch.empty((kv, H // 8, d), dtype=torch.float32, device=device)
     hga_build_summaries(shape, k_hist, C, G)

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.hga_abi_version() == 1
+    assert L.hga_abi_version() == 2
     assert L.hga_status_string(0) == b"HGA_OK"
     assert L.hga_status_string(3) == b"HGA_ERR_WORKSPACE"
     assert L.hga_status_string(99) == b"HGA_ERR_UNKNOWN"
@@ -68,6 +68,9 @@ FAKE = 0x10000  # never dereferenced: validation fails first
     ("softmax_scale", 0.0, hga.HGA_ERR_INVALID_ARG),
     ("dtype", 7, hga.HGA_ERR_INVALID_ARG),
     ("hist_loc", 5, hga.HGA_ERR_INVALID_ARG),
+    ("hist_stride", 14336 - 64, hga.HGA_ERR_INVALID_ARG),   # below hist_len
+    ("hist_stride", 14336 + 8, hga.HGA_ERR_INVALID_ARG),    # not a multiple of 64
+    ("hist_stride", -64, hga.HGA_ERR_INVALID_ARG),
 ])
 def test_invalid_shapes_are_rejected(L, field, value, status):
     s = _shape(**{field: value})
@@ -75,6 +78,16 @@ def test_invalid_shapes_are_rejected(L, field, value, status):
     assert st == status
     assert L.hga_last_error() != b""
     assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ROUTE) == 0
+
+
+def test_history_stride_is_accepted(L):
+    """A history buffer with room to grow: stride above hist_len is valid and
+    does not change any workspace size."""
+    s = _shape()
+    grown = _shape(hist_stride=14336 + 2048)
+    for op in (hga.HGA_OP_ROUTE, hga.HGA_OP_ATTN_FWD, hga.HGA_OP_ATTN_BWD):
+        assert L.hga_workspace_size(ctypes.byref(grown), op) == L.hga_workspace_size(ctypes.byref(s), op)
+    assert grown.hist_rows == 14336 + 2048 and s.hist_rows == 14336
 
 
 def test_null_shape_and_null_pointers(L):
