@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -32,6 +33,10 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--tbptt-max-hist", type=int, default=0,
+                    help="instead of the step benchmark: run the segment-wise driver from an "
+                         "empty history up to this many history tokens and report the cost "
+                         "of a segment (route + fwd + bwd + close) against history length")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB (one plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -127,8 +132,73 @@ def cpu_baseline(w, inp, budget_s):
                       f"{t_total:.1f} s"}
 
 
+def tbptt_sweep(args):
+    """Per-segment cost of the segment-wise driver as the history grows: one
+    JSON line with a point per power-of-two history length (and the last).
+    Segment inputs follow the synthetic recipe's distributions (N(0,1)/sqrt(d)
+    Q, K, V with an N(0, 0.5^2) offset per 64-token chunk of K, N(0,1) dO),
+    drawn on the GPU so that long sweeps do not wait on the host."""
+    import torch
+    from long_context_fine_amd import hga, synth, tbptt
+
+    hga.lib()
+    w = synth.WORKLOADS[args.workload]
+    S, d, kv, nq = w.seg_len, w.head_dim, w.n_kv_heads, w.n_q_heads
+    max_hist = (args.tbptt_max_hist // S) * S
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    hist = tbptt.LayerHistory(nq, kv, d, S, max_hist, w.top_k_chunks, w.top_k_groups,
+                              w.torch_dtype, w.softmax_scale, hist_on_host=w.hist_on_host,
+                              device=dev)
+    train = not w.hist_on_host
+    a = 1.0 / math.sqrt(d)
+
+    def segment_inputs():
+        q = (torch.randn((nq, S, d), generator=gen, device=dev) * a).to(w.torch_dtype)
+        off = torch.randn((kv, S // 64, 1, d), generator=gen, device=dev) * 0.5
+        k = (torch.randn((kv, S // 64, 64, d), generator=gen, device=dev) * a + off)
+        k = k.reshape(kv, S, d).to(w.torch_dtype)
+        v = (torch.randn((kv, S, d), generator=gen, device=dev) * a).to(w.torch_dtype)
+        d_o = torch.randn((nq, S, d), generator=gen, device=dev).to(w.torch_dtype)
+        return q, k, v, d_o
+
+    points, marks = [], set()
+    h = S
+    while h <= max_hist - S:
+        marks.add(h)
+        h *= 2
+    marks.add(max_hist - S)
+    while hist.hist_len + S <= max_hist:
+        q, k, v, d_o = segment_inputs()
+        timed = hist.hist_len in marks or hist.hist_len == 0
+        reps = 10 if timed else 1
+        if timed:
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+        for _ in range(reps):            # the same segment again: identical work
+            o, lse = hist.forward(q, k, v)
+            if train:
+                hist.backward(q, k, v, o, lse, d_o)
+        if timed:
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / reps
+            points.append({"hist_len": hist.hist_len, "ms_per_segment": round(ms, 4),
+                           "query_tokens_per_s": round(S / (ms * 1e-3), 1)})
+        hist.close_segment(k, v)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "tbptt", "workload": w.name, "pass": "fwd+bwd" if train else "fwd",
+                      "history": "pinned host" if w.hist_on_host else "hbm", "seg_len": S,
+                      "points": points,
+                      "note": "per segment: route + attention (+ backward); close_segment "
+                              "(append K/V, summaries) runs outside the timing"}), flush=True)
+
+
 def main():
     args = parse()
+    if args.tbptt_max_hist:
+        return tbptt_sweep(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
