@@ -29,8 +29,14 @@ Readings where the pages are silent (each listed in the design notes):
   * top-k order = score descending, then index ascending (lowest index wins a
     tie); NaN counts as -inf, -0 equals +0;
   * selections are emitted in ascending index order, padded with -1;
-  * every history chunk (all lie before the segment) is eligible;
-  * the local window is the whole active segment, causal; no sink window;
+  * every history chunk (all lie before the segment) is eligible, except the
+    sink: the first n_sink history chunks are attended in full by every query
+    (the "fixed sink" window beside the routed chunks [gist 2.1]) and are
+    therefore not ranked, so no token is counted twice;
+  * the local window is the W most recent segment tokens, causal: query i
+    attends segment keys t with i - W < t <= i (W = S by default, the whole
+    segment); routing covers the closed history only, so with W < S older
+    segment tokens are not attended;
   * the gathered history is detached: no gradient reaches K_hist / V_hist.
 
 Precision: the routing decisions (summaries, block queries, scores) are taken
@@ -124,19 +130,21 @@ def chunk_scores(qbar: np.ndarray, C: np.ndarray) -> np.ndarray:
     return out
 
 
-def route_chunks(qbar: np.ndarray, C: np.ndarray, k_c: int):
+def route_chunks(qbar: np.ndarray, C: np.ndarray, k_c: int, n_sink: int = 0):
     """Chunk selection [gist 2.1 "Chunk Selection"].
 
-    Every history chunk precedes the active segment, so all n_C chunks are
-    candidates for every query block. Returns (sel int32 [n_B][n_kv][k_c]
-    ascending, -1 padded; scores float32 [n_B][n_kv][n_C]).
+    Every history chunk precedes the active segment; the candidates are the
+    chunks after the sink, m in [n_sink, n_C), for every query block (the sink
+    chunks are attended in full anyway). Returns (sel int32 [n_B][n_kv][k_c]
+    ascending, -1 padded; scores float32 [n_B][n_kv][n_C] of all chunks).
     """
     sc = chunk_scores(qbar, C)
     n_B, n_kv, n_C = sc.shape
+    s0 = min(n_sink, n_C)
     sel = np.full((n_B, n_kv, k_c), -1, dtype=np.int32)
     for b in range(n_B):
         for j in range(n_kv):
-            top = topk_lowest_index(sc[b, j], k_c)
+            top = s0 + topk_lowest_index(sc[b, j, s0:], k_c)
             sel[b, j, : top.shape[0]] = top
     return sel, sc
 
@@ -173,13 +181,13 @@ def route_groups(qbar: np.ndarray, G: np.ndarray, sel_chunks: np.ndarray, k_g: i
     return sel
 
 
-def route(q, k_hist, n_kv, k_c, k_g):
+def route(q, k_hist, n_kv, k_c, k_g, n_sink: int = 0):
     """The whole routing step from raw inputs: summaries, block queries,
     chunk top-k, group top-k. Returns (sel_chunks, sel_groups, aux)."""
     C = chunk_summaries(k_hist)
     G = group_summaries(k_hist)
     qbar = block_queries(q, n_kv)
-    sel_c, sc = route_chunks(qbar, C, k_c)
+    sel_c, sc = route_chunks(qbar, C, k_c, n_sink)
     sel_g = route_groups(qbar, G, sel_c, k_g)
     return sel_c, sel_g, dict(C=C, G=G, qbar=qbar, chunk_scores=sc)
 
@@ -187,28 +195,40 @@ def route(q, k_hist, n_kv, k_c, k_g):
 # ---------------------------------------------------------------------------
 # Exact-token attention [gist 2.1 "Exact-Token Attention"; pith F1]
 # ---------------------------------------------------------------------------
-def attended_history_tokens(sel_groups_bj: np.ndarray) -> np.ndarray:
-    """History token ids 8n .. 8n+7 of every selected group n >= 0."""
-    return np.array([GROUP * int(n) + u for n in sel_groups_bj if n >= 0
+def attended_history_tokens(sel_groups_bj: np.ndarray, n_sink_tokens: int = 0) -> np.ndarray:
+    """History token ids: the sink tokens 0 .. n_sink_tokens-1, then
+    8n .. 8n+7 of every selected group n >= 0."""
+    return np.array(list(range(n_sink_tokens)) +
+                    [GROUP * int(n) + u for n in sel_groups_bj if n >= 0
                      for u in range(GROUP)], dtype=np.int64)
 
 
-def _block_keys(k_hist, v_hist, k_seg, v_seg, sel_groups, b, j):
-    hist = attended_history_tokens(sel_groups[b, j])
-    n_loc = BLOCK * (b + 1)                  # segment keys 0 .. 64b+63
+def _window(window, S):
+    return S if window is None or window <= 0 else min(int(window), S)
+
+
+def _block_keys(k_hist, v_hist, k_seg, v_seg, sel_groups, b, j, n_sink_tokens=0, window=None):
+    """Keys of query block b: the history tokens, then the segment keys any
+    of its 64 rows may attend, [loc0, 64b+63]."""
+    hist = attended_history_tokens(sel_groups[b, j], min(n_sink_tokens, k_hist.shape[1]))
+    W = _window(window, k_seg.shape[1])
+    loc0 = max(0, BLOCK * b - W + 1)
+    loc1 = BLOCK * (b + 1)
     Kc = np.concatenate([np.asarray(k_hist[j][hist], F64),
-                         np.asarray(k_seg[j][:n_loc], F64)], axis=0)
+                         np.asarray(k_seg[j][loc0:loc1], F64)], axis=0)
     Vc = np.concatenate([np.asarray(v_hist[j][hist], F64),
-                         np.asarray(v_seg[j][:n_loc], F64)], axis=0)
-    return Kc, Vc, hist.shape[0], n_loc
+                         np.asarray(v_seg[j][loc0:loc1], F64)], axis=0)
+    return Kc, Vc, hist.shape[0], loc0, loc1 - loc0
 
 
-def _block_probs(Qb, Kc, n_hist, n_loc, b, scale):
-    """Softmax over [gathered history || causal segment] for 64 query rows."""
+def _block_probs(Qb, Kc, n_hist, loc0, n_loc, b, scale, W):
+    """Softmax over [history || segment window] for 64 query rows: row i may
+    attend segment key t iff i - W < t <= i."""
     s = scale * (Qb @ Kc.T)                          # (64, n_hist + n_loc)
     qpos = BLOCK * b + np.arange(BLOCK)[:, None]     # segment position of row
-    kpos = np.arange(n_loc)[None, :]
-    allowed = np.concatenate([np.ones((BLOCK, n_hist), bool), kpos <= qpos], axis=1)
+    kpos = loc0 + np.arange(n_loc)[None, :]
+    allowed = np.concatenate([np.ones((BLOCK, n_hist), bool),
+                              (kpos <= qpos) & (kpos > qpos - W)], axis=1)
     s = np.where(allowed, s, -np.inf)
     M = s.max(axis=1, keepdims=True)
     e = np.exp(s - M)
@@ -216,9 +236,10 @@ def _block_probs(Qb, Kc, n_hist, n_loc, b, scale):
     return e / ell, (M + np.log(ell))[:, 0]
 
 
-def attn_fwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale):
+def attn_fwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale, n_sink_tokens=0, window=None):
     """O[h][i] = softmax(scale * Q[h][i] . K_t) weighted sum of V_t over
-    t in {selected history tokens of block i//64, KV head h//r} U {segment 0..i}.
+    t in {sink tokens} U {selected history tokens of block i//64, KV head h//r}
+    U {segment keys i-W+1 .. i} (W = window, default the whole segment).
 
     Returns (O float64 [n_q][S][d], LSE float64 [n_q][S]).
     """
@@ -230,16 +251,17 @@ def attn_fwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale):
     for h in range(n_q):
         j = h // r
         for b in range(S // BLOCK):
-            Kc, Vc, n_hist, n_loc = _block_keys(k_hist, v_hist, k_seg, v_seg,
-                                                sel_groups, b, j)
+            Kc, Vc, n_hist, loc0, n_loc = _block_keys(k_hist, v_hist, k_seg, v_seg, sel_groups,
+                                                      b, j, n_sink_tokens, window)
             Qb = np.asarray(q[h, BLOCK * b: BLOCK * (b + 1)], F64)
-            P, lse = _block_probs(Qb, Kc, n_hist, n_loc, b, scale)
+            P, lse = _block_probs(Qb, Kc, n_hist, loc0, n_loc, b, scale, _window(window, S))
             O[h, BLOCK * b: BLOCK * (b + 1)] = P @ Vc
             LSE[h, BLOCK * b: BLOCK * (b + 1)] = lse
     return O, LSE
 
 
-def attn_bwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale, d_o):
+def attn_bwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale, d_o, n_sink_tokens=0,
+             window=None):
     """Gradients of sum(O * dO) w.r.t. Q, K_seg, V_seg [gist 2.1, gist 2.2].
 
     The history K/V is detached (no gradient); routing is a stop-gradient step,
@@ -256,16 +278,16 @@ def attn_bwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale, d_o):
         j = h // r
         for b in range(S // BLOCK):
             rows = slice(BLOCK * b, BLOCK * (b + 1))
-            Kc, Vc, n_hist, n_loc = _block_keys(k_hist, v_hist, k_seg, v_seg,
-                                                sel_groups, b, j)
+            Kc, Vc, n_hist, loc0, n_loc = _block_keys(k_hist, v_hist, k_seg, v_seg, sel_groups,
+                                                      b, j, n_sink_tokens, window)
             Qb = np.asarray(q[h, rows], F64)
             dOb = np.asarray(d_o[h, rows], F64)
-            P, _ = _block_probs(Qb, Kc, n_hist, n_loc, b, scale)
+            P, _ = _block_probs(Qb, Kc, n_hist, loc0, n_loc, b, scale, _window(window, S))
             dP = dOb @ Vc.T
             dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
             dQ[h, rows] = scale * (dS @ Kc)
-            dK[j, :n_loc] += scale * (dS[:, n_hist:].T @ Qb)
-            dV[j, :n_loc] += P[:, n_hist:].T @ dOb
+            dK[j, loc0:loc0 + n_loc] += scale * (dS[:, n_hist:].T @ Qb)
+            dV[j, loc0:loc0 + n_loc] += P[:, n_hist:].T @ dOb
     return dQ, dK, dV
 
 
@@ -302,7 +324,7 @@ def within_tolerance(got, ref, tol: float) -> bool:
     return err <= tol * max(1.0, mx) and rel <= tol
 
 
-def check_selection(qbar, C, G, sel_chunks, sel_groups, k_c, k_g, gap=1e-5):
+def check_selection(qbar, C, G, sel_chunks, sel_groups, k_c, k_g, gap=1e-5, n_sink=0):
     """Validate a selection against this oracle, allowing near-tie swaps.
 
     Per (block b, KV head j):
@@ -319,14 +341,15 @@ def check_selection(qbar, C, G, sel_chunks, sel_groups, k_c, k_g, gap=1e-5):
     for b in range(n_B):
         for j in range(n_kv):
             got_c = [int(x) for x in sel_chunks[b, j]]
-            want_n = min(k_c, n_C)
+            s0 = min(n_sink, n_C)
+            want_n = min(k_c, n_C - s0)
             ids = [x for x in got_c if x >= 0]
             if (len(ids) != want_n or got_c[len(ids):] != [-1] * (k_c - len(ids))
-                    or any(x >= n_C for x in ids)
+                    or any(x >= n_C or x < s0 for x in ids)
                     or any(ids[i] >= ids[i + 1] for i in range(len(ids) - 1))):
                 fails.append((b, j, "chunk set malformed", got_c))
                 continue
-            ref_c = topk_lowest_index(sc[b, j], k_c)
+            ref_c = s0 + topk_lowest_index(sc[b, j, s0:], k_c)
             tau = float(np.min(sc[b, j][ref_c])) if ref_c.size else 0.0
             diff = set(ids) ^ set(int(x) for x in ref_c)
             bad = [m for m in diff if not abs(float(sc[b, j, m]) - tau) < gap]

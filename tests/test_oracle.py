@@ -343,6 +343,127 @@ def test_backward_full_budget_matches_torch_autograd():
 
 
 # ---------------------------------------------------------------------------
+# sink and local window: explicit key sets, closed forms, autograd
+# ---------------------------------------------------------------------------
+def _mask_sink_window(sel_groups, n_q, n_kv, H, S, n_sink_tokens, W):
+    """allowed[h, i, t]: history token t < n_sink_tokens, or in a group selected
+    for (i//64, h//r); segment token t = H + u with i - W < u <= i."""
+    r = n_q // n_kv
+    allowed = np.zeros((n_q, S, H + S), bool)
+    for h in range(n_q):
+        for i in range(S):
+            allowed[h, i, :min(n_sink_tokens, H)] = True
+            for n in sel_groups[i // 64, h // r]:
+                if n >= 0:
+                    allowed[h, i, 8 * n: 8 * n + 8] = True
+            allowed[h, i, H + max(0, i - W + 1): H + i + 1] = True
+    return allowed
+
+
+@pytest.mark.parametrize("n_sink,W", [(1, 128), (2, 64), (0, 96), (3, 1), (8, 200)])
+def test_sink_and_window_match_explicit_key_sets(n_sink, W):
+    w = _small(seg_len=192)
+    inp = _np(synth.make_inputs(w, seed=20 + n_sink))
+    sel_c, sel_g, aux = orc.route(inp["q"], inp["k_hist"], 2, 3, 6, n_sink=n_sink)
+    O, LSE = orc.attn_fwd(inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"],
+                          sel_g, w.softmax_scale, n_sink_tokens=64 * n_sink, window=W)
+    allowed = _mask_sink_window(sel_g, w.n_q_heads, w.n_kv_heads, w.hist_len, w.seg_len,
+                                64 * n_sink, W)
+    k_all = np.concatenate([inp["k_hist"], inp["k_seg"]], axis=1)
+    v_all = np.concatenate([inp["v_hist"], inp["v_seg"]], axis=1)
+    ref, ref_lse = _sdpa_with_key_mask(inp["q"], k_all, v_all, allowed, w.softmax_scale)
+    assert np.max(np.abs(O - ref)) < 1e-12
+    assert np.max(np.abs(LSE - ref_lse)) < 1e-12
+
+
+def test_sink_chunks_are_never_routed():
+    # the history's best chunk lies inside the sink: routing must pick others
+    w = _small(hist_len=512, n_kv_heads=1, n_q_heads=1, seg_len=64)
+    inp = _np(synth.make_inputs(w, seed=30))
+    qbar = orc.block_queries(inp["q"], 1)[0, 0]
+    kh = inp["k_hist"].copy()
+    kh[0, 0:64] += 50.0 * qbar / np.linalg.norm(qbar)      # chunk 0: best by far
+    sel_c0, _, _ = orc.route(inp["q"], kh, 1, 3, 6)
+    assert 0 in sel_c0[0, 0]
+    sel_c, sel_g, aux = orc.route(inp["q"], kh, 1, 3, 6, n_sink=2)
+    ids = [int(x) for x in sel_c[0, 0] if x >= 0]
+    assert len(ids) == 3 and min(ids) >= 2
+    # the same selection as ranking the non-sink chunks by brute force
+    sc = aux["chunk_scores"][0, 0]
+    ref = sorted(sorted(range(2, 8), key=lambda m: (-sc[m], m))[:3])
+    assert ids == ref
+    assert all(int(n) // 8 >= 2 for n in sel_g[0, 0] if n >= 0)
+
+
+def test_sink_longer_than_history_routes_nothing():
+    w = _small(hist_len=128)
+    inp = _np(synth.make_inputs(w, seed=31))
+    sel_c, sel_g, _ = orc.route(inp["q"], inp["k_hist"], 2, 3, 6, n_sink=4)
+    assert (sel_c == -1).all() and (sel_g == -1).all()
+
+
+def test_window_of_one_attends_only_itself_closed_form():
+    # no history, W = 1: each query sees exactly its own key, so O = V_i and
+    # LSE = scale * q_i . k_i
+    w = _small(hist_len=0)
+    inp = _np(synth.make_inputs(w, seed=32))
+    sel = np.full((w.seg_len // 64, w.n_kv_heads, 6), -1, np.int32)
+    O, LSE = orc.attn_fwd(inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"],
+                          sel, w.softmax_scale, window=1)
+    r = w.n_q_heads // w.n_kv_heads
+    for h in range(w.n_q_heads):
+        assert np.max(np.abs(O[h] - inp["v_seg"][h // r])) < 1e-15
+        lse = w.softmax_scale * np.einsum("sd,sd->s", inp["q"][h], inp["k_seg"][h // r])
+        assert np.max(np.abs(LSE[h] - lse)) < 1e-12
+
+
+def test_window_covering_the_segment_changes_nothing():
+    w = _small()
+    inp = _np(synth.make_inputs(w, seed=33))
+    _, sel, _ = orc.route(inp["q"], inp["k_hist"], 2, 3, 6)
+    a = orc.attn_fwd(inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"], sel,
+                     w.softmax_scale)
+    b = orc.attn_fwd(inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"], sel,
+                     w.softmax_scale, window=w.seg_len)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("n_sink,W", [(2, 64), (1, 100)])
+def test_backward_with_sink_and_window_matches_torch_autograd(n_sink, W):
+    w = _small(seg_len=192)
+    inp = _np(synth.make_inputs(w, seed=40 + W))
+    _, sel, _ = orc.route(inp["q"], inp["k_hist"], 2, 3, 6, n_sink=n_sink)
+    dQ, dK, dV = orc.attn_bwd(inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"],
+                              sel, w.softmax_scale, inp["d_o"], n_sink_tokens=64 * n_sink, window=W)
+    q = torch.from_numpy(inp["q"]).requires_grad_(True)
+    ks = torch.from_numpy(inp["k_seg"]).requires_grad_(True)
+    vs = torch.from_numpy(inp["v_seg"]).requires_grad_(True)
+    r = w.n_q_heads // w.n_kv_heads
+    k_all = torch.cat([torch.from_numpy(inp["k_hist"]), ks], 1).repeat_interleave(r, 0)
+    v_all = torch.cat([torch.from_numpy(inp["v_hist"]), vs], 1).repeat_interleave(r, 0)
+    allowed = torch.from_numpy(_mask_sink_window(sel, w.n_q_heads, w.n_kv_heads, w.hist_len,
+                                                 w.seg_len, 64 * n_sink, W))
+    out = F.scaled_dot_product_attention(q, k_all, v_all, attn_mask=allowed, scale=w.softmax_scale)
+    (out * torch.from_numpy(inp["d_o"])).sum().backward()
+    assert np.max(np.abs(q.grad.numpy() - dQ)) < 1e-12
+    assert np.max(np.abs(ks.grad.numpy() - dK)) < 1e-12
+    assert np.max(np.abs(vs.grad.numpy() - dV)) < 1e-12
+
+
+def test_selection_checker_honours_the_sink():
+    w = _small()
+    inp = _np(synth.make_inputs(w, seed=34))
+    sel_c, sel_g, aux = orc.route(inp["q"], inp["k_hist"], 2, 3, 6, n_sink=2)
+    ok = orc.check_selection(aux["qbar"], aux["C"], aux["G"], sel_c, sel_g, 3, 6, n_sink=2)
+    assert ok["ok"]
+    bad = sel_c.copy()
+    bad[0, 0, 0] = 0                                   # a sink chunk may not be routed
+    bad[0, 0] = np.sort(bad[0, 0])
+    assert not orc.check_selection(aux["qbar"], aux["C"], aux["G"], bad, sel_g, 3, 6,
+                                   n_sink=2)["ok"]
+
+
+# ---------------------------------------------------------------------------
 # the parity criteria: selection checker and non-vacuous output tolerance
 # ---------------------------------------------------------------------------
 def test_selection_checker_accepts_oracle_and_rejects_clear_swaps():
