@@ -24,7 +24,11 @@
  *   - one routing decision per (query block, KV head), shared by its r heads
  *     and 64 queries;
  *   - selections are written in ascending index order, padded with -1;
- *   - no sink window.
+ *   - the "fixed sink and local windows" beside the routed chunks (gist.science
+ *     §2.1 "Chunk Selection"): the first n_sink_chunks history chunks are
+ *     attended in full and not ranked; the local window is the W most recent
+ *     segment tokens (default: the whole segment). Routing covers the closed
+ *     history only, so with W < seg_len older segment tokens are not attended.
  *
  * Layouts (contiguous, head-major, batch 1; "dtype" = hga_shape.dtype, i.e.
  * fp32 or bf16 stored as raw 16-bit words):
@@ -97,6 +101,12 @@ typedef struct {
                              multiple of 64, >= hist_len. Summaries then hold
                              hist_stride/64 chunk and hist_stride/8 group rows
                              per KV head, so a history can grow in place */
+  int32_t n_sink_chunks;  /* >= 0: the first n_sink_chunks history chunks (the
+                             fixed sink) are attended in full by every query
+                             and are not ranked by the router */
+  int32_t local_window;   /* >= 0: query i attends segment keys t with
+                             i - W < t <= i, W = local_window (0 or >= seg_len:
+                             the whole segment, causal) */
 } hga_shape;
 
 /* Chunk and group summaries (gist.science Technical Summary §2.1, "Chunk
@@ -107,7 +117,8 @@ typedef struct {
  *   group_sum[j][n] = mean of k_hist[j][8n .. 8n+7] for its 8 groups n.
  * tok_begin, tok_end: multiples of 64 with 0 <= tok_begin <= tok_end <= hist_len
  * (incremental use: summarise only the tokens of a newly closed segment).
- * k_hist must be in device memory. Summaries outside the range are untouched. */
+ * k_hist lives where shape->hist_loc says (device or pinned host); summaries are
+ * device memory. Summaries outside the range are untouched. */
 hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist,
                                int64_t tok_begin, int64_t tok_end,
                                float* chunk_sum, float* group_sum, void* stream);
@@ -115,7 +126,8 @@ hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist,
 /* Two-level routing (gist.science Technical Summary §2.1, "Chunk Selection",
  * "Group Selection"; routing runs without gradient). For each query block b
  * and KV head j: qbar = block query; chunk scores qbar . chunk_sum[j][m] over
- * all hist_len/64 history chunks; keep top_k_chunks; group scores over the 8
+ * the history chunks after the sink, m in [n_sink_chunks, hist_len/64); keep
+ * top_k_chunks; group scores over the 8
  * groups of each kept chunk; keep top_k_groups. Both lists are ascending and
  * padded with -1 when fewer candidates exist (e.g. hist_len == 0).
  * ws: device workspace of at least hga_workspace_size(shape, HGA_OP_ROUTE)
@@ -127,8 +139,10 @@ hga_status hga_route(const hga_shape* shape, const void* q, const float* chunk_s
 /* Exact-token attention forward (gist.science Technical Summary §2.1,
  * "Exact-Token Attention"; pith.science review, Figure 1: summaries select
  * regions, attention uses exact K/V only). For query i of head h (block
- * b = i/64, KV head j = h/r) the keys are the 8 tokens of every group
- * n >= 0 in sel_groups[b][j] (history) and segment tokens 0..i (causal):
+ * b = i/64, KV head j = h/r) the keys are the sink tokens
+ * 0 .. 64*n_sink_chunks-1, the 8 tokens of every group n >= 0 in
+ * sel_groups[b][j] (history) and segment tokens i-W+1 .. i (the local window,
+ * W = whole segment by default, causal):
  *   o[h][i] = sum_t softmax_t(scale * q[h][i] . k_t) v_t
  *   lse[h][i] = log sum_t exp(scale * q[h][i] . k_t)
  * sel_groups entries must be -1 or in [0, hist_len/8); the library does not

@@ -32,6 +32,11 @@ struct FwdParams {
   float* lse;
   const void* k_staged;
   const void* v_staged;
+  const void* k_sink;     // sink rows: [n_kv][sink_stride][D], first n_sink_tiles*64 used
+  const void* v_sink;
+  int64_t sink_stride;
+  int n_sink_tiles;       // fixed sink, in 64-token tiles (chunks)
+  int window;             // local window W in tokens (<= seg_len)
   int block_begin;
   int n_blocks_here;
   int n_q, n_kv, r;
@@ -75,7 +80,7 @@ __device__ __forceinline__ const T* hist_row(const FwdParams& p, const T* base, 
 // registers while the current pair of tiles (double-buffered in LDS) is used.
 // K and V both sit row-major in LDS; V^T reaches the MFMA through transposed
 // LDS reads (ds_read_b64_tr_b16).
-template <int D, int HPW>
+template <int D, int HPW, bool EXT>
 __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
   constexpr int NT = 256 * HPW;       // threads
   constexpr int GT = NT / 2;          // threads per parity group
@@ -130,7 +135,11 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
     build_hist_tile_list(sel_s, p.k_g, hlist, &n_hist_s);
     __syncthreads();
     const int n_hist = n_hist_s;
-    const int n_tiles = n_hist + b + 1;
+    const int n_sink = EXT ? p.n_sink_tiles : 0;
+    const int seg_t0 = seg_first_tile<EXT>(b, p.window);
+    // tiles: sink (whole chunks), routed history (8 groups each), segment window
+    const int n_pre = n_sink + n_hist;
+    const int n_tiles = n_pre + b - seg_t0 + 1;
     const int n_iter = (n_tiles + 1) / 2;
     const int q_tok = b * kBlockQ + qrow0 + l32;
     const int64_t staged_row0 =
@@ -141,15 +150,18 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
     // rows instead: finite values whose scores are masked to -inf.
     auto rowptr = [&](int t, int kq, int which) -> const uint16_t* {
       const uint16_t* seg = which ? vs_g : ks_g;
-      if (t < n_hist) {
-        const int slot = hlist[t] * 8 + kq / 2;
+      if (t < n_sink)
+        return static_cast<const uint16_t*>(which ? p.v_sink : p.k_sink) +
+               (static_cast<int64_t>(j) * p.sink_stride + t * kTile + kq * 4) * D;
+      if (t < n_pre) {
+        const int slot = hlist[t - n_sink] * 8 + kq / 2;
         const int n = slot < p.k_g ? sel_s[slot] : -1;
         if (n < 0) return seg + (kq % 2) * 4 * D;
         if (kst) return (which ? vst : kst) + (staged_row0 + slot * kGroup + (kq % 2) * 4) * D;
         return (which ? vh : kh) +
                (static_cast<int64_t>(j) * p.hist_rows + static_cast<int64_t>(n) * kGroup + (kq % 2) * 4) * D;
       }
-      return seg + static_cast<int64_t>((t - n_hist) * kTile + kq * 4) * D;
+      return seg + static_cast<int64_t>((seg_t0 + t - n_pre) * kTile + kq * 4) * D;
     };
 
     bf16x8 qreg[NKS];
@@ -163,7 +175,10 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-    float m_run = -INFINITY;  // running max (scaled, log2 domain), same in both lane halves
+    // running max (scaled, log2 domain), same in both lane halves; a finite
+    // floor so a row whose first tiles are all masked (local window) keeps
+    // exp2(-inf - m) = 0 instead of NaN
+    float m_run = -1e30f;
     float l_run = 0.f;        // partial row sum over this lane's keys
 
     TileRegs<D, GT> kr, vr;
@@ -188,26 +203,18 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
         // kt*32 + 8*(v/4) + 4*hh + v%4 of the tile) takes part; all ones
         // except on a history tile with empty slots or the diagonal tile
         uint32_t keep = 0xffffffffu;
-        const bool diag = t - n_hist == b;
-        if (t < n_hist) {
-          const uint32_t gm = hist_group_mask(sel_s, p.k_g, hlist[t]);
+        const int s_idx = seg_t0 + t - n_pre;
+        const bool seg_edge = t >= n_pre && seg_tile_masked<EXT>(s_idx, b, p.window);
+        if (t >= n_sink && t < n_pre) {
+          const uint32_t gm = hist_group_mask(sel_s, p.k_g, hlist[t - n_sink]);
 #pragma unroll
           for (int gi = 0; gi < 8; ++gi)
             if (!((gm >> gi) & 1u)) keep &= ~(0xfu << (4 * gi));
-        } else if (diag) {
-          // causal: key <= query row; per subtile the kept elements are a
-          // prefix of v (keys rise with v): n = sum_g clamp(x - 8g + 1, 0, 4)
-          keep = 0u;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const int x = qrow0 + l32 - kt * 32 - 4 * hh;
-            int n = 0;
-#pragma unroll
-            for (int gi = 0; gi < 4; ++gi) n += min(max(x - 8 * gi + 1, 0), 4);
-            keep |= static_cast<uint32_t>((1ull << n) - 1ull) << (16 * kt);
-          }
+        } else if (seg_edge) {
+          // causal diagonal and/or local-window start
+          keep = window_keep<EXT>(q_tok, s_idx * kTile, p.window, hh);
         }
-        const bool masked = diag || __builtin_amdgcn_readfirstlane(keep == 0xffffffffu ? 0 : 1) != 0;
+        const bool masked = seg_edge || __builtin_amdgcn_readfirstlane(keep == 0xffffffffu ? 0 : 1) != 0;
         const uint16_t* kbuf = smem[cur][grp];
         const uint16_t* vbuf = kbuf + kTile * KS;
 
@@ -366,15 +373,24 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
   }
   float m_run = -INFINITY, l_run = 0.f;
   const int n_hist_tiles = (p.k_g + 7) / 8;
+  const int n_sink = p.n_sink_tiles;
+  const int seg_t0 = seg_first_tile<true>(b, p.window);
+  const float* k_sink = static_cast<const float*>(p.k_sink) + static_cast<int64_t>(j) * p.sink_stride * D;
+  const float* v_sink = static_cast<const float*>(p.v_sink) + static_cast<int64_t>(j) * p.sink_stride * D;
   __syncthreads();
-  for (int tile = 0; tile < n_hist_tiles + b + 1; ++tile) {
-    const bool is_hist = tile < n_hist_tiles;
-    const int st = tile - n_hist_tiles;
+  for (int tile = 0; tile < n_sink + n_hist_tiles + b - seg_t0 + 1; ++tile) {
+    const bool is_sink = tile < n_sink;
+    const bool is_hist = !is_sink && tile < n_sink + n_hist_tiles;
+    const int ht = tile - n_sink;
+    const int st = seg_t0 + tile - n_sink - n_hist_tiles;
     for (int kk = 0; kk < kTile; ++kk) {
-      const float* ksrc = is_hist ? hist_row(p, kh, kst, sel_s, b, j, tile, kk, D)
-                                  : ks_g + static_cast<int64_t>(st * kTile + kk) * D;
-      const float* vsrc = is_hist ? hist_row(p, vh, vst, sel_s, b, j, tile, kk, D)
-                                  : vs_g + static_cast<int64_t>(st * kTile + kk) * D;
+      const int64_t sink_off = static_cast<int64_t>(tile * kTile + kk) * D;
+      const float* ksrc = is_sink ? k_sink + sink_off
+                          : is_hist ? hist_row(p, kh, kst, sel_s, b, j, ht, kk, D)
+                                    : ks_g + static_cast<int64_t>(st * kTile + kk) * D;
+      const float* vsrc = is_sink ? v_sink + sink_off
+                          : is_hist ? hist_row(p, vh, vst, sel_s, b, j, ht, kk, D)
+                                    : vs_g + static_cast<int64_t>(st * kTile + kk) * D;
       for (int e = a; e < D; e += kWave) {
         Kt[kk][e] = ksrc ? ksrc[e] : 0.f;
         Vt[kk][e] = vsrc ? vsrc[e] : 0.f;
@@ -385,11 +401,14 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
     float tmax = -INFINITY;
     for (int kk = 0; kk < kTile; ++kk) {
       bool valid;
-      if (is_hist) {
-        const int slot = tile * 8 + kk / kGroup;
+      if (is_sink) {
+        valid = true;
+      } else if (is_hist) {
+        const int slot = ht * 8 + kk / kGroup;
         valid = slot < p.k_g && sel_s[slot] >= 0;
       } else {
-        valid = !(st == b && kk > a);
+        const int key = st * kTile + kk;
+        valid = key <= q_tok && key > q_tok - p.window;
       }
       float s = 0.f;
       for (int e = 0; e < D; ++e) s += qr[e] * Kt[kk][e];
@@ -422,12 +441,17 @@ hipError_t launch_d(const hga_shape& s, FwdParams& p, hipStream_t st, hipEvent_t
                           st, ev0, ev1, 0, p);
   } else {
     const int n_pairs = (p.n_blocks_here + 1) / 2;
-    if (p.r % 2 == 0)
-      hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3(n_pairs * s.n_kv_heads * (p.r / 2)),
-                            dim3(512), 0, st, ev0, ev1, 0, p);
-    else
-      hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(n_pairs * s.n_kv_heads * p.r), dim3(256),
-                            0, st, ev0, ev1, 0, p);
+    // sink or local window: the extended kernels; otherwise the plain ones
+    const bool ext = p.window < s.seg_len || p.n_sink_tiles > 0;
+    if (p.r % 2 == 0) {
+      const dim3 grid(n_pairs * s.n_kv_heads * (p.r / 2));
+      if (ext) hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2, true>), grid, dim3(512), 0, st, ev0, ev1, 0, p);
+      else hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2, false>), grid, dim3(512), 0, st, ev0, ev1, 0, p);
+    } else {
+      const dim3 grid(n_pairs * s.n_kv_heads * p.r);
+      if (ext) hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1, true>), grid, dim3(256), 0, st, ev0, ev1, 0, p);
+      else hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1, false>), grid, dim3(256), 0, st, ev0, ev1, 0, p);
+    }
   }
   return hipGetLastError();
 }
@@ -437,7 +461,8 @@ hipError_t launch_d(const hga_shape& s, FwdParams& p, hipStream_t st, hipEvent_t
 hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist,
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, void* o, float* lse,
-                           const void* k_staged, const void* v_staged, int32_t block_begin,
+                           const void* k_staged, const void* v_staged, const void* k_sink,
+                           const void* v_sink, int64_t sink_stride, int32_t block_begin,
                            int32_t block_end, hipStream_t stream, hipEvent_t ev_start,
                            hipEvent_t ev_stop) {
   if (block_end <= block_begin) return hipSuccess;
@@ -445,6 +470,9 @@ hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist
   p.q = q; p.k_hist = k_hist; p.v_hist = v_hist; p.k_seg = k_seg; p.v_seg = v_seg;
   p.sel = sel_groups; p.o = o; p.lse = lse;
   p.k_staged = k_staged; p.v_staged = v_staged;
+  p.k_sink = k_sink; p.v_sink = v_sink; p.sink_stride = sink_stride;
+  p.n_sink_tiles = sink_chunks(s);
+  p.window = local_window(s);
   p.block_begin = block_begin;
   p.n_blocks_here = block_end - block_begin;
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads;

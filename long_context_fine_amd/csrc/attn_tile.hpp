@@ -292,6 +292,44 @@ __device__ __forceinline__ void build_hist_tile_list(const int32_t* sel_s, int k
   }
 }
 
+// Keep bitmask of a segment tile whose first key is key0, for the lane's query
+// row i and local window W: bit kt*16 + v is set iff key
+// key0 + kt*32 + 8*(v/4) + 4*hh + v%4 satisfies i - W < key <= i. Within a
+// subtile and lane half the keys rise with v, so the kept slots lie between
+// two prefix counts: n(x) = sum_g clamp(x - 8g + 1, 0, 4). WIN = false: no
+// window (W >= the segment), only the causal bound.
+template <bool WIN>
+__device__ __forceinline__ uint32_t window_keep(int i, int key0, int W, int hh) {
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int x = i - (key0 + kt * 32 + 4 * hh);
+    int n_hi = 0, n_lo = 0;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      n_hi += min(max(x - 8 * gi + 1, 0), 4);
+      if (WIN) n_lo += min(max(x - W - 8 * gi + 1, 0), 4);
+    }
+    keep |= static_cast<uint32_t>(((1ull << n_hi) - 1ull) & ~((1ull << n_lo) - 1ull)) << (16 * kt);
+  }
+  return keep;
+}
+
+// Whether segment tile s_idx (<= b) needs masking for query block b: it holds
+// keys after some query of the block (the diagonal) or at or before some
+// query's window start.
+template <bool WIN>
+__device__ __forceinline__ bool seg_tile_masked(int s_idx, int b, int W) {
+  return s_idx >= b || (WIN && s_idx * kTile <= b * kBlockQ + kBlockQ - 1 - W);
+}
+
+// First segment tile any query of block b attends with local window W.
+template <bool WIN>
+__device__ __forceinline__ int seg_first_tile(int b, int W) {
+  const int k = b * kBlockQ - W + 1;
+  return WIN && k > 0 ? k / kTile : 0;
+}
+
 __device__ __forceinline__ uint32_t hist_group_mask(const int32_t* sel_s, int k_g, int ht) {
   uint32_t m = 0;
 #pragma unroll

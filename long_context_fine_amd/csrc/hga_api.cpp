@@ -82,6 +82,9 @@ hga_status check_shape(const hga_shape* s) {
       (s->hist_stride < s->hist_len || s->hist_stride % hga::kChunk || s->hist_stride / hga::kGroup > INT32_MAX / 2))
     return fail(HGA_ERR_INVALID_ARG, "hist_stride %lld must be 0 or a multiple of 64 >= hist_len %lld",
                 static_cast<long long>(s->hist_stride), static_cast<long long>(s->hist_len));
+  if (s->n_sink_chunks < 0 || s->local_window < 0)
+    return fail(HGA_ERR_INVALID_ARG, "n_sink_chunks %d and local_window %d must be >= 0", s->n_sink_chunks,
+                s->local_window);
   if (s->seg_len <= 0 || s->seg_len % hga::kBlockQ)
     return fail(HGA_ERR_INVALID_ARG, "seg_len %d is not a positive multiple of 64", s->seg_len);
   if (!(std::isfinite(s->softmax_scale) && s->softmax_scale > 0.f))
@@ -121,9 +124,15 @@ size_t staging_bytes_per_buffer(const hga_shape& s) {
          s.head_dim * elem_bytes(s);
 }
 
+// Sink rows staged once per call for the pinned-host tier: [n_kv][sink*64][D].
+size_t sink_bytes(const hga_shape& s) {
+  return static_cast<size_t>(s.n_kv_heads) * hga::sink_chunks(s) * hga::kChunk * s.head_dim * elem_bytes(s);
+}
+
 size_t fwd_workspace_bytes(const hga_shape& s) {
   if (s.hist_loc != HGA_HIST_HOST_PINNED) return 0;
-  return 4 * align256(staging_bytes_per_buffer(s));  // {K, V} x 2 buffers
+  // {K, V} x 2 gather buffers, then the K and V sink rows
+  return 4 * align256(staging_bytes_per_buffer(s)) + 2 * align256(sink_bytes(s));
 }
 
 struct SideResources {
@@ -275,7 +284,8 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   const int n_blocks = s.seg_len / hga::kBlockQ;
   if (s.hist_loc == HGA_HIST_DEVICE || s.hist_len == 0) {
     const hipError_t e = hga::launch_attn_fwd(s, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse,
-                                              nullptr, nullptr, 0, n_blocks, st,
+                                              nullptr, nullptr, k_hist, v_hist, hga::hist_rows(s), 0,
+                                              n_blocks, st,
                                               hga::timer_event(HGA_KERNEL_ATTN_FWD, 0),
                                               hga::timer_event(HGA_KERNEL_ATTN_FWD, 1));
     if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
@@ -301,10 +311,25 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   char* base = static_cast<char*>(ws);
   void* kbuf[2] = {base, base + buf};
   void* vbuf[2] = {base + 2 * buf, base + 3 * buf};
+  const int n_sink_rows = hga::sink_chunks(s) * hga::kChunk;
+  void* ksink = base + 4 * buf;
+  void* vsink = base + 4 * buf + align256(sink_bytes(s));
   hipError_t e;
   // the side stream must see everything already enqueued on `stream` (sel_groups)
   if ((e = hipEventRecord(r->start, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(r->side, r->start, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  // sink rows: one strided copy per tensor, ahead of the first gather on the
+  // side stream (the first attention phase waits for that gather)
+  if (n_sink_rows > 0) {
+    const size_t row = static_cast<size_t>(s.head_dim) * elem_bytes(s);
+    const size_t pitch = static_cast<size_t>(hga::hist_rows(s)) * row;
+    if ((e = hipMemcpy2DAsync(ksink, n_sink_rows * row, k_hist, pitch, n_sink_rows * row, s.n_kv_heads,
+                              hipMemcpyHostToDevice, r->side)) != hipSuccess)
+      return hip_fail(e, "sink copy");
+    if ((e = hipMemcpy2DAsync(vsink, n_sink_rows * row, v_hist, pitch, n_sink_rows * row, s.n_kv_heads,
+                              hipMemcpyHostToDevice, r->side)) != hipSuccess)
+      return hip_fail(e, "sink copy");
+  }
   // timers (hga_set_kernel_events) span the whole call: GATHER from the start
   // of the first gather to the end of the last, ATTN_FWD from the start of the
   // first attention phase to the end of the last (waits in between included)
@@ -322,8 +347,8 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
       return hip_fail(e, "gather launch");
     if ((e = hipEventRecord(r->gathered[x], r->side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(st, r->gathered[x], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-    if ((e = hga::launch_attn_fwd(s, q, kd, vd, k_seg, v_seg, sel_groups, o, lse, kbuf[x], vbuf[x], b0,
-                                  b1, st, first ? hga::timer_event(HGA_KERNEL_ATTN_FWD, 0) : nullptr,
+    if ((e = hga::launch_attn_fwd(s, q, kd, vd, k_seg, v_seg, sel_groups, o, lse, kbuf[x], vbuf[x],
+                                  ksink, vsink, n_sink_rows, b0, b1, st, first ? hga::timer_event(HGA_KERNEL_ATTN_FWD, 0) : nullptr,
                                   last ? hga::timer_event(HGA_KERNEL_ATTN_FWD, 1) : nullptr)) != hipSuccess)
       return hip_fail(e, "attn_fwd launch");
     if ((e = hipEventRecord(r->consumed[x], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");

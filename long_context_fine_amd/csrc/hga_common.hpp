@@ -124,6 +124,15 @@ __device__ __forceinline__ float sum8_f32(float x) {
 // Rows per KV head in k_hist / v_hist (and x64 / x8 in the chunk / group
 // summaries): hist_stride when set, else hist_len.
 inline int64_t hist_rows(const hga_shape& s) { return s.hist_stride ? s.hist_stride : s.hist_len; }
+// Sink chunks actually present (the sink cannot exceed the history).
+inline int sink_chunks(const hga_shape& s) {
+  const int64_t n_c = s.hist_len / kChunk;
+  return static_cast<int>(s.n_sink_chunks < n_c ? s.n_sink_chunks : n_c);
+}
+// Local window in tokens, clamped to the segment (0 means the whole segment).
+inline int local_window(const hga_shape& s) {
+  return s.local_window <= 0 || s.local_window > s.seg_len ? s.seg_len : s.local_window;
+}
 
 // Timing events of kernel `id` (hga_kernel) set by hga_set_kernel_events, or
 // nullptr: which = 0 is stamped with the start of the entry point's first
@@ -144,10 +153,13 @@ hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_h
                          hipEvent_t ev_start, hipEvent_t ev_stop);
 // staged != nullptr: history rows come from gathered buffers laid out as
 // [n_blocks][n_kv][top_k_groups*8][head_dim] for blocks [block_begin, block_end).
+// Sink rows (the first sink_chunks(s)*64 history tokens) come from k_sink /
+// v_sink, [n_kv][sink_stride][head_dim].
 hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist,
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, void* o, float* lse,
-                           const void* k_staged, const void* v_staged, int32_t block_begin,
+                           const void* k_staged, const void* v_staged, const void* k_sink,
+                           const void* v_sink, int64_t sink_stride, int32_t block_begin,
                            int32_t block_end, hipStream_t stream, hipEvent_t ev_start,
                            hipEvent_t ev_stop);
 hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist,

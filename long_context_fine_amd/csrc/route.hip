@@ -63,7 +63,7 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const T* __restrict__ q, const float* __restrict__ csum, const float* __restrict__ gsum,
-    int seg_len, int n_kv, int r, int n_chunks, int chunk_rows, int k_c, int k_g,
+    int seg_len, int n_kv, int r, int chunk0, int n_chunks, int chunk_rows, int k_c, int k_g,
     float* __restrict__ ws_scores,
     int32_t* __restrict__ sel_chunks, int32_t* __restrict__ sel_groups) {
   constexpr int TPR = D / 8;            // threads per Q row (8 elements each)
@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
   // ---- 2. chunk scores ----------------------------------------------------
   float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
-  const float* cbase = csum + static_cast<int64_t>(j) * chunk_rows * D;
+  // ranked chunks are chunk0 .. chunk0 + n_chunks - 1 (the sink is attended in full)
+  const float* cbase = csum + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
   score_rows<D, 8>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
   __syncthreads();
 
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 #pragma unroll
     for (int e = 0; e < kRegKeys; ++e) {
       const int m = wave * kWave + lane + e * kThreads;
-      keys[e] = m < n_chunks ? rank_key(sc[m], static_cast<uint32_t>(m)) : 0ull;
+      keys[e] = m < n_chunks ? rank_key(sc[m], static_cast<uint32_t>(chunk0 + m)) : 0ull;
     }
     const bool in_regs = n_chunks <= kRegKeys * kThreads;
     uint64_t prev = ~0ull;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
           if (keys[e] < prev && keys[e] > local) local = keys[e];
       } else {
         for (int m = wave * kWave + lane; m < n_chunks; m += kThreads) {
-          const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(m));
+          const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(chunk0 + m));
           if (k < prev && k > local) local = k;
         }
       }
@@ -245,12 +246,13 @@ template <typename T, int D>
 hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const float* gs,
                     int32_t* sc_out, int32_t* sg_out, void* ws, hipStream_t st) {
   const int n_blocks = s.seg_len / kBlockQ;
-  const int n_chunks = static_cast<int>(s.hist_len / kChunk);
+  const int chunk0 = sink_chunks(s);
+  const int n_chunks = static_cast<int>(s.hist_len / kChunk) - chunk0;  // ranked chunks
   const int r = s.n_q_heads / s.n_kv_heads;
   float* scores = static_cast<float*>(ws);
   hipExtLaunchKernelGGL((route_kernel<T, D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
                         timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
-                        static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, n_chunks,
+                        static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
                         static_cast<int>(hist_rows(s) / kChunk),
                         s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out);
   return hipGetLastError();

@@ -42,6 +42,7 @@ class Shape(ctypes.Structure):
         ("hist_len", ctypes.c_int64), ("seg_len", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
         ("hist_loc", ctypes.c_int32), ("hist_stride", ctypes.c_int64),
+        ("n_sink_chunks", ctypes.c_int32), ("local_window", ctypes.c_int32),
     ]
 
     @property
@@ -100,12 +101,13 @@ def lib() -> ctypes.CDLL:
 def make_shape(n_q_heads: int, n_kv_heads: int, head_dim: int, hist_len: int, seg_len: int,
                top_k_chunks: int, top_k_groups: int, dtype=torch.bfloat16,
                softmax_scale: float | None = None, hist_on_host: bool = False,
-               hist_stride: int = 0) -> Shape:
+               hist_stride: int = 0, n_sink_chunks: int = 0, local_window: int = 0) -> Shape:
     return Shape(n_q_heads, n_kv_heads, head_dim, 64, 8, 64, top_k_chunks, top_k_groups,
                  hist_len, seg_len,
                  softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(head_dim),
                  HGA_BF16 if dtype == torch.bfloat16 else HGA_F32,
-                 HGA_HIST_HOST_PINNED if hist_on_host else HGA_HIST_DEVICE, hist_stride)
+                 HGA_HIST_HOST_PINNED if hist_on_host else HGA_HIST_DEVICE, hist_stride,
+                 n_sink_chunks, local_window)
 
 
 def _check(status: int) -> None:

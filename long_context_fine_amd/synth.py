@@ -46,6 +46,8 @@ class Workload:
     input_scale: float
     backward: bool = False
     hist_on_host: bool = False
+    n_sink_chunks: int = 0  # history chunks attended in full (fixed sink)
+    local_window: int = 0   # segment tokens each query sees (0: the whole causal segment)
 
     @property
     def softmax_scale(self) -> float:

@@ -11,6 +11,10 @@ state for one layer and sequences the library's calls around it:
     dq, dk, dv = h.backward(q, k_seg, v_seg, o, lse, d_o)
     h.close_segment(k_seg, v_seg)                # detach: append K/V, summarise
 
+The first `n_sink_chunks` history chunks form a fixed sink attended by every
+query, and `local_window` limits the segment keys each query sees (0: the
+whole causal segment).
+
 History K/V live in one buffer per tensor with room for `max_hist` tokens per
 KV head ([n_kv][max_hist][d], device memory or page-locked host memory), and the
 summaries in [n_kv][max_hist/64][d] / [n_kv][max_hist/8][d]; the library reads
@@ -31,12 +35,14 @@ class LayerHistory:
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, seg_len: int,
                  max_hist: int, top_k_chunks: int, top_k_groups: int,
                  dtype=torch.bfloat16, softmax_scale: float | None = None,
-                 hist_on_host: bool = False, device="cuda"):
+                 hist_on_host: bool = False, device="cuda", n_sink_chunks: int = 0,
+                 local_window: int = 0):
         if max_hist <= 0 or max_hist % 64 or seg_len % 64:
             raise ValueError("max_hist must be a positive multiple of 64 and seg_len a multiple of 64")
         self.n_q, self.n_kv, self.d, self.seg_len = n_q_heads, n_kv_heads, head_dim, seg_len
         self.max_hist, self.k_c, self.k_g = max_hist, top_k_chunks, top_k_groups
         self.dtype, self.scale, self.on_host = dtype, softmax_scale, hist_on_host
+        self.n_sink, self.window = n_sink_chunks, local_window
         self.device = torch.device(device)
         kv = (n_kv_heads, max_hist, head_dim)
         if hist_on_host:
@@ -66,7 +72,8 @@ class LayerHistory:
                               self.hist_len if hist_len is None else hist_len, self.seg_len,
                               self.k_c, self.k_g, self.dtype, self.scale,
                               self.on_host if hist_on_host is None else hist_on_host,
-                              hist_stride=self.max_hist)
+                              hist_stride=self.max_hist, n_sink_chunks=self.n_sink,
+                              local_window=self.window)
 
     def forward(self, q, k_seg, v_seg):
         """Route the segment's query blocks over the current history and run

@@ -71,6 +71,8 @@ FAKE = 0x10000  # never dereferenced: validation fails first
     ("hist_stride", 14336 - 64, hga.HGA_ERR_INVALID_ARG),   # below hist_len
     ("hist_stride", 14336 + 8, hga.HGA_ERR_INVALID_ARG),    # not a multiple of 64
     ("hist_stride", -64, hga.HGA_ERR_INVALID_ARG),
+    ("n_sink_chunks", -1, hga.HGA_ERR_INVALID_ARG),
+    ("local_window", -5, hga.HGA_ERR_INVALID_ARG),
 ])
 def test_invalid_shapes_are_rejected(L, field, value, status):
     s = _shape(**{field: value})
@@ -127,6 +129,16 @@ def test_workspace_sizes_and_undersized_workspace(L):
     st = L.hga_attn_fwd(ctypes.byref(host), *([FAKE] * 8), FAKE, n_fwd - 1, None)
     assert st == hga.HGA_ERR_WORKSPACE
     assert L.hga_attn_bwd(ctypes.byref(host), *([FAKE] * 13), 1 << 30, None) == hga.HGA_ERR_UNSUPPORTED
+    # sink rows staged per call: + {K, V} x [8][2*64][128] bf16; the sink is
+    # clamped to the history (224 chunks)
+    sink = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED, n_sink_chunks=2, local_window=1024)
+    assert L.hga_workspace_size(ctypes.byref(sink), hga.HGA_OP_ATTN_FWD) == n_fwd + 2 * (8 * 128 * 128 * 2)
+    huge = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED, n_sink_chunks=1000)
+    assert L.hga_workspace_size(ctypes.byref(huge), hga.HGA_OP_ATTN_FWD) == n_fwd + 2 * (8 * 14336 * 128 * 2)
+    # a device-resident sink or a window needs no workspace of its own
+    dev = _shape(n_sink_chunks=4, local_window=512)
+    for op in (hga.HGA_OP_ROUTE, hga.HGA_OP_ATTN_FWD, hga.HGA_OP_ATTN_BWD):
+        assert L.hga_workspace_size(ctypes.byref(dev), op) == L.hga_workspace_size(ctypes.byref(s), op)
 
 
 def test_summary_range_checks(L):

@@ -34,7 +34,8 @@ def _say(*a):
 def _shape(w: synth.Workload):
     return hga.make_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.hist_len, w.seg_len,
                           w.top_k_chunks, w.top_k_groups, w.torch_dtype, w.softmax_scale,
-                          hist_on_host=w.hist_on_host)
+                          hist_on_host=w.hist_on_host, n_sink_chunks=w.n_sink_chunks,
+                          local_window=w.local_window)
 
 
 def _f32(t):
@@ -53,7 +54,10 @@ def _assert_close(name, got, ref, tol):
 
 def run_case(w: synth.Workload, seed: int, check_bwd: bool):
     _say(f"[case] {w.name} seed={seed} H={w.hist_len} S={w.seg_len} nq={w.n_q_heads} "
-         f"nkv={w.n_kv_heads} d={w.head_dim} kc={w.top_k_chunks} kg={w.top_k_groups} {w.dtype}")
+         f"nkv={w.n_kv_heads} d={w.head_dim} kc={w.top_k_chunks} kg={w.top_k_groups} {w.dtype} "
+         f"sink={w.n_sink_chunks} window={w.local_window}")
+    sink_tok = 64 * w.n_sink_chunks
+    window = w.local_window or None
     inp = synth.make_inputs(w, seed, with_grad_out=check_bwd)
     a = {k: _f32(v) for k, v in inp.items()}
     g = _dev(inp)
@@ -71,13 +75,14 @@ def run_case(w: synth.Workload, seed: int, check_bwd: bool):
         assert np.max(np.abs(_f32(G) - G_ref)) <= 2e-6 * kmax
     qbar = orc.block_queries(a["q"], w.n_kv_heads)
     sc_np, sg_np = sel_c.cpu().numpy(), sel_g.cpu().numpy()
-    rep = orc.check_selection(qbar, C_ref, G_ref, sc_np, sg_np, w.top_k_chunks, w.top_k_groups)
+    rep = orc.check_selection(qbar, C_ref, G_ref, sc_np, sg_np, w.top_k_chunks, w.top_k_groups,
+                              n_sink=w.n_sink_chunks)
     _say(f"  route: ok={rep['ok']} chunk_exemptions={rep['chunk_exemptions']} "
          f"group_exemptions={rep['group_exemptions']} failures={rep['failures'][:3]}")
     assert rep["ok"]
 
     O_ref, LSE_ref = orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"],
-                                  sg_np, w.softmax_scale)
+                                  sg_np, w.softmax_scale, n_sink_tokens=sink_tok, window=window)
     tol = TOL[w.dtype]
     _assert_close("O", _f32(o), O_ref, tol)
     _assert_close("LSE", _f32(lse), LSE_ref, tol)
@@ -87,7 +92,8 @@ def run_case(w: synth.Workload, seed: int, check_bwd: bool):
                                   sel_g, o, lse, g["d_o"])
         torch.cuda.synchronize()
         dQ, dK, dV = orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"],
-                                  sg_np, w.softmax_scale, a["d_o"])
+                                  sg_np, w.softmax_scale, a["d_o"], n_sink_tokens=sink_tok,
+                                  window=window)
         _assert_close("dQ", _f32(dq), dQ, tol)
         _assert_close("dK_seg", _f32(dk), dK, tol)
         _assert_close("dV_seg", _f32(dv), dV, tol)
@@ -95,9 +101,10 @@ def run_case(w: synth.Workload, seed: int, check_bwd: bool):
     return out
 
 
-def _w(name, n_q, n_kv, d, H, S, kc, kg, dtype, bwd=True):
+def _w(name, n_q, n_kv, d, H, S, kc, kg, dtype, bwd=True, sink=0, window=0):
     return synth.Workload(name, n_q, n_kv, d, H, S, kc, kg, dtype,
-                          1.0 if dtype == "f32" else 1.0 / math.sqrt(d), backward=bwd)
+                          1.0 if dtype == "f32" else 1.0 / math.sqrt(d), backward=bwd,
+                          n_sink_chunks=sink, local_window=window)
 
 
 SMALL = [
@@ -118,6 +125,24 @@ SMALL = [
 @pytest.mark.parametrize("seed", [0, 1])
 def test_small_cases_match_oracle(w, seed):
     run_case(w, seed, check_bwd=True)
+
+
+# fixed sink chunks and a local segment window beside the routed chunks
+SINK_WINDOW = [
+    _w("f32_sink1_w100", 4, 2, 128, 512, 192, 3, 10, "f32", sink=1, window=100),
+    _w("bf16_sink2_w96_ragged", 8, 2, 128, 1536, 320, 5, 13, "bf16", sink=2, window=96),
+    _w("bf16_r3_d64_sink1_w64", 6, 2, 64, 1024, 192, 3, 20, "bf16", sink=1, window=64),
+    _w("bf16_window1", 4, 2, 128, 512, 256, 4, 16, "bf16", window=1),
+    _w("bf16_mha_sink3_w128", 4, 4, 128, 1024, 192, 4, 16, "bf16", sink=3, window=128),
+    _w("bf16_sink_covers_history", 4, 1, 128, 128, 128, 2, 8, "bf16", sink=4, window=65),
+    _w("bf16_no_history_w70", 4, 2, 128, 0, 256, 4, 8, "bf16", sink=2, window=70),
+    _w("bf16_window_is_segment", 8, 2, 64, 1024, 256, 4, 16, "bf16", sink=1, window=256),
+]
+
+
+@pytest.mark.parametrize("w", SINK_WINDOW, ids=[w.name for w in SINK_WINDOW])
+def test_sink_and_local_window_match_oracle(w):
+    run_case(w, 3, check_bwd=True)
 
 
 def test_route_with_scores_in_workspace():
@@ -248,6 +273,23 @@ def test_qwen3_8b_131k_forward_and_pinned_host_tier():
     o2, lse2 = hga.attn_fwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"])
     torch.cuda.synchronize()
     assert torch.equal(C2, r["C"]) and torch.equal(G2, r["G"])
+    assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
+
+
+def test_pinned_host_tier_with_sink_is_bit_identical():
+    # sink rows are staged from host memory once per call; routed groups are
+    # gathered per phase (6 query blocks: two phases, the second partial)
+    w = _w("bf16_host_sink2_w96", 8, 2, 128, 1536, 384, 5, 13, "bf16", bwd=False, sink=2, window=96)
+    r = run_case(w, 4, check_bwd=False)
+    sh = _shape(w.replace(hist_on_host=True))
+    kh = torch.empty(r["inp"]["k_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty(r["inp"]["v_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
+    kh.copy_(r["inp"]["k_hist"])
+    vh.copy_(r["inp"]["v_hist"])
+    _say("[case] pinned-host history with sink 2, window 96")
+    g = r["g"]
+    o2, lse2 = hga.attn_fwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"])
+    torch.cuda.synchronize()
     assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
 
 

@@ -51,12 +51,15 @@ def _close(name, got, ref, tol=2e-2):
     assert orc.within_tolerance(got, ref, tol), (name, err, rel)
 
 
-def test_segments_match_oracle_on_growing_history():
+@pytest.mark.parametrize("sink,window", [(0, 0), (1, 96)])
+def test_segments_match_oracle_on_growing_history(sink, window):
     segs, k_all, v_all = _sequence(5)
-    h = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, top_k_chunks=K_C, top_k_groups=K_G)
+    h = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, top_k_chunks=K_C, top_k_groups=K_G,
+                           n_sink_chunks=sink, local_window=window)
+    extra = dict(n_sink_tokens=64 * sink, window=window or None)
     scale = 1.0 / math.sqrt(D)
     for i, sg in enumerate(segs):
-        print(f"[case] tbptt segment {i} history {h.hist_len}", flush=True)
+        print(f"[case] tbptt segment {i} history {h.hist_len} sink {sink} window {window}", flush=True)
         g = {k: v.cuda() for k, v in sg.items()}
         o, lse = h.forward(g["q"], g["k"], g["v"])
         dq, dk, dv = h.backward(g["q"], g["k"], g["v"], o, lse, g["d_o"])
@@ -72,14 +75,15 @@ def test_segments_match_oracle_on_growing_history():
             assert np.max(np.abs(_f32(h.group_sum[:, :H // 8]) - G_ref)) <= 2e-6 * kmax
             qbar = orc.block_queries(_f32(sg["q"]), N_KV)
             rep = orc.check_selection(qbar, C_ref, G_ref, h.sel_chunks.cpu().numpy(),
-                                      h.sel_groups.cpu().numpy(), K_C, K_G)
+                                      h.sel_groups.cpu().numpy(), K_C, K_G, n_sink=sink)
             assert rep["ok"], rep["failures"][:3]
         sel = h.sel_groups.cpu().numpy()
-        O_ref, L_ref = orc.attn_fwd(_f32(sg["q"]), kh, vh, _f32(sg["k"]), _f32(sg["v"]), sel, scale)
+        O_ref, L_ref = orc.attn_fwd(_f32(sg["q"]), kh, vh, _f32(sg["k"]), _f32(sg["v"]), sel, scale,
+                                    **extra)
         _close("O", _f32(o), O_ref)
         _close("LSE", _f32(lse), L_ref)
         dQ, dK, dV = orc.attn_bwd(_f32(sg["q"]), kh, vh, _f32(sg["k"]), _f32(sg["v"]), sel, scale,
-                                  _f32(sg["d_o"]))
+                                  _f32(sg["d_o"]), **extra)
         _close("dQ", _f32(dq), dQ)
         _close("dK", _f32(dk), dK)
         _close("dV", _f32(dv), dV)
