@@ -37,6 +37,10 @@ def parse():
                     help="instead of the step benchmark: run the segment-wise driver from an "
                          "empty history up to this many history tokens and report the cost "
                          "of a segment (route + fwd + bwd + close) against history length")
+    ap.add_argument("--sink-chunks", type=int, default=0,
+                    help="history chunks attended in full by every query (fixed sink)")
+    ap.add_argument("--local-window", type=int, default=0,
+                    help="segment tokens each query attends (0: the whole causal segment)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB (one plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -49,15 +53,18 @@ def kernel_work(w, s):
     nq, kv, kc, kg = w.n_q_heads, w.n_kv_heads, w.top_k_chunks, w.top_k_groups
     e = 2 if w.dtype == "bf16" else 4
     n_B, n_C = S // 64, H // 64
+    n_sink = min(w.n_sink_chunks, n_C)     # sink chunks: attended in full, not ranked
+    n_rank = n_C - n_sink
+    W = S if w.local_window <= 0 else min(w.local_window, S)
     seg_tokens = min(S, H)                 # incremental summaries: newest closed segment
-    hist_tok = kg * 8                      # routed history tokens per (block, KV head)
-    pairs_hist = S * hist_tok              # per query head
-    pairs_causal = S * (S + 1) // 2
+    hist_tok = min(kg, 8 * min(kc, n_rank)) * 8   # routed history tokens per (block, KV head)
+    pairs_hist = S * (hist_tok + 64 * n_sink)     # per query head
+    pairs_causal = W * (W + 1) // 2 + (S - W) * W  # query i sees min(i + 1, W) segment keys
     work = {
         "summaries": ("hbm", kv * seg_tokens * d * e + kv * (seg_tokens // 64 + seg_tokens // 8) * d * 4),
         # Q once, the chunk summaries once, the 8*k_c candidate group summaries per
         # (block, KV head), the selections written
-        "route": ("hbm", nq * S * d * e + kv * n_C * d * 4 + n_B * kv * 8 * kc * d * 4
+        "route": ("hbm", nq * S * d * e + kv * n_rank * d * 4 + n_B * kv * 8 * min(kc, n_rank) * d * 4
                   + n_B * kv * (kc + kg) * 4),
         "attn_fwd": ("mfma", 4 * d * nq * (pairs_hist + pairs_causal)),
     }
@@ -113,11 +120,14 @@ def cpu_baseline(w, inp, budget_s):
     n_steps, t_total = 0, 0.0
     while n_steps < 5 and (n_steps == 0 or t_total < budget_s):
         t0 = time.perf_counter()
-        _, sel_g, _ = orc.route(a["q"], a["k_hist"], w.n_kv_heads, w.top_k_chunks, w.top_k_groups)
-        orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel_g, w.softmax_scale)
+        _, sel_g, _ = orc.route(a["q"], a["k_hist"], w.n_kv_heads, w.top_k_chunks, w.top_k_groups,
+                                n_sink=w.n_sink_chunks)
+        extra = dict(n_sink_tokens=64 * w.n_sink_chunks, window=w.local_window or None)
+        orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel_g, w.softmax_scale,
+                     **extra)
         if w.backward:
             orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel_g,
-                         w.softmax_scale, a["d_o"])
+                         w.softmax_scale, a["d_o"], **extra)
         t_total += time.perf_counter() - t0
         n_steps += 1
     cores = 1
@@ -214,9 +224,13 @@ def main():
         sys.exit(1)
     hga.lib()
     w = synth.WORKLOADS[args.workload]
+    if args.sink_chunks or args.local_window:
+        w = w.replace(name=f"{w.name}_sink{args.sink_chunks}_win{args.local_window}",
+                      n_sink_chunks=args.sink_chunks, local_window=args.local_window)
     s = hga.make_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.hist_len, w.seg_len,
                        w.top_k_chunks, w.top_k_groups, w.torch_dtype, w.softmax_scale,
-                       hist_on_host=w.hist_on_host)
+                       hist_on_host=w.hist_on_host, n_sink_chunks=w.n_sink_chunks,
+                       local_window=w.local_window)
     inp = synth.make_inputs(w, args.seed, with_grad_out=w.backward)
     dev = torch.device("cuda:0")
     g = {k: v.to(dev) for k, v in inp.items() if k not in ("k_hist", "v_hist")}
@@ -356,6 +370,7 @@ def main():
                    "hist_len": w.hist_len, "seg_len": w.seg_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "top_k_chunks": w.top_k_chunks, "top_k_groups": w.top_k_groups,
+                   "n_sink_chunks": w.n_sink_chunks, "local_window": w.local_window,
                    "pass": "fwd+bwd" if w.backward else "fwd",
                    "history": "pinned host" if w.hist_on_host else "hbm"},
         "roofline": roof,

@@ -256,6 +256,13 @@ def test_qwen3_8b_16k_forward_backward():
     run_case(synth.WORKLOADS["qwen3_8b_16k_fwdbwd"], 1, check_bwd=True)
 
 
+def test_qwen3_8b_16k_forward_backward_with_sink_and_window():
+    # one sink chunk and a 1,024-token local window beside the 32 routed groups
+    w = synth.WORKLOADS["qwen3_8b_16k_fwdbwd"].replace(name="qwen3_8b_16k_fwdbwd_sink1_win1024",
+                                                       n_sink_chunks=1, local_window=1024)
+    run_case(w, 7, check_bwd=True)
+
+
 def test_qwen3_8b_131k_forward_and_pinned_host_tier():
     w = synth.WORKLOADS["qwen3_8b_131k_fwd"]
     r = run_case(w, 2, check_bwd=False)
