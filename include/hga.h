@@ -80,7 +80,12 @@ typedef enum {
 
 typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
 typedef enum { HGA_HIST_DEVICE = 0, HGA_HIST_HOST_PINNED = 1 } hga_hist_loc;
-typedef enum { HGA_OP_ROUTE = 0, HGA_OP_ATTN_FWD = 1, HGA_OP_ATTN_BWD = 2 } hga_op;
+typedef enum {
+  HGA_OP_ROUTE = 0,
+  HGA_OP_ATTN_FWD = 1,
+  HGA_OP_ATTN_BWD = 2,
+  HGA_OP_ROUTE_CACHED = 3
+} hga_op;
 
 /* Problem description shared by every call. */
 typedef struct {
@@ -117,8 +122,11 @@ typedef struct {
  *   group_sum[j][n] = mean of k_hist[j][8n .. 8n+7] for its 8 groups n.
  * tok_begin, tok_end: multiples of 64 with 0 <= tok_begin <= tok_end <= hist_len
  * (incremental use: summarise only the tokens of a newly closed segment).
- * k_hist lives where shape->hist_loc says (device or pinned host); summaries are
- * device memory. Summaries outside the range are untouched. */
+ * k_hist lives where shape->hist_loc says (device or pinned host); chunk_sum
+ * is device memory; group_sum is device memory or page-locked host memory
+ * (hipHostMalloc; recognised by its pointer attributes, written over the host
+ * link) for use with hga_route_cached. Summaries outside the range are
+ * untouched. */
 hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist,
                                int64_t tok_begin, int64_t tok_end,
                                float* chunk_sum, float* group_sum, void* stream);
@@ -135,6 +143,43 @@ hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist,
 hga_status hga_route(const hga_shape* shape, const void* q, const float* chunk_sum,
                      const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Group-summary cache (gist.science Technical Summary §2.2, "Tiered Memory
+ * Hierarchy", and pith.science review, Figure 2 caption: device memory keeps
+ * every chunk summary but only a cache of group summaries; the rest of the
+ * history lives in host memory). The cache is one device buffer of
+ * hga_gcache_bytes(shape, n_slots) bytes holding n_slots chunk slots per KV
+ * head, each with the 8 group summaries of one chunk, plus the chunk-to-slot
+ * tables. It is tied to (n_kv_heads, head_dim, hist_stride or hist_len,
+ * n_slots): reset it before first use and whenever the history it mirrors is
+ * rewritten; appending history (growing hist_len under a fixed hist_stride)
+ * keeps it valid. 1 <= n_slots <= 16384; 0 is returned for invalid input.
+ * Layout (each part starts on a 256-byte boundary, in this order), readable
+ * for inspection: slot_of_chunk int32 [n_kv][P/64] (-1: not cached),
+ * chunk_of_slot int32 [n_kv][n_slots] (-1: empty), hand int32 [n_kv] (next
+ * slot of the clock), data fp32 [n_kv][n_slots][8][head_dim]. */
+size_t hga_gcache_bytes(const hga_shape* shape, int32_t n_slots);
+
+/* Empties the cache (every slot free, clock hands at slot 0), on `stream`. */
+hga_status hga_gcache_reset(const hga_shape* shape, void* cache, int32_t n_slots, void* stream);
+
+/* hga_route with the group summaries in page-locked host memory (group_sum_host,
+ * [n_kv][P/8][head_dim] fp32, P = hist_stride or hist_len) behind the cache.
+ * Same selections, bit for bit, as hga_route on the same summaries. Runs as
+ * three kernels on `stream`: chunk selection for every block; one cache update
+ * per KV head (the union of the chunks the blocks kept: cached ones are hits
+ * and stay; each miss, in ascending chunk order, takes the next slot in clock
+ * order that no hit of this call holds, and its 8 rows are copied from host
+ * memory); group selection from the cache. Requires
+ * n_slots >= (seg_len/64) * top_k_chunks (every kept chunk fits) and
+ * (seg_len/64) * top_k_chunks <= 8192. stats (device, optional): per KV head
+ * {hits, misses} of this call, int32 [n_kv][2]. ws:
+ * hga_workspace_size(shape, HGA_OP_ROUTE_CACHED) bytes, 256-byte aligned.
+ * Calls that share one cache must be ordered (one stream). */
+hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* chunk_sum,
+                            const float* group_sum_host, void* cache, int32_t n_slots,
+                            int32_t* sel_chunks, int32_t* sel_groups, int32_t* stats,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /* Exact-token attention forward (gist.science Technical Summary §2.1,
  * "Exact-Token Attention"; pith.science review, Figure 1: summaries select
@@ -180,12 +225,13 @@ hga_status hga_gather_groups(const hga_shape* shape, const void* k_hist,
 /* Internal kernels, for hga_set_kernel_events. */
 typedef enum {
   HGA_KERNEL_SUMMARIES = 0,    /* hga_build_summaries */
-  HGA_KERNEL_ROUTE = 1,        /* hga_route */
+  HGA_KERNEL_ROUTE = 1,        /* hga_route; hga_route_cached (all three kernels) */
   HGA_KERNEL_GATHER = 2,       /* hga_gather_groups, pinned-host tier gathers */
   HGA_KERNEL_ATTN_FWD = 3,     /* hga_attn_fwd */
   HGA_KERNEL_BWD_DQ = 4,       /* hga_attn_bwd: dQ (and rowsum(dO * O)) */
   HGA_KERNEL_BWD_DKDV = 5,     /* hga_attn_bwd: dK, dV of the segment (+ partial sum) */
-  HGA_KERNEL_COUNT = 6
+  HGA_KERNEL_GCACHE = 6,       /* hga_route_cached: the cache update */
+  HGA_KERNEL_COUNT = 7
 } hga_kernel;
 
 /* Instrumentation: while set, the launches of `kernel` stamp ev_start with

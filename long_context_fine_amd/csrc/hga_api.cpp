@@ -15,7 +15,6 @@
 #include "hga_common.hpp"
 
 namespace hga {
-size_t route_workspace_bytes(const hga_shape& s);
 size_t bwd_workspace_bytes(const hga_shape& s);
 }  // namespace hga
 
@@ -207,6 +206,7 @@ size_t hga_workspace_size(const hga_shape* shape, int32_t op) {
   if (st != HGA_OK) return 0;
   switch (op) {
     case HGA_OP_ROUTE: return hga::route_workspace_bytes(*shape);
+    case HGA_OP_ROUTE_CACHED: return hga::route_cached_workspace_bytes(*shape);
     case HGA_OP_ATTN_FWD: return fwd_workspace_bytes(*shape);
     case HGA_OP_ATTN_BWD: return hga::bwd_workspace_bytes(*shape);
   }
@@ -226,7 +226,22 @@ hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist, int64
   HGA_REQUIRE(k_hist && chunk_sum && group_sum, "k_hist, chunk_sum and group_sum must be non-NULL");
   const void* kd = k_hist;
   if (s.hist_loc == HGA_HIST_HOST_PINNED) HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
-  const hipError_t e = hga::launch_build_summaries(s, kd, tok_begin, tok_end, chunk_sum, group_sum,
+  float* gd = group_sum;
+  {
+    // group summaries may live in page-locked host memory (the cached route)
+    hipPointerAttribute_t attr;
+    const hipError_t pe = hipPointerGetAttributes(&attr, group_sum);
+    if (pe != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(HGA_ERR_INVALID_ARG, "group_sum is neither device memory nor page-locked host memory");
+    }
+    if (attr.type == hipMemoryTypeHost) {
+      const void* p = nullptr;
+      HGA_TRY(host_to_device_ptr(group_sum, &p, "group_sum"));
+      gd = static_cast<float*>(const_cast<void*>(p));
+    }
+  }
+  const hipError_t e = hga::launch_build_summaries(s, kd, tok_begin, tok_end, chunk_sum, gd,
                                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "build_summaries launch");
   return ok();
@@ -248,6 +263,64 @@ hga_status hga_route(const hga_shape* shape, const void* q, const float* chunk_s
   const hipError_t e = hga::launch_route(s, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "route launch");
+  return ok();
+}
+
+// Validated cache size, or 0 with the error recorded.
+size_t gcache_bytes_checked(const hga_shape& s, int32_t n_slots) {
+  if (n_slots < 1 || n_slots > hga::kGcacheMaxSlots) {
+    fail(HGA_ERR_INVALID_ARG, "n_slots %d outside [1, %d]", n_slots, hga::kGcacheMaxSlots);
+    return 0;
+  }
+  return hga::gcache_layout(s, nullptr, n_slots).bytes;
+}
+
+size_t hga_gcache_bytes(const hga_shape* shape, int32_t n_slots) {
+  if (check_shape(shape) != HGA_OK) return 0;
+  return gcache_bytes_checked(*shape, n_slots);
+}
+
+hga_status hga_gcache_reset(const hga_shape* shape, void* cache, int32_t n_slots, void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_REQUIRE(cache, "cache must be non-NULL");
+  if (gcache_bytes_checked(s, n_slots) == 0) return HGA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(cache) % 256) return fail(HGA_ERR_INVALID_ARG, "cache must be 256-byte aligned");
+  const hipError_t e = hga::launch_gcache_reset(s, hga::gcache_layout(s, cache, n_slots),
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gcache reset launch");
+  return ok();
+}
+
+hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* chunk_sum,
+                            const float* group_sum_host, void* cache, int32_t n_slots,
+                            int32_t* sel_chunks, int32_t* sel_groups, int32_t* stats, void* ws,
+                            size_t ws_bytes, void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_REQUIRE(q && sel_chunks && sel_groups && cache, "q, sel_chunks, sel_groups and cache must be non-NULL");
+  HGA_REQUIRE(s.hist_len == 0 || (chunk_sum && group_sum_host),
+              "chunk_sum and group_sum_host must be non-NULL when hist_len > 0");
+  if (gcache_bytes_checked(s, n_slots) == 0) return HGA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(cache) % 256) return fail(HGA_ERR_INVALID_ARG, "cache must be 256-byte aligned");
+  const int64_t per_call = static_cast<int64_t>(s.seg_len / hga::kBlockQ) * s.top_k_chunks;
+  if (per_call > hga::kGcacheMaxSelected)
+    return fail(HGA_ERR_UNSUPPORTED, "seg_len/64 * top_k_chunks = %lld exceeds %d", static_cast<long long>(per_call),
+                hga::kGcacheMaxSelected);
+  if (n_slots < per_call)
+    return fail(HGA_ERR_INVALID_ARG, "n_slots %d below seg_len/64 * top_k_chunks = %lld (chunks kept per call)",
+                n_slots, static_cast<long long>(per_call));
+  const size_t need = hga::route_cached_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "route_cached needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const void* gd = nullptr;
+  if (s.hist_len > 0) HGA_TRY(host_to_device_ptr(group_sum_host, &gd, "group_sum_host"));
+  const hipError_t e = hga::launch_route_cached(s, q, chunk_sum, hga::gcache_layout(s, cache, n_slots),
+                                                static_cast<const float*>(gd), sel_chunks, sel_groups, stats,
+                                                ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route_cached launch");
   return ok();
 }
 

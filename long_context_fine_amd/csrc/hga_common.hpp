@@ -147,6 +147,28 @@ hipError_t launch_build_summaries(const hga_shape& s, const void* k_hist, int64_
 hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,
                         const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
                         void* ws, hipStream_t stream);
+
+// Group-summary cache state, one caller buffer in 256-byte aligned parts:
+// slot_of_chunk [n_kv][hist_rows/64] (-1: not cached), chunk_of_slot
+// [n_kv][n_slots] (-1: empty), hand [n_kv] (clock position), data
+// [n_kv][n_slots][8][head_dim] fp32 (the 8 group summaries of a chunk).
+constexpr int kGcacheMaxSelected = 8192;  // seg_len/64 * top_k_chunks per call
+constexpr int kGcacheMaxSlots = 16384;
+struct GcacheLayout {
+  int32_t* slot_of_chunk;
+  int32_t* chunk_of_slot;
+  int32_t* hand;
+  float* data;
+  int n_slots;
+  size_t bytes;
+};
+GcacheLayout gcache_layout(const hga_shape& s, void* cache, int n_slots);
+size_t route_workspace_bytes(const hga_shape& s);
+size_t route_cached_workspace_bytes(const hga_shape& s);
+hipError_t launch_gcache_reset(const hga_shape& s, const GcacheLayout& L, hipStream_t stream);
+hipError_t launch_route_cached(const hga_shape& s, const void* q, const float* chunk_sum,
+                               const GcacheLayout& L, const float* group_sum_dev, int32_t* sel_chunks,
+                               int32_t* sel_groups, int32_t* stats, void* ws, hipStream_t stream);
 hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_hist,
                          const int32_t* sel_groups, void* k_out, void* v_out,
                          int32_t block_begin, int32_t block_end, hipStream_t stream,

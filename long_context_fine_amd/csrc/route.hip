@@ -12,6 +12,11 @@
 //   5. group top-k by rank counting; candidates are enumerated in ascending
 //      group id, so ballot prefix counts place the output in ascending order.
 // HBM/latency bound. Deterministic.
+//
+// With group summaries in host memory (the group-summary cache) the same
+// kernel runs in two halves around gcache_update_kernel: phases 1-3 (and q-bar
+// kept in the workspace), then the cache update for all blocks of a KV head,
+// then phases 4-5 reading group rows from the cache slots.
 #include "hga_common.hpp"
 
 namespace hga {
@@ -60,12 +65,23 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
   }
 }
 
-template <typename T, int D>
+enum RouteMode { kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2 };
+
+// Group rows of the cache: [n_kv][n_slots][8][D] fp32, slot of each chunk in
+// slot_of_chunk[n_kv][chunk_rows] (-1: not cached).
+struct CacheView {
+  const int32_t* slot_of_chunk;
+  const float* data;
+  int n_slots;
+};
+
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const T* __restrict__ q, const float* __restrict__ csum, const float* __restrict__ gsum,
     int seg_len, int n_kv, int r, int chunk0, int n_chunks, int chunk_rows, int k_c, int k_g,
     float* __restrict__ ws_scores,
-    int32_t* __restrict__ sel_chunks, int32_t* __restrict__ sel_groups) {
+    int32_t* __restrict__ sel_chunks, int32_t* __restrict__ sel_groups,
+    float* __restrict__ ws_qbar, CacheView cache) {
   constexpr int TPR = D / 8;            // threads per Q row (8 elements each)
   constexpr int RG = kThreads / TPR;    // row groups
   constexpr int NW = kThreads / kWave;
@@ -79,13 +95,17 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ __attribute__((aligned(16))) uint64_t gkey[kMaxCand];
   __shared__ uint64_t wmask[kMaxCand / kWave];
   __shared__ int32_t cnt_s[kThreads / 2];
+  __shared__ int32_t slot_s[kMaxTopKChunks];
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int b = blockIdx.x, j = blockIdx.y;
   const int64_t bj = static_cast<int64_t>(b) * n_kv + j;
 
   // ---- 1. block query ----------------------------------------------------
-  {
+  if constexpr (MODE == kRouteGroups) {
+    if (t < D) qv[t] = ws_qbar[bj * D + t];
+    __syncthreads();
+  } else {
     const int dc = t % TPR, rg = t / TPR;
     const int rows = kBlockQ * r;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -104,84 +124,104 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       float s = 0.f;
       for (int g = 0; g < RG; ++g) s += part[g][t];
       qv[t] = s * (1.0f / static_cast<float>(rows));
+      if constexpr (MODE == kRouteChunks) ws_qbar[bj * D + t] = qv[t];
     }
     __syncthreads();
   }
 
-  // ---- 2. chunk scores ----------------------------------------------------
-  float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
-  // ranked chunks are chunk0 .. chunk0 + n_chunks - 1 (the sink is attended in full)
-  const float* cbase = csum + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
-  score_rows<D, 8>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
-  __syncthreads();
+  int kc_eff;
+  if constexpr (MODE == kRouteGroups) {
+    // kept chunks (ascending, -1 padded) from the first half, with their slots
+    const int c = t < k_c ? sel_chunks[bj * k_c + t] : -1;
+    if (c >= 0) {
+      sorted[t] = c;
+      slot_s[t] = cache.slot_of_chunk[static_cast<int64_t>(j) * chunk_rows + c];
+    }
+    kc_eff = __syncthreads_count(c >= 0);
+  } else {
+    // ---- 2. chunk scores ----------------------------------------------------
+    float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
+    // ranked chunks are chunk0 .. chunk0 + n_chunks - 1 (the sink is attended in full)
+    const float* cbase = csum + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
+    score_rows<D, 8>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
+    __syncthreads();
 
-  // ---- 3. chunk top-k: per-wave top-k over strided elements, then merge ---
-  const int kc_eff = min(k_c, n_chunks);
-  {
-    // keys of this lane's strided share kept in registers across the rounds
-    // when the share is small (the common case), else re-read each round
-    constexpr int kRegKeys = 8;
-    uint64_t keys[kRegKeys];
-#pragma unroll
-    for (int e = 0; e < kRegKeys; ++e) {
-      const int m = wave * kWave + lane + e * kThreads;
-      keys[e] = m < n_chunks ? rank_key(sc[m], static_cast<uint32_t>(chunk0 + m)) : 0ull;
-    }
-    const bool in_regs = n_chunks <= kRegKeys * kThreads;
-    uint64_t prev = ~0ull;
-    for (int round = 0; round < kc_eff; ++round) {
-      uint64_t local = 0;
-      if (in_regs) {
-#pragma unroll
-        for (int e = 0; e < kRegKeys; ++e)
-          if (keys[e] < prev && keys[e] > local) local = keys[e];
-      } else {
-        for (int m = wave * kWave + lane; m < n_chunks; m += kThreads) {
-          const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(chunk0 + m));
-          if (k < prev && k > local) local = k;
-        }
+    // ---- 3. chunk top-k: per-wave top-k over strided elements, then merge ---
+    kc_eff = min(k_c, n_chunks);
+    {
+      // keys of this lane's strided share kept in registers across the rounds
+      // when the share is small (the common case), else re-read each round
+      constexpr int kRegKeys = 8;
+      uint64_t keys[kRegKeys];
+  #pragma unroll
+      for (int e = 0; e < kRegKeys; ++e) {
+        const int m = wave * kWave + lane + e * kThreads;
+        keys[e] = m < n_chunks ? rank_key(sc[m], static_cast<uint32_t>(chunk0 + m)) : 0ull;
       }
-      prev = wave_max_u64(local);      // 0 once this wave has no element left
-      if (lane == 0) wcand[wave][round] = prev;
-    }
-  }
-  __syncthreads();
-  {
-    // t < NW*kc_eff: candidate (wave t / kc_eff, round t % kc_eff)
-    if (t < NW * kc_eff) {
-      const uint64_t mine = wcand[t / kc_eff][t % kc_eff];
-      // candidates are the first kc_eff slots of each wave's row, read two
-      // keys at a time
-      int rank = 0;
-      for (int w2 = 0; w2 < NW; ++w2) {
-        const ulonglong2* row = reinterpret_cast<const ulonglong2*>(wcand[w2]);
-#pragma unroll 4
-        for (int o2 = 0; o2 < (kc_eff + 1) / 2; ++o2) {
-          const ulonglong2 c = row[o2];
-          rank += c.x > mine;
-          rank += (2 * o2 + 1 < kc_eff) && c.y > mine;
+      const bool in_regs = n_chunks <= kRegKeys * kThreads;
+      uint64_t prev = ~0ull;
+      for (int round = 0; round < kc_eff; ++round) {
+        uint64_t local = 0;
+        if (in_regs) {
+  #pragma unroll
+          for (int e = 0; e < kRegKeys; ++e)
+            if (keys[e] < prev && keys[e] > local) local = keys[e];
+        } else {
+          for (int m = wave * kWave + lane; m < n_chunks; m += kThreads) {
+            const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(chunk0 + m));
+            if (k < prev && k > local) local = k;
+          }
         }
+        prev = wave_max_u64(local);      // 0 once this wave has no element left
+        if (lane == 0) wcand[wave][round] = prev;
       }
-      // keys are unique (index in the low bits); the kc_eff best are all valid
-      if (rank < kc_eff) part[0][rank] = __uint_as_float(rank_key_index(mine));
     }
     __syncthreads();
-    if (t < kc_eff) {
-      const int id = static_cast<int>(__float_as_uint(part[0][t]));
-      int pos = 0;
-      for (int u = 0; u < kc_eff; ++u) pos += static_cast<int>(__float_as_uint(part[0][u])) < id;
-      sorted[pos] = id;
+    {
+      // t < NW*kc_eff: candidate (wave t / kc_eff, round t % kc_eff)
+      if (t < NW * kc_eff) {
+        const uint64_t mine = wcand[t / kc_eff][t % kc_eff];
+        // candidates are the first kc_eff slots of each wave's row, read two
+        // keys at a time
+        int rank = 0;
+        for (int w2 = 0; w2 < NW; ++w2) {
+          const ulonglong2* row = reinterpret_cast<const ulonglong2*>(wcand[w2]);
+  #pragma unroll 4
+          for (int o2 = 0; o2 < (kc_eff + 1) / 2; ++o2) {
+            const ulonglong2 c = row[o2];
+            rank += c.x > mine;
+            rank += (2 * o2 + 1 < kc_eff) && c.y > mine;
+          }
+        }
+        // keys are unique (index in the low bits); the kc_eff best are all valid
+        if (rank < kc_eff) part[0][rank] = __uint_as_float(rank_key_index(mine));
+      }
+      __syncthreads();
+      if (t < kc_eff) {
+        const int id = static_cast<int>(__float_as_uint(part[0][t]));
+        int pos = 0;
+        for (int u = 0; u < kc_eff; ++u) pos += static_cast<int>(__float_as_uint(part[0][u])) < id;
+        sorted[pos] = id;
+      }
+      __syncthreads();
+      if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
     }
-    __syncthreads();
-    if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
   }
+  if constexpr (MODE == kRouteChunks) return;
 
   // ---- 4. group scores for the 8 groups of every kept chunk ----------------
   const int n_cand = kc_eff * (kChunk / kGroup);
-  const float* gbase = gsum + static_cast<int64_t>(j) * chunk_rows * (kChunk / kGroup) * D;
-  score_rows<D, 4>(qv, n_cand, [&](int c) {
-    return gbase + (static_cast<int64_t>(sorted[c / 8]) * 8 + (c % 8)) * D;
-  }, gsc);
+  if constexpr (MODE == kRouteGroups) {
+    const float* cbase = cache.data + static_cast<int64_t>(j) * cache.n_slots * (kChunk / kGroup) * D;
+    score_rows<D, 4>(qv, n_cand, [&](int c) {
+      return cbase + (static_cast<int64_t>(slot_s[c / 8]) * 8 + (c % 8)) * D;
+    }, gsc);
+  } else {
+    const float* gbase = gsum + static_cast<int64_t>(j) * chunk_rows * (kChunk / kGroup) * D;
+    score_rows<D, 4>(qv, n_cand, [&](int c) {
+      return gbase + (static_cast<int64_t>(sorted[c / 8]) * 8 + (c % 8)) * D;
+    }, gsc);
+  }
   __syncthreads();
   for (int c = t; c < n_cand; c += kThreads)
     gkey[c] = rank_key(gsc[c], static_cast<uint32_t>(sorted[c / 8] * 8 + (c % 8)));
@@ -242,6 +282,182 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   for (int p = kg_eff + t; p < k_g; p += kThreads) sel_groups[bj * k_g + p] = -1;
 }
 
+
+// ---------------------------------------------------------------------------
+// Group-summary cache update, one workgroup per KV head, between the two
+// halves of the route: the chunks kept by all query blocks of head j are
+// sorted and de-duplicated; cached ones are hits and pin their slots; each
+// miss (ascending chunk id) takes the next unpinned slot in clock order from
+// the head's hand, evicting whatever chunk held it, and its 8 group rows are
+// copied from host memory over the host link. Deterministic; no atomics.
+// ---------------------------------------------------------------------------
+constexpr int kUpdThreads = 1024;
+constexpr int kUpdWaves = kUpdThreads / kWave;
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Exclusive prefix sum of v over the workgroup in thread order; *total gets
+// the sum. Contains barriers: every thread must call it.
+__device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int inc = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < kUpdWaves ? wsum[lane] : 0;
+    const int wi = wave_incl_scan(w, lane);
+    if (lane < kUpdWaves) wsum[lane] = wi - w;
+    if (lane == kUpdWaves - 1) wsum[kUpdWaves] = wi;
+  }
+  __syncthreads();
+  const int r = wsum[wave] + inc - v;
+  *total = wsum[kUpdWaves];
+  __syncthreads();
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kUpdThreads) void gcache_update_kernel(
+    const int32_t* __restrict__ sel_chunks, int n_blocks, int n_kv, int k_c,
+    const float* __restrict__ g_src, int chunk_rows, int32_t* __restrict__ slot_of_chunk,
+    int32_t* __restrict__ chunk_of_slot, int32_t* __restrict__ hand, float* __restrict__ data,
+    int n_slots, int32_t* __restrict__ stats) {
+  __shared__ int32_t list[kGcacheMaxSelected];   // kept chunk ids of all blocks, sorted
+  __shared__ int32_t miss[kGcacheMaxSelected];   // missed chunks, ascending
+  __shared__ int32_t assign[kGcacheMaxSelected]; // their slots
+  __shared__ uint8_t pinned[kGcacheMaxSlots];
+  __shared__ int32_t wsum[kUpdWaves + 1];
+  constexpr int kNone = 0x7fffffff;
+  const int t = threadIdx.x, j = blockIdx.x;
+  const int64_t soc0 = static_cast<int64_t>(j) * chunk_rows;
+  const int64_t cos0 = static_cast<int64_t>(j) * n_slots;
+
+  const int n = n_blocks * k_c;
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int i = t; i < P; i += kUpdThreads) {
+    int c = kNone;
+    if (i < n) {
+      const int v = sel_chunks[(static_cast<int64_t>(i / k_c) * n_kv + j) * k_c + i % k_c];
+      if (v >= 0) c = v;
+    }
+    list[i] = c;
+  }
+  for (int i = t; i < n_slots; i += kUpdThreads) pinned[i] = 0;
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int k = 2; k <= P; k <<= 1)
+    for (int h = k >> 1; h > 0; h >>= 1) {
+      for (int i = t; i < P; i += kUpdThreads) {
+        const int ix = i ^ h;
+        if (ix > i) {
+          const int a = list[i], c = list[ix];
+          if ((a > c) == ((i & k) == 0)) {
+            list[i] = c;
+            list[ix] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+  // hits pin their slots; misses are numbered in ascending chunk order (each
+  // thread owns E consecutive entries of the sorted list)
+  const int E = (P + kUpdThreads - 1) / kUpdThreads;
+  auto first_of_run = [&](int i) { return i < P && list[i] != kNone && (i == 0 || list[i - 1] != list[i]); };
+  int hits_here = 0, misses_here = 0;
+  for (int e = 0; e < E; ++e) {
+    const int i = t * E + e;
+    if (!first_of_run(i)) continue;
+    const int sl = slot_of_chunk[soc0 + list[i]];
+    if (sl >= 0) {
+      pinned[sl] = 1;
+      ++hits_here;
+    } else {
+      ++misses_here;
+    }
+  }
+  int n_hit, n_miss;
+  (void)block_scan_excl(hits_here, &n_hit, wsum);
+  int m = block_scan_excl(misses_here, &n_miss, wsum);
+  for (int e = 0; e < E; ++e) {
+    const int i = t * E + e;
+    if (first_of_run(i) && slot_of_chunk[soc0 + list[i]] < 0) miss[m++] = list[i];
+  }
+
+  // the k-th unpinned slot in clock order from the hand serves miss k (the
+  // host guarantees n_slots >= n_blocks * k_c, so there are enough)
+  const int h0 = hand[j];
+  const int F = (n_slots + kUpdThreads - 1) / kUpdThreads;
+  int free_here = 0;
+  for (int f = 0; f < F; ++f) {
+    const int i = t * F + f;
+    if (i < n_slots && !pinned[(h0 + i) % n_slots]) ++free_here;
+  }
+  int n_free;
+  int rk = block_scan_excl(free_here, &n_free, wsum);
+  for (int f = 0; f < F; ++f) {
+    const int i = t * F + f;
+    if (i >= n_slots) break;
+    const int p = (h0 + i) % n_slots;
+    if (pinned[p]) continue;
+    if (rk < n_miss) {
+      assign[rk] = p;
+      if (rk == n_miss - 1) hand[j] = (p + 1) % n_slots;
+    }
+    ++rk;
+  }
+  __syncthreads();
+
+  // tables: an evicted chunk is never one of this call's misses
+  for (int k = t; k < n_miss; k += kUpdThreads) {
+    const int p = assign[k];
+    const int old = chunk_of_slot[cos0 + p];
+    if (old >= 0) slot_of_chunk[soc0 + old] = -1;
+    slot_of_chunk[soc0 + miss[k]] = p;
+    chunk_of_slot[cos0 + p] = miss[k];
+  }
+  // rows: 8 group summaries (8*D floats) per missed chunk, 4 loads in flight
+  // per thread across the host link
+  constexpr int V4 = kGroup * D / 4;
+  const int64_t total = static_cast<int64_t>(n_miss) * V4;
+  const float4* src = reinterpret_cast<const float4*>(g_src + soc0 * (kChunk / kGroup) * D);
+  float4* dst = reinterpret_cast<float4*>(data + cos0 * (kChunk / kGroup) * D);
+  for (int64_t x0 = t; x0 < total; x0 += 4 * kUpdThreads) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t x = x0 + u * kUpdThreads;
+      if (x < total) v[u] = src[static_cast<int64_t>(miss[x / V4]) * V4 + x % V4];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t x = x0 + u * kUpdThreads;
+      if (x < total) dst[static_cast<int64_t>(assign[x / V4]) * V4 + x % V4] = v[u];
+    }
+  }
+  if (t == 0 && stats) {
+    stats[2 * j] = n_hit;
+    stats[2 * j + 1] = n_miss;
+  }
+}
+
+__global__ void gcache_reset_kernel(int32_t* __restrict__ slot_of_chunk, int64_t n_soc,
+                                    int32_t* __restrict__ chunk_of_slot, int64_t n_cos,
+                                    int32_t* __restrict__ hand, int n_kv) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n_soc) slot_of_chunk[i] = -1;
+  if (i < n_cos) chunk_of_slot[i] = -1;
+  if (i < n_kv) hand[i] = 0;
+}
+
 template <typename T, int D>
 hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const float* gs,
                     int32_t* sc_out, int32_t* sg_out, void* ws, hipStream_t st) {
@@ -250,11 +466,40 @@ hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const fl
   const int n_chunks = static_cast<int>(s.hist_len / kChunk) - chunk0;  // ranked chunks
   const int r = s.n_q_heads / s.n_kv_heads;
   float* scores = static_cast<float*>(ws);
-  hipExtLaunchKernelGGL((route_kernel<T, D>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteFull>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
                         timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
                         static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
                         static_cast<int>(hist_rows(s) / kChunk),
-                        s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out);
+                        s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, nullptr, CacheView{});
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_cached_t(const hga_shape& s, const void* q, const float* cs, const GcacheLayout& L,
+                           const float* g_src, int32_t* sc_out, int32_t* sg_out, int32_t* stats,
+                           void* ws, hipStream_t st) {
+  const int n_blocks = s.seg_len / kBlockQ;
+  const int chunk0 = sink_chunks(s);
+  const int n_chunks = static_cast<int>(s.hist_len / kChunk) - chunk0;
+  const int chunk_rows = static_cast<int>(hist_rows(s) / kChunk);
+  const int r = s.n_q_heads / s.n_kv_heads;
+  float* scores = static_cast<float*>(ws);
+  float* qbar = reinterpret_cast<float*>(static_cast<char*>(ws) + route_workspace_bytes(s));
+  const dim3 grid(n_blocks, s.n_kv_heads);
+  const CacheView view{L.slot_of_chunk, L.data, L.n_slots};
+  // ROUTE spans both halves and the update between them; GCACHE the update
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteChunks>), grid, dim3(kThreads), 0, st,
+                        timer_event(HGA_KERNEL_ROUTE, 0), nullptr, 0,
+                        static_cast<const T*>(q), cs, nullptr, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
+                        chunk_rows, s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, qbar, view);
+  hipExtLaunchKernelGGL((gcache_update_kernel<D>), dim3(s.n_kv_heads), dim3(kUpdThreads), 0, st,
+                        timer_event(HGA_KERNEL_GCACHE, 0), timer_event(HGA_KERNEL_GCACHE, 1), 0,
+                        static_cast<const int32_t*>(sc_out), n_blocks, s.n_kv_heads, s.top_k_chunks, g_src,
+                        chunk_rows, L.slot_of_chunk, L.chunk_of_slot, L.hand, L.data, L.n_slots, stats);
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteGroups>), grid, dim3(kThreads), 0, st,
+                        nullptr, timer_event(HGA_KERNEL_ROUTE, 1), 0,
+                        static_cast<const T*>(q), cs, nullptr, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
+                        chunk_rows, s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, qbar, view);
   return hipGetLastError();
 }
 
@@ -266,6 +511,49 @@ size_t route_workspace_bytes(const hga_shape& s) {
   const size_t n_blocks = s.seg_len / kBlockQ;
   const size_t n_chunks = static_cast<size_t>(s.hist_len / kChunk);
   return align256(sizeof(float) * n_blocks * s.n_kv_heads * (n_chunks ? n_chunks : 1));
+}
+
+GcacheLayout gcache_layout(const hga_shape& s, void* cache, int n_slots) {
+  const size_t n_soc = static_cast<size_t>(s.n_kv_heads) * (hist_rows(s) / kChunk);
+  const size_t n_cos = static_cast<size_t>(s.n_kv_heads) * n_slots;
+  const size_t o_cos = align256(sizeof(int32_t) * n_soc);
+  const size_t o_hand = o_cos + align256(sizeof(int32_t) * n_cos);
+  const size_t o_data = o_hand + align256(sizeof(int32_t) * s.n_kv_heads);
+  char* base = static_cast<char*>(cache);
+  GcacheLayout L;
+  L.slot_of_chunk = base ? reinterpret_cast<int32_t*>(base) : nullptr;
+  L.chunk_of_slot = base ? reinterpret_cast<int32_t*>(base + o_cos) : nullptr;
+  L.hand = base ? reinterpret_cast<int32_t*>(base + o_hand) : nullptr;
+  L.data = base ? reinterpret_cast<float*>(base + o_data) : nullptr;
+  L.n_slots = n_slots;
+  L.bytes = o_data + align256(sizeof(float) * n_cos * (kChunk / kGroup) * s.head_dim);
+  return L;
+}
+
+size_t route_cached_workspace_bytes(const hga_shape& s) {
+  const size_t n_blocks = s.seg_len / kBlockQ;
+  return route_workspace_bytes(s) + align256(sizeof(float) * n_blocks * s.n_kv_heads * s.head_dim);
+}
+
+hipError_t launch_gcache_reset(const hga_shape& s, const GcacheLayout& L, hipStream_t stream) {
+  const int64_t n_soc = static_cast<int64_t>(s.n_kv_heads) * (hist_rows(s) / kChunk);
+  const int64_t n_cos = static_cast<int64_t>(s.n_kv_heads) * L.n_slots;
+  int64_t n = n_soc > n_cos ? n_soc : n_cos;
+  if (n < s.n_kv_heads) n = s.n_kv_heads;
+  hipLaunchKernelGGL(gcache_reset_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                     L.slot_of_chunk, n_soc, L.chunk_of_slot, n_cos, L.hand, s.n_kv_heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_cached(const hga_shape& s, const void* q, const float* chunk_sum,
+                               const GcacheLayout& L, const float* group_sum_dev, int32_t* sel_chunks,
+                               int32_t* sel_groups, int32_t* stats, void* ws, hipStream_t stream) {
+  const bool bf = s.dtype == HGA_BF16;
+  if (s.head_dim == 128)
+    return bf ? launch_cached_t<uint16_t, 128>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream)
+              : launch_cached_t<float, 128>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream);
+  return bf ? launch_cached_t<uint16_t, 64>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream)
+            : launch_cached_t<float, 64>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream);
 }
 
 hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,

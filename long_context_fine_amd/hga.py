@@ -18,13 +18,14 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so"
 HGA_OK, HGA_ERR_INVALID_ARG, HGA_ERR_UNSUPPORTED, HGA_ERR_WORKSPACE, HGA_ERR_HIP = range(5)
 HGA_F32, HGA_BF16 = 0, 1
 HGA_HIST_DEVICE, HGA_HIST_HOST_PINNED = 0, 1
-HGA_OP_ROUTE, HGA_OP_ATTN_FWD, HGA_OP_ATTN_BWD = 0, 1, 2
+HGA_OP_ROUTE, HGA_OP_ATTN_FWD, HGA_OP_ATTN_BWD, HGA_OP_ROUTE_CACHED = 0, 1, 2, 3
 
 EXPORTS = ("hga_build_summaries", "hga_route", "hga_attn_fwd", "hga_attn_bwd",
            "hga_gather_groups", "hga_workspace_size", "hga_status_string",
-           "hga_last_error", "hga_abi_version", "hga_set_kernel_events")
+           "hga_last_error", "hga_abi_version", "hga_set_kernel_events",
+           "hga_gcache_bytes", "hga_gcache_reset", "hga_route_cached")
 
-KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv")
+KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv", "gcache")
 
 
 class HGAError(RuntimeError):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         "hga_attn_fwd": [SP, P, P, P, P, P, P, P, P, P, SZ, P],
         "hga_attn_bwd": [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "hga_gather_groups": [SP, P, P, P, P, P, P],
+        "hga_gcache_reset": [SP, P, I32, P],
+        "hga_route_cached": [SP, P, P, P, P, I32, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -86,6 +89,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.hga_workspace_size.argtypes = [SP, I32]
     L.hga_workspace_size.restype = SZ
+    L.hga_gcache_bytes.argtypes = [SP, I32]
+    L.hga_gcache_bytes.restype = SZ
     L.hga_status_string.argtypes = [ctypes.c_int]
     L.hga_status_string.restype = ctypes.c_char_p
     L.hga_last_error.argtypes = []
@@ -170,7 +175,8 @@ def hga_build_summaries(shape: Shape, k_hist, chunk_sum, group_sum, tok_begin=0,
         ctypes.byref(shape), _ptr(k_hist, (kv, H, d), shape.torch_dtype, "k_hist", not host),
         tok_begin, tok_end,
         _ptr(chunk_sum, (kv, H // 64, d), torch.float32, "chunk_sum"),
-        _ptr(group_sum, (kv, H // 8, d), torch.float32, "group_sum"), _stream(stream)))
+        _ptr(group_sum, (kv, H // 8, d), torch.float32, "group_sum", group_sum.is_cuda),
+        _stream(stream)))
 
 
 def hga_route(shape: Shape, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws=None,
@@ -232,6 +238,69 @@ def hga_gather_groups(shape: Shape, k_hist, v_hist, sel_groups, k_out, v_out, st
         _ptr(v_hist, (kv, H, d), dt, "v_hist", not host),
         _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
         _ptr(k_out, out_shape, dt, "k_out"), _ptr(v_out, out_shape, dt, "v_out"), _stream(stream)))
+
+
+def hga_gcache_bytes(shape: Shape, n_slots: int) -> int:
+    return int(lib().hga_gcache_bytes(ctypes.byref(shape), n_slots))
+
+
+def hga_gcache_reset(shape: Shape, cache, n_slots: int, stream=None) -> None:
+    _check(lib().hga_gcache_reset(ctypes.byref(shape), _ptr(cache, name="cache"), n_slots,
+                                  _stream(stream)))
+
+
+def hga_route_cached(shape: Shape, q, chunk_sum, group_sum_host, cache, n_slots: int, sel_chunks,
+                     sel_groups, stats=None, ws=None, stream=None) -> None:
+    H, kv, d, S = shape.hist_rows, shape.n_kv_heads, shape.head_dim, shape.seg_len
+    if ws is None:
+        ws = alloc_workspace(shape, HGA_OP_ROUTE_CACHED, q.device)
+    _check(lib().hga_route_cached(
+        ctypes.byref(shape), _ptr(q, (shape.n_q_heads, S, d), shape.torch_dtype, "q"),
+        _ptr(chunk_sum, (kv, H // 64, d), torch.float32, "chunk_sum"),
+        _ptr(group_sum_host, (kv, H // 8, d), torch.float32, "group_sum_host", False),
+        _ptr(cache, name="cache"), n_slots,
+        _ptr(sel_chunks, (shape.n_blocks, kv, shape.top_k_chunks), torch.int32, "sel_chunks"),
+        _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        _ptr(stats, (kv, 2), torch.int32, "stats"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class GroupSummaryCache:
+    """One device buffer holding the group-summary cache of a history with the
+    shape's KV heads, head_dim and row capacity (hist_stride or hist_len)."""
+
+    def __init__(self, shape: Shape, n_slots: int, device="cuda"):
+        self.n_slots, self.n_kv, self.d = n_slots, shape.n_kv_heads, shape.head_dim
+        self.chunk_rows = shape.hist_rows // 64
+        n = hga_gcache_bytes(shape, n_slots)
+        if n == 0:
+            _check(HGA_ERR_INVALID_ARG)
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self.reset(shape)
+
+    def reset(self, shape: Shape, stream=None) -> None:
+        hga_gcache_reset(shape, self.buf, self.n_slots, stream)
+
+    def route(self, shape: Shape, q, chunk_sum, group_sum_host, sel_chunks, sel_groups, stats=None,
+              ws=None, stream=None) -> None:
+        hga_route_cached(shape, q, chunk_sum, group_sum_host, self.buf, self.n_slots, sel_chunks,
+                         sel_groups, stats, ws, stream)
+
+    def tables(self):
+        """Views of the buffer's parts (layout of include/hga.h): slot_of_chunk
+        [n_kv][rows/64], chunk_of_slot [n_kv][n_slots], hand [n_kv], data
+        [n_kv][n_slots][8][d]."""
+        def a256(x):
+            return (x + 255) // 256 * 256
+        kv, ns = self.n_kv, self.n_slots
+        o1 = a256(4 * kv * self.chunk_rows)
+        o2 = o1 + a256(4 * kv * ns)
+        o3 = o2 + a256(4 * kv)
+        b = self.buf
+        return (b[:4 * kv * self.chunk_rows].view(torch.int32).view(kv, self.chunk_rows),
+                b[o1:o1 + 4 * kv * ns].view(torch.int32).view(kv, ns),
+                b[o2:o2 + 4 * kv].view(torch.int32),
+                b[o3:o3 + 4 * kv * ns * 8 * self.d].view(torch.float32).view(kv, ns, 8, self.d))
 
 
 # ---------------------------------------------------------------------------

@@ -11,6 +11,10 @@ state for one layer and sequences the library's calls around it:
     dq, dk, dv = h.backward(q, k_seg, v_seg, o, lse, d_o)
     h.close_segment(k_seg, v_seg)                # detach: append K/V, summarise
 
+With `group_cache_slots` > 0 the group summaries live in page-locked host
+memory and routing reads them through an HBM cache of that many chunk slots
+per KV head (`hga_route_cached`; per-call hits and misses in `cache_stats`).
+
 The first `n_sink_chunks` history chunks form a fixed sink attended by every
 query, and `local_window` limits the segment keys each query sees (0: the
 whole causal segment).
@@ -36,7 +40,7 @@ class LayerHistory:
                  max_hist: int, top_k_chunks: int, top_k_groups: int,
                  dtype=torch.bfloat16, softmax_scale: float | None = None,
                  hist_on_host: bool = False, device="cuda", n_sink_chunks: int = 0,
-                 local_window: int = 0):
+                 local_window: int = 0, group_cache_slots: int = 0):
         if max_hist <= 0 or max_hist % 64 or seg_len % 64:
             raise ValueError("max_hist must be a positive multiple of 64 and seg_len a multiple of 64")
         self.n_q, self.n_kv, self.d, self.seg_len = n_q_heads, n_kv_heads, head_dim, seg_len
@@ -53,8 +57,13 @@ class LayerHistory:
             self.v_hist = torch.empty(kv, dtype=dtype, device=self.device)
         self.chunk_sum = torch.zeros((n_kv_heads, max_hist // 64, head_dim), dtype=torch.float32,
                                      device=self.device)
-        self.group_sum = torch.zeros((n_kv_heads, max_hist // 8, head_dim), dtype=torch.float32,
-                                     device=self.device)
+        if group_cache_slots:
+            # group summaries in page-locked host memory behind an HBM cache
+            self.group_sum = torch.zeros((n_kv_heads, max_hist // 8, head_dim), dtype=torch.float32,
+                                         pin_memory=True)
+        else:
+            self.group_sum = torch.zeros((n_kv_heads, max_hist // 8, head_dim), dtype=torch.float32,
+                                         device=self.device)
         self.hist_len = 0
         n_blocks = seg_len // 64
         self.sel_chunks = torch.empty((n_blocks, n_kv_heads, top_k_chunks), dtype=torch.int32,
@@ -62,7 +71,10 @@ class LayerHistory:
         self.sel_groups = torch.empty((n_blocks, n_kv_heads, top_k_groups), dtype=torch.int32,
                                       device=self.device)
         full = self.shape(max_hist)           # workspaces sized for the full history
-        self.ws_route = hga.alloc_workspace(full, hga.HGA_OP_ROUTE, self.device)
+        self.gcache = hga.GroupSummaryCache(full, group_cache_slots, self.device) if group_cache_slots else None
+        self.cache_stats = torch.zeros((n_kv_heads, 2), dtype=torch.int32, device=self.device)
+        self.ws_route = hga.alloc_workspace(
+            full, hga.HGA_OP_ROUTE_CACHED if group_cache_slots else hga.HGA_OP_ROUTE, self.device)
         self.ws_fwd = hga.alloc_workspace(full, hga.HGA_OP_ATTN_FWD, self.device)
         self.ws_bwd = None if hist_on_host else hga.alloc_workspace(full, hga.HGA_OP_ATTN_BWD,
                                                                      self.device)
@@ -80,8 +92,12 @@ class LayerHistory:
         exact-token attention; returns (o, lse). The selections stay in
         `sel_groups` for the backward."""
         s = self.shape()
-        hga.hga_route(s, q, self.chunk_sum, self.group_sum, self.sel_chunks, self.sel_groups,
-                      self.ws_route)
+        if self.gcache is not None:
+            self.gcache.route(s, q, self.chunk_sum, self.group_sum, self.sel_chunks, self.sel_groups,
+                              self.cache_stats, self.ws_route)
+        else:
+            hga.hga_route(s, q, self.chunk_sum, self.group_sum, self.sel_chunks, self.sel_groups,
+                          self.ws_route)
         o = torch.empty_like(q)
         lse = torch.empty((self.n_q, self.seg_len), dtype=torch.float32, device=q.device)
         hga.hga_attn_fwd(s, q, self.k_hist, self.v_hist, k_seg, v_seg, self.sel_groups, o, lse,

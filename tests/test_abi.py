@@ -141,6 +141,34 @@ def test_workspace_sizes_and_undersized_workspace(L):
         assert L.hga_workspace_size(ctypes.byref(dev), op) == L.hga_workspace_size(ctypes.byref(s), op)
 
 
+def test_group_summary_cache_sizes_and_checks(L):
+    s = _shape()                                          # H = 14336: 224 chunks, 8 KV heads
+    a = lambda x: (x + 255) // 256 * 256
+    assert L.hga_gcache_bytes(ctypes.byref(s), 512) == \
+        a(8 * 224 * 4) + a(8 * 512 * 4) + a(8 * 4) + 8 * 512 * 8 * 128 * 4
+    assert L.hga_gcache_bytes(ctypes.byref(s), 0) == 0
+    assert L.hga_gcache_bytes(ctypes.byref(s), 16385) == 0
+    assert L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ROUTE_CACHED) == \
+        32 * 8 * 224 * 4 + 32 * 8 * 128 * 4                # chunk scores + block queries
+    n_ws = 1 << 30
+    # 32 blocks x 16 kept chunks need 512 slots
+    st = L.hga_route_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 511, FAKE, FAKE, None, FAKE, n_ws, None)
+    assert st == hga.HGA_ERR_INVALID_ARG and b"511" in L.hga_last_error()
+    st = L.hga_route_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 512, FAKE, FAKE, None, FAKE, 16, None)
+    assert st == hga.HGA_ERR_WORKSPACE
+    st = L.hga_route_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE + 8, 512, FAKE, FAKE, None, FAKE, n_ws,
+                            None)
+    assert st == hga.HGA_ERR_INVALID_ARG                  # misaligned cache
+    long = _shape(seg_len=65536)                           # 1024 blocks x 16 chunks > 8192
+    st = L.hga_route_cached(ctypes.byref(long), FAKE, FAKE, FAKE, FAKE, 16384, FAKE, FAKE, None, FAKE, n_ws,
+                            None)
+    assert st == hga.HGA_ERR_UNSUPPORTED
+    assert L.hga_route_cached(ctypes.byref(s), FAKE, FAKE, FAKE, None, 512, FAKE, FAKE, None, FAKE, n_ws,
+                              None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_gcache_reset(ctypes.byref(s), None, 512, None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_gcache_reset(ctypes.byref(s), FAKE, 0, None) == hga.HGA_ERR_INVALID_ARG
+
+
 def test_summary_range_checks(L):
     s = _shape()
     assert L.hga_build_summaries(ctypes.byref(s), FAKE, 64, 32, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG

@@ -93,6 +93,29 @@ def test_segments_match_oracle_on_growing_history(sink, window):
     assert torch.equal(h.k_hist[:, :N_SEG * S].cpu(), k_all)
 
 
+def test_group_summary_cache_gives_identical_segments():
+    # group summaries in host memory behind a 6-slot HBM cache (the 2 blocks x
+    # 3 chunks of one call; later segments evict)
+    segs, _, _ = _sequence(7)
+    dev = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, top_k_chunks=K_C, top_k_groups=K_G)
+    cached = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, top_k_chunks=K_C, top_k_groups=K_G,
+                                group_cache_slots=6)
+    for i, sg in enumerate(segs):
+        print(f"[case] tbptt group-summary cache segment {i}", flush=True)
+        g = {k: v.cuda() for k, v in sg.items()}
+        o1, l1 = dev.forward(g["q"], g["k"], g["v"])
+        o2, l2 = cached.forward(g["q"], g["k"], g["v"])
+        torch.cuda.synchronize()
+        assert torch.equal(dev.sel_chunks, cached.sel_chunks)
+        assert torch.equal(dev.sel_groups, cached.sel_groups)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        print(f"  hits/misses {cached.cache_stats.cpu().tolist()}", flush=True)
+        dev.close_segment(g["k"], g["v"])
+        cached.close_segment(g["k"], g["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(dev.group_sum.cpu(), cached.group_sum)
+
+
 def test_pinned_host_history_forward_is_bit_identical():
     segs, _, _ = _sequence(6)
     dev = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, top_k_chunks=K_C, top_k_groups=K_G)
