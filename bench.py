@@ -41,13 +41,16 @@ def parse():
                     help="history chunks attended in full by every query (fixed sink)")
     ap.add_argument("--local-window", type=int, default=0,
                     help="segment tokens each query attends (0: the whole causal segment)")
+    ap.add_argument("--group-cache-slots", type=int, default=0,
+                    help="keep group summaries in page-locked host memory behind an HBM cache "
+                         "of this many chunk slots per KV head (hga_route_cached)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB (one plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
-def kernel_work(w, s):
+def kernel_work(w, s, n_slots=0):
     """Algorithmic bytes / flops per launch of each kernel (see the design notes)."""
     S, H, d = w.seg_len, w.hist_len, w.head_dim
     nq, kv, kc, kg = w.n_q_heads, w.n_kv_heads, w.top_k_chunks, w.top_k_groups
@@ -73,6 +76,8 @@ def kernel_work(w, s):
         work["bwd_dkdv"] = ("mfma", 8 * d * nq * pairs_causal)
     if w.hist_on_host:
         work["gather"] = ("host", n_B * kv * hist_tok * d * e * 2)
+    if n_slots:
+        work["gcache"] = ("host", 0)        # rows moved depend on the call's misses
     return work
 
 
@@ -227,6 +232,8 @@ def main():
     if args.sink_chunks or args.local_window:
         w = w.replace(name=f"{w.name}_sink{args.sink_chunks}_win{args.local_window}",
                       n_sink_chunks=args.sink_chunks, local_window=args.local_window)
+    if args.group_cache_slots:
+        w = w.replace(name=f"{w.name}_gcache{args.group_cache_slots}")
     s = hga.make_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.hist_len, w.seg_len,
                        w.top_k_chunks, w.top_k_groups, w.torch_dtype, w.softmax_scale,
                        hist_on_host=w.hist_on_host, n_sink_chunks=w.n_sink_chunks,
@@ -247,12 +254,21 @@ def main():
     s_dev = hga.make_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.hist_len, w.seg_len,
                            w.top_k_chunks, w.top_k_groups, w.torch_dtype, w.softmax_scale)
     C, G = hga.summaries(s_dev, k_dev)      # summaries of all earlier segments
+    n_slots = args.group_cache_slots
+    if n_slots:
+        # group summaries in page-locked host memory, an HBM cache in front
+        G_dev = G
+        G = torch.empty(G_dev.shape, dtype=torch.float32, pin_memory=True)
+        G.copy_(G_dev)
+        del G_dev
+        cache = hga.GroupSummaryCache(s, n_slots, dev)
+        cstats = torch.zeros((w.n_kv_heads, 2), dtype=torch.int32, device=dev)
     n_B = w.seg_len // 64
     sel_c = torch.empty((n_B, w.n_kv_heads, w.top_k_chunks), dtype=torch.int32, device=dev)
     sel_g = torch.empty((n_B, w.n_kv_heads, w.top_k_groups), dtype=torch.int32, device=dev)
     o = torch.empty_like(g["q"])
     lse = torch.empty((w.n_q_heads, w.seg_len), dtype=torch.float32, device=dev)
-    ws_r = hga.alloc_workspace(s, hga.HGA_OP_ROUTE, dev)
+    ws_r = hga.alloc_workspace(s, hga.HGA_OP_ROUTE_CACHED if n_slots else hga.HGA_OP_ROUTE, dev)
     ws_f = hga.alloc_workspace(s, hga.HGA_OP_ATTN_FWD, dev)
     if w.backward:
         dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k_seg"]), torch.empty_like(g["v_seg"])
@@ -261,7 +277,10 @@ def main():
 
     def step():
         hga.hga_build_summaries(s_dev, k_dev, C, G, tok0, w.hist_len)
-        hga.hga_route(s, g["q"], C, G, sel_c, sel_g, ws_r)
+        if n_slots:
+            cache.route(s, g["q"], C, G, sel_c, sel_g, cstats, ws_r)
+        else:
+            hga.hga_route(s, g["q"], C, G, sel_c, sel_g, ws_r)
         hga.hga_attn_fwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"], sel_g, o, lse, ws_f)
         if w.backward:
             hga.hga_attn_bwd(s, g["q"], g["k_hist"], g["v_hist"], g["k_seg"], g["v_seg"], sel_g, o, lse,
@@ -277,7 +296,7 @@ def main():
     # breakdown and picks the dominant kernel, and (2) the timed region stamps
     # only that kernel, whose durations there give the roofline.
     names = list(hga.KERNELS)
-    work = kernel_work(w, s)
+    work = kernel_work(w, s, n_slots)
 
     def new_events(n):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -304,6 +323,8 @@ def main():
     def entry(name, us):
         kind, amount = work[name]
         ent = {"avg_us": round(us, 3)}
+        if amount == 0:
+            return ent
         if kind == "mfma":
             ent["tflops"] = round(amount / (us * 1e-6) / 1e12, 2)
             ent["gflop_per_launch"] = round(amount / 1e9, 3)
@@ -381,6 +402,37 @@ def main():
         "kernels": kernels,
         "routed_history_tokens_per_block": density,
     }
+    if n_slots:
+        # steady state above: the same queries every step, so every kept chunk
+        # hits after the first call. Cold calls: reset, then route (all misses).
+        steady = cstats.cpu()
+        rid, gid = names.index("route"), names.index("gcache")
+        n_cold = 10
+        ev_r, ev_u = new_events(n_cold), new_events(n_cold)
+        torch.cuda.synchronize()
+        for i in range(n_cold):
+            cache.reset(s)
+            hga.hga_set_kernel_events(rid, *ev_r[i])
+            hga.hga_set_kernel_events(gid, *ev_u[i])
+            cache.route(s, g["q"], C, G, sel_c, sel_g, cstats, ws_r)
+        torch.cuda.synchronize()
+        hga.hga_set_kernel_events(rid, None, None)
+        hga.hga_set_kernel_events(gid, None, None)
+        cold = cstats.cpu()
+        upd_us = avg_us(ev_u)
+        moved = int(cold[:, 1].sum()) * 8 * w.head_dim * 4      # 8 fp32 group rows per miss
+        out["gcache"] = {
+            "slots_per_kv_head": n_slots,
+            "cache_mib": round(cache.buf.numel() / 2 ** 20, 2),
+            "group_summaries_in_host_mib": round(G.numel() * 4 / 2 ** 20, 2),
+            "steady": {"hits": int(steady[:, 0].sum()), "misses": int(steady[:, 1].sum()),
+                       "route_us": kernels["route"]["avg_us"],
+                       "update_us": kernels["gcache"]["avg_us"]},
+            "cold": {"hits": int(cold[:, 0].sum()), "misses": int(cold[:, 1].sum()),
+                     "route_us": round(avg_us(ev_r), 3), "update_us": round(upd_us, 3),
+                     "host_mib": round(moved / 2 ** 20, 2),
+                     "host_gbs": round(moved / (upd_us * 1e-6) / 1e9, 1)},
+        }
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2 ** 20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

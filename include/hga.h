@@ -171,8 +171,8 @@ hga_status hga_gcache_reset(const hga_shape* shape, void* cache, int32_t n_slots
  * and stay; each miss, in ascending chunk order, takes the next slot in clock
  * order that no hit of this call holds, and its 8 rows are copied from host
  * memory); group selection from the cache. Requires
- * n_slots >= (seg_len/64) * top_k_chunks (every kept chunk fits) and
- * (seg_len/64) * top_k_chunks <= 8192. stats (device, optional): per KV head
+ * n_slots >= (seg_len/64) * top_k_chunks (every kept chunk fits),
+ * (seg_len/64) * top_k_chunks <= 8192 and P/64 <= 131072 chunks. stats (device, optional): per KV head
  * {hits, misses} of this call, int32 [n_kv][2]. ws:
  * hga_workspace_size(shape, HGA_OP_ROUTE_CACHED) bytes, 256-byte aligned.
  * Calls that share one cache must be ordered (one stream). */

@@ -307,6 +307,9 @@ hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* 
   if (per_call > hga::kGcacheMaxSelected)
     return fail(HGA_ERR_UNSUPPORTED, "seg_len/64 * top_k_chunks = %lld exceeds %d", static_cast<long long>(per_call),
                 hga::kGcacheMaxSelected);
+  if (hga::hist_rows(s) / hga::kChunk > hga::kGcacheMaxChunks)
+    return fail(HGA_ERR_UNSUPPORTED, "history of %lld rows exceeds the cached route's %d chunks",
+                static_cast<long long>(hga::hist_rows(s)), hga::kGcacheMaxChunks);
   if (n_slots < per_call)
     return fail(HGA_ERR_INVALID_ARG, "n_slots %d below seg_len/64 * top_k_chunks = %lld (chunks kept per call)",
                 n_slots, static_cast<long long>(per_call));

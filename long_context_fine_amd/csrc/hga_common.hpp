@@ -154,6 +154,7 @@ hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_su
 // [n_kv][n_slots][8][head_dim] fp32 (the 8 group summaries of a chunk).
 constexpr int kGcacheMaxSelected = 8192;  // seg_len/64 * top_k_chunks per call
 constexpr int kGcacheMaxSlots = 16384;
+constexpr int kGcacheMaxChunks = 131072;  // hist_rows/64 (8.4M history tokens)
 struct GcacheLayout {
   int32_t* slot_of_chunk;
   int32_t* chunk_of_slot;

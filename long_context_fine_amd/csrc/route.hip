@@ -286,10 +286,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 // ---------------------------------------------------------------------------
 // Group-summary cache update, one workgroup per KV head, between the two
 // halves of the route: the chunks kept by all query blocks of head j are
-// sorted and de-duplicated; cached ones are hits and pin their slots; each
-// miss (ascending chunk id) takes the next unpinned slot in clock order from
-// the head's hand, evicting whatever chunk held it, and its 8 group rows are
-// copied from host memory over the host link. Deterministic; no atomics.
+// de-duplicated through an LDS bitmap over chunk ids; cached ones are hits and
+// pin their slots; each miss (ascending chunk id) takes the next unpinned slot
+// in clock order from the head's hand, evicting whatever chunk held it, and
+// its 8 group rows are copied from host memory over the host link.
+// Deterministic (the only atomics are bitwise ORs into the bitmap).
 // ---------------------------------------------------------------------------
 constexpr int kUpdThreads = 1024;
 constexpr int kUpdWaves = kUpdThreads / kWave;
@@ -329,68 +330,52 @@ __global__ __launch_bounds__(kUpdThreads) void gcache_update_kernel(
     const float* __restrict__ g_src, int chunk_rows, int32_t* __restrict__ slot_of_chunk,
     int32_t* __restrict__ chunk_of_slot, int32_t* __restrict__ hand, float* __restrict__ data,
     int n_slots, int32_t* __restrict__ stats) {
-  __shared__ int32_t list[kGcacheMaxSelected];   // kept chunk ids of all blocks, sorted
-  __shared__ int32_t miss[kGcacheMaxSelected];   // missed chunks, ascending
-  __shared__ int32_t assign[kGcacheMaxSelected]; // their slots
+  __shared__ uint32_t bits[kGcacheMaxChunks / 32];  // chunks kept by some block
+  __shared__ int32_t miss[kGcacheMaxSelected];      // missed chunks, ascending
+  __shared__ int32_t assign[kGcacheMaxSelected];    // their slots
   __shared__ uint8_t pinned[kGcacheMaxSlots];
   __shared__ int32_t wsum[kUpdWaves + 1];
-  constexpr int kNone = 0x7fffffff;
   const int t = threadIdx.x, j = blockIdx.x;
   const int64_t soc0 = static_cast<int64_t>(j) * chunk_rows;
   const int64_t cos0 = static_cast<int64_t>(j) * n_slots;
+  const int n_words = (chunk_rows + 31) / 32;
 
-  const int n = n_blocks * k_c;
-  int P = 1;
-  while (P < n) P <<= 1;
-  for (int i = t; i < P; i += kUpdThreads) {
-    int c = kNone;
-    if (i < n) {
-      const int v = sel_chunks[(static_cast<int64_t>(i / k_c) * n_kv + j) * k_c + i % k_c];
-      if (v >= 0) c = v;
-    }
-    list[i] = c;
-  }
+  for (int i = t; i < n_words; i += kUpdThreads) bits[i] = 0u;
   for (int i = t; i < n_slots; i += kUpdThreads) pinned[i] = 0;
   __syncthreads();
-  // bitonic sort, ascending
-  for (int k = 2; k <= P; k <<= 1)
-    for (int h = k >> 1; h > 0; h >>= 1) {
-      for (int i = t; i < P; i += kUpdThreads) {
-        const int ix = i ^ h;
-        if (ix > i) {
-          const int a = list[i], c = list[ix];
-          if ((a > c) == ((i & k) == 0)) {
-            list[i] = c;
-            list[ix] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  const int n = n_blocks * k_c;
+  for (int i = t; i < n; i += kUpdThreads) {
+    const int c = sel_chunks[(static_cast<int64_t>(i / k_c) * n_kv + j) * k_c + i % k_c];
+    if (c >= 0) atomicOr(&bits[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
 
-  // hits pin their slots; misses are numbered in ascending chunk order (each
-  // thread owns E consecutive entries of the sorted list)
-  const int E = (P + kUpdThreads - 1) / kUpdThreads;
-  auto first_of_run = [&](int i) { return i < P && list[i] != kNone && (i == 0 || list[i - 1] != list[i]); };
+  // each thread owns WPT consecutive bitmap words, i.e. an ascending run of
+  // chunk ids: look the chunks up, pin the hits, count hits and misses
+  const int WPT = (n_words + kUpdThreads - 1) / kUpdThreads;
+  const int w0 = t * WPT, w1 = min(w0 + WPT, n_words);
   int hits_here = 0, misses_here = 0;
-  for (int e = 0; e < E; ++e) {
-    const int i = t * E + e;
-    if (!first_of_run(i)) continue;
-    const int sl = slot_of_chunk[soc0 + list[i]];
-    if (sl >= 0) {
-      pinned[sl] = 1;
-      ++hits_here;
-    } else {
-      ++misses_here;
+  for (int w = w0; w < w1; ++w) {
+    for (uint32_t m = bits[w]; m; m &= m - 1) {
+      const int c = w * 32 + __builtin_ctz(m);
+      const int sl = slot_of_chunk[soc0 + c];
+      if (sl >= 0) {
+        pinned[sl] = 1;
+        ++hits_here;
+      } else {
+        ++misses_here;
+      }
     }
   }
-  int n_hit, n_miss;
-  (void)block_scan_excl(hits_here, &n_hit, wsum);
-  int m = block_scan_excl(misses_here, &n_miss, wsum);
-  for (int e = 0; e < E; ++e) {
-    const int i = t * E + e;
-    if (first_of_run(i) && slot_of_chunk[soc0 + list[i]] < 0) miss[m++] = list[i];
-  }
+  int packed_total;
+  const int base = block_scan_excl(hits_here | (misses_here << 16), &packed_total, wsum);
+  const int n_hit = packed_total & 0xffff, n_miss = packed_total >> 16;
+  int k = base >> 16;
+  for (int w = w0; w < w1; ++w)
+    for (uint32_t m = bits[w]; m; m &= m - 1) {
+      const int c = w * 32 + __builtin_ctz(m);
+      if (slot_of_chunk[soc0 + c] < 0) miss[k++] = c;
+    }
 
   // the k-th unpinned slot in clock order from the hand serves miss k (the
   // host guarantees n_slots >= n_blocks * k_c, so there are enough)
@@ -417,12 +402,12 @@ __global__ __launch_bounds__(kUpdThreads) void gcache_update_kernel(
   __syncthreads();
 
   // tables: an evicted chunk is never one of this call's misses
-  for (int k = t; k < n_miss; k += kUpdThreads) {
-    const int p = assign[k];
+  for (int q = t; q < n_miss; q += kUpdThreads) {
+    const int p = assign[q];
     const int old = chunk_of_slot[cos0 + p];
     if (old >= 0) slot_of_chunk[soc0 + old] = -1;
-    slot_of_chunk[soc0 + miss[k]] = p;
-    chunk_of_slot[cos0 + p] = miss[k];
+    slot_of_chunk[soc0 + miss[q]] = p;
+    chunk_of_slot[cos0 + p] = miss[q];
   }
   // rows: 8 group summaries (8*D floats) per missed chunk, 4 loads in flight
   // per thread across the host link

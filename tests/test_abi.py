@@ -163,6 +163,10 @@ def test_group_summary_cache_sizes_and_checks(L):
     st = L.hga_route_cached(ctypes.byref(long), FAKE, FAKE, FAKE, FAKE, 16384, FAKE, FAKE, None, FAKE, n_ws,
                             None)
     assert st == hga.HGA_ERR_UNSUPPORTED
+    huge = _shape(hist_len=131072 * 64 + 64)              # chunk ids beyond the dedupe bitmap
+    st = L.hga_route_cached(ctypes.byref(huge), FAKE, FAKE, FAKE, FAKE, 512, FAKE, FAKE, None, FAKE, n_ws,
+                            None)
+    assert st == hga.HGA_ERR_UNSUPPORTED
     assert L.hga_route_cached(ctypes.byref(s), FAKE, FAKE, FAKE, None, 512, FAKE, FAKE, None, FAKE, n_ws,
                               None) == hga.HGA_ERR_INVALID_ARG
     assert L.hga_gcache_reset(ctypes.byref(s), None, 512, None) == hga.HGA_ERR_INVALID_ARG
