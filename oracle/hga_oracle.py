@@ -43,6 +43,10 @@ Precision: the routing decisions (summaries, block queries, scores) are taken
 in float32, the precision the kernels decide them in; attention forward and
 backward run in float64.
 
+Decode: the step's query block is the n_new newest tokens (their mean query
+routes); the open segment (not yet summarised) plays the role of the active
+segment, and the history is every closed chunk.
+
 Parity pins live in tests/test_oracle.py (dense-attention equivalence through
 torch's SDPA, brute-force top-k, closed forms, finite differences). No function
 here is left unpinned.
@@ -289,6 +293,79 @@ def attn_bwd(q, k_hist, v_hist, k_seg, v_seg, sel_groups, scale, d_o, n_sink_tok
             dK[j, loc0:loc0 + n_loc] += scale * (dS[:, n_hist:].T @ Qb)
             dV[j, loc0:loc0 + n_loc] += P[:, n_hist:].T @ dOb
     return dQ, dK, dV
+
+
+# ---------------------------------------------------------------------------
+# Decode / retrieval step [gist §3 "Key Contributions": the trained adapter can
+# run with HGA for retrieval and generation; gist 2.1 for the routing and the
+# key set; gist 2.2 for the closed history and the open segment]
+# ---------------------------------------------------------------------------
+def decode_query_mean(q_new: np.ndarray, n_kv: int) -> np.ndarray:
+    """qbar[j] = mean of the n_new newest queries over the r heads of KV head
+    j: the decode step's query block. float32 [n_kv][d]."""
+    n_q, n_new, d = q_new.shape
+    if n_q % n_kv:
+        raise ValueError("bad query shape")
+    r = n_q // n_kv
+    acc = np.zeros((n_kv, d), dtype=F32)
+    for j in range(n_kv):
+        for h in range(j * r, (j + 1) * r):
+            for i in range(n_new):
+                acc[j] += np.asarray(q_new[h, i], F32)
+    acc *= F32(1.0 / (n_new * r))
+    return acc
+
+
+def decode_step(q_new, k_hist, v_hist, k_tail, v_tail, k_c, k_g, scale, n_sink=0, window=None,
+                sel_groups=None):
+    """One decode step of one sequence.
+
+    The history (k_hist / v_hist [n_kv][H][d], H a multiple of 64) is closed
+    and summarised; the open segment (k_tail / v_tail [n_kv][T][d], not yet
+    summarised) ends with the n_new tokens whose queries are q_new
+    [n_q][n_new][d], at open-segment positions T - n_new .. T - 1. Routing as
+    in training, with the n_new queries as the query block; query i at
+    position p attends the sink tokens, the tokens of the selected groups and
+    the open-segment tokens t with p - W < t <= p (W = window, default the
+    whole open segment). sel_groups [n_kv][k_g], if given, replaces the
+    routed selection in the attention (to judge a kernel's outputs with its
+    own selection).
+
+    Returns (sel_chunks int32 [n_kv][k_c], sel_groups int32 [n_kv][k_g],
+    O float64 [n_q][n_new][d], LSE float64 [n_q][n_new]).
+    """
+    n_q, n_new, d = q_new.shape
+    n_kv, T, _ = k_tail.shape
+    H = k_hist.shape[1]
+    if n_new > T:
+        raise ValueError("the open segment must hold the new tokens")
+    r = n_q // n_kv
+    qbar = decode_query_mean(q_new, n_kv)[None]           # one query block
+    if H:
+        sel_c, _ = route_chunks(qbar, chunk_summaries(k_hist), k_c, n_sink)
+        sel_g = route_groups(qbar, group_summaries(k_hist), sel_c, k_g)
+    else:
+        sel_c = np.full((1, n_kv, k_c), -1, np.int32)
+        sel_g = np.full((1, n_kv, k_g), -1, np.int32)
+    use = sel_g[0] if sel_groups is None else np.asarray(sel_groups)
+    W = T if window is None or window <= 0 else min(int(window), T)
+    sink_tok = min(n_sink * CHUNK, H)
+    O = np.zeros((n_q, n_new, d), F64)
+    LSE = np.zeros((n_q, n_new), F64)
+    for h in range(n_q):
+        j = h // r
+        hist = attended_history_tokens(use[j], sink_tok)
+        for i in range(n_new):
+            p = T - n_new + i
+            loc = np.arange(max(0, p - W + 1), p + 1)
+            K = np.concatenate([np.asarray(k_hist[j][hist], F64), np.asarray(k_tail[j][loc], F64)])
+            V = np.concatenate([np.asarray(v_hist[j][hist], F64), np.asarray(v_tail[j][loc], F64)])
+            sc = scale * (K @ np.asarray(q_new[h, i], F64))
+            m = sc.max()
+            e = np.exp(sc - m)
+            O[h, i] = (e @ V) / e.sum()
+            LSE[h, i] = m + np.log(e.sum())
+    return sel_c[0], sel_g[0], O, LSE
 
 
 # ---------------------------------------------------------------------------

@@ -532,3 +532,94 @@ def test_output_tolerance_is_not_vacuous():
             assert not orc.within_tolerance(g_bad[i], g_ref[i], tol)
         assert orc.within_tolerance(torch.from_numpy(g_ref[i]).bfloat16().double().numpy(),
                                     g_ref[i], tol)
+
+
+# ---------------------------------------------------------------------------
+# decode step: pinned to the training block, to SDPA and to a closed form
+# ---------------------------------------------------------------------------
+def test_decode_query_mean_closed_form():
+    # q[h][i] = (h * n_new + i) * 1 -> mean over the r heads of KV head j and
+    # the n_new rows = j * r * n_new + (r * n_new - 1) / 2
+    n_q, n_kv, n_new, d = 6, 2, 3, 8
+    q = np.zeros((n_q, n_new, d))
+    for h in range(n_q):
+        for i in range(n_new):
+            q[h, i] = h * n_new + i
+    qbar = orc.decode_query_mean(q, n_kv)
+    r = n_q // n_kv
+    for j in range(n_kv):
+        assert np.all(qbar[j] == np.float32(j * r * n_new + (r * n_new - 1) / 2))
+
+
+def test_decode_of_a_full_block_equals_the_training_block():
+    # 64 new tokens at the end of a 128-token open segment are query block 1
+    # of training with that segment: same routing, same outputs
+    w = _small(hist_len=512, seg_len=128, top_k_chunks=3, top_k_groups=6)
+    inp = _np(synth.make_inputs(w, seed=31))
+    sel_c, sel_g, _ = orc.route(inp["q"], inp["k_hist"], 2, 3, 6, n_sink=1)
+    O, LSE = orc.attn_fwd(inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"],
+                          sel_g, w.softmax_scale, n_sink_tokens=64, window=100)
+    dc, dg, Od, Ld = orc.decode_step(inp["q"][:, 64:], inp["k_hist"], inp["v_hist"], inp["k_seg"],
+                                     inp["v_seg"], 3, 6, w.softmax_scale, n_sink=1, window=100)
+    assert np.array_equal(dc, sel_c[1]) and np.array_equal(dg, sel_g[1])
+    assert np.max(np.abs(Od - O[:, 64:])) < 1e-12 and np.max(np.abs(Ld - LSE[:, 64:])) < 1e-12
+
+
+@pytest.mark.parametrize("T,n_new,n_sink,W", [(77, 1, 0, None), (77, 3, 1, 20), (5, 2, 2, 3),
+                                              (130, 4, 0, 1)])
+def test_decode_matches_sdpa_with_explicit_keys(T, n_new, n_sink, W):
+    # ragged open segment; keys: sink, selected groups, window of the open
+    # segment ending at each new token
+    rng = np.random.default_rng(T * 7 + n_new)
+    n_q, n_kv, d, H = 4, 2, 16, 512
+    q = rng.standard_normal((n_q, n_new, d))
+    kh, vh = rng.standard_normal((n_kv, H, d)), rng.standard_normal((n_kv, H, d))
+    kt, vt = rng.standard_normal((n_kv, T, d)), rng.standard_normal((n_kv, T, d))
+    scale = 0.25
+    sc, sg, O, LSE = orc.decode_step(q, kh, vh, kt, vt, 3, 7, scale, n_sink=n_sink, window=W)
+    r = n_q // n_kv
+    Wd = T if W is None else W
+    allowed = np.zeros((n_q, n_new, H + T), bool)
+    for h in range(n_q):
+        for i in range(n_new):
+            allowed[h, i, :64 * n_sink] = True
+            for n in sg[h // r]:
+                if n >= 0:
+                    allowed[h, i, 8 * n:8 * n + 8] = True
+            p = T - n_new + i
+            allowed[h, i, H + max(0, p - Wd + 1):H + p + 1] = True
+    ref, ref_lse = _sdpa_with_key_mask(q, np.concatenate([kh, kt], 1), np.concatenate([vh, vt], 1),
+                                       allowed, scale)
+    assert np.max(np.abs(O - ref)) < 1e-12 and np.max(np.abs(LSE - ref_lse)) < 1e-12
+    # the sink is never routed; routed groups lie inside routed chunks
+    assert (sc[sc >= 0] >= n_sink).all()
+    for j in range(n_kv):
+        assert set(int(g) // 8 for g in sg[j] if g >= 0) <= set(int(c) for c in sc[j] if c >= 0)
+
+
+def test_decode_full_budget_is_dense_causal_attention():
+    rng = np.random.default_rng(3)
+    n_q, n_kv, d, H, T, n_new = 4, 1, 16, 256, 40, 2
+    q = rng.standard_normal((n_q, n_new, d))
+    kh, vh = rng.standard_normal((n_kv, H, d)), rng.standard_normal((n_kv, H, d))
+    kt, vt = rng.standard_normal((n_kv, T, d)), rng.standard_normal((n_kv, T, d))
+    sc, sg, O, LSE = orc.decode_step(q, kh, vh, kt, vt, 4, 32, 0.3)
+    assert (sg[0] == np.arange(32)).all()
+    pos = H + T - n_new + np.arange(n_new)[:, None]
+    allowed = np.broadcast_to(np.arange(H + T)[None, :] <= pos, (n_q, n_new, H + T)).copy()
+    ref, ref_lse = _sdpa_with_key_mask(q, np.concatenate([kh, kt], 1), np.concatenate([vh, vt], 1),
+                                       allowed, 0.3)
+    assert np.max(np.abs(O - ref)) < 1e-12 and np.max(np.abs(LSE - ref_lse)) < 1e-12
+
+
+def test_decode_without_history_attends_the_open_segment():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((2, 1, 8))
+    kt, vt = rng.standard_normal((1, 9, 8)), rng.standard_normal((1, 9, 8))
+    empty = np.zeros((1, 0, 8))
+    sc, sg, O, _ = orc.decode_step(q, empty, empty, kt, vt, 2, 4, 1.0)
+    assert (sc == -1).all() and (sg == -1).all()
+    for h in range(2):
+        s = kt[0] @ q[h, 0]
+        p = np.exp(s - s.max())
+        assert np.allclose(O[h, 0], p @ vt[0] / p.sum(), rtol=0, atol=1e-13)
