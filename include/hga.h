@@ -181,6 +181,42 @@ hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* 
                             int32_t* sel_chunks, int32_t* sel_groups, int32_t* stats,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Decode step for a batch of sequences (gist.science §3 "Key Contributions":
+ * the trained adapter runs with HGA for retrieval and generation; the routing
+ * and key set of §2.1 with the history / open-segment split of §2.2).
+ * Sequence b has a closed, summarised history of hist_lens[b] tokens and an
+ * open segment of tail_lens[b] tokens that ends with its n_new newest tokens,
+ * whose queries are q[b]. The step routes with the mean of those queries over
+ * the r heads of each KV head (as hga_route does for a 64-query block) and,
+ * for new token i at open-segment position p = tail_lens[b] - n_new + i,
+ * attends the sink tokens, the tokens of the selected groups and the
+ * open-segment tokens t with p - W < t <= p (W = local_window, default the
+ * whole open segment):
+ *   o[b][h][i] = sum_t softmax_t(scale * q[b][h][i] . k_t) v_t, lse likewise.
+ * Layouts (device memory; P = hist_stride or hist_len is the history
+ * capacity, T = seg_len the open-segment capacity):
+ *   q, o           [batch][n_q][n_new][head_dim]        (dtype)
+ *   k_hist, v_hist [batch][n_kv][P][head_dim]           (dtype)
+ *   chunk_sum      [batch][n_kv][P/64][head_dim]        fp32 (hga_build_summaries per sequence)
+ *   group_sum      [batch][n_kv][P/8][head_dim]         fp32
+ *   k_tail, v_tail [batch][n_kv][T][head_dim]           (dtype)
+ *   hist_lens, tail_lens  int32 [batch], device memory: read by the kernels,
+ *                  clamped to [0, P] (rounded down to whole chunks) and to
+ *                  [n_new, T]
+ *   sel_chunks [batch][n_kv][top_k_chunks], sel_groups [batch][n_kv][top_k_groups]
+ *   lse            fp32 [batch][n_q][n_new]
+ * Requires hist_loc = HGA_HIST_DEVICE, 1 <= n_new <= seg_len and
+ * r * n_new <= 16 (r = n_q_heads / n_kv_heads). ws:
+ * hga_decode_workspace_size(shape, batch, n_new) bytes, 256-byte aligned. */
+size_t hga_decode_workspace_size(const hga_shape* shape, int32_t batch, int32_t n_new);
+
+hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, const void* q,
+                      const void* k_hist, const void* v_hist, const float* chunk_sum,
+                      const float* group_sum, const void* k_tail, const void* v_tail,
+                      const int32_t* hist_lens, const int32_t* tail_lens,
+                      int32_t* sel_chunks, int32_t* sel_groups, void* o, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Exact-token attention forward (gist.science Technical Summary §2.1,
  * "Exact-Token Attention"; pith.science review, Figure 1: summaries select
  * regions, attention uses exact K/V only). For query i of head h (block
@@ -231,7 +267,8 @@ typedef enum {
   HGA_KERNEL_BWD_DQ = 4,       /* hga_attn_bwd: dQ (and rowsum(dO * O)) */
   HGA_KERNEL_BWD_DKDV = 5,     /* hga_attn_bwd: dK, dV of the segment (+ partial sum) */
   HGA_KERNEL_GCACHE = 6,       /* hga_route_cached: the cache update */
-  HGA_KERNEL_COUNT = 7
+  HGA_KERNEL_DECODE = 7,       /* hga_decode: attention pieces + merge (its route stamps ROUTE) */
+  HGA_KERNEL_COUNT = 8
 } hga_kernel;
 
 /* Instrumentation: while set, the launches of `kernel` stamp ev_start with

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libhga.so")
-SOURCES = ["hga_api.cpp", "summaries.hip", "route.hip", "gather.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["hga_api.cpp", "summaries.hip", "route.hip", "gather.hip", "attn_fwd.hip", "attn_bwd.hip",
+           "decode.hip"]
 ARCH = "gfx950"
 
 

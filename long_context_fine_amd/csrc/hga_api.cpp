@@ -327,6 +327,57 @@ hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* 
   return ok();
 }
 
+// Decode validation; 0 bytes (with the error recorded) when invalid.
+hga_status decode_check(const hga_shape& s, int32_t batch, int32_t n_new) {
+  if (s.hist_loc != HGA_HIST_DEVICE)
+    return fail(HGA_ERR_UNSUPPORTED, "decode needs device-resident history (hist_loc = HGA_HIST_DEVICE)");
+  if (batch < 1) return fail(HGA_ERR_INVALID_ARG, "batch %d must be >= 1", batch);
+  if (n_new < 1 || n_new > s.seg_len)
+    return fail(HGA_ERR_INVALID_ARG, "n_new %d outside [1, seg_len = %d]", n_new, s.seg_len);
+  const int r = s.n_q_heads / s.n_kv_heads;
+  if (r * n_new > 16)
+    return fail(HGA_ERR_UNSUPPORTED, "r * n_new = %d query rows per KV head exceed 16", r * n_new);
+  return HGA_OK;
+}
+
+size_t decode_ws_parts(const hga_shape& s, int32_t batch, int32_t n_new, size_t* route_part) {
+  *route_part = hga::decode_route_workspace_bytes(s, batch);
+  return *route_part + hga::decode_attn_workspace_bytes(s, batch, n_new);
+}
+
+size_t hga_decode_workspace_size(const hga_shape* shape, int32_t batch, int32_t n_new) {
+  if (check_shape(shape) != HGA_OK || decode_check(*shape, batch, n_new) != HGA_OK) return 0;
+  size_t route_part;
+  return decode_ws_parts(*shape, batch, n_new, &route_part);
+}
+
+hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, const void* q,
+                      const void* k_hist, const void* v_hist, const float* chunk_sum,
+                      const float* group_sum, const void* k_tail, const void* v_tail,
+                      const int32_t* hist_lens, const int32_t* tail_lens, int32_t* sel_chunks,
+                      int32_t* sel_groups, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_TRY(decode_check(s, batch, n_new));
+  HGA_REQUIRE(q && k_tail && v_tail && hist_lens && tail_lens && sel_chunks && sel_groups && o && lse,
+              "q, k_tail, v_tail, hist_lens, tail_lens, sel_chunks, sel_groups, o and lse must be non-NULL");
+  HGA_REQUIRE(hga::hist_rows(s) == 0 || (k_hist && v_hist && chunk_sum && group_sum),
+              "k_hist, v_hist, chunk_sum and group_sum must be non-NULL when the history capacity is > 0");
+  size_t route_part;
+  const size_t need = decode_ws_parts(s, batch, n_new, &route_part);
+  if (!ws || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hga::launch_decode_route(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks,
+                                          sel_groups, ws, st);
+  if (e != hipSuccess) return hip_fail(e, "decode route launch");
+  e = hga::launch_decode_attn(s, batch, n_new, q, k_hist, v_hist, k_tail, v_tail, sel_groups, hist_lens,
+                              tail_lens, o, lse, static_cast<char*>(ws) + route_part, st);
+  if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  return ok();
+}
+
 hga_status hga_gather_groups(const hga_shape* shape, const void* k_hist, const void* v_hist,
                              const int32_t* sel_groups, void* k_out, void* v_out, void* stream) {
   HGA_TRY(check_shape(shape));

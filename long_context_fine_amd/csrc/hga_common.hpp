@@ -167,6 +167,15 @@ GcacheLayout gcache_layout(const hga_shape& s, void* cache, int n_slots);
 size_t route_workspace_bytes(const hga_shape& s);
 size_t route_cached_workspace_bytes(const hga_shape& s);
 hipError_t launch_gcache_reset(const hga_shape& s, const GcacheLayout& L, hipStream_t stream);
+hipError_t launch_decode_route(const hga_shape& s, int batch, int n_new, const void* q,
+                               const float* chunk_sum, const float* group_sum, const int32_t* hist_lens,
+                               int32_t* sel_chunks, int32_t* sel_groups, void* ws, hipStream_t stream);
+size_t decode_route_workspace_bytes(const hga_shape& s, int batch);
+size_t decode_attn_workspace_bytes(const hga_shape& s, int batch, int n_new);
+hipError_t launch_decode_attn(const hga_shape& s, int batch, int n_new, const void* q, const void* k_hist,
+                              const void* v_hist, const void* k_tail, const void* v_tail,
+                              const int32_t* sel_groups, const int32_t* hist_lens, const int32_t* tail_lens,
+                              void* o, float* lse, void* ws, hipStream_t stream);
 hipError_t launch_route_cached(const hga_shape& s, const void* q, const float* chunk_sum,
                                const GcacheLayout& L, const float* group_sum_dev, int32_t* sel_chunks,
                                int32_t* sel_groups, int32_t* stats, void* ws, hipStream_t stream);

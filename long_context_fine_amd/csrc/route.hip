@@ -65,7 +65,18 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
   }
 }
 
-enum RouteMode { kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2 };
+enum RouteMode { kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2, kRouteDecode = 3 };
+
+// Decode: blockIdx.x is a sequence of the batch, the query block is its
+// seg_len newest tokens (q [batch][n_q][seg_len][D]); summaries are
+// [batch][n_kv][chunk_rows][D] and [batch][n_kv][8*chunk_rows][D]; the
+// sequence's history length comes from hist_lens (clamped to the capacity,
+// whole chunks).
+struct DecodeView {
+  const int32_t* hist_lens;
+  int n_sink;
+  int n_q;
+};
 
 // Group rows of the cache: [n_kv][n_slots][8][D] fp32, slot of each chunk in
 // slot_of_chunk[n_kv][chunk_rows] (-1: not cached).
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     int seg_len, int n_kv, int r, int chunk0, int n_chunks, int chunk_rows, int k_c, int k_g,
     float* __restrict__ ws_scores,
     int32_t* __restrict__ sel_chunks, int32_t* __restrict__ sel_groups,
-    float* __restrict__ ws_qbar, CacheView cache) {
+    float* __restrict__ ws_qbar, CacheView cache, DecodeView dec) {
   constexpr int TPR = D / 8;            // threads per Q row (8 elements each)
   constexpr int RG = kThreads / TPR;    // row groups
   constexpr int NW = kThreads / kWave;
@@ -100,6 +111,15 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int b = blockIdx.x, j = blockIdx.y;
   const int64_t bj = static_cast<int64_t>(b) * n_kv + j;
+  if constexpr (MODE == kRouteDecode) {
+    int hb = dec.hist_lens[b];
+    hb = hb < 0 ? 0 : (hb > chunk_rows * kChunk ? chunk_rows * kChunk : hb);
+    const int nc = hb / kChunk;
+    chunk0 = dec.n_sink < nc ? dec.n_sink : nc;
+    n_chunks = nc - chunk0;
+    csum += static_cast<int64_t>(b) * n_kv * chunk_rows * D;
+    gsum += static_cast<int64_t>(b) * n_kv * chunk_rows * (kChunk / kGroup) * D;
+  }
 
   // ---- 1. block query ----------------------------------------------------
   if constexpr (MODE == kRouteGroups) {
@@ -107,13 +127,19 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     __syncthreads();
   } else {
     const int dc = t % TPR, rg = t / TPR;
-    const int rows = kBlockQ * r;
+    const int rows = (MODE == kRouteDecode ? seg_len : kBlockQ) * r;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll 8
     for (int row = rg; row < rows; row += RG) {
-      const int h = j * r + row / kBlockQ, i = b * kBlockQ + row % kBlockQ;
+      int64_t qrow;
+      if constexpr (MODE == kRouteDecode) {
+        qrow = (static_cast<int64_t>(b) * dec.n_q + j * r + row / seg_len) * seg_len + row % seg_len;
+      } else {
+        const int h = j * r + row / kBlockQ, i = b * kBlockQ + row % kBlockQ;
+        qrow = static_cast<int64_t>(h) * seg_len + i;
+      }
       float v[8];
-      Elem<T>::load8(q + (static_cast<int64_t>(h) * seg_len + i) * D + dc * 8, v);
+      Elem<T>::load8(q + qrow * D + dc * 8, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
@@ -140,7 +166,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     kc_eff = __syncthreads_count(c >= 0);
   } else {
     // ---- 2. chunk scores ----------------------------------------------------
-    float* sc = n_chunks <= kLdsScores ? sc_lds : ws_scores + bj * n_chunks;
+    float* sc = n_chunks <= kLdsScores ? sc_lds
+                                       : ws_scores + bj * (MODE == kRouteDecode ? chunk_rows : n_chunks);
     // ranked chunks are chunk0 .. chunk0 + n_chunks - 1 (the sink is attended in full)
     const float* cbase = csum + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
     score_rows<D, 8>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
@@ -455,7 +482,7 @@ hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const fl
                         timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
                         static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
                         static_cast<int>(hist_rows(s) / kChunk),
-                        s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, nullptr, CacheView{});
+                        s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, nullptr, CacheView{}, DecodeView{});
   return hipGetLastError();
 }
 
@@ -476,7 +503,7 @@ hipError_t launch_cached_t(const hga_shape& s, const void* q, const float* cs, c
   hipExtLaunchKernelGGL((route_kernel<T, D, kRouteChunks>), grid, dim3(kThreads), 0, st,
                         timer_event(HGA_KERNEL_ROUTE, 0), nullptr, 0,
                         static_cast<const T*>(q), cs, nullptr, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
-                        chunk_rows, s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, qbar, view);
+                        chunk_rows, s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, qbar, view, DecodeView{});
   hipExtLaunchKernelGGL((gcache_update_kernel<D>), dim3(s.n_kv_heads), dim3(kUpdThreads), 0, st,
                         timer_event(HGA_KERNEL_GCACHE, 0), timer_event(HGA_KERNEL_GCACHE, 1), 0,
                         static_cast<const int32_t*>(sc_out), n_blocks, s.n_kv_heads, s.top_k_chunks, g_src,
@@ -484,7 +511,7 @@ hipError_t launch_cached_t(const hga_shape& s, const void* q, const float* cs, c
   hipExtLaunchKernelGGL((route_kernel<T, D, kRouteGroups>), grid, dim3(kThreads), 0, st,
                         nullptr, timer_event(HGA_KERNEL_ROUTE, 1), 0,
                         static_cast<const T*>(q), cs, nullptr, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
-                        chunk_rows, s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, qbar, view);
+                        chunk_rows, s.top_k_chunks, s.top_k_groups, scores, sc_out, sg_out, qbar, view, DecodeView{});
   return hipGetLastError();
 }
 
@@ -539,6 +566,36 @@ hipError_t launch_route_cached(const hga_shape& s, const void* q, const float* c
               : launch_cached_t<float, 128>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream);
   return bf ? launch_cached_t<uint16_t, 64>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream)
             : launch_cached_t<float, 64>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(const hga_shape& s, int batch, int n_new, const void* q, const float* cs,
+                           const float* gs, const int32_t* hist_lens, int32_t* sc_out, int32_t* sg_out,
+                           void* ws, hipStream_t st) {
+  const int r = s.n_q_heads / s.n_kv_heads;
+  const int chunk_rows = static_cast<int>(hist_rows(s) / kChunk);
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecode>), dim3(batch, s.n_kv_heads), dim3(kThreads), 0, st,
+                        timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
+                        static_cast<const T*>(q), cs, gs, n_new, s.n_kv_heads, r, 0, 0, chunk_rows,
+                        s.top_k_chunks, s.top_k_groups, static_cast<float*>(ws), sc_out, sg_out, nullptr,
+                        CacheView{}, DecodeView{hist_lens, s.n_sink_chunks, s.n_q_heads});
+  return hipGetLastError();
+}
+
+// Chunk scores of every (sequence, KV head) when a history exceeds the LDS.
+size_t decode_route_workspace_bytes(const hga_shape& s, int batch) {
+  return align256(sizeof(float) * batch * s.n_kv_heads * (hist_rows(s) / kChunk + 1));
+}
+
+hipError_t launch_decode_route(const hga_shape& s, int batch, int n_new, const void* q,
+                               const float* chunk_sum, const float* group_sum, const int32_t* hist_lens,
+                               int32_t* sel_chunks, int32_t* sel_groups, void* ws, hipStream_t stream) {
+  const bool bf = s.dtype == HGA_BF16;
+  if (s.head_dim == 128)
+    return bf ? launch_decode_t<uint16_t, 128>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream)
+              : launch_decode_t<float, 128>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream);
+  return bf ? launch_decode_t<uint16_t, 64>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream)
+            : launch_decode_t<float, 64>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream);
 }
 
 hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,

@@ -23,9 +23,10 @@ HGA_OP_ROUTE, HGA_OP_ATTN_FWD, HGA_OP_ATTN_BWD, HGA_OP_ROUTE_CACHED = 0, 1, 2, 3
 EXPORTS = ("hga_build_summaries", "hga_route", "hga_attn_fwd", "hga_attn_bwd",
            "hga_gather_groups", "hga_workspace_size", "hga_status_string",
            "hga_last_error", "hga_abi_version", "hga_set_kernel_events",
-           "hga_gcache_bytes", "hga_gcache_reset", "hga_route_cached")
+           "hga_gcache_bytes", "hga_gcache_reset", "hga_route_cached",
+           "hga_decode_workspace_size", "hga_decode")
 
-KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv", "gcache")
+KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv", "gcache", "decode")
 
 
 class HGAError(RuntimeError):
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "hga_gather_groups": [SP, P, P, P, P, P, P],
         "hga_gcache_reset": [SP, P, I32, P],
         "hga_route_cached": [SP, P, P, P, P, I32, P, P, P, P, SZ, P],
+        "hga_decode": [SP, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -91,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.hga_workspace_size.restype = SZ
     L.hga_gcache_bytes.argtypes = [SP, I32]
     L.hga_gcache_bytes.restype = SZ
+    L.hga_decode_workspace_size.argtypes = [SP, I32, I32]
+    L.hga_decode_workspace_size.restype = SZ
     L.hga_status_string.argtypes = [ctypes.c_int]
     L.hga_status_string.restype = ctypes.c_char_p
     L.hga_last_error.argtypes = []
@@ -263,6 +267,46 @@ def hga_route_cached(shape: Shape, q, chunk_sum, group_sum_host, cache, n_slots:
         _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
         _ptr(stats, (kv, 2), torch.int32, "stats"),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hga_decode_workspace_size(shape: Shape, batch: int, n_new: int) -> int:
+    return int(lib().hga_decode_workspace_size(ctypes.byref(shape), batch, n_new))
+
+
+def hga_decode(shape: Shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens,
+               tail_lens, sel_chunks, sel_groups, o, lse, ws=None, stream=None) -> None:
+    """One decode step for a batch (layouts of include/hga.h: q [B][n_q][n_new][d],
+    history [B][n_kv][P][d], open segment [B][n_kv][T][d], lengths int32 [B] on the GPU)."""
+    B, nq, n_new, d = q.shape
+    kv, P, T, dt = shape.n_kv_heads, shape.hist_rows, shape.seg_len, shape.torch_dtype
+    if ws is None:
+        n = hga_decode_workspace_size(shape, B, n_new)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().hga_decode(
+        ctypes.byref(shape), B, n_new, _ptr(q, (B, shape.n_q_heads, n_new, d), dt, "q"),
+        _ptr(k_hist, (B, kv, P, d), dt, "k_hist"), _ptr(v_hist, (B, kv, P, d), dt, "v_hist"),
+        _ptr(chunk_sum, (B, kv, P // 64, d), torch.float32, "chunk_sum"),
+        _ptr(group_sum, (B, kv, P // 8, d), torch.float32, "group_sum"),
+        _ptr(k_tail, (B, kv, T, d), dt, "k_tail"), _ptr(v_tail, (B, kv, T, d), dt, "v_tail"),
+        _ptr(hist_lens, (B,), torch.int32, "hist_lens"), _ptr(tail_lens, (B,), torch.int32, "tail_lens"),
+        _ptr(sel_chunks, (B, kv, shape.top_k_chunks), torch.int32, "sel_chunks"),
+        _ptr(sel_groups, (B, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        _ptr(o, (B, nq, n_new, d), dt, "o"), _ptr(lse, (B, nq, n_new), torch.float32, "lse"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def decode(shape: Shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens, tail_lens,
+           ws=None):
+    """Allocate the outputs and run hga_decode: (o, lse, sel_chunks, sel_groups)."""
+    B, nq, n_new, _ = q.shape
+    dev = q.device
+    sc = torch.empty((B, shape.n_kv_heads, shape.top_k_chunks), dtype=torch.int32, device=dev)
+    sg = torch.empty((B, shape.n_kv_heads, shape.top_k_groups), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, nq, n_new), dtype=torch.float32, device=dev)
+    hga_decode(shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens, tail_lens,
+               sc, sg, o, lse, ws)
+    return o, lse, sc, sg
 
 
 class GroupSummaryCache:

@@ -125,6 +125,27 @@ def make_inputs(w: Workload, seed: int = 0, with_grad_out: bool | None = None) -
     return out
 
 
+def make_decode_inputs(w: Workload, hist_lens, tail_lens, n_new: int, seed: int = 0) -> dict:
+    """A decode batch: sequence b is make_inputs(w, seed + b) with history
+    capacity w.hist_len and open-segment capacity w.seg_len; its
+    hist_lens[b] oldest history tokens and tail_lens[b] open-segment tokens are
+    the live ones, and its new tokens' queries are the segment queries at
+    positions tail_lens[b] - n_new .. tail_lens[b] - 1. CPU tensors:
+    q [B,n_q,n_new,d], k_hist/v_hist [B,n_kv,P,d], k_tail/v_tail [B,n_kv,T,d],
+    hist_lens/tail_lens int32 [B]."""
+    seqs = [make_inputs(w, seed + b) for b in range(len(hist_lens))]
+    q = torch.stack([x["q"][:, t - n_new:t] for x, t in zip(seqs, tail_lens)]).contiguous()
+    return {
+        "q": q,
+        "k_hist": torch.stack([x["k_hist"] for x in seqs]).contiguous(),
+        "v_hist": torch.stack([x["v_hist"] for x in seqs]).contiguous(),
+        "k_tail": torch.stack([x["k_seg"] for x in seqs]).contiguous(),
+        "v_tail": torch.stack([x["v_seg"] for x in seqs]).contiguous(),
+        "hist_lens": torch.tensor(list(hist_lens), dtype=torch.int32),
+        "tail_lens": torch.tensor(list(tail_lens), dtype=torch.int32),
+    }
+
+
 def to_numpy64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a CPU tensor (fp32 or bf16) to float64 numpy."""
     return t.detach().to(torch.float64).numpy()

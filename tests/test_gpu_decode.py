@@ -1,0 +1,126 @@
+"""Decode step on the GPU (hga_decode, through the C ABI) against the oracle's
+decode_step, per sequence of a ragged batch: routing through the selection
+checker (exact up to near-ties), outputs with the oracle fed the GPU's own
+selection, to the same tolerance as the training path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_fine_amd import hga, synth
+from oracle import hga_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hga.lib()
+
+
+def _f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new, seed, sink=0,
+               window=0, check_outputs=True):
+    print(f"[case] decode nq={n_q} nkv={n_kv} d={d} P={P} T={T} kc={k_c} kg={k_g} {dtype} "
+          f"hist={list(hist_lens)} tail={list(tail_lens)} n_new={n_new} sink={sink} W={window}",
+          flush=True)
+    w = synth.Workload("decode", n_q, n_kv, d, P, T, k_c, k_g, dtype,
+                       1.0 if dtype == "f32" else 1.0 / math.sqrt(d))
+    inp = synth.make_decode_inputs(w, hist_lens, tail_lens, n_new, seed)
+    g = {k: v.cuda() for k, v in inp.items()}
+    B = len(hist_lens)
+    s = hga.make_shape(n_q, n_kv, d, P, T, k_c, k_g, w.torch_dtype, w.softmax_scale,
+                       n_sink_chunks=sink, local_window=window)
+    C = torch.zeros((B, n_kv, P // 64, d), dtype=torch.float32, device="cuda")
+    G = torch.zeros((B, n_kv, P // 8, d), dtype=torch.float32, device="cuda")
+    for b in range(B):
+        if hist_lens[b]:
+            sb = hga.make_shape(n_q, n_kv, d, hist_lens[b], T, k_c, k_g, w.torch_dtype,
+                                hist_stride=P)
+            hga.hga_build_summaries(sb, g["k_hist"][b], C[b], G[b])
+    o, lse, sc, sg = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
+                                g["hist_lens"], g["tail_lens"])
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    for b in range(B):
+        H, Tb = hist_lens[b], tail_lens[b]
+        qb = _f64(inp["q"][b])
+        kh, vh = _f64(inp["k_hist"][b][:, :H]), _f64(inp["v_hist"][b][:, :H])
+        kt, vt = _f64(inp["k_tail"][b][:, :Tb]), _f64(inp["v_tail"][b][:, :Tb])
+        sc_b, sg_b = sc[b].cpu().numpy(), sg[b].cpu().numpy()
+        if H:
+            qbar = orc.decode_query_mean(qb, n_kv)[None]
+            rep = orc.check_selection(qbar, orc.chunk_summaries(kh), orc.group_summaries(kh),
+                                      sc_b[None], sg_b[None], k_c, k_g, n_sink=sink)
+            print(f"  seq {b}: route ok={rep['ok']} exemptions={rep['chunk_exemptions']}/"
+                  f"{rep['group_exemptions']}", flush=True)
+            assert rep["ok"], rep["failures"][:3]
+        else:
+            assert (sc_b == -1).all() and (sg_b == -1).all()
+        if not check_outputs:
+            continue
+        _, _, O_ref, L_ref = orc.decode_step(qb, kh, vh, kt, vt, k_c, k_g, w.softmax_scale,
+                                             n_sink=sink, window=window or None, sel_groups=sg_b)
+        for name, got, ref in (("O", _f64(o[b]), O_ref), ("LSE", _f64(lse[b]), L_ref)):
+            err, rel = orc.error_stats(got, ref)
+            print(f"  seq {b} {name}: max|d|={err:.3e} rel_l2={rel:.3e}", flush=True)
+            assert orc.within_tolerance(got, ref, tol), (b, name, err, rel)
+    return o, lse, sc, sg
+
+
+def test_decode_ragged_batch_one_new_token():
+    run_decode(8, 2, 128, 1024, 256, 4, 16, "bf16", [1024, 512, 0, 64, 960], [256, 1, 130, 77, 200],
+               n_new=1, seed=0)
+
+
+def test_decode_two_new_tokens_with_sink_and_window():
+    run_decode(8, 2, 128, 2048, 192, 5, 13, "bf16", [2048, 640, 128], [192, 50, 3], n_new=2, seed=1,
+               sink=1, window=50)
+
+
+def test_decode_sixteen_query_rows_d64():
+    # r = 4 heads x 4 new tokens; a window of 1 keeps only each token itself
+    run_decode(8, 2, 64, 1024, 128, 3, 20, "bf16", [1024, 320], [128, 4], n_new=4, seed=2)
+    run_decode(8, 2, 64, 1024, 128, 3, 20, "bf16", [704, 64], [100, 9], n_new=4, seed=3, window=1)
+
+
+def test_decode_fp32_mha():
+    run_decode(2, 2, 64, 512, 128, 3, 10, "f32", [512, 256], [128, 65], n_new=1, seed=4)
+
+
+def test_decode_lengths_are_clamped_to_the_buffers():
+    # a history beyond the capacity reads as full, a ragged one as whole chunks
+    # and an open segment shorter than n_new as n_new tokens
+    w = dict(n_q=4, n_kv=1, d=128, P=512, T=128, k_c=2, k_g=8, dtype="bf16")
+    a = run_decode(**w, hist_lens=[512, 448], tail_lens=[128, 2], n_new=2, seed=5, check_outputs=False)
+    inp_lens = [(10 ** 6, 1000), (490, 1)]
+    wl = synth.Workload("decode", 4, 1, 128, 512, 128, 2, 8, "bf16", 1.0 / math.sqrt(128))
+    inp = synth.make_decode_inputs(wl, [512, 448], [128, 2], 2, 5)
+    g = {k: v.cuda() for k, v in inp.items()}
+    g["hist_lens"] = torch.tensor([x for x, _ in inp_lens], dtype=torch.int32, device="cuda")
+    g["tail_lens"] = torch.tensor([y for _, y in inp_lens], dtype=torch.int32, device="cuda")
+    s = hga.make_shape(4, 1, 128, 512, 128, 2, 8, torch.bfloat16)
+    C = torch.zeros((2, 1, 8, 128), dtype=torch.float32, device="cuda")
+    G = torch.zeros((2, 1, 64, 128), dtype=torch.float32, device="cuda")
+    for b, H in enumerate([512, 448]):
+        hga.hga_build_summaries(hga.make_shape(4, 1, 128, H, 128, 2, 8, torch.bfloat16, hist_stride=512),
+                                g["k_hist"][b], C[b], G[b])
+    o, lse, sc, sg = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
+                                g["hist_lens"], g["tail_lens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, a[0]) and torch.equal(lse, a[1]) and torch.equal(sg, a[3])
+
+
+def test_decode_qwen3_8b_131k():
+    # Qwen3-8B layer shapes, 129,024-token history capacity, 2,048-token open
+    # segment, one new token per sequence, ragged lengths
+    run_decode(32, 8, 128, 129024, 2048, 16, 32, "bf16", [129024, 100032], [2048, 517], n_new=1,
+               seed=6)
