@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--group-cache-slots", type=int, default=0,
                     help="keep group summaries in page-locked host memory behind an HBM cache "
                          "of this many chunk slots per KV head (hga_route_cached)")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="run the decode step instead: this many sequences of the workload's "
+                         "history length, ragged, one JSON line")
+    ap.add_argument("--decode-new", type=int, default=1, help="new tokens per sequence and step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB (one plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -210,10 +214,138 @@ def tbptt_sweep(args):
                               "(append K/V, summaries) runs outside the timing"}), flush=True)
 
 
+def decode_bench(args):
+    """Decode step (hga_decode) for a ragged batch: sequence b holds a history
+    of H - 64 * ((13 b) % 32) tokens (H = the workload's history length) and
+    an open segment of max(n_new, 64 * ((37 b) % 32 + 1)) tokens; inputs follow
+    the synthetic recipe's distributions, drawn on the GPU. One JSON line."""
+    import torch
+    from long_context_fine_amd import hga, synth
+
+    hga.lib()
+    w = synth.WORKLOADS[args.workload]
+    B, n_new = args.decode_batch, args.decode_new
+    S, d, kv, nq, H = w.seg_len, w.head_dim, w.n_kv_heads, w.n_q_heads, w.hist_len
+    r = nq // kv
+    e = 2 if w.dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    a = 1.0 / math.sqrt(d)
+    hist_lens = [max(0, H - 64 * ((13 * b) % 32)) for b in range(B)]
+    tail_lens = [max(n_new, 64 * ((37 * b) % 32 + 1)) for b in range(B)]
+    tail_lens = [min(t, S) for t in tail_lens]
+
+    def keys(n):
+        off = torch.randn((B, kv, n // 64, 1, d), generator=gen, device=dev) * 0.5
+        k = torch.randn((B, kv, n // 64, 64, d), generator=gen, device=dev) * a + off
+        return k.reshape(B, kv, n, d).to(w.torch_dtype)
+
+    q = (torch.randn((B, nq, n_new, d), generator=gen, device=dev) * a).to(w.torch_dtype)
+    k_hist = keys(H)
+    v_hist = (torch.randn((B, kv, H, d), generator=gen, device=dev) * a).to(w.torch_dtype)
+    k_tail = keys(S)
+    v_tail = (torch.randn((B, kv, S, d), generator=gen, device=dev) * a).to(w.torch_dtype)
+    s = hga.make_shape(nq, kv, d, H, S, w.top_k_chunks, w.top_k_groups, w.torch_dtype,
+                       w.softmax_scale, n_sink_chunks=args.sink_chunks, local_window=args.local_window)
+    C = torch.zeros((B, kv, H // 64, d), dtype=torch.float32, device=dev)
+    G = torch.zeros((B, kv, H // 8, d), dtype=torch.float32, device=dev)
+    for b in range(B):
+        if hist_lens[b]:
+            sb = hga.make_shape(nq, kv, d, hist_lens[b], S, w.top_k_chunks, w.top_k_groups,
+                                w.torch_dtype, hist_stride=H)
+            hga.hga_build_summaries(sb, k_hist[b], C[b], G[b])
+    hl = torch.tensor(hist_lens, dtype=torch.int32, device=dev)
+    tl = torch.tensor(tail_lens, dtype=torch.int32, device=dev)
+    sc = torch.empty((B, kv, w.top_k_chunks), dtype=torch.int32, device=dev)
+    sg = torch.empty((B, kv, w.top_k_groups), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, nq, n_new), dtype=torch.float32, device=dev)
+    ws = torch.empty(hga.hga_decode_workspace_size(s, B, n_new), dtype=torch.uint8, device=dev)
+
+    def step():
+        hga.hga_decode(s, q, k_hist, v_hist, C, G, k_tail, v_tail, hl, tl, sc, sg, o, lse, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # algorithmic bytes: route reads the new queries, every ranked chunk
+    # summary and the 8 * k_c candidate group summaries; attention reads the
+    # K and V rows of every attended key once (plus queries and outputs)
+    W = S if args.local_window <= 0 else min(args.local_window, S)
+    sel = None
+    route_b = attn_b = 0
+    step()
+    torch.cuda.synchronize()
+    sel = sg.cpu()
+    for b in range(B):
+        n_c = hist_lens[b] // 64
+        sink = min(args.sink_chunks, n_c)
+        kc = min(w.top_k_chunks, n_c - sink)
+        route_b += kv * (r * n_new * d * e + (n_c - sink) * d * 4 + 8 * kc * d * 4
+                         + (w.top_k_chunks + w.top_k_groups) * 4)
+        t_lo = max(0, tail_lens[b] - n_new - W + 1)
+        for j in range(kv):
+            n_keys = 64 * sink + 8 * int((sel[b, j] >= 0).sum()) + tail_lens[b] - t_lo
+            attn_b += n_keys * d * e * 2 + 2 * r * n_new * d * e
+
+    names = list(hga.KERNELS)
+    ids = {"route": names.index("route"), "decode": names.index("decode")}
+
+    def new_events(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for x, y in ev:
+            x.record()
+            y.record()
+        return ev
+
+    n_cal = min(args.steps, 20)
+    cal = {k: new_events(n_cal) for k in ids}
+    torch.cuda.synchronize()
+    for i in range(n_cal):
+        for k, kid in ids.items():
+            hga.hga_set_kernel_events(kid, *cal[k][i])
+        step()
+    torch.cuda.synchronize()
+    for kid in ids.values():
+        hga.hga_set_kernel_events(kid, None, None)
+    us = {k: sum(x.elapsed_time(y) for x, y in ev) * 1e3 / len(ev) for k, ev in cal.items()}
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = 1e3 * elapsed / args.steps
+    gbs = {"route": route_b / (us["route"] * 1e-6) / 1e9, "decode": attn_b / (us["decode"] * 1e-6) / 1e9}
+    dom = max(us, key=us.get)
+    print(json.dumps({
+        "mode": "decode", "metric": "decode tokens/s (HGA route + attention, one layer)",
+        "value": round(B * n_new * args.steps / elapsed, 1), "unit": "tokens/s",
+        "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype,
+        "data": "synthetic: GPU-drawn N(0,1)/sqrt(d) Q, K, V with N(0,0.5^2) per-chunk key offsets",
+        "config": {"workload": w.name, "batch": B, "n_new": n_new, "history_capacity": H,
+                   "hist_lens": [min(hist_lens), max(hist_lens)],
+                   "tail_lens": [min(tail_lens), max(tail_lens)], "n_sink_chunks": args.sink_chunks,
+                   "local_window": args.local_window, "top_k_chunks": w.top_k_chunks,
+                   "top_k_groups": w.top_k_groups},
+        "kernels": {"route": {"avg_us": round(us["route"], 3), "gbs": round(gbs["route"], 1),
+                              "mib_per_launch": round(route_b / 2 ** 20, 3)},
+                    "decode_attn+merge": {"avg_us": round(us["decode"], 3), "gbs": round(gbs["decode"], 1),
+                                          "mib_per_launch": round(attn_b / 2 ** 20, 3)}},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(gbs[dom], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs[dom] / PEAK_HBM_GBS, 4), "traffic": None},
+    }))
+
+
 def main():
     args = parse()
     if args.tbptt_max_hist:
         return tbptt_sweep(args)
+    if args.decode_batch:
+        return decode_bench(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "

@@ -4,15 +4,18 @@
 // (gist.science Technical Summary §2.1 "Exact-Token Attention"; §3: the
 // adapter runs with HGA for retrieval and generation).
 //
-// HBM-bound (each key row is read once for r * n_new query rows), so the
-// kernel is VALU: D/8 lanes per key row (16-byte loads, one wave instruction
-// covers 64/(D/8) whole rows), the virtual key list of a (sequence, KV head)
-// [sink | routed groups | open-segment window] split into 256-key pieces, one
-// workgroup each. A piece: scores of all its keys for all query rows to LDS,
-// max and sum per row, then P.V; the unnormalised partial O with its (max,
-// sum) goes to the workspace and decode_merge_kernel combines the pieces of
-// each query row in a fixed order. Deterministic; no atomics.
-#include "hga_common.hpp"
+// HBM-bound: each key row is read once for r * n_new query rows. The virtual
+// key list of a (sequence, KV head) [sink | routed groups | open-segment
+// window] is split into 256-key pieces, one workgroup each. A piece: scores
+// of all its keys for all query rows to LDS, max and sum per row, then P.V;
+// the unnormalised partial O with its (max, sum) goes to the workspace and
+// decode_merge_kernel combines the pieces of each query row in a fixed order.
+// bf16: Q.K^T on MFMA (32 keys x the query rows as columns, K rows loaded
+// straight from memory as A operands) and P.V on the VALU with each lane
+// owning D/64 output dimensions (one coalesced row read per key, no
+// cross-lane sums). fp32: VALU throughout, D/8 lanes per key row.
+// Deterministic; no atomics.
+#include "attn_tile.hpp"
 
 namespace hga {
 namespace {
@@ -61,12 +64,14 @@ __device__ __forceinline__ SeqKeys seq_keys(const DecodeParams& p, int b) {
   return s;
 }
 
+// Sum over the LPK lanes of a key row (in-row DPP adds).
 template <int LPK>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < LPK; o <<= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  static_assert(LPK == 8 || LPK == 16, "a key row spans 8 or 16 lanes");
+  return LPK == 16 ? sum16_f32(x) : sum8_f32(x);
 }
+
+constexpr int kDecUnroll = 4;  // key steps whose loads are issued together
 
 template <typename T, int D, int NQ>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p) {
@@ -117,33 +122,46 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
   }
 
   // ---- scores of every key of the piece, all query rows -------------------
+  // (kDecUnroll key steps per pass: their loads are all in flight before
+  // the first is used)
   const T* kh = static_cast<const T*>(p.k_hist);
   const T* kt = static_cast<const T*>(p.k_tail);
-  for (int base = wave * KPW; base < nk; base += KPS) {
-    const int kk = base + kin;
-    const bool live = kk < nk;
-    int tpos = -1;
-    const T* row = live ? key_row(k0 + kk, kh, kt, tpos) : nullptr;
-    float kf[8];
-    if (row) {
-      Elem<T>::load8(row + sub * 8, kf);
-    } else {
+  for (int base = wave * KPW; base < nk; base += kDecUnroll * KPS) {
+    const T* rowp[kDecUnroll];
+    int tpos[kDecUnroll];
+    float kf[kDecUnroll][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = 0.f;
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int kk = base + u * KPS + kin;
+      tpos[u] = -1;
+      rowp[u] = kk < nk ? key_row(k0 + kk, kh, kt, tpos[u]) : nullptr;
     }
 #pragma unroll
-    for (int rq = 0; rq < NQ; ++rq) {
-      float d = 0.f;
+    for (int u = 0; u < kDecUnroll; ++u) {
+      if (rowp[u]) {
+        Elem<T>::load8(rowp[u] + sub * 8, kf[u]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qr[rq][e], kf[e], d);
-      d = group_sum<LPK>(d);
-      if (live && sub == 0 && rq < R) {
-        bool ok = row != nullptr;
-        if (tpos >= 0) {
-          const int qpos = sk.tb - p.n_new + rq % p.n_new;   // open-segment position of the row
-          ok = tpos <= qpos && tpos > qpos - p.window;
+        for (int e = 0; e < 8; ++e) kf[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int kk = base + u * KPS + kin;
+#pragma unroll
+      for (int rq = 0; rq < NQ; ++rq) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qr[rq][e], kf[u][e], d);
+        d = group_sum<LPK>(d);
+        if (kk < nk && sub == 0 && rq < R) {
+          bool ok = rowp[u] != nullptr;
+          if (tpos[u] >= 0) {
+            const int qpos = sk.tb - p.n_new + rq % p.n_new;   // open-segment position of the row
+            ok = tpos[u] <= qpos && tpos[u] > qpos - p.window;
+          }
+          s_lds[rq][kk] = ok ? d * p.scale_log2 : -INFINITY;
         }
-        s_lds[rq][kk] = ok ? d * p.scale_log2 : -INFINITY;
       }
     }
   }
@@ -180,19 +198,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
     for (int e = 0; e < 8; ++e) acc[rq][e] = 0.f;
   const T* vh = static_cast<const T*>(p.v_hist);
   const T* vt = static_cast<const T*>(p.v_tail);
-  for (int base = wave * KPW; base < nk; base += KPS) {
-    const int kk = base + kin;
-    if (kk >= nk) continue;
-    int tpos;
-    const T* row = key_row(k0 + kk, vh, vt, tpos);
-    if (!row) continue;
-    float vf[8];
-    Elem<T>::load8(row + sub * 8, vf);
+  for (int base = wave * KPW; base < nk; base += kDecUnroll * KPS) {
+    const T* rowp[kDecUnroll];
+    float vf[kDecUnroll][8];
 #pragma unroll
-    for (int rq = 0; rq < NQ; ++rq) {
-      const float pr = rq < R ? s_lds[rq][kk] : 0.f;
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int kk = base + u * KPS + kin;
+      int tpos;
+      rowp[u] = kk < nk ? key_row(k0 + kk, vh, vt, tpos) : nullptr;
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[rq][e] = fmaf(pr, vf[e], acc[rq][e]);
+    for (int u = 0; u < kDecUnroll; ++u) {
+      if (rowp[u]) {
+        Elem<T>::load8(rowp[u] + sub * 8, vf[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int kk = base + u * KPS + kin;
+      if (!rowp[u]) continue;
+#pragma unroll
+      for (int rq = 0; rq < NQ; ++rq) {
+        const float pr = rq < R ? s_lds[rq][kk] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[rq][e] = fmaf(pr, vf[u][e], acc[rq][e]);
+      }
     }
   }
   // sum the wave's key groups (lanes with equal sub), then the waves in LDS
@@ -215,6 +248,184 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += o_lds[w][rq][dd];
     const int64_t row = (static_cast<int64_t>(b) * p.n_q + j * p.r + rq / p.n_new) * p.n_new + rq % p.n_new;
+    p.part[(row * p.n_piece + piece) * D + dd] = v;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodeParams p) {
+  constexpr int NKS = D / 16;                   // MFMA k-steps over head_dim
+  constexpr int NW = kDecThreads / kWave;
+  constexpr int KT = 32;                        // keys per MFMA tile
+  constexpr int TPW = kDecKeys / (NW * KT);     // tiles per wave
+  constexpr int DPL = D / kWave;                // output dims per lane in P.V
+  constexpr int QR = 16;                        // query rows (host-checked bound)
+  // rows padded by 4 floats: the 32 query rows' 16-byte score stores spread over the banks
+  __shared__ __attribute__((aligned(16))) float s_lds[QR][kDecKeys + 4];
+  __shared__ int32_t kinfo[kDecKeys];           // -1 plain, -2 masked, >= 0 open-segment position
+  __shared__ float o_lds[NW][QR][D];
+  const int piece = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, lane = t % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int l32 = lane % 32, hh = lane / 32;
+
+  const SeqKeys sk = seq_keys(p, b);
+  const int k0 = piece * kDecKeys;
+  if (k0 >= sk.n_keys) return;
+  const int nk = min(kDecKeys, sk.n_keys - k0);
+  const int R = p.r * p.n_new;
+  const int n_routed = p.k_g * kGroup;
+  const int64_t hrow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.P;
+  const int64_t trow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.T;
+  const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
+  const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist);
+  const uint16_t* vh = static_cast<const uint16_t*>(p.v_hist);
+  const uint16_t* kt = static_cast<const uint16_t*>(p.k_tail);
+  const uint16_t* vt = static_cast<const uint16_t*>(p.v_tail);
+
+  // element offset of virtual key v's row and whether it is an open-segment
+  // row; an empty routed slot (or v past the piece) reads the first attended
+  // open-segment row, a finite row whose weight is zero
+  auto resolve = [&](int v, bool& tail, int& info) -> int64_t {
+    if (v < k0 + nk) {
+      if (v < sk.sink) { tail = false; info = -1; return (hrow0 + v) * D; }
+      const int u = v - sk.sink;
+      if (u < n_routed) {
+        const int g = sel_bj[u / kGroup];
+        if (g >= 0) { tail = false; info = -1; return (hrow0 + static_cast<int64_t>(g) * kGroup + u % kGroup) * D; }
+      } else {
+        tail = true;
+        info = sk.t_lo + u - n_routed;
+        return (trow0 + info) * D;
+      }
+    }
+    tail = true;
+    info = -2;
+    return (trow0 + sk.t_lo) * D;
+  };
+
+  // ---- scores: S^T = K . Q^T per 32-key tile ------------------------------
+  bf16x8 qreg[NKS];
+  {
+    const bool live = l32 < R;
+    // rows of KV head j: (j*r + rq / n_new) * n_new + rq % n_new = j*r*n_new + rq
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                         ((static_cast<int64_t>(b) * p.n_q + j * p.r) * p.n_new + (live ? l32 : 0)) * D + hh * 8;
+#pragma unroll
+    for (int ss = 0; ss < NKS; ++ss) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ss * 16);
+      qreg[ss] = live ? v : bf16x8{};
+    }
+  }
+  bf16x8 ka[TPW][NKS];
+  int info[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int kk = (wave * TPW + tt) * KT + l32;
+    bool tail;
+    const int64_t off = resolve(k0 + kk, tail, info[tt]);
+    const uint16_t* kp = (tail ? kt : kh) + off + hh * 8;
+#pragma unroll
+    for (int ss = 0; ss < NKS; ++ss) ka[tt][ss] = *reinterpret_cast<const bf16x8*>(kp + ss * 16);
+  }
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tile0 = (wave * TPW + tt) * KT;
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int ss = 0; ss < NKS; ++ss) acc = mfma32(ka[tt][ss], qreg[ss], acc);
+    if (hh == 0) kinfo[tile0 + l32] = info[tt];
+    if (l32 < R) {
+      // acc[v]: key tile0 + 8*(v/4) + 4*hh + v%4, query row l32
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        *reinterpret_cast<float4*>(&s_lds[l32][tile0 + 8 * v4 + 4 * hh]) =
+            make_float4(acc[4 * v4] * p.scale_log2, acc[4 * v4 + 1] * p.scale_log2,
+                        acc[4 * v4 + 2] * p.scale_log2, acc[4 * v4 + 3] * p.scale_log2);
+    }
+  }
+  __syncthreads();
+
+  // ---- per row: mask, max, probabilities in place, sum --------------------
+  for (int rq = wave; rq < R; rq += NW) {
+    const int qpos = sk.tb - p.n_new + rq % p.n_new;
+    float m = -INFINITY;
+    for (int kk = lane; kk < kDecKeys; kk += kWave) {
+      const int inf = kinfo[kk];
+      const bool ok = inf == -1 || (inf >= 0 && inf <= qpos && inf > qpos - p.window);
+      const float sc = ok ? s_lds[rq][kk] : -INFINITY;
+      s_lds[rq][kk] = sc;
+      m = fmaxf(m, sc);
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    float l = 0.f;
+    for (int kk = lane; kk < kDecKeys; kk += kWave) {
+      const float e = m == -INFINITY ? 0.f : exp2f(s_lds[rq][kk] - m);
+      s_lds[rq][kk] = e;
+      l += e;
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) l += __shfl_xor(l, o, kWave);
+    if (lane == 0) {
+      float* ml = p.part_ml + ((static_cast<int64_t>(b) * p.n_q + j * p.r) * p.n_new + rq) * p.n_piece * 2 + piece * 2;
+      ml[0] = m;
+      ml[1] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- P . V: each lane owns DPL dims; a wave takes a quarter of the keys --
+  float acc[QR][DPL];
+#pragma unroll
+  for (int rq = 0; rq < QR; ++rq)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[rq][e] = 0.f;
+  constexpr int KPI = 16;                       // keys per pass: their row loads in flight together
+  const int kq0 = wave * (kDecKeys / NW);
+  for (int kk = kq0; kk < kq0 + kDecKeys / NW && kk < nk; kk += KPI) {
+    float vf[KPI][DPL];
+#pragma unroll
+    for (int u = 0; u < KPI; ++u) {
+      bool tail;
+      int inf;
+      const int64_t off = resolve(k0 + kk + u, tail, inf);
+      const uint16_t* vp = (tail ? vt : vh) + off + lane * DPL;
+      if (DPL == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
+        vf[u][0] = __uint_as_float(w << 16);
+        vf[u][DPL - 1] = __uint_as_float(w & 0xffff0000u);
+      } else {
+        vf[u][0] = bf16_to_f32(vp[0]);
+      }
+    }
+#pragma unroll
+    for (int rq = 0; rq < QR; ++rq) {
+      if (rq < R) {
+#pragma unroll
+        for (int u4 = 0; u4 < KPI; u4 += 4) {
+          const float4 p4 = *reinterpret_cast<const float4*>(&s_lds[rq][kk + u4]);  // zero past nk
+#pragma unroll
+          for (int e = 0; e < DPL; ++e)
+            acc[rq][e] += p4.x * vf[u4][e] + p4.y * vf[u4 + 1][e] + p4.z * vf[u4 + 2][e] + p4.w * vf[u4 + 3][e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rq = 0; rq < QR; ++rq)
+    if (rq < R)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o_lds[wave][rq][lane * DPL + e] = acc[rq][e];
+  __syncthreads();
+  for (int x = t; x < R * D; x += kDecThreads) {
+    const int rq = x / D, dd = x % D;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += o_lds[w][rq][dd];
+    const int64_t row = (static_cast<int64_t>(b) * p.n_q + j * p.r) * p.n_new + rq;
     p.part[(row * p.n_piece + piece) * D + dd] = v;
   }
 }
@@ -246,7 +457,9 @@ hipError_t launch_td(const hga_shape& s, DecodeParams& p, int batch, hipStream_t
   const dim3 grid(p.n_piece, s.n_kv_heads, batch);
   const int R = p.r * p.n_new;
   hipEvent_t e0 = timer_event(HGA_KERNEL_DECODE, 0), e1 = timer_event(HGA_KERNEL_DECODE, 1);
-  if (R <= 4)
+  if constexpr (sizeof(T) == 2)
+    hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+  else if (R <= 4)
     hipExtLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
   else if (R <= 8)
     hipExtLaunchKernelGGL((decode_attn_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);

@@ -120,6 +120,12 @@ __device__ __forceinline__ float sum8_f32(float x) {
   x += __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(x)));
   return x;
 }
+// Sum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ float sum16_f32(float x) {
+  x = sum8_f32(x);
+  x += __uint_as_float(dpp_u32<kDppRowMirror>(__float_as_uint(x)));
+  return x;
+}
 
 // Rows per KV head in k_hist / v_hist (and x64 / x8 in the chunk / group
 // summaries): hist_stride when set, else hist_len.
