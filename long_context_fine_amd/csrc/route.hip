@@ -67,7 +67,7 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
 
 enum RouteMode { kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2, kRouteDecode = 3 };
 
-// Decode: blockIdx.x is a sequence of the batch, the query block is its
+// Decode: blockIdx.y is a sequence of the batch, the query block is its
 // seg_len newest tokens (q [batch][n_q][seg_len][D]); summaries are
 // [batch][n_kv][chunk_rows][D] and [batch][n_kv][8*chunk_rows][D]; the
 // sequence's history length comes from hist_lens (clamped to the capacity,
@@ -109,7 +109,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ int32_t slot_s[kMaxTopKChunks];
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  const int b = blockIdx.x, j = blockIdx.y;
+  // KV head fastest: with 8 KV heads all workgroups of head j run on one XCD
+  // (round-robin dispatch), whose L2 then holds that head's chunk summaries
+  const int j = blockIdx.x, b = blockIdx.y;
   const int64_t bj = static_cast<int64_t>(b) * n_kv + j;
   if constexpr (MODE == kRouteDecode) {
     int hb = dec.hist_lens[b];
@@ -478,7 +480,7 @@ hipError_t launch_t(const hga_shape& s, const void* q, const float* cs, const fl
   const int n_chunks = static_cast<int>(s.hist_len / kChunk) - chunk0;  // ranked chunks
   const int r = s.n_q_heads / s.n_kv_heads;
   float* scores = static_cast<float*>(ws);
-  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteFull>), dim3(n_blocks, s.n_kv_heads), dim3(kThreads), 0, st,
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteFull>), dim3(s.n_kv_heads, n_blocks), dim3(kThreads), 0, st,
                         timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
                         static_cast<const T*>(q), cs, gs, s.seg_len, s.n_kv_heads, r, chunk0, n_chunks,
                         static_cast<int>(hist_rows(s) / kChunk),
@@ -497,7 +499,7 @@ hipError_t launch_cached_t(const hga_shape& s, const void* q, const float* cs, c
   const int r = s.n_q_heads / s.n_kv_heads;
   float* scores = static_cast<float*>(ws);
   float* qbar = reinterpret_cast<float*>(static_cast<char*>(ws) + route_workspace_bytes(s));
-  const dim3 grid(n_blocks, s.n_kv_heads);
+  const dim3 grid(s.n_kv_heads, n_blocks);
   const CacheView view{L.slot_of_chunk, L.data, L.n_slots};
   // ROUTE spans both halves and the update between them; GCACHE the update
   hipExtLaunchKernelGGL((route_kernel<T, D, kRouteChunks>), grid, dim3(kThreads), 0, st,
@@ -574,7 +576,7 @@ hipError_t launch_decode_t(const hga_shape& s, int batch, int n_new, const void*
                            void* ws, hipStream_t st) {
   const int r = s.n_q_heads / s.n_kv_heads;
   const int chunk_rows = static_cast<int>(hist_rows(s) / kChunk);
-  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecode>), dim3(batch, s.n_kv_heads), dim3(kThreads), 0, st,
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecode>), dim3(s.n_kv_heads, batch), dim3(kThreads), 0, st,
                         timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
                         static_cast<const T*>(q), cs, gs, n_new, s.n_kv_heads, r, 0, 0, chunk_rows,
                         s.top_k_chunks, s.top_k_groups, static_cast<float*>(ws), sc_out, sg_out, nullptr,
