@@ -27,30 +27,38 @@ constexpr int kLdsScores = 4096;  // chunk scores kept in LDS up to this many ch
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Dot products of qv with `n` rows of `base` (row length D floats), 8 lanes per
-// row, 8 rows per wave pass, UNROLL passes in flight; results to out[row].
+// Dot products of qv with `n` rows (row length D floats, row_ptr(i) gives row
+// i), 8 lanes per row, 8 rows per wave pass; results to out[row]. Load c of
+// lane sub reads floats [32c + 4 sub, 32c + 4 sub + 4): the 8 lanes of a row
+// read one whole 128-byte line per instruction. Software-pipelined: the loads
+// of the next UNROLL passes are in flight while the current ones are reduced;
+// rows past n re-read row n-1 (branch-free) and are not written.
 template <int D, int UNROLL, class RowPtr>
 __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_ptr, float* out) {
   constexpr int LPR = 8;                 // lanes per row
   constexpr int EPL = D / LPR;           // elements per lane (16 or 8)
   constexpr int RPP = kWave / LPR;       // rows per wave pass
   constexpr int NW = kThreads / kWave;
+  constexpr int STEP = NW * RPP * UNROLL;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   static_assert(LPR == 8, "sum8_f32 reduces groups of 8 lanes");
   const int sub = lane % LPR;
   float qr[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) qr[e] = qv[sub * EPL + e];
-  for (int r0 = wave * RPP; r0 < n; r0 += NW * RPP * UNROLL) {
-    float4 v[UNROLL][EPL / 4];
+  for (int c = 0; c < EPL / 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qr[4 * c + e] = qv[c * 4 * LPR + sub * 4 + e];
+  using Buf = float4[UNROLL][EPL / 4];
+  auto load = [&](int r0, Buf& v) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int row = r0 + u * NW * RPP + lane / LPR;
-      const float* src = row < n ? row_ptr(row) + sub * EPL : nullptr;
+      const int row = min(r0 + u * NW * RPP + lane / LPR, n - 1);
+      const float4* src = reinterpret_cast<const float4*>(row_ptr(row) + sub * 4);
 #pragma unroll
-      for (int c = 0; c < EPL / 4; ++c)
-        v[u][c] = src ? reinterpret_cast<const float4*>(src)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int c = 0; c < EPL / 4; ++c) v[u][c] = src[c * LPR];
     }
+  };
+  auto reduce = [&](int r0, const Buf& v) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       float s = 0.f;
@@ -62,7 +70,51 @@ __device__ __forceinline__ void score_rows(const float* qv, int n, RowPtr row_pt
       const int row = r0 + u * NW * RPP + lane / LPR;
       if (row < n && sub == 0) out[row] = s;
     }
+  };
+  Buf va, vb;
+  int r0 = wave * RPP;
+  if (r0 < n) load(r0, va);
+  while (r0 < n) {
+    if (r0 + STEP < n) load(r0 + STEP, vb);
+    reduce(r0, va);
+    r0 += STEP;
+    if (r0 >= n) break;
+    if (r0 + STEP < n) load(r0 + STEP, va);
+    reduce(r0, vb);
+    r0 += STEP;
   }
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Exclusive prefix sum of v over a workgroup of NT threads in thread order;
+// *total gets the sum. wsum: NT/64 + 1 ints of LDS. Contains barriers: every
+// thread must call it.
+template <int NT>
+__device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
+  constexpr int NWV = NT / kWave;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int inc = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < NWV ? wsum[lane] : 0;
+    const int wi = wave_incl_scan(w, lane);
+    if (lane < NWV) wsum[lane] = wi - w;
+    if (lane == NWV - 1) wsum[NWV] = wi;
+  }
+  __syncthreads();
+  const int r = wsum[wave] + inc - v;
+  *total = wsum[NWV];
+  __syncthreads();
+  return r;
 }
 
 enum RouteMode { kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2, kRouteDecode = 3 };
@@ -100,7 +152,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ float part[RG][D + 1];
   __shared__ float qv[D];
   __shared__ float sc_lds[kLdsScores];
-  __shared__ __attribute__((aligned(16))) uint64_t wcand[NW][kMaxTopKChunks];
+  __shared__ int32_t hist_s[kThreads];       // radix-select digit histogram (256 bins)
+  __shared__ int32_t rsel[3];
+  __shared__ int32_t scan_ws[NW + 1];
   __shared__ int32_t sorted[kMaxTopKChunks];
   __shared__ float gsc[kMaxCand];
   __shared__ __attribute__((aligned(16))) uint64_t gkey[kMaxCand];
@@ -172,65 +226,71 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
                                        : ws_scores + bj * (MODE == kRouteDecode ? chunk_rows : n_chunks);
     // ranked chunks are chunk0 .. chunk0 + n_chunks - 1 (the sink is attended in full)
     const float* cbase = csum + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
-    score_rows<D, 8>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
+    score_rows<D, 4>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
     __syncthreads();
 
-    // ---- 3. chunk top-k: per-wave top-k over strided elements, then merge ---
+    // ---- 3. chunk top-k: exact radix select over the order-preserving score
+    // keys (8-bit digits, most significant first, LDS histograms) until the
+    // threshold bin is taken whole or the key is fixed in all 32 bits; equal
+    // keys at the threshold go to the lowest indices. The kept chunks are then
+    // written in ascending index order by one ordered compaction.
     kc_eff = min(k_c, n_chunks);
+    static_assert(kThreads == 256, "one histogram bin per thread");
     {
-      // keys of this lane's strided share kept in registers across the rounds
-      // when the share is small (the common case), else re-read each round
-      constexpr int kRegKeys = 8;
-      uint64_t keys[kRegKeys];
-  #pragma unroll
-      for (int e = 0; e < kRegKeys; ++e) {
-        const int m = wave * kWave + lane + e * kThreads;
-        keys[e] = m < n_chunks ? rank_key(sc[m], static_cast<uint32_t>(chunk0 + m)) : 0ull;
-      }
-      const bool in_regs = n_chunks <= kRegKeys * kThreads;
-      uint64_t prev = ~0ull;
-      for (int round = 0; round < kc_eff; ++round) {
-        uint64_t local = 0;
-        if (in_regs) {
-  #pragma unroll
-          for (int e = 0; e < kRegKeys; ++e)
-            if (keys[e] < prev && keys[e] > local) local = keys[e];
-        } else {
-          for (int m = wave * kWave + lane; m < n_chunks; m += kThreads) {
-            const uint64_t k = rank_key(sc[m], static_cast<uint32_t>(chunk0 + m));
-            if (k < prev && k > local) local = k;
-          }
+      uint32_t prefix = 0u, pmask = 0u;
+      int need = kc_eff;        // keys still to take among those equal to prefix under pmask
+      bool exact = false;       // threshold fixed in all 32 bits: ties resolved by index
+      for (int shift = 24; shift >= 0 && kc_eff > 0; shift -= 8) {
+        hist_s[t] = 0;
+        __syncthreads();
+        for (int m = t; m < n_chunks; m += kThreads) {
+          const uint32_t k = score_key(sc[m]);
+          if ((k & pmask) == prefix) atomicAdd(&hist_s[(k >> shift) & 255u], 1);
         }
-        prev = wave_max_u64(local);      // 0 once this wave has no element left
-        if (lane == 0) wcand[wave][round] = prev;
-      }
-    }
-    __syncthreads();
-    {
-      // t < NW*kc_eff: candidate (wave t / kc_eff, round t % kc_eff)
-      if (t < NW * kc_eff) {
-        const uint64_t mine = wcand[t / kc_eff][t % kc_eff];
-        // candidates are the first kc_eff slots of each wave's row, read two
-        // keys at a time
-        int rank = 0;
-        for (int w2 = 0; w2 < NW; ++w2) {
-          const ulonglong2* row = reinterpret_cast<const ulonglong2*>(wcand[w2]);
-  #pragma unroll 4
-          for (int o2 = 0; o2 < (kc_eff + 1) / 2; ++o2) {
-            const ulonglong2 c = row[o2];
-            rank += c.x > mine;
-            rank += (2 * o2 + 1 < kc_eff) && c.y > mine;
-          }
+        __syncthreads();
+        const int bin = kThreads - 1 - t;           // thread order = bins descending
+        const int h = hist_s[bin];
+        int total;
+        const int at_or_above = block_scan_excl<kThreads>(h, &total, scan_ws) + h;
+        if (at_or_above >= need && at_or_above - h < need) {
+          rsel[0] = bin;
+          rsel[1] = at_or_above - h;
+          rsel[2] = h;
         }
-        // keys are unique (index in the low bits); the kc_eff best are all valid
-        if (rank < kc_eff) part[0][rank] = __uint_as_float(rank_key_index(mine));
+        __syncthreads();
+        prefix |= static_cast<uint32_t>(rsel[0]) << shift;
+        pmask |= 255u << shift;
+        need -= rsel[1];
+        const bool whole = rsel[2] == need;
+        __syncthreads();                            // rsel is rewritten next pass
+        if (whole) break;
+        if (shift == 0) exact = true;
       }
-      __syncthreads();
-      if (t < kc_eff) {
-        const int id = static_cast<int>(__float_as_uint(part[0][t]));
-        int pos = 0;
-        for (int u = 0; u < kc_eff; ++u) pos += static_cast<int>(__float_as_uint(part[0][u])) < id;
-        sorted[pos] = id;
+      // ordered compaction: thread t owns chunks [t*E, t*E + E)
+      const int E = (n_chunks + kThreads - 1) / kThreads;
+      const int m0 = min(t * E, n_chunks), m1 = min(m0 + E, n_chunks);
+      int tie_rank = 0, total;
+      if (exact) {
+        int ties = 0;
+        for (int m = m0; m < m1; ++m) ties += score_key(sc[m]) == prefix;
+        tie_rank = block_scan_excl<kThreads>(ties, &total, scan_ws);
+      }
+      auto taken = [&](uint32_t k, int& tr) {
+        const uint32_t km = k & pmask;
+        if (km > prefix) return true;
+        if (km != prefix || kc_eff == 0) return false;
+        return !exact || tr++ < need;
+      };
+      int n_here = 0;
+      {
+        int tr = tie_rank;
+        for (int m = m0; m < m1; ++m) n_here += taken(score_key(sc[m]), tr);
+      }
+      int pos = block_scan_excl<kThreads>(n_here, &total, scan_ws);
+      {
+        int tr = tie_rank;
+        for (int m = m0; m < m1; ++m)
+          if (taken(score_key(sc[m]), tr)) sorted[pos++] = chunk0 + m;
       }
       __syncthreads();
       if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
@@ -324,35 +384,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 constexpr int kUpdThreads = 1024;
 constexpr int kUpdWaves = kUpdThreads / kWave;
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
-  return v;
-}
-
-// Exclusive prefix sum of v over the workgroup in thread order; *total gets
-// the sum. Contains barriers: every thread must call it.
-__device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int inc = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) wsum[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    const int w = lane < kUpdWaves ? wsum[lane] : 0;
-    const int wi = wave_incl_scan(w, lane);
-    if (lane < kUpdWaves) wsum[lane] = wi - w;
-    if (lane == kUpdWaves - 1) wsum[kUpdWaves] = wi;
-  }
-  __syncthreads();
-  const int r = wsum[wave] + inc - v;
-  *total = wsum[kUpdWaves];
-  __syncthreads();
-  return r;
-}
-
 template <int D>
 __global__ __launch_bounds__(kUpdThreads) void gcache_update_kernel(
     const int32_t* __restrict__ sel_chunks, int n_blocks, int n_kv, int k_c,
@@ -397,7 +428,7 @@ __global__ __launch_bounds__(kUpdThreads) void gcache_update_kernel(
     }
   }
   int packed_total;
-  const int base = block_scan_excl(hits_here | (misses_here << 16), &packed_total, wsum);
+  const int base = block_scan_excl<kUpdThreads>(hits_here | (misses_here << 16), &packed_total, wsum);
   const int n_hit = packed_total & 0xffff, n_miss = packed_total >> 16;
   int k = base >> 16;
   for (int w = w0; w < w1; ++w)
@@ -416,7 +447,7 @@ __global__ __launch_bounds__(kUpdThreads) void gcache_update_kernel(
     if (i < n_slots && !pinned[(h0 + i) % n_slots]) ++free_here;
   }
   int n_free;
-  int rk = block_scan_excl(free_here, &n_free, wsum);
+  int rk = block_scan_excl<kUpdThreads>(free_here, &n_free, wsum);
   for (int f = 0; f < F; ++f) {
     const int i = t * F + f;
     if (i >= n_slots) break;
