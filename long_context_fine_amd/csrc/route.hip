@@ -96,8 +96,9 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 
 // Exclusive prefix sum of v over a workgroup of NT threads in thread order;
 // *total gets the sum. wsum: NT/64 + 1 ints of LDS. Contains barriers: every
-// thread must call it.
-template <int NT>
+// thread must call it. Without the trailing barrier the caller must pass
+// another barrier before wsum is written again.
+template <int NT, bool kTrailingBarrier = true>
 __device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
   constexpr int NWV = NT / kWave;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -113,7 +114,7 @@ __device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
   __syncthreads();
   const int r = wsum[wave] + inc - v;
   *total = wsum[NWV];
-  __syncthreads();
+  if (kTrailingBarrier) __syncthreads();
   return r;
 }
 
@@ -152,9 +153,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ float part[RG][D + 1];
   __shared__ float qv[D];
   __shared__ float sc_lds[kLdsScores];
-  __shared__ int32_t hist_s[kThreads];       // radix-select digit histogram (256 bins)
-  __shared__ int32_t rsel[3];
+  __shared__ int32_t hist_s[2][kThreads];    // radix-select digit histograms (256 bins), by pass parity
+  __shared__ int32_t rsel[2][3];
   __shared__ int32_t scan_ws[NW + 1];
+  __shared__ int32_t gtmp_s[kMaxTopKChunks];  // kept chunk ids before ordering
+  __shared__ int32_t n_app;
   __shared__ int32_t sorted[kMaxTopKChunks];
   __shared__ float gsc[kMaxCand];
   __shared__ __attribute__((aligned(16))) uint64_t gkey[kMaxCand];
@@ -240,54 +243,64 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       uint32_t prefix = 0u, pmask = 0u;
       int need = kc_eff;        // keys still to take among those equal to prefix under pmask
       bool exact = false;       // threshold fixed in all 32 bits: ties resolved by index
-      for (int shift = 24; shift >= 0 && kc_eff > 0; shift -= 8) {
-        hist_s[t] = 0;
-        __syncthreads();
+      // histograms and selections alternate between two buffers by pass, so
+      // a pass needs four barriers: counts done, two in the scan, selection
+      hist_s[0][t] = 0;
+      __syncthreads();
+      int hb = 0;
+      for (int shift = 24; shift >= 0 && kc_eff > 0; shift -= 8, hb ^= 1) {
         for (int m = t; m < n_chunks; m += kThreads) {
           const uint32_t k = score_key(sc[m]);
-          if ((k & pmask) == prefix) atomicAdd(&hist_s[(k >> shift) & 255u], 1);
+          if ((k & pmask) == prefix) atomicAdd(&hist_s[hb][(k >> shift) & 255u], 1);
         }
         __syncthreads();
         const int bin = kThreads - 1 - t;           // thread order = bins descending
-        const int h = hist_s[bin];
+        const int h = hist_s[hb][bin];
+        hist_s[hb ^ 1][t] = 0;                      // the next pass's histogram
         int total;
-        const int at_or_above = block_scan_excl<kThreads>(h, &total, scan_ws) + h;
+        const int at_or_above = block_scan_excl<kThreads, false>(h, &total, scan_ws) + h;
         if (at_or_above >= need && at_or_above - h < need) {
-          rsel[0] = bin;
-          rsel[1] = at_or_above - h;
-          rsel[2] = h;
+          rsel[hb][0] = bin;
+          rsel[hb][1] = at_or_above - h;
+          rsel[hb][2] = h;
         }
         __syncthreads();
-        prefix |= static_cast<uint32_t>(rsel[0]) << shift;
+        prefix |= static_cast<uint32_t>(rsel[hb][0]) << shift;
         pmask |= 255u << shift;
-        need -= rsel[1];
-        const bool whole = rsel[2] == need;
-        __syncthreads();                            // rsel is rewritten next pass
-        if (whole) break;
+        need -= rsel[hb][1];
+        if (rsel[hb][2] == need) break;             // the whole bin is kept
         if (shift == 0) exact = true;
       }
-      // ordered compaction: thread t owns chunks [t*E, t*E + E)
-      const int E = (n_chunks + kThreads - 1) / kThreads;
-      const int m0 = min(t * E, n_chunks), m1 = min(m0 + E, n_chunks);
-      int tie_rank = 0, total;
-      if (exact) {
-        int ties = 0;
+      if (!exact) {
+        // every key with the prefix under the mask, or above it, is kept: the
+        // kc_eff chunk ids are appended in any order, then placed by rank
+        // (ids are unique, so the result is fixed)
+        if (t == 0) n_app = 0;
+        __syncthreads();
+        for (int m = t; m < n_chunks && kc_eff > 0; m += kThreads)
+          if ((score_key(sc[m]) & pmask) >= prefix) gtmp_s[atomicAdd(&n_app, 1)] = chunk0 + m;
+        __syncthreads();
+        if (t < kc_eff) {
+          const int id = gtmp_s[t];
+          int pos = 0;
+          for (int u = 0; u < kc_eff; ++u) pos += gtmp_s[u] < id;
+          sorted[pos] = id;
+        }
+      } else {
+        // equal keys at the threshold: the need lowest indices among them.
+        // Ordered compaction, thread t owns chunks [t*E, t*E + E)
+        const int E = (n_chunks + kThreads - 1) / kThreads;
+        const int m0 = min(t * E, n_chunks), m1 = min(m0 + E, n_chunks);
+        int total, ties = 0;
         for (int m = m0; m < m1; ++m) ties += score_key(sc[m]) == prefix;
-        tie_rank = block_scan_excl<kThreads>(ties, &total, scan_ws);
-      }
-      auto taken = [&](uint32_t k, int& tr) {
-        const uint32_t km = k & pmask;
-        if (km > prefix) return true;
-        if (km != prefix || kc_eff == 0) return false;
-        return !exact || tr++ < need;
-      };
-      int n_here = 0;
-      {
-        int tr = tie_rank;
-        for (int m = m0; m < m1; ++m) n_here += taken(score_key(sc[m]), tr);
-      }
-      int pos = block_scan_excl<kThreads>(n_here, &total, scan_ws);
-      {
+        const int tie_rank = block_scan_excl<kThreads>(ties, &total, scan_ws);
+        auto taken = [&](uint32_t k, int& tr) { return k > prefix || (k == prefix && tr++ < need); };
+        int n_here = 0;
+        {
+          int tr = tie_rank;
+          for (int m = m0; m < m1; ++m) n_here += taken(score_key(sc[m]), tr);
+        }
+        int pos = block_scan_excl<kThreads>(n_here, &total, scan_ws);
         int tr = tie_rank;
         for (int m = m0; m < m1; ++m)
           if (taken(score_key(sc[m]), tr)) sorted[pos++] = chunk0 + m;
