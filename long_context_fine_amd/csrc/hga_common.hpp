@@ -74,9 +74,6 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 __device__ __forceinline__ uint64_t rank_key(float s, uint32_t idx) {
   return (static_cast<uint64_t>(score_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
 }
-__device__ __forceinline__ uint32_t rank_key_index(uint64_t k) {
-  return 0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu);
-}
 
 // Cross-lane moves through DPP (a VALU operand modifier, no LDS round trip).
 // CTRL is the gfx9 dpp_ctrl code, ROW_MASK selects the 16-lane rows written;
@@ -86,32 +83,10 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL,
                                                            ROW_MASK, 0xf, false));
 }
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(v));
-  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(v >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 constexpr int kDppQuadXor1 = 0xb1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4e;     // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
-constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> next row
-constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
-
-// Maximum over the wave, returned to every lane (all lanes active).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
-  v = mx(v, dpp_u64<kDppQuadXor1>(v));
-  v = mx(v, dpp_u64<kDppQuadXor2>(v));
-  v = mx(v, dpp_u64<kDppRowHalfMirror>(v));   // max of each 8 lanes
-  v = mx(v, dpp_u64<kDppRowMirror>(v));       // max of each 16-lane row
-  v = mx(v, dpp_u64<kDppRowBcast15, 0xa>(v)); // rows 1, 3: max of rows {0,1}, {2,3}
-  v = mx(v, dpp_u64<kDppRowBcast31, 0xc>(v)); // row 3: max of all rows
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 
 // Sum over each aligned group of 8 lanes, returned to all 8 (all lanes active).
 __device__ __forceinline__ float sum8_f32(float x) {

@@ -1,22 +1,27 @@
-// Two-level content routing, one workgroup per (query block b, KV head j):
+// Two-level content routing, one workgroup per (query block b, KV head j),
+// the KV head the fastest grid index (a head's workgroups share one XCD's L2):
 //   1. block query qbar = mean of the block's 64 queries over the r heads of j
 //      (reads its 64 KiB of Q once, 16-byte loads);
-//   2. chunk scores qbar . C[j][m] for every history chunk (16 lanes per chunk,
-//      coalesced 512-byte rows; C[j] stays in L2 across the 32 blocks);
-//   3. chunk top-k: each wave takes the k_c best of its strided share in k_c
-//      rounds of a wave-wide max over 64-bit keys strictly below the previous
-//      one (key = order-preserving fp32 bits, then the complemented index, so
-//      the maximum is the best score with the lowest index); the 4*k_c wave
-//      candidates are merged by rank counting;
+//   2. chunk scores qbar . C[j][m] for every ranked history chunk (8 lanes per
+//      512-byte row, whole 128-byte lines per load instruction, the next rows
+//      in flight while the current ones are reduced);
+//   3. chunk top-k by exact radix select over order-preserving 32-bit score
+//      keys (8-bit digit histograms in LDS, most significant digit first),
+//      ties at the threshold key going to the lowest index, then the kept
+//      chunks in ascending order;
 //   4. scores of the 8 groups of every kept chunk (reads 8*k_c rows of G);
-//   5. group top-k by rank counting; candidates are enumerated in ascending
-//      group id, so ballot prefix counts place the output in ascending order.
-// HBM/latency bound. Deterministic.
+//   5. group top-k by rank counting over 64-bit keys (score key, then the
+//      complemented index, so larger means better and lower index); the
+//      candidates are enumerated in ascending group id, so ballot prefix
+//      counts place the output in ascending order.
+// HBM/latency bound. Deterministic: the only atomics are integer adds into
+// LDS histograms and counters, whose results do not depend on their order.
 //
 // With group summaries in host memory (the group-summary cache) the same
 // kernel runs in two halves around gcache_update_kernel: phases 1-3 (and q-bar
 // kept in the workspace), then the cache update for all blocks of a KV head,
-// then phases 4-5 reading group rows from the cache slots.
+// then phases 4-5 reading group rows from the cache slots. For a decode batch
+// it runs with one sequence per workgroup row (decode mode).
 #include "hga_common.hpp"
 
 namespace hga {
