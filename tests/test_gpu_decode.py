@@ -124,3 +124,38 @@ def test_decode_qwen3_8b_131k():
     # segment, one new token per sequence, ragged lengths
     run_decode(32, 8, 128, 129024, 2048, 16, 32, "bf16", [129024, 100032], [2048, 517], n_new=1,
                seed=6)
+
+
+def test_decode_retrieves_a_planted_needle():
+    # retrieval: one history chunk of sequence 0, far back, gets keys aligned
+    # with the new token's query; routing must select it and most attention
+    # mass must land on it (the output moves toward that chunk's values)
+    n_q, n_kv, d, P, T = 8, 2, 128, 8192, 128
+    w = synth.Workload("decode", n_q, n_kv, d, P, T, 4, 16, "bf16", 1.0 / math.sqrt(d))
+    inp = synth.make_decode_inputs(w, [P], [T], 1, 9)
+    needle = 17                                  # chunk 17 of 128
+    r = n_q // n_kv
+    for j in range(n_kv):
+        qdir = inp["q"][0, j * r:(j + 1) * r, 0].float().mean(0)
+        qdir = qdir / qdir.norm()
+        inp["k_hist"][0, j, 64 * needle:64 * needle + 64] = (qdir * 200.0).to(torch.bfloat16)
+        inp["v_hist"][0, j, 64 * needle:64 * needle + 64] = 1.0
+    g = {k: v.cuda() for k, v in inp.items()}
+    s = hga.make_shape(n_q, n_kv, d, P, T, 4, 16, torch.bfloat16)
+    C = torch.zeros((1, n_kv, P // 64, d), dtype=torch.float32, device="cuda")
+    G = torch.zeros((1, n_kv, P // 8, d), dtype=torch.float32, device="cuda")
+    hga.hga_build_summaries(s, g["k_hist"][0], C[0], G[0])
+    o, lse, sc, sg = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
+                                g["hist_lens"], g["tail_lens"])
+    torch.cuda.synchronize()
+    print("[case] decode needle: chunks", sc[0].tolist(), flush=True)
+    for j in range(n_kv):
+        assert needle in sc[0, j].tolist()
+        assert set(range(8 * needle, 8 * needle + 8)) <= set(sg[0, j].tolist())
+    # the needle's values (all ones) dominate: every output coordinate near 1
+    assert float(o.float().mean()) > 0.9
+    _, _, O_ref, L_ref = orc.decode_step(_f64(inp["q"][0]), _f64(inp["k_hist"][0]), _f64(inp["v_hist"][0]),
+                                         _f64(inp["k_tail"][0]), _f64(inp["v_tail"][0]), 4, 16,
+                                         w.softmax_scale, sel_groups=sg[0].cpu().numpy())
+    assert orc.within_tolerance(_f64(o[0]), O_ref, TOL["bf16"])
+    assert orc.within_tolerance(_f64(lse[0]), L_ref, TOL["bf16"])
