@@ -534,6 +534,32 @@ def main():
         "kernels": kernels,
         "routed_history_tokens_per_block": density,
     }
+    if not w.hist_on_host and w.hist_len > 0:
+        # The standalone device gather (hga_gather_groups) of this step's
+        # selections, timed after the step loop. It is not part of the step
+        # (the attention kernel gathers K/V rows into LDS itself); it shows the
+        # gather's own HBM rate: every routed group's K and V rows read once
+        # and written once (empty slots, zero-filled, are not counted).
+        gid = names.index("gather")
+        e = 2 if w.dtype == "bf16" else 4
+        out_shape = (n_B, w.n_kv_heads, w.top_k_groups * 8, w.head_dim)
+        ko = torch.empty(out_shape, dtype=w.torch_dtype, device=dev)
+        vo = torch.empty_like(ko)
+        n_g = 20
+        ev_g = new_events(n_g)
+        torch.cuda.synchronize()
+        for i in range(n_g):
+            hga.hga_set_kernel_events(gid, *ev_g[i])
+            hga.hga_gather_groups(s, g["k_hist"], g["v_hist"], sel_g, ko, vo)
+        torch.cuda.synchronize()
+        hga.hga_set_kernel_events(gid, None, None)
+        g_us = avg_us(ev_g)
+        g_bytes = int((sel_cpu >= 0).sum()) * 8 * w.head_dim * e * 2 * 2
+        out["gather_device"] = {"avg_us": round(g_us, 3), "mib_per_launch": round(g_bytes / 2 ** 20, 3),
+                                "gbs": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
+                                "frac_hbm": round(g_bytes / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                "note": "hga_gather_groups on this step's selections, outside the "
+                                        "step; bytes = routed K and V rows read + written"}
     if n_slots:
         # steady state above: the same queries every step, so every kept chunk
         # hits after the first call. Cold calls: reset, then route (all misses).
