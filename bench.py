@@ -143,8 +143,14 @@ def cpu_baseline(w, inp, budget_s):
     if threadpool_info is not None:
         cores = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
     del np
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": w.seg_len * n_steps / t_total, "unit": "query tokens/s", "cores": cores,
-            "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": model, "kind": "oracle",
             "sample": f"{n_steps} whole step(s) of the same workload (route incl. full summaries, "
                       f"attention fwd{'+bwd' if w.backward else ''} over all {w.seg_len // 64} "
                       f"query blocks x {w.n_q_heads} heads), numpy fp32 routing / fp64 attention, "
@@ -489,6 +495,12 @@ def main():
     value = w.seg_len * args.steps / elapsed
     dus = avg_us(timed_ev)
     kernels[dom] = entry(dom, dus)
+    per_launch = sorted(a.elapsed_time(b) * 1e3 for a, b in timed_ev)
+
+    def pct(q):
+        return round(per_launch[min(len(per_launch) - 1, int(q * len(per_launch)))], 3)
+
+    kernels[dom]["us_p10_p50_p90"] = [pct(0.1), pct(0.5), pct(0.9)]
     kind, amount = work[dom]
     if kind == "mfma":
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -560,6 +572,54 @@ def main():
                                 "frac_hbm": round(g_bytes / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                                 "note": "hga_gather_groups on this step's selections, outside the "
                                         "step; bytes = routed K and V rows read + written"}
+    if not w.hist_on_host and not n_slots:
+        # Cold-cache route (and device gather): reading a 512 MiB buffer before
+        # each call evicts the 256 MB Infinity Cache and the L2s (with clean
+        # lines, so no write-backs land in the call), so the call's bytes come
+        # from HBM (the timed steps above run warm: the 16K history fits the
+        # cache).
+        flush = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+        flush_sum = torch.empty((), dtype=torch.float32, device=dev)
+        rid = names.index("route")
+        n_cold = 10
+        ev_rc = new_events(n_cold)
+        torch.cuda.synchronize()
+        for i in range(n_cold):
+            torch.sum(flush, dim=0, out=flush_sum)
+            hga.hga_set_kernel_events(rid, *ev_rc[i])
+            hga.hga_route(s, g["q"], C, G, sel_c, sel_g, ws_r)
+        torch.cuda.synchronize()
+        hga.hga_set_kernel_events(rid, None, None)
+        rc_us = avg_us(ev_rc)
+        out["route"]["cold"] = {"avg_us": round(rc_us, 3),
+                                "gbs": round(route_bytes / (rc_us * 1e-6) / 1e9, 1),
+                                "frac_hbm": round(route_bytes / (rc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        if "gather_device" in out:
+            ev_gc = new_events(n_cold)
+            torch.cuda.synchronize()
+            for i in range(n_cold):
+                torch.sum(flush, dim=0, out=flush_sum)
+                hga.hga_set_kernel_events(gid, *ev_gc[i])
+                hga.hga_gather_groups(s, g["k_hist"], g["v_hist"], sel_g, ko, vo)
+            torch.cuda.synchronize()
+            hga.hga_set_kernel_events(gid, None, None)
+            gc_us = avg_us(ev_gc)
+            out["gather_device"]["cold"] = {"avg_us": round(gc_us, 3),
+                                            "gbs": round(g_bytes / (gc_us * 1e-6) / 1e9, 1),
+                                            "frac_hbm": round(g_bytes / (gc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del flush, flush_sum
+    # device memory the layer call holds (MiB): history K/V, summaries,
+    # segment tensors (Q, K, V, O, LSE and, with the backward, dO, dQ, dK, dV),
+    # selections and workspaces
+    mib = lambda *ts: round(sum(t.numel() * t.element_size() for t in ts) / 2 ** 20, 2)
+    seg_ts = [g["q"], g["k_seg"], g["v_seg"], o, lse] + ([g["d_o"], dq, dk, dv] if w.backward else [])
+    out["hbm_footprint_mib"] = {
+        "history_kv": 0.0 if w.hist_on_host else mib(g["k_hist"], g["v_hist"]),
+        "summaries": mib(C) + (0.0 if n_slots else mib(G)),
+        "segment": mib(*seg_ts),
+        "selections": mib(sel_c, sel_g),
+        "workspaces": mib(ws_r, ws_f, *([ws_b] if w.backward else [])),
+    }
     if n_slots:
         # steady state above: the same queries every step, so every kept chunk
         # hits after the first call. Cold calls: reset, then route (all misses).
