@@ -256,6 +256,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
           for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
           bf16x8 ka = lds_a_row_swz<D>(kbuf, kt * 32, 0, ln);
           bf16x8 va = lds_a_row_swz<D>(vbuf, kt * 32, 0, ln);
+          // raised wave priority over each MFMA cluster (two waves per SIMD:
+          // the one with MFMAs ready issues first)
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int s = 0; s < NKS; ++s) {
             bf16x8 kn = ka, vn = va;
@@ -274,6 +277,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
             va = vn;
             __builtin_amdgcn_sched_barrier(0);
           }
+          __builtin_amdgcn_s_setprio(0);
           bf16x8 a0 = lds_a_tr_swz<D>(kbuf, kt * 32, 0, ln);
           bf16x8 a1 = lds_a_tr_swz<D>(kbuf, kt * 32 + 16, 0, ln);
           if (masked) {
@@ -289,6 +293,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
           }
           const bf16x8 ds0 = acc_to_bf16x8(sacc, 0);
           const bf16x8 ds1 = acc_to_bf16x8(sacc, 8);
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
             bf16x8 n0 = a0, n1 = a1;
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
             a1 = n1;
             __builtin_amdgcn_sched_barrier(0);
           }
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       wait_vmem();

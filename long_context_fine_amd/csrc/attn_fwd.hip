@@ -224,6 +224,10 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
+        // raised wave priority over each MFMA cluster: of the two waves on a
+        // SIMD, the one with MFMAs ready issues first while the other one's
+        // softmax and LDS work fills the gaps
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
 #pragma unroll
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
             sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- mask, online softmax (raw scores; scale folded into exp2) ------
         if (masked) {
@@ -279,6 +284,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
         l_run += psum;
 
         // ---- O^T += V^T . P^T --------------------------------------------
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -286,6 +292,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
             for (int ksi = 0; ksi < 2; ++ksi)
               oacc[dt] = mfma32(lds_a_tr(vbuf, VS, kt * 32 + ksi * 16, dt * 32, lane), pb[kt][ksi], oacc[dt]);
+        __builtin_amdgcn_s_setprio(0);
       }
       if (more) {
         kr.store_rows(gtid, smem[cur ^ 1][grp], KS);
