@@ -252,14 +252,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
   }
 }
 
-template <int D>
+// QR: query rows provisioned in LDS and registers (R = r * n_new <= QR); a
+// smaller QR for the common R <= 4 or 8 frees LDS and registers for more
+// resident workgroups, which hide the row loads.
+template <int D, int QR>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodeParams p) {
+  static_assert(QR <= 32, "query rows are the 32 columns of the score MFMA");
   constexpr int NKS = D / 16;                   // MFMA k-steps over head_dim
   constexpr int NW = kDecThreads / kWave;
   constexpr int KT = 32;                        // keys per MFMA tile
   constexpr int TPW = kDecKeys / (NW * KT);     // tiles per wave
   constexpr int DPL = D / kWave;                // output dims per lane in P.V
-  constexpr int QR = 16;                        // query rows (host-checked bound)
   // rows padded by 4 floats: the 32 query rows' 16-byte score stores spread over the banks
   __shared__ __attribute__((aligned(16))) float s_lds[QR][kDecKeys + 4];
   __shared__ int32_t kinfo[kDecKeys];           // -1 plain, -2 masked, >= 0 open-segment position
@@ -457,9 +460,14 @@ hipError_t launch_td(const hga_shape& s, DecodeParams& p, int batch, hipStream_t
   const dim3 grid(p.n_piece, s.n_kv_heads, batch);
   const int R = p.r * p.n_new;
   hipEvent_t e0 = timer_event(HGA_KERNEL_DECODE, 0), e1 = timer_event(HGA_KERNEL_DECODE, 1);
-  if constexpr (sizeof(T) == 2)
-    hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
-  else if (R <= 4)
+  if constexpr (sizeof(T) == 2) {
+    if (R <= 4)
+      hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 4>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+    else if (R <= 8)
+      hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+    else
+      hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 16>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+  } else if (R <= 4)
     hipExtLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
   else if (R <= 8)
     hipExtLaunchKernelGGL((decode_attn_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
