@@ -123,7 +123,15 @@ __device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
   return r;
 }
 
-enum RouteMode { kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2, kRouteDecode = 3 };
+enum RouteMode {
+  kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2, kRouteDecode = 3,
+  // decode with the chunk scan split over n_part workgroups per (sequence,
+  // KV head): each ranks one contiguous part of the chunks and keeps its own
+  // top k_c (with scores); a merge then keeps the top k_c of those candidates
+  // and runs the group steps. Exact: every chunk of the overall top k_c is in
+  // the top k_c of its part, under the same (score, lower index) order.
+  kRouteDecodePart = 4, kRouteDecodeMerge = 5
+};
 
 // Decode: blockIdx.y is a sequence of the batch, the query block is its
 // seg_len newest tokens (q [batch][n_q][seg_len][D]); summaries are
@@ -134,6 +142,9 @@ struct DecodeView {
   const int32_t* hist_lens;
   int n_sink;
   int n_q;
+  int n_part = 1;              // split decode: parts per (sequence, KV head)
+  int32_t* cand_id = nullptr;  // [batch][n_kv][n_part][k_c] kept chunk ids (-1: none)
+  float* cand_sc = nullptr;    // their scores
 };
 
 // Group rows of the cache: [n_kv][n_slots][8][D] fp32, slot of each chunk in
@@ -175,7 +186,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   // (round-robin dispatch), whose L2 then holds that head's chunk summaries
   const int j = blockIdx.x, b = blockIdx.y;
   const int64_t bj = static_cast<int64_t>(b) * n_kv + j;
-  if constexpr (MODE == kRouteDecode) {
+  constexpr bool kDec = MODE == kRouteDecode || MODE == kRouteDecodePart || MODE == kRouteDecodeMerge;
+  if constexpr (kDec) {
     int hb = dec.hist_lens[b];
     hb = hb < 0 ? 0 : (hb > chunk_rows * kChunk ? chunk_rows * kChunk : hb);
     const int nc = hb / kChunk;
@@ -183,20 +195,26 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     n_chunks = nc - chunk0;
     csum += static_cast<int64_t>(b) * n_kv * chunk_rows * D;
     gsum += static_cast<int64_t>(b) * n_kv * chunk_rows * (kChunk / kGroup) * D;
+    if constexpr (MODE == kRouteDecodePart) {  // this workgroup's part of the ranked chunks
+      const int per = (n_chunks + dec.n_part - 1) / dec.n_part;
+      const int lo = min(n_chunks, static_cast<int>(blockIdx.z) * per);
+      chunk0 += lo;
+      n_chunks = min(n_chunks - lo, per);
+    }
   }
 
   // ---- 1. block query ----------------------------------------------------
-  if constexpr (MODE == kRouteGroups) {
+  if constexpr (MODE == kRouteGroups || MODE == kRouteDecodeMerge) {
     if (t < D) qv[t] = ws_qbar[bj * D + t];
     __syncthreads();
   } else {
     const int dc = t % TPR, rg = t / TPR;
-    const int rows = (MODE == kRouteDecode ? seg_len : kBlockQ) * r;
+    const int rows = (kDec ? seg_len : kBlockQ) * r;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll 8
     for (int row = rg; row < rows; row += RG) {
       int64_t qrow;
-      if constexpr (MODE == kRouteDecode) {
+      if constexpr (kDec) {
         qrow = (static_cast<int64_t>(b) * dec.n_q + j * r + row / seg_len) * seg_len + row % seg_len;
       } else {
         const int h = j * r + row / kBlockQ, i = b * kBlockQ + row % kBlockQ;
@@ -215,6 +233,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       for (int g = 0; g < RG; ++g) s += part[g][t];
       qv[t] = s * (1.0f / static_cast<float>(rows));
       if constexpr (MODE == kRouteChunks) ws_qbar[bj * D + t] = qv[t];
+      if constexpr (MODE == kRouteDecodePart) {
+        if (blockIdx.z == 0) ws_qbar[bj * D + t] = qv[t];
+      }
     }
     __syncthreads();
   }
@@ -228,10 +249,54 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       slot_s[t] = cache.slot_of_chunk[static_cast<int64_t>(j) * chunk_rows + c];
     }
     kc_eff = __syncthreads_count(c >= 0);
+  } else if constexpr (MODE == kRouteDecodeMerge) {
+    // ---- 3'. top k_c of the parts' candidates (ids ascending within a part,
+    // parts in chunk order, so candidate order is chunk order): rank count
+    // over 64-bit keys (score key, complemented id; 0 marks an empty slot)
+    const int ncc = dec.n_part * k_c;          // host-checked: ncc < kMaxCand
+    const int64_t c0 = bj * ncc;
+    for (int c = t; c <= ncc; c += kThreads) {
+      const int id = c < ncc ? dec.cand_id[c0 + c] : -1;
+      gkey[c] = id >= 0 ? rank_key(dec.cand_sc[c0 + c], static_cast<uint32_t>(id)) : 0ull;
+    }
+    __syncthreads();
+    const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(gkey);
+    for (int cb = 0; cb < ncc; cb += kThreads) {
+      const int c = cb + t;
+      bool take = false;
+      if (c < ncc) {
+        const uint64_t mine = gkey[c];
+        if (mine != 0ull) {
+          int beaten = 0;
+#pragma unroll 4
+          for (int o2 = 0; o2 < (ncc + 1) / 2; ++o2) {
+            const ulonglong2 x = k2[o2];
+            beaten += (x.x > mine) + (x.y > mine);
+          }
+          take = beaten < k_c;
+        }
+      }
+      const uint64_t m = __ballot(take);
+      if (lane == 0) wmask[cb / kWave + wave] = m;
+    }
+    __syncthreads();
+    int total = 0;
+    for (int w2 = 0; w2 < (ncc + kWave - 1) / kWave; ++w2) total += __popcll(wmask[w2]);
+    kc_eff = total;
+    for (int c = t; c < ncc; c += kThreads) {
+      const uint64_t m = wmask[c / kWave];
+      if ((m >> (c % kWave)) & 1ull) {
+        int pos = __popcll(m & ((1ull << (c % kWave)) - 1ull));
+        for (int w2 = 0; w2 < c / kWave; ++w2) pos += __popcll(wmask[w2]);
+        sorted[pos] = dec.cand_id[c0 + c];
+      }
+    }
+    __syncthreads();
+    if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
   } else {
     // ---- 2. chunk scores ----------------------------------------------------
     float* sc = n_chunks <= kLdsScores ? sc_lds
-                                       : ws_scores + bj * (MODE == kRouteDecode ? chunk_rows : n_chunks);
+                                       : ws_scores + bj * (kDec ? chunk_rows : n_chunks);
     // ranked chunks are chunk0 .. chunk0 + n_chunks - 1 (the sink is attended in full)
     const float* cbase = csum + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
     score_rows<D, 4>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
@@ -311,10 +376,20 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
           if (taken(score_key(sc[m]), tr)) sorted[pos++] = chunk0 + m;
       }
       __syncthreads();
-      if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
+      if constexpr (MODE == kRouteDecodePart) {
+        // this part's kept chunks and their scores, for the merge
+        if (t < k_c) {
+          const int64_t o = (bj * dec.n_part + blockIdx.z) * k_c + t;
+          const bool v = t < kc_eff;
+          dec.cand_id[o] = v ? sorted[t] : -1;
+          dec.cand_sc[o] = v ? sc[sorted[t] - chunk0] : 0.f;
+        }
+      } else {
+        if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
+      }
     }
   }
-  if constexpr (MODE == kRouteChunks) return;
+  if constexpr (MODE == kRouteChunks || MODE == kRouteDecodePart) return;
 
   // ---- 4. group scores for the 8 groups of every kept chunk ----------------
   const int n_cand = kc_eff * (kChunk / kGroup);
@@ -619,24 +694,82 @@ hipError_t launch_route_cached(const hga_shape& s, const void* q, const float* c
             : launch_cached_t<float, 64>(s, q, chunk_sum, L, group_sum_dev, sel_chunks, sel_groups, stats, ws, stream);
 }
 
+// Parts per (sequence, KV head) for the decode route: split the chunk scan
+// only when the batch leaves most CUs idle (at most 32 (sequence, KV head)
+// pairs; from 64 pairs on the two launches and the merge cost what the split
+// saves), each part fits the LDS scores and the merge's candidates fit its
+// key array.
+int decode_route_parts(const hga_shape& s, int batch) {
+  const int64_t rows = hist_rows(s) / kChunk;
+  const int64_t wgs = static_cast<int64_t>(batch) * s.n_kv_heads;
+  if (wgs > 32 || rows < 2 * kThreads) return 1;
+  const int64_t want = (2 * kThreads + wgs - 1) / wgs;
+  int P = static_cast<int>(want < 8 ? want : 8);
+  while (P > 1 && P * s.top_k_chunks >= kMaxTopKChunks * (kChunk / kGroup)) --P;
+  if (P <= 1 || (rows + P - 1) / P > kLdsScores) return 1;
+  return P;
+}
+
+struct DecodeRouteWs {
+  size_t scores, qbar, cand;  // byte offsets
+  size_t bytes;
+};
+
+// [chunk scores, above 4,096 chunks per (sequence, KV head), unsplit only]
+// [q-bar [batch][n_kv][D] fp32] [candidate ids] [candidate scores]
+DecodeRouteWs decode_route_ws(const hga_shape& s, int batch) {
+  DecodeRouteWs w{};
+  const int P = decode_route_parts(s, batch);
+  w.scores = 0;
+  size_t off = align256(sizeof(float) * batch * s.n_kv_heads * (hist_rows(s) / kChunk + 1));
+  if (P > 1) {
+    const size_t nc = static_cast<size_t>(batch) * s.n_kv_heads * P * s.top_k_chunks;
+    w.qbar = off;
+    off += align256(sizeof(float) * batch * s.n_kv_heads * s.head_dim);
+    w.cand = off;
+    off += 2 * align256(sizeof(int32_t) * nc);
+  }
+  w.bytes = off;
+  return w;
+}
+
 template <typename T, int D>
 hipError_t launch_decode_t(const hga_shape& s, int batch, int n_new, const void* q, const float* cs,
                            const float* gs, const int32_t* hist_lens, int32_t* sc_out, int32_t* sg_out,
                            void* ws, hipStream_t st) {
   const int r = s.n_q_heads / s.n_kv_heads;
   const int chunk_rows = static_cast<int>(hist_rows(s) / kChunk);
-  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecode>), dim3(s.n_kv_heads, batch), dim3(kThreads), 0, st,
-                        timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
-                        static_cast<const T*>(q), cs, gs, n_new, s.n_kv_heads, r, 0, 0, chunk_rows,
-                        s.top_k_chunks, s.top_k_groups, static_cast<float*>(ws), sc_out, sg_out, nullptr,
-                        CacheView{}, DecodeView{hist_lens, s.n_sink_chunks, s.n_q_heads});
+  const int P = decode_route_parts(s, batch);
+  if (P == 1) {
+    hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecode>), dim3(s.n_kv_heads, batch), dim3(kThreads), 0, st,
+                          timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
+                          static_cast<const T*>(q), cs, gs, n_new, s.n_kv_heads, r, 0, 0, chunk_rows,
+                          s.top_k_chunks, s.top_k_groups, static_cast<float*>(ws), sc_out, sg_out, nullptr,
+                          CacheView{}, DecodeView{hist_lens, s.n_sink_chunks, s.n_q_heads});
+    return hipGetLastError();
+  }
+  const DecodeRouteWs w = decode_route_ws(s, batch);
+  char* base = static_cast<char*>(ws);
+  float* qbar = reinterpret_cast<float*>(base + w.qbar);
+  const size_t nc = static_cast<size_t>(batch) * s.n_kv_heads * P * s.top_k_chunks;
+  DecodeView dv{hist_lens, s.n_sink_chunks, s.n_q_heads};
+  dv.n_part = P;
+  dv.cand_id = reinterpret_cast<int32_t*>(base + w.cand);
+  dv.cand_sc = reinterpret_cast<float*>(base + w.cand + align256(sizeof(int32_t) * nc));
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecodePart>), dim3(s.n_kv_heads, batch, P), dim3(kThreads), 0,
+                        st, timer_event(HGA_KERNEL_ROUTE, 0), nullptr, 0, static_cast<const T*>(q), cs, gs, n_new,
+                        s.n_kv_heads, r, 0, 0, chunk_rows, s.top_k_chunks, s.top_k_groups,
+                        static_cast<float*>(ws), sc_out, sg_out, qbar, CacheView{}, dv);
+  hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecodeMerge>), dim3(s.n_kv_heads, batch), dim3(kThreads), 0, st,
+                        nullptr, timer_event(HGA_KERNEL_ROUTE, 1), 0, static_cast<const T*>(q), cs, gs, n_new,
+                        s.n_kv_heads, r, 0, 0, chunk_rows, s.top_k_chunks, s.top_k_groups,
+                        static_cast<float*>(ws), sc_out, sg_out, qbar, CacheView{}, dv);
   return hipGetLastError();
 }
 
-// Chunk scores of every (sequence, KV head) when a history exceeds the LDS.
-size_t decode_route_workspace_bytes(const hga_shape& s, int batch) {
-  return align256(sizeof(float) * batch * s.n_kv_heads * (hist_rows(s) / kChunk + 1));
-}
+// Chunk scores of every (sequence, KV head) when a history exceeds the LDS,
+// or (small batches) the split route's q-bar and candidates.
+size_t decode_route_workspace_bytes(const hga_shape& s, int batch) { return decode_route_ws(s, batch).bytes; }
 
 hipError_t launch_decode_route(const hga_shape& s, int batch, int n_new, const void* q,
                                const float* chunk_sum, const float* group_sum, const int32_t* hist_lens,

@@ -119,6 +119,43 @@ def test_decode_lengths_are_clamped_to_the_buffers():
     assert torch.equal(o, a[0]) and torch.equal(lse, a[1]) and torch.equal(sg, a[3])
 
 
+# Small batches split the chunk scan of each (sequence, KV head) over several
+# workgroups (history capacity of 32,768+ tokens and fewer than 256
+# (sequence, KV head) pairs): ragged histories from full to empty, some with
+# fewer chunks than parts, against the oracle.
+@pytest.mark.parametrize("n_new,sink,window", [(1, 0, 0), (2, 1, 40)])
+def test_decode_split_route_ragged(n_new, sink, window):
+    run_decode(8, 2, 128, 32768, 256, 16, 32, "bf16", [32768, 20032, 192, 0], [256, 100, 7, 40],
+               n_new=n_new, seed=10 + n_new, sink=sink, window=window)
+
+
+def test_decode_split_route_matches_unsplit():
+    # the same four sequences alone (32 (sequence, KV head) pairs: split
+    # route) and tiled to a batch of 32 (256 pairs: one workgroup each) give
+    # bit-identical selections and outputs
+    n_q, n_kv, d, P, T = 32, 8, 128, 32768, 256
+    hist, tail = [32768, 26624, 4096, 64], [256, 33, 128, 1]
+    w = synth.Workload("decode", n_q, n_kv, d, P, T, 16, 32, "bf16", 1.0 / math.sqrt(d))
+    print(f"[case] decode split vs unsplit P={P} hist={hist}", flush=True)
+    inp = synth.make_decode_inputs(w, hist, tail, 1, 21)
+    g = {k: v.cuda() for k, v in inp.items()}
+    s = hga.make_shape(n_q, n_kv, d, P, T, 16, 32, torch.bfloat16, w.softmax_scale)
+    C = torch.zeros((4, n_kv, P // 64, d), dtype=torch.float32, device="cuda")
+    G = torch.zeros((4, n_kv, P // 8, d), dtype=torch.float32, device="cuda")
+    for b in range(4):
+        sb = hga.make_shape(n_q, n_kv, d, hist[b], T, 16, 32, torch.bfloat16, hist_stride=P)
+        hga.hga_build_summaries(sb, g["k_hist"][b], C[b], G[b])
+    o4, lse4, sc4, sg4 = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
+                                    g["hist_lens"], g["tail_lens"])
+    rep = lambda x: x.repeat((8,) + (1,) * (x.dim() - 1))
+    o32, lse32, sc32, sg32 = hga.decode(s, rep(g["q"]), rep(g["k_hist"]), rep(g["v_hist"]), rep(C), rep(G),
+                                        rep(g["k_tail"]), rep(g["v_tail"]), rep(g["hist_lens"]),
+                                        rep(g["tail_lens"]))
+    torch.cuda.synchronize()
+    assert torch.equal(sc32[:4], sc4) and torch.equal(sg32[:4], sg4)
+    assert torch.equal(o32[:4], o4) and torch.equal(lse32[:4], lse4)
+
+
 def test_decode_qwen3_8b_131k():
     # Qwen3-8B layer shapes, 129,024-token history capacity, 2,048-token open
     # segment, one new token per sequence, ragged lengths
