@@ -21,7 +21,7 @@ namespace hga {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecKeys = 256;  // keys per piece (one workgroup)
+constexpr int kDecKeys = 256;  // keys per piece (one workgroup); bf16 small batches: 128
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct DecodeParams {
@@ -41,6 +41,7 @@ struct DecodeParams {
   int64_t P;           // history rows per (sequence, KV head)
   int T;               // open-segment rows per (sequence, KV head)
   int k_g, n_sink, window, n_piece;
+  int piece_keys;      // keys per piece (kDecKeys, or 128 for small bf16 batches)
   float scale_log2;
 };
 
@@ -254,18 +255,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
 
 // QR: query rows provisioned in LDS and registers (R = r * n_new <= QR); a
 // smaller QR for the common R <= 4 or 8 frees LDS and registers for more
-// resident workgroups, which hide the row loads.
-template <int D, int QR>
+// resident workgroups, which hide the row loads. KEYS: keys per piece (128
+// for small batches, so that more workgroups share the rows to load).
+template <int D, int QR, int KEYS>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodeParams p) {
   static_assert(QR <= 32, "query rows are the 32 columns of the score MFMA");
+  static_assert(KEYS % (kDecThreads / kWave * 32) == 0, "whole 32-key tiles per wave");
   constexpr int NKS = D / 16;                   // MFMA k-steps over head_dim
   constexpr int NW = kDecThreads / kWave;
   constexpr int KT = 32;                        // keys per MFMA tile
-  constexpr int TPW = kDecKeys / (NW * KT);     // tiles per wave
+  constexpr int TPW = KEYS / (NW * KT);     // tiles per wave
   constexpr int DPL = D / kWave;                // output dims per lane in P.V
   // rows padded by 4 floats: the 32 query rows' 16-byte score stores spread over the banks
-  __shared__ __attribute__((aligned(16))) float s_lds[QR][kDecKeys + 4];
-  __shared__ int32_t kinfo[kDecKeys];           // -1 plain, -2 masked, >= 0 open-segment position
+  __shared__ __attribute__((aligned(16))) float s_lds[QR][KEYS + 4];
+  __shared__ int32_t kinfo[KEYS];           // -1 plain, -2 masked, >= 0 open-segment position
   __shared__ float o_lds[NW][QR][D];
   const int piece = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t % kWave;
@@ -273,9 +276,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   const int l32 = lane % 32, hh = lane / 32;
 
   const SeqKeys sk = seq_keys(p, b);
-  const int k0 = piece * kDecKeys;
+  const int k0 = piece * KEYS;
   if (k0 >= sk.n_keys) return;
-  const int nk = min(kDecKeys, sk.n_keys - k0);
+  const int nk = min(KEYS, sk.n_keys - k0);
   const int R = p.r * p.n_new;
   const int n_routed = p.k_g * kGroup;
   const int64_t hrow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.P;
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   for (int rq = wave; rq < R; rq += NW) {
     const int qpos = sk.tb - p.n_new + rq % p.n_new;
     float m = -INFINITY;
-    for (int kk = lane; kk < kDecKeys; kk += kWave) {
+    for (int kk = lane; kk < KEYS; kk += kWave) {
       const int inf = kinfo[kk];
       const bool ok = inf == -1 || (inf >= 0 && inf <= qpos && inf > qpos - p.window);
       const float sc = ok ? s_lds[rq][kk] : -INFINITY;
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
     float l = 0.f;
-    for (int kk = lane; kk < kDecKeys; kk += kWave) {
+    for (int kk = lane; kk < KEYS; kk += kWave) {
       const float e = m == -INFINITY ? 0.f : exp2f(s_lds[rq][kk] - m);
       s_lds[rq][kk] = e;
       l += e;
@@ -387,8 +390,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[rq][e] = 0.f;
   constexpr int KPI = 16;                       // keys per pass: their row loads in flight together
-  const int kq0 = wave * (kDecKeys / NW);
-  for (int kk = kq0; kk < kq0 + kDecKeys / NW && kk < nk; kk += KPI) {
+  const int kq0 = wave * (KEYS / NW);
+  for (int kk = kq0; kk < kq0 + KEYS / NW && kk < nk; kk += KPI) {
     float vf[KPI][DPL];
 #pragma unroll
     for (int u = 0; u < KPI; ++u) {
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const int64_t row = blockIdx.x;                // (b * n_q + h) * n_new + i
   const int b = static_cast<int>(row / (static_cast<int64_t>(p.n_q) * p.n_new));
   const SeqKeys sk = seq_keys(p, b);
-  const int n = (sk.n_keys + kDecKeys - 1) / kDecKeys;
+  const int n = (sk.n_keys + p.piece_keys - 1) / p.piece_keys;
   const float* ml = p.part_ml + row * p.n_piece * 2;
   float m = -INFINITY;
   for (int s = 0; s < n; ++s) m = fmaxf(m, ml[2 * s]);
@@ -461,12 +464,21 @@ hipError_t launch_td(const hga_shape& s, DecodeParams& p, int batch, hipStream_t
   const int R = p.r * p.n_new;
   hipEvent_t e0 = timer_event(HGA_KERNEL_DECODE, 0), e1 = timer_event(HGA_KERNEL_DECODE, 1);
   if constexpr (sizeof(T) == 2) {
-    if (R <= 4)
-      hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 4>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
-    else if (R <= 8)
-      hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
-    else
-      hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 16>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+    if (p.piece_keys == 128) {
+      if (R <= 4)
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 4, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+      else if (R <= 8)
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+      else
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 16, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+    } else {
+      if (R <= 4)
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 4, kDecKeys>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+      else if (R <= 8)
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8, kDecKeys>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+      else
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 16, kDecKeys>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+    }
   } else if (R <= 4)
     hipExtLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
   else if (R <= 8)
@@ -480,16 +492,31 @@ hipError_t launch_td(const hga_shape& s, DecodeParams& p, int batch, hipStream_t
 
 }  // namespace
 
-int decode_pieces(const hga_shape& s) {
+namespace {
+// Keys attended per (sequence, KV head) at most: sink, routed groups, open segment.
+int64_t decode_max_keys(const hga_shape& s) {
   const int64_t P = hist_rows(s);
   const int64_t sink = static_cast<int64_t>(s.n_sink_chunks) * kChunk < P ? s.n_sink_chunks * kChunk : P;
-  const int64_t keys = sink + static_cast<int64_t>(s.top_k_groups) * kGroup + s.seg_len;
-  return static_cast<int>((keys + kDecKeys - 1) / kDecKeys);
+  return sink + static_cast<int64_t>(s.top_k_groups) * kGroup + s.seg_len;
+}
+}  // namespace
+
+// Keys per piece: kDecKeys, or 128 for bf16 when 256-key pieces would give
+// the attention launch fewer than 512 workgroups.
+int decode_piece_keys(const hga_shape& s, int batch) {
+  if (s.dtype != HGA_BF16) return kDecKeys;
+  const int64_t wgs = static_cast<int64_t>(batch) * s.n_kv_heads * ((decode_max_keys(s) + kDecKeys - 1) / kDecKeys);
+  return wgs < 512 ? 128 : kDecKeys;
+}
+
+int decode_pieces(const hga_shape& s, int batch) {
+  const int pk = decode_piece_keys(s, batch);
+  return static_cast<int>((decode_max_keys(s) + pk - 1) / pk);
 }
 
 size_t decode_attn_workspace_bytes(const hga_shape& s, int batch, int n_new) {
   const size_t rows = static_cast<size_t>(batch) * s.n_q_heads * n_new;
-  const size_t n = decode_pieces(s);
+  const size_t n = decode_pieces(s, batch);
   return ((rows * n * s.head_dim * sizeof(float) + 255) & ~size_t(255)) + rows * n * 2 * sizeof(float);
 }
 
@@ -502,7 +529,7 @@ hipError_t launch_decode_attn(const hga_shape& s, int batch, int n_new, const vo
   p.sel = sel_groups; p.hist_lens = hist_lens; p.tail_lens = tail_lens; p.o = o; p.lse = lse;
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads; p.n_new = n_new;
   p.P = hist_rows(s); p.T = s.seg_len; p.k_g = s.top_k_groups; p.n_sink = s.n_sink_chunks;
-  p.window = local_window(s); p.n_piece = decode_pieces(s);
+  p.window = local_window(s); p.n_piece = decode_pieces(s, batch); p.piece_keys = decode_piece_keys(s, batch);
   p.scale_log2 = s.softmax_scale * 1.4426950408889634f;
   const size_t rows = static_cast<size_t>(batch) * s.n_q_heads * n_new;
   p.part = static_cast<float*>(ws);

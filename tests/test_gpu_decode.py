@@ -132,7 +132,8 @@ def test_decode_split_route_ragged(n_new, sink, window):
 def test_decode_split_route_matches_unsplit():
     # the same four sequences alone (32 (sequence, KV head) pairs: split
     # route) and tiled to a batch of 32 (256 pairs: one workgroup each) give
-    # bit-identical selections and outputs
+    # bit-identical selections; the attention splits the keys into pieces of
+    # 128 (small batch) or 256, so its outputs agree to rounding
     n_q, n_kv, d, P, T = 32, 8, 128, 32768, 256
     hist, tail = [32768, 26624, 4096, 64], [256, 33, 128, 1]
     w = synth.Workload("decode", n_q, n_kv, d, P, T, 16, 32, "bf16", 1.0 / math.sqrt(d))
@@ -153,7 +154,9 @@ def test_decode_split_route_matches_unsplit():
                                         rep(g["tail_lens"]))
     torch.cuda.synchronize()
     assert torch.equal(sc32[:4], sc4) and torch.equal(sg32[:4], sg4)
-    assert torch.equal(o32[:4], o4) and torch.equal(lse32[:4], lse4)
+    o_ref = o4.float()
+    assert (o32[:4].float() - o_ref).abs().max() <= 1e-2 * o_ref.abs().max()
+    assert (lse32[:4] - lse4).abs().max() <= 1e-5 * lse4.abs().max()
 
 
 def test_decode_qwen3_8b_131k():
