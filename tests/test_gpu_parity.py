@@ -285,17 +285,24 @@ def test_qwen3_8b_131k_forward_and_pinned_host_tier():
     assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
 
 
-def test_pinned_host_tier_with_sink_is_bit_identical():
+HOST_TIER = [
     # sink rows are staged from host memory once per call; routed groups are
     # gathered per phase (6 query blocks: two phases, the second partial)
-    w = _w("bf16_host_sink2_w96", 8, 2, 128, 1536, 384, 5, 13, "bf16", bwd=False, sink=2, window=96)
+    _w("bf16_host_sink2_w96", 8, 2, 128, 1536, 384, 5, 13, "bf16", bwd=False, sink=2, window=96),
+    _w("bf16_host_d64", 8, 2, 64, 1024, 320, 4, 16, "bf16", bwd=False),   # d = 64, 5 blocks
+    _w("f32_host_d64", 4, 2, 64, 512, 256, 3, 10, "f32", bwd=False),      # fp32 rows over the link
+]
+
+
+@pytest.mark.parametrize("w", HOST_TIER, ids=[w.name for w in HOST_TIER])
+def test_pinned_host_tier_is_bit_identical(w):
     r = run_case(w, 4, check_bwd=False)
     sh = _shape(w.replace(hist_on_host=True))
-    kh = torch.empty(r["inp"]["k_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
-    vh = torch.empty(r["inp"]["v_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
+    kh = torch.empty(r["inp"]["k_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
+    vh = torch.empty(r["inp"]["v_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
     kh.copy_(r["inp"]["k_hist"])
     vh.copy_(r["inp"]["v_hist"])
-    _say("[case] pinned-host history with sink 2, window 96")
+    _say(f"[case] {w.name}: the same call with history in pinned host memory")
     g = r["g"]
     o2, lse2 = hga.attn_fwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"])
     torch.cuda.synchronize()
