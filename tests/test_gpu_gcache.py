@@ -68,14 +68,15 @@ def _check_tables(cache, model, G_host, n_chunk_rows):
             assert torch.equal(data[j, p], G_host[j, 8 * c:8 * c + 8]), f"slot {p} rows, chunk {c}"
 
 
-def _inputs(n_q, n_kv, d, H, S, seed):
-    w = synth.Workload("gcache", n_q, n_kv, d, H, S, 1, 1, "bf16", 1.0 / math.sqrt(d))
+def _inputs(n_q, n_kv, d, H, S, seed, dtype="bf16"):
+    w = synth.Workload("gcache", n_q, n_kv, d, H, S, 1, 1, dtype, 1.0 / math.sqrt(d))
     return synth.make_inputs(w, seed)
 
 
-def _run_sequence(n_q, n_kv, d, H, S, k_c, k_g, n_slots, seeds, sink=0, check_oracle=True):
-    base = _inputs(n_q, n_kv, d, H, S, seeds[0])
-    s = hga.make_shape(n_q, n_kv, d, H, S, k_c, k_g, torch.bfloat16, n_sink_chunks=sink)
+def _run_sequence(n_q, n_kv, d, H, S, k_c, k_g, n_slots, seeds, sink=0, check_oracle=True, dtype="bf16"):
+    base = _inputs(n_q, n_kv, d, H, S, seeds[0], dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s = hga.make_shape(n_q, n_kv, d, H, S, k_c, k_g, tdt, n_sink_chunks=sink)
     k_hist = base["k_hist"].cuda()
     C, G_dev = hga.summaries(s, k_hist)
     G_host = torch.empty(G_dev.shape, dtype=torch.float32, pin_memory=True)
@@ -91,7 +92,7 @@ def _run_sequence(n_q, n_kv, d, H, S, k_c, k_g, n_slots, seeds, sink=0, check_or
     for i, seed in enumerate(seeds):
         print(f"[case] gcache H={H} S={S} kc={k_c} slots={n_slots} sink={sink} call {i} seed {seed}",
               flush=True)
-        q = _inputs(n_q, n_kv, d, H, S, seed)["q"].cuda()
+        q = _inputs(n_q, n_kv, d, H, S, seed, dtype)["q"].cuda()
         sc = torch.empty((n_B, n_kv, k_c), dtype=torch.int32, device="cuda")
         sg = torch.empty((n_B, n_kv, k_g), dtype=torch.int32, device="cuda")
         cache.route(s, q, C, G_host, sc, sg, stats)
@@ -130,6 +131,11 @@ def test_cache_larger_than_a_call_keeps_earlier_chunks():
 
 def test_cache_with_sink_ranks_after_it():
     _run_sequence(8, 2, 128, 4096, 320, 5, 13, 25, seeds=[8, 9], sink=2)
+
+
+def test_cache_with_fp32_inputs():
+    # fp32 queries and keys (the fp32 instances of the route kernel)
+    _run_sequence(4, 2, 64, 4096, 256, 4, 12, 32, seeds=[11, 12, 11], dtype="f32")
 
 
 def test_cache_at_131k_full_size():
