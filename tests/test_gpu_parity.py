@@ -120,6 +120,7 @@ SMALL = [
     _w("bf16_max_budget", 4, 1, 128, 8192, 128, 64, 512, "bf16"),     # largest k_c, k_g: 64 history tiles
     _w("bf16_r8_d128", 16, 2, 128, 1024, 192, 4, 16, "bf16"),         # GQA 8: four head-group dK/dV partials
     _w("bf16_r6_d64", 12, 2, 64, 512, 128, 3, 12, "bf16"),            # GQA 6, d = 64: three groups of two heads
+    _w("bf16_budget_1_1", 4, 2, 128, 1024, 192, 1, 1, "bf16"),        # one chunk, one group: a 7/8-empty tile
 ]
 
 
