@@ -72,7 +72,8 @@ def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new,
         for name, got, ref in (("O", _f64(o[b]), O_ref), ("LSE", _f64(lse[b]), L_ref)):
             err, rel = orc.error_stats(got, ref)
             print(f"  seq {b} {name}: max|d|={err:.3e} rel_l2={rel:.3e}", flush=True)
-            assert orc.within_tolerance(got, ref, tol), (b, name, err, rel)
+            ok = orc.lse_within(got, ref) if name == "LSE" else orc.within_tolerance(got, ref, tol)
+            assert ok, (b, name, err, rel)
     return o, lse, sc, sg
 
 
@@ -198,4 +199,4 @@ def test_decode_retrieves_a_planted_needle():
                                          _f64(inp["k_tail"][0]), _f64(inp["v_tail"][0]), 4, 16,
                                          w.softmax_scale, sel_groups=sg[0].cpu().numpy())
     assert orc.within_tolerance(_f64(o[0]), O_ref, TOL["bf16"])
-    assert orc.within_tolerance(_f64(lse[0]), L_ref, TOL["bf16"])
+    assert orc.lse_within(_f64(lse[0]), L_ref)

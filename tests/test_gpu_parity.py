@@ -1,9 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs. Index parity: exact, except near-ties (oracle score gap
 < 1e-5), judged by the oracle's checker. Output parity: max|got-ref| <=
-tol * max(1, max|ref|) and ||got-ref||_2 <= tol * ||ref||_2 with tol = 2e-2
-(bf16) / 1e-4 (fp32), computed with the oracle's attention fed the GPU's own
-selections."""
+tol * max(1, max|ref|), and ||got-ref||_2 <= tol * ||ref||_2 over the whole
+tensor and over every (head, 64-row block) slice, with tol = 2e-2 (bf16) /
+1e-4 (fp32); LSE element by element within 1e-4 * max(1, |ref|) in every
+dtype. The oracle's attention is fed the GPU's own selections."""
 import math
 import sys
 
@@ -47,9 +48,16 @@ def _dev(inp):
 
 
 def _assert_close(name, got, ref, tol):
+    """LSE: the fp32 bar element by element; everything else: max-abs, whole
+    tensor and per-(head, 64-row block) relative L2 at the dtype's bar."""
     err, rel = orc.error_stats(got, ref)
-    _say(f"  {name}: max|d|={err:.3e} rel_l2={rel:.3e} (tol {tol:g}) max|ref|={np.abs(ref).max():.3e}")
-    assert orc.within_tolerance(got, ref, tol), f"{name}: max {err}, rel {rel} vs {tol}"
+    worst = float(orc.slice_rel_l2(got, ref).max()) if np.size(ref) else 0.0
+    _say(f"  {name}: max|d|={err:.3e} rel_l2={rel:.3e} worst_slice={worst:.3e} (tol {tol:g}) "
+         f"max|ref|={np.abs(ref).max():.3e}")
+    if name == "LSE":
+        assert orc.lse_within(got, ref), f"LSE: max {err} vs fp32 bar {orc.LSE_TOL}"
+    else:
+        assert orc.within_tolerance(got, ref, tol), f"{name}: max {err}, rel {rel}, slice {worst} vs {tol}"
 
 
 def run_case(w: synth.Workload, seed: int, check_bwd: bool):

@@ -623,3 +623,124 @@ def test_decode_without_history_attends_the_open_segment():
         s = kt[0] @ q[h, 0]
         p = np.exp(s - s.max())
         assert np.allclose(O[h, 0], p @ vt[0] / p.sum(), rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# localized errors: the per-slice part of the criterion and the LSE bar
+# ---------------------------------------------------------------------------
+def test_one_wrong_slice_fails_among_a_thousand():
+    """32 heads x 32 query blocks, as at the Qwen3-8B layer: one (head, block)
+    slice 50% off moves the whole-tensor relative L2 by only ~1.6%, under the
+    2e-2 bar, so only the per-slice part catches it; so do 8 zeroed rows of
+    one slice and a single row with its sign flipped."""
+    rng = np.random.default_rng(21)
+    ref = 0.01 * rng.standard_normal((32, 2048, 16))
+    tol = 2e-2
+    assert orc.within_tolerance(torch.from_numpy(ref).bfloat16().double().numpy(), ref, tol)
+    bad = ref.copy()
+    bad[3, 5 * 64:6 * 64] *= 1.5
+    assert orc.error_stats(bad, ref)[1] < tol          # the whole-tensor part alone passes
+    assert not orc.within_tolerance(bad, ref, tol)
+    rows = ref.copy()
+    rows[17, 64 * 30 + 3:64 * 30 + 11] = 0.0
+    assert orc.error_stats(rows, ref)[1] < tol
+    assert not orc.within_tolerance(rows, ref, tol)
+    flip = ref.copy()
+    flip[0, 2047] *= -1.0
+    assert not orc.within_tolerance(flip, ref, tol)
+    sl = orc.slice_rel_l2(bad, ref)
+    assert sl.shape == (32, 32) and sl[3, 5] == pytest.approx(0.5) and np.delete(sl.ravel(), 3 * 32 + 5).max() == 0
+
+
+def test_slices_follow_the_head_and_block_axes():
+    # LSE-like [n][T] arrays and ragged T: the last slice is the partial run
+    ref = np.ones((2, 130))
+    got = ref.copy()
+    got[1, 128:] = 2.0
+    sl = orc.slice_rel_l2(got, ref)
+    assert sl.shape == (2, 3)
+    assert sl[1, 2] == pytest.approx(1.0) and sl[:, :2].max() == 0 and sl[0].max() == 0
+
+
+def test_lse_is_held_to_the_fp32_bar():
+    rng = np.random.default_rng(22)
+    ref = 7.0 + rng.standard_normal((8, 256))
+    assert orc.lse_within(ref.astype(np.float32).astype(np.float64), ref)
+    off = ref.copy()
+    off[2, 100] += 2e-3                                   # 2.5e-4 relative at |LSE| ~ 8
+    assert not orc.lse_within(off, ref)
+    # bf16 rounding of an LSE of ~7 moves it by up to 0.016: far outside the bar
+    assert not orc.lse_within(torch.from_numpy(ref).bfloat16().double().numpy(), ref)
+    small = np.full((1, 4), 0.25)
+    assert orc.lse_within(small + 0.9e-4, small) and not orc.lse_within(small + 1.1e-4, small)
+
+
+# ---------------------------------------------------------------------------
+# routing with several KV heads: brute force and per-head plants
+# ---------------------------------------------------------------------------
+def _bruteforce_route(q, k, n_kv, k_c, k_g):
+    """Route written out with Python loops over explicit head lists, float64
+    arithmetic and full sorts: query head h belongs to KV head h // r; the
+    block query of (b, j) averages rows 64b..64b+63 of heads jr..jr+r-1; chunk
+    m averages keys 64m..64m+63 of KV head j; ranking is higher score, then
+    lower index."""
+    n_q, S, d = q.shape
+    H = k.shape[1]
+    r = n_q // n_kv
+    n_B, n_C = S // 64, H // 64
+    sel_c = np.full((n_B, n_kv, k_c), -1, np.int64)
+    sel_g = np.full((n_B, n_kv, k_g), -1, np.int64)
+    for b in range(n_B):
+        for j in range(n_kv):
+            heads = [h for h in range(n_q) if h // r == j]
+            qb = [sum(float(q[h, i, e]) for h in heads for i in range(64 * b, 64 * b + 64)) / (64 * len(heads))
+                  for e in range(d)]
+            def score(lo, n):
+                return sum(qb[e] * sum(float(k[j, t, e]) for t in range(lo, lo + n)) / n for e in range(d))
+            ranked = sorted(range(n_C), key=lambda m: (-score(64 * m, 64), m))[:k_c]
+            chunks = sorted(ranked)
+            sel_c[b, j, :len(chunks)] = chunks
+            cand = [8 * m + u for m in chunks for u in range(8)]
+            top = sorted(sorted(cand, key=lambda n: (-score(8 * n, 8), n))[:k_g])
+            sel_g[b, j, :len(top)] = top
+    return sel_c, sel_g
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(6, 3), (4, 2), (8, 2)])
+def test_route_several_kv_heads_matches_bruteforce(n_q, n_kv):
+    """Small-integer inputs keep every sum exact in float32 and float64 alike,
+    so the oracle's selections must equal the brute force's for every
+    (block, KV head), ties (frequent with so few values) included."""
+    rng = np.random.default_rng(n_q * 10 + n_kv)
+    d, H, S = 4, 512, 128
+    q = rng.integers(0, 3, (n_q, S, d)).astype(np.float64)
+    k = rng.integers(-1, 3, (n_kv, H, d)).astype(np.float64)
+    k[:, 64 * 2:64 * 3] = 1.0                 # whole-chunk ties across heads
+    k[:, 64 * 5:64 * 6] = 1.0
+    got_c, got_g, _ = orc.route(q, k, n_kv, 3, 5)
+    want_c, want_g = _bruteforce_route(q, k, n_kv, 3, 5)
+    assert np.array_equal(got_c, want_c)
+    assert np.array_equal(got_g, want_g)
+
+
+def test_route_planted_chunk_differs_per_kv_head():
+    """KV head j gets its own planted chunk m_j and group g_j along its own
+    query direction u_j; every block of head j must route to exactly them
+    (top-1 chunk, top-1 group) and never to another head's plant."""
+    n_q, n_kv, d, H, S = 6, 3, 16, 1024, 192
+    rng = np.random.default_rng(23)
+    q = 0.1 * rng.standard_normal((n_q, S, d))
+    k = 0.1 * rng.standard_normal((n_kv, H, d))
+    u = np.linalg.qr(rng.standard_normal((d, n_kv)))[0].T          # orthonormal directions
+    plant_c, plant_g = [3, 11, 7], [3 * 8 + 5, 11 * 8 + 0, 7 * 8 + 7]
+    for h in range(n_q):
+        q[h] += 2.0 * u[h // (n_q // n_kv)]
+    for j in range(n_kv):
+        k[j, 64 * plant_c[j]:64 * plant_c[j] + 64] += 3.0 * u[j]
+        k[j, 8 * plant_g[j]:8 * plant_g[j] + 8] += 3.0 * u[j]
+    sel_c, sel_g, aux = orc.route(q, k, n_kv, 1, 1)
+    for b in range(S // 64):
+        for j in range(n_kv):
+            assert sel_c[b, j].tolist() == [plant_c[j]]
+            assert sel_g[b, j].tolist() == [plant_g[j]]
+            assert int(np.argmax(aux["chunk_scores"][b, j])) == plant_c[j]
