@@ -44,10 +44,11 @@
  *
  * Ownership: the caller allocates every buffer and the workspace; the library
  * allocates no device memory and keeps no state between calls except, for the
- * pinned-host history tier, one side stream and two events per device, created
- * on first use. Every pointer is a device pointer except k_hist / v_hist under
- * HGA_HIST_HOST_PINNED, which must come from hipHostMalloc (page-locked,
- * mapped) memory.
+ * pinned-host history tier, one side stream and five events per device,
+ * created on first use; host-tier calls on one device from several threads
+ * take turns while they enqueue (they share that side stream). Every pointer
+ * is a device pointer except k_hist / v_hist under HGA_HIST_HOST_PINNED, which
+ * must come from hipHostMalloc (page-locked, mapped) memory.
  *
  * Streams: `stream` is a hipStream_t (NULL = the null stream). All work is
  * enqueued asynchronously on it; calls return before the GPU finishes.
@@ -226,8 +227,9 @@ hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, cons
  * W = whole segment by default, causal):
  *   o[h][i] = sum_t softmax_t(scale * q[h][i] . k_t) v_t
  *   lse[h][i] = log sum_t exp(scale * q[h][i] . k_t)
- * sel_groups entries must be -1 or in [0, hist_len/8); the library does not
- * re-check them on the device. ws: hga_workspace_size(shape, HGA_OP_ATTN_FWD)
+ * sel_groups entries are group ids in [0, hist_len/8) or -1 (empty slot); the
+ * kernels treat any other value as -1, so no entry can make them read outside
+ * the history. ws: hga_workspace_size(shape, HGA_OP_ATTN_FWD)
  * bytes (zero for device-resident history; staging for the pinned-host tier,
  * whose gathers run on an internal side stream fenced back to `stream`). */
 hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_hist,
@@ -241,7 +243,8 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
  * dv_seg for the active segment; history K/V, summaries and selections get no
  * gradient. o and lse are the forward's outputs. Deterministic: no atomics.
  * ws: hga_workspace_size(shape, HGA_OP_ATTN_BWD) bytes. k_hist / v_hist must
- * be in device memory (HGA_HIST_DEVICE). */
+ * be in device memory (HGA_HIST_DEVICE). sel_groups as for hga_attn_fwd: ids
+ * outside [0, hist_len/8) count as -1. */
 hga_status hga_attn_bwd(const hga_shape* shape, const void* q, const void* k_hist,
                         const void* v_hist, const void* k_seg, const void* v_seg,
                         const int32_t* sel_groups, const void* o, const float* lse,
@@ -252,7 +255,8 @@ hga_status hga_attn_bwd(const hga_shape* shape, const void* q, const void* k_his
  * §2.2 "Tiered Memory Hierarchy": only the selected groups' exact K/V are
  * brought into the working set). Copies the 8 tokens of every selected group
  * into k_out / v_out [seg_len/64][n_kv_heads][top_k_groups*8][head_dim]
- * (dtype), zero-filling the rows of -1 entries. k_hist / v_hist live where
+ * (dtype), zero-filling the rows of -1 entries and of ids outside
+ * [0, hist_len/8). k_hist / v_hist live where
  * shape->hist_loc says (device or pinned host); outputs are device memory. */
 hga_status hga_gather_groups(const hga_shape* shape, const void* k_hist,
                              const void* v_hist, const int32_t* sel_groups,

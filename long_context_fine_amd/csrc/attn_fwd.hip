@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
     if (half == 1 && b_lo >= b_hi) break;  // odd count: the middle block runs once
     const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
     __syncthreads();
-    for (int i = tid; i < p.k_g; i += NT) sel_s[i] = sel_bj[i];
+    for (int i = tid; i < p.k_g; i += NT) sel_s[i] = valid_group(sel_bj[i], p.hist_len / kGroup);
     __syncthreads();
     build_hist_tile_list(sel_s, p.k_g, hlist, &n_hist_s);
     __syncthreads();
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
   const float* ks_g = static_cast<const float*>(p.k_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const float* vs_g = static_cast<const float*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
-  for (int i = a; i < p.k_g; i += kWave) sel_s[i] = sel_bj[i];
+  for (int i = a; i < p.k_g; i += kWave) sel_s[i] = valid_group(sel_bj[i], p.hist_len / kGroup);
 
   float qr[D], acc[D];
   for (int e = 0; e < D; ++e) {

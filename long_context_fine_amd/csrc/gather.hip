@@ -5,7 +5,8 @@
 // address space (the pinned-host history tier); in the latter case every load
 // crosses the host link, so each workgroup keeps 8 independent 16-byte loads
 // per thread in flight before storing. One workgroup moves 8 groups (64 rows)
-// of K and of V; empty slots (-1 or beyond k_g) are zero-filled.
+// of K and of V; empty slots (-1, an id outside the history, or beyond k_g)
+// are zero-filled.
 #include "hga_common.hpp"
 
 namespace hga {
@@ -17,7 +18,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint8_t* __restrict__ k_hist, const uint8_t* __restrict__ v_hist,
     const int32_t* __restrict__ sel, uint8_t* __restrict__ k_out, uint8_t* __restrict__ v_out,
-    int elem_bytes, int64_t hist_rows, int n_kv, int k_g, int block_begin) {
+    int elem_bytes, int64_t hist_rows, int64_t n_groups, int n_kv, int k_g, int block_begin) {
   const int row_bytes = D * elem_bytes;
   const int cpr = row_bytes / 16;            // 16-byte chunks per row
   const int rows_per_pass = kThreads / cpr;  // 16 or 8 (bf16) / 8 or 4 (fp32)
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
       dst[u] = -1;
       if (row < 64 && slot < k_g) {
         dst[u] = (out_base + static_cast<int64_t>(slot) * kGroup + row % kGroup) * row_bytes + c * 16;
-        const int n = sel_bj[slot];
+        const int n = valid_group(sel_bj[slot], n_groups);
         if (n >= 0) {
           const int64_t src = (static_cast<int64_t>(j) * hist_rows + static_cast<int64_t>(n) * kGroup +
                                row % kGroup) * row_bytes + c * 16;
@@ -78,12 +79,12 @@ hipError_t launch_gather(const hga_shape& s, const void* k_hist, const void* v_h
     hipExtLaunchKernelGGL((gather_kernel<128>), grid, dim3(kThreads), 0, stream, ev_start, ev_stop, 0,
                        static_cast<const uint8_t*>(k_hist), static_cast<const uint8_t*>(v_hist),
                        sel_groups, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), elem,
-                       hist_rows(s), s.n_kv_heads, s.top_k_groups, block_begin);
+                       hist_rows(s), s.hist_len / kGroup, s.n_kv_heads, s.top_k_groups, block_begin);
   else
     hipExtLaunchKernelGGL((gather_kernel<64>), grid, dim3(kThreads), 0, stream, ev_start, ev_stop, 0,
                        static_cast<const uint8_t*>(k_hist), static_cast<const uint8_t*>(v_hist),
                        sel_groups, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), elem,
-                       hist_rows(s), s.n_kv_heads, s.top_k_groups, block_begin);
+                       hist_rows(s), s.hist_len / kGroup, s.n_kv_heads, s.top_k_groups, block_begin);
   return hipGetLastError();
 }
 

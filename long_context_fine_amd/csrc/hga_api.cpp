@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -134,7 +135,12 @@ size_t fwd_workspace_bytes(const hga_shape& s) {
   return 4 * align256(staging_bytes_per_buffer(s)) + 2 * align256(sink_bytes(s));
 }
 
+// The pinned-host tier's side stream and events, one set per device. A call
+// holds `mu` for its whole enqueue sequence: calls from several threads on one
+// device then record and wait on these events in turn, so every wait sees the
+// record its own call made (the side stream is shared either way).
 struct SideResources {
+  std::mutex mu;
   hipStream_t side = nullptr;
   hipEvent_t start = nullptr;
   hipEvent_t gathered[2] = {nullptr, nullptr};
@@ -142,7 +148,7 @@ struct SideResources {
 };
 
 std::mutex g_side_mu;
-std::unordered_map<int, SideResources> g_side;
+std::unordered_map<int, std::unique_ptr<SideResources>> g_side;
 
 hga_status side_resources(SideResources** out) {
   int dev = 0;
@@ -151,16 +157,16 @@ hga_status side_resources(SideResources** out) {
   std::lock_guard<std::mutex> lock(g_side_mu);
   auto it = g_side.find(dev);
   if (it == g_side.end()) {
-    SideResources r;
-    if ((e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking)) != hipSuccess)
+    std::unique_ptr<SideResources> r(new SideResources);
+    if ((e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking)) != hipSuccess)
       return hip_fail(e, "hipStreamCreateWithFlags");
-    hipEvent_t* evs[5] = {&r.start, &r.gathered[0], &r.gathered[1], &r.consumed[0], &r.consumed[1]};
+    hipEvent_t* evs[5] = {&r->start, &r->gathered[0], &r->gathered[1], &r->consumed[0], &r->consumed[1]};
     for (hipEvent_t* ev : evs)
       if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "hipEventCreateWithFlags");
-    it = g_side.emplace(dev, r).first;
+    it = g_side.emplace(dev, std::move(r)).first;
   }
-  *out = &it->second;
+  *out = it->second.get();
   return HGA_OK;
 }
 
@@ -434,6 +440,7 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   HGA_TRY(host_to_device_ptr(v_hist, &vd, "v_hist"));
   SideResources* r = nullptr;
   HGA_TRY(side_resources(&r));
+  std::lock_guard<std::mutex> call_lock(r->mu);
   const size_t buf = align256(staging_bytes_per_buffer(s));
   char* base = static_cast<char*>(ws);
   void* kbuf[2] = {base, base + buf};

@@ -102,6 +102,13 @@ __device__ __forceinline__ float sum16_f32(float x) {
   return x;
 }
 
+// A selected group id as the attention and gather kernels use it: ids outside
+// the history's groups [0, n_groups) count as empty slots, exactly like -1, so
+// a bad selection can never address memory outside the history.
+__device__ __forceinline__ int32_t valid_group(int32_t n, int64_t n_groups) {
+  return n >= 0 && n < n_groups ? n : -1;
+}
+
 // Rows per KV head in k_hist / v_hist (and x64 / x8 in the chunk / group
 // summaries): hist_stride when set, else hist_len.
 inline int64_t hist_rows(const hga_shape& s) { return s.hist_stride ? s.hist_stride : s.hist_len; }

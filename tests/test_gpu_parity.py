@@ -335,3 +335,98 @@ def test_autograd_function_matches_explicit_calls():
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), o_ref)
     assert torch.equal(q.grad, dq) and torch.equal(ks.grad, dk) and torch.equal(vs.grad, dv)
+
+
+def test_out_of_range_group_ids_count_as_empty_slots():
+    """Selection entries outside [0, hist_len/8) -- one past the end, far past
+    it, inside the buffer's spare capacity (hist_stride > hist_len), or
+    negative other than -1 -- are empty slots: forward, backward and the
+    standalone gather give bit for bit what -1 in those slots gives, and that
+    matches the oracle fed -1 there."""
+    w = _w("bf16_bad_ids", 8, 2, 128, 1024, 192, 4, 24, "bf16")
+    inp = synth.make_inputs(w, 13, with_grad_out=True)
+    a = {k: _f32(v) for k, v in inp.items()}
+    g = _dev(inp)
+    # the history lives in a buffer with room for 2,048 rows per KV head
+    P = 2048
+    kh = torch.zeros((2, P, 128), dtype=torch.bfloat16, device="cuda")
+    vh = torch.zeros((2, P, 128), dtype=torch.bfloat16, device="cuda")
+    kh[:, :1024] = g["k_hist"]
+    vh[:, :1024] = g["v_hist"]
+    kh[:, 1024:] = 5.0                           # spare capacity: never attended
+    vh[:, 1024:] = 5.0
+    s = hga.make_shape(8, 2, 128, 1024, 192, 4, 24, torch.bfloat16, w.softmax_scale, hist_stride=P)
+    rng = np.random.default_rng(14)
+    clean = np.sort(rng.choice(128, (3, 2, 24)), axis=-1).astype(np.int32)
+    bad = clean.copy()
+    slots = rng.random(clean.shape) < 0.3
+    junk = np.array([128, 129, 200, 255, 1 << 30, (1 << 31) - 1, -2, -7, -(1 << 31)], np.int64)
+    bad[slots] = junk[rng.integers(0, junk.size, int(slots.sum()))].astype(np.int32)
+    bad[1, 1, :] = 128 + np.arange(24)           # a whole block of out-of-range ids
+    clean[slots] = -1
+    clean[1, 1, :] = -1
+    _say(f"[case] bad ids: {int((bad != clean).sum())} slots")
+    res = {}
+    for name, sel in (("bad", bad), ("clean", clean)):
+        st = torch.from_numpy(sel).cuda()
+        o, lse = hga.attn_fwd(s, g["q"], kh, vh, g["k_seg"], g["v_seg"], st)
+        grads = hga.attn_bwd(s, g["q"], kh, vh, g["k_seg"], g["v_seg"], st, o, lse, g["d_o"])
+        ko = torch.full((3, 2, 24 * 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+        vo = torch.full_like(ko, 7.0)
+        hga.hga_gather_groups(s, kh, vh, st, ko, vo)
+        res[name] = (o, lse, *grads, ko, vo)
+    torch.cuda.synchronize()
+    for x, y in zip(res["bad"], res["clean"]):
+        assert torch.equal(x, y)
+    o, lse, dq, dk, dv, ko, _ = res["clean"]
+    assert (ko[1, 1] == 0).all()
+    O_ref, L_ref = orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], clean,
+                                w.softmax_scale)
+    dQ, dK, dV = orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], clean,
+                              w.softmax_scale, a["d_o"])
+    for n, x, y in (("O", o, O_ref), ("LSE", lse, L_ref), ("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
+        _assert_close(n, _f32(x), y, 2e-2)
+
+
+def test_pinned_host_tier_from_two_threads():
+    """Two threads make pinned-host forward calls on one device, each on its
+    own stream with its own workspace: both results equal the single-thread
+    result bit for bit (the calls share the library's side stream and events
+    and take turns while they enqueue)."""
+    import threading
+    w = _w("bf16_host_threads", 8, 2, 128, 1536, 512, 5, 13, "bf16", bwd=False)
+    r = run_case(w, 5, check_bwd=False)
+    sh = _shape(w.replace(hist_on_host=True))
+    kh = torch.empty(r["inp"]["k_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty(r["inp"]["v_hist"].shape, dtype=torch.bfloat16, pin_memory=True)
+    kh.copy_(r["inp"]["k_hist"])
+    vh.copy_(r["inp"]["v_hist"])
+    g = r["g"]
+    outs, errs = {}, []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                ws = hga.alloc_workspace(sh, hga.HGA_OP_ATTN_FWD)
+                res = []
+                for _ in range(4):
+                    o = torch.empty_like(g["q"])
+                    lse = torch.empty((8, 512), dtype=torch.float32, device="cuda")
+                    hga.hga_attn_fwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"], o, lse, ws)
+                    res.append((o, lse))
+            st.synchronize()
+            outs[i] = res
+        except Exception as e:                   # reported by the main thread
+            errs.append(e)
+
+    _say("[case] pinned-host tier from two threads")
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=60)
+    assert not errs, errs
+    for i in range(2):
+        for o, lse in outs[i]:
+            assert torch.equal(o, r["o"]) and torch.equal(lse, r["lse"])
