@@ -649,17 +649,63 @@ def test_one_wrong_slice_fails_among_a_thousand():
     flip[0, 2047] *= -1.0
     assert not orc.within_tolerance(flip, ref, tol)
     sl = orc.slice_rel_l2(bad, ref)
-    assert sl.shape == (32, 32) and sl[3, 5] == pytest.approx(0.5) and np.delete(sl.ravel(), 3 * 32 + 5).max() == 0
+    assert sl.shape == (32, 32) and sl[3, 5] == pytest.approx(0.5, rel=0.1)
+    assert np.delete(sl.ravel(), 3 * 32 + 5).max() == 0
 
 
 def test_slices_follow_the_head_and_block_axes():
     # LSE-like [n][T] arrays and ragged T: the last slice is the partial run
     ref = np.ones((2, 130))
     got = ref.copy()
-    got[1, 128:] = 2.0
+    got[1, 64:128] = 1.25
     sl = orc.slice_rel_l2(got, ref)
     assert sl.shape == (2, 3)
-    assert sl[1, 2] == pytest.approx(1.0) and sl[:, :2].max() == 0 and sl[0].max() == 0
+    assert sl[1, 1] == pytest.approx(0.25) and sl[0].max() == 0 and sl[1, 0] == 0 and sl[1, 2] == 0
+    # a slice far smaller than the typical one is measured against the
+    # root-mean-square slice norm (here 8: 64 ones per slice)
+    got = ref.copy()
+    got[1, 128:] = 2.0                                   # the 2-row tail, 100% off
+    sl = orc.slice_rel_l2(got, ref)
+    rms = math.sqrt((64 + 64 + 2) / 3)
+    assert sl[1, 2] == pytest.approx(math.sqrt(2) / rms)
+
+
+def test_small_slices_admit_bf16_rounding_of_o_and_ds():
+    """With no history and a 70-token window, the first query block's rows see
+    1..64 keys that share one chunk offset, and dQ cancels that offset almost
+    exactly. Rounding the forward output O (which enters dS through
+    D = dO . O) and dS itself to bf16, as a bf16 kernel stores and multiplies
+    them, then moves those slices by ~2% of their own norm (half the typical
+    slice norm); the criterion must accept that rounding and still reject a
+    5%-wrong slice there."""
+    w = synth.Workload("bf16_nohist_w70", 4, 2, 128, 0, 256, 4, 8, "bf16", 1 / math.sqrt(128),
+                       backward=True, n_sink_chunks=2, local_window=70)
+    a = _np(synth.make_inputs(w, seed=3, with_grad_out=True))
+    sel = np.full((4, 2, 8), -1, np.int32)
+    dQ, _, _ = orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel,
+                            w.softmax_scale, a["d_o"], window=70)
+
+    def bf(x):
+        return torch.from_numpy(np.asarray(x)).to(torch.bfloat16).double().numpy()
+
+    rounded = np.zeros_like(dQ)
+    for h in range(4):
+        for b in range(4):
+            rows = slice(64 * b, 64 * b + 64)
+            Kc, Vc, nh, loc0, nl = orc._block_keys(a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"],
+                                                   sel, b, h // 2, 0, 70)
+            P, _ = orc._block_probs(a["q"][h, rows], Kc, nh, loc0, nl, b, w.softmax_scale, 70)
+            D = (a["d_o"][h, rows] * bf(P @ Vc)).sum(axis=1, keepdims=True)
+            dS = bf(P * (a["d_o"][h, rows] @ Vc.T - D))
+            rounded[h, rows] = w.softmax_scale * (dS @ Kc)
+    own = max(np.linalg.norm(rounded[h, :64] - dQ[h, :64]) / np.linalg.norm(dQ[h, :64]) for h in range(4))
+    assert own > 0.01                                    # the effect is real
+    assert orc.within_tolerance(rounded, dQ, 2e-2)
+    # an error of 5% of the typical slice norm, placed in a small first-block slice
+    rms = np.sqrt(np.mean([np.sum(dQ[h, 64 * s:64 * s + 64] ** 2) for h in range(4) for s in range(4)]))
+    bad = dQ.copy()
+    bad[0, :64] += 0.05 * rms * dQ[0, :64] / np.linalg.norm(dQ[0, :64])
+    assert not orc.within_tolerance(bad, dQ, 2e-2)
 
 
 def test_lse_is_held_to_the_fp32_bar():
