@@ -76,13 +76,53 @@ def kernel_work(w, s, n_slots=0):
         "attn_fwd": ("mfma", 4 * d * nq * (pairs_hist + pairs_causal)),
     }
     if w.backward:
+        # the backward's algorithmic work is 6*d per attended pair for dQ (S, dP,
+        # dQ) and 4*d per causal segment pair for dK and dV (dV, dK); the dK/dV
+        # kernel also recomputes S and dP (kernel_executed_work), which is not
+        # the method's work and is not credited here
         work["bwd_dq"] = ("mfma", 6 * d * nq * (pairs_hist + pairs_causal))
-        work["bwd_dkdv"] = ("mfma", 8 * d * nq * pairs_causal)
+        work["bwd_dkdv"] = ("mfma", 4 * d * nq * pairs_causal)
     if w.hist_on_host:
         work["gather"] = ("host", n_B * kv * hist_tok * d * e * 2)
     if n_slots:
         work["gcache"] = ("host", 0)        # rows moved depend on the call's misses
     return work
+
+
+def kernel_executed_work(w):
+    """MFMA flops a kernel executes per launch where that differs from its
+    algorithmic work: the dK/dV kernel recomputes S = Q.K^T and dP = dO.V^T
+    (4*d per causal pair) next to dV and dK."""
+    if not w.backward:
+        return {}
+    S, d, nq = w.seg_len, w.head_dim, w.n_q_heads
+    W = S if w.local_window <= 0 else min(w.local_window, S)
+    pairs_causal = W * (W + 1) // 2 + (S - W) * W
+    return {"bwd_dkdv": 8 * d * nq * pairs_causal}
+
+
+PEAK_HOST_LINK_GBS = 64.0    # PCIe Gen5 x16, one direction
+
+
+def host_link_rate(dev, mib=256, reps=5):
+    """Pinned host -> device copy rate over the host link (GB/s): the best of
+    `reps` timed hipMemcpyAsync copies of a page-locked buffer."""
+    import torch
+    src = torch.empty(mib * 2 ** 20, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(src.shape, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, src.numel() / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    return best
 
 
 KERNEL_SOURCES = {
@@ -118,30 +158,41 @@ def recorded_traffic(workload, kernel):
 
 
 def cpu_baseline(w, inp, budget_s):
-    """The oracle, as it stands, timed on this host for whole steps."""
+    """The oracle, as it stands, timed on this host for whole steps: with the
+    BLAS thread pool at its default size (`cores` threads), and for one step
+    with a single thread."""
     import numpy as np
     from oracle import hga_oracle as orc
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
     except ImportError:                     # pragma: no cover
-        threadpool_info = None
+        threadpool_info = threadpool_limits = None
     a = {k: v.float().numpy() for k, v in inp.items()}
-    n_steps, t_total = 0, 0.0
-    while n_steps < 5 and (n_steps == 0 or t_total < budget_s):
+    extra = dict(n_sink_tokens=64 * w.n_sink_chunks, window=w.local_window or None)
+
+    def one_step():
         t0 = time.perf_counter()
         _, sel_g, _ = orc.route(a["q"], a["k_hist"], w.n_kv_heads, w.top_k_chunks, w.top_k_groups,
                                 n_sink=w.n_sink_chunks)
-        extra = dict(n_sink_tokens=64 * w.n_sink_chunks, window=w.local_window or None)
         orc.attn_fwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel_g, w.softmax_scale,
                      **extra)
         if w.backward:
             orc.attn_bwd(a["q"], a["k_hist"], a["v_hist"], a["k_seg"], a["v_seg"], sel_g,
                          w.softmax_scale, a["d_o"], **extra)
-        t_total += time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    n_steps, t_total = 0, 0.0
+    while n_steps < 5 and (n_steps == 0 or t_total < budget_s):
+        t_total += one_step()
         n_steps += 1
     cores = 1
     if threadpool_info is not None:
         cores = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1 = one_step()
+        single = {"value": w.seg_len / t1, "cores": 1, "sample": f"1 whole step, {t1:.1f} s"}
     del np
     model = None
     try:
@@ -154,7 +205,8 @@ def cpu_baseline(w, inp, budget_s):
             "sample": f"{n_steps} whole step(s) of the same workload (route incl. full summaries, "
                       f"attention fwd{'+bwd' if w.backward else ''} over all {w.seg_len // 64} "
                       f"query blocks x {w.n_q_heads} heads), numpy fp32 routing / fp64 attention, "
-                      f"{t_total:.1f} s"}
+                      f"{t_total:.1f} s",
+            "single_thread": single}
 
 
 def tbptt_sweep(args):
@@ -458,6 +510,9 @@ def main():
     for kid in cal:
         hga.hga_set_kernel_events(kid, None, None)
 
+    executed = kernel_executed_work(w)
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
     def entry(name, us):
         kind, amount = work[name]
         ent = {"avg_us": round(us, 3)}
@@ -466,6 +521,11 @@ def main():
         if kind == "mfma":
             ent["tflops"] = round(amount / (us * 1e-6) / 1e12, 2)
             ent["gflop_per_launch"] = round(amount / 1e9, 3)
+            if name in executed:
+                # MFMA work the kernel runs, recomputation included: its MFMA
+                # utilisation, not a throughput of the method
+                ent["executed_gflop_per_launch"] = round(executed[name] / 1e9, 3)
+                ent["mfma_util_executed"] = round(executed[name] / (us * 1e-6) / 1e12 / peak_mfma, 4)
         else:
             ent["gbs"] = round(amount / (us * 1e-6) / 1e9, 1)
             ent["mib_per_launch"] = round(amount / 2 ** 20, 3)
@@ -503,11 +563,23 @@ def main():
     kernels[dom]["us_p10_p50_p90"] = [pct(0.1), pct(0.5), pct(0.9)]
     kind, amount = work[dom]
     if kind == "mfma":
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        peak = peak_mfma
         ach = amount / (dus * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                 "traffic": recorded_traffic(w.name, dom)}
+        if dom in executed:
+            roof["mfma_util_executed"] = kernels[dom]["mfma_util_executed"]
+    elif kind == "host":
+        # history in page-locked host memory: the routed groups cross the host
+        # link, so the link is the roofline (theoretical, and a pinned copy
+        # measured in this run)
+        ach = amount / (dus * 1e-6) / 1e9
+        link = host_link_rate(dev)
+        roof = {"kernel": dom, "bound": "host_link", "achieved": round(ach, 1),
+                "peak": PEAK_HOST_LINK_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HOST_LINK_GBS, 4),
+                "measured_link_gbs": round(link, 1), "frac_of_measured": round(ach / link, 4),
+                "traffic": None}
     else:
         ach = amount / (dus * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
