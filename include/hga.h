@@ -145,6 +145,22 @@ hga_status hga_route(const hga_shape* shape, const void* q, const float* chunk_s
                      const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* hga_route without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same kernels and results, bit for bit, as hga_route;
+ * the workspace is a static device array of HGA_NOALLOC_SCRATCH_BYTES in the
+ * library, one per device, held until the process ends (its address is looked
+ * up on the first call on a device). Returns HGA_ERR_WORKSPACE, with nothing
+ * enqueued, when hga_workspace_size(shape, HGA_OP_ROUTE) exceeds that size.
+ * Calls no allocating routine. Every call on one device shares that device's
+ * array and leaves its contents behind (nothing in it needs to start at zero:
+ * each call writes what it reads), so calls that overlap on one device (other
+ * streams, other threads) race: the caller must order them. */
+#define HGA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+hga_status hga_route_noalloc(const hga_shape* shape, const void* q, const float* chunk_sum,
+                             const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
+                             void* stream);
+
 /* Group-summary cache (gist.science Technical Summary §2.2, "Tiered Memory
  * Hierarchy", and pith.science review, Figure 2 caption: device memory keeps
  * every chunk summary but only a cache of group summaries; the rest of the

@@ -19,6 +19,13 @@ namespace hga {
 size_t bwd_workspace_bytes(const hga_shape& s);
 }  // namespace hga
 
+// Workspace of hga_route_noalloc: a static device array, one copy per device,
+// each held until the process ends. Host code never passes `scratch` itself
+// (on the host the name is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current (scratch_address).
+static __device__ __align__(256) unsigned char scratch[HGA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -172,6 +179,29 @@ hga_status side_resources(SideResources** out) {
 
 std::atomic<hipEvent_t> g_timer_ev[HGA_KERNEL_COUNT][2];
 
+// Workspace of hga_route_noalloc: the file-scope array `scratch` below.
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;
+
+hga_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(HGA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    }
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return HGA_OK;
+}
+
 }  // namespace
 
 namespace hga {
@@ -266,6 +296,26 @@ hga_status hga_route(const hga_shape* shape, const void* q, const float* chunk_s
     return fail(HGA_ERR_WORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (reinterpret_cast<uintptr_t>(ws) % 256)
     return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const hipError_t e = hga::launch_route(s, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+  return ok();
+}
+
+hga_status hga_route_noalloc(const hga_shape* shape, const void* q, const float* chunk_sum,
+                             const float* group_sum, int32_t* sel_chunks, int32_t* sel_groups,
+                             void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  HGA_REQUIRE(q && sel_chunks && sel_groups, "q, sel_chunks and sel_groups must be non-NULL");
+  HGA_REQUIRE(s.hist_len == 0 || (chunk_sum && group_sum),
+              "chunk_sum and group_sum must be non-NULL when hist_len > 0");
+  const size_t need = hga::route_workspace_bytes(s);
+  if (need > HGA_NOALLOC_SCRATCH_BYTES)
+    return fail(HGA_ERR_WORKSPACE, "route needs %zu workspace bytes, above the %zu-byte static scratch", need,
+                static_cast<size_t>(HGA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  HGA_TRY(scratch_address(&ws));
   const hipError_t e = hga::launch_route(s, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "route launch");

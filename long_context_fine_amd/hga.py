@@ -24,7 +24,7 @@ EXPORTS = ("hga_build_summaries", "hga_route", "hga_attn_fwd", "hga_attn_bwd",
            "hga_gather_groups", "hga_workspace_size", "hga_status_string",
            "hga_last_error", "hga_abi_version", "hga_set_kernel_events",
            "hga_gcache_bytes", "hga_gcache_reset", "hga_route_cached",
-           "hga_decode_workspace_size", "hga_decode")
+           "hga_decode_workspace_size", "hga_decode", "hga_route_noalloc")
 
 KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv", "gcache", "decode")
 
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "hga_build_summaries": [SP, P, I64, I64, P, P, P],
         "hga_route": [SP, P, P, P, P, P, P, SZ, P],
+        "hga_route_noalloc": [SP, P, P, P, P, P, P],
         "hga_attn_fwd": [SP, P, P, P, P, P, P, P, P, P, SZ, P],
         "hga_attn_bwd": [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "hga_gather_groups": [SP, P, P, P, P, P, P],
@@ -195,6 +196,19 @@ def hga_route(shape: Shape, q, chunk_sum, group_sum, sel_chunks, sel_groups, ws=
         _ptr(sel_chunks, (shape.n_blocks, kv, shape.top_k_chunks), torch.int32, "sel_chunks"),
         _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hga_route_noalloc(shape: Shape, q, chunk_sum, group_sum, sel_chunks, sel_groups,
+                      stream=None) -> None:
+    """hga_route with the library's static per-device scratch as its workspace."""
+    H, kv, d, S = shape.hist_rows, shape.n_kv_heads, shape.head_dim, shape.seg_len
+    _check(lib().hga_route_noalloc(
+        ctypes.byref(shape), _ptr(q, (shape.n_q_heads, S, d), shape.torch_dtype, "q"),
+        _ptr(chunk_sum, (kv, H // 64, d), torch.float32, "chunk_sum"),
+        _ptr(group_sum, (kv, H // 8, d), torch.float32, "group_sum"),
+        _ptr(sel_chunks, (shape.n_blocks, kv, shape.top_k_chunks), torch.int32, "sel_chunks"),
+        _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        _stream(stream)))
 
 
 def hga_attn_fwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, ws=None,

@@ -188,3 +188,14 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(hga, "_LIB_PATH", str(tmp_path / "libhga.so"))
     with pytest.raises(RuntimeError, match="missing"):
         hga.lib()
+
+
+def test_route_noalloc_rejects_shapes_beyond_its_scratch(L):
+    # 1,024 query blocks x 8 KV heads x 4,160 chunks of scores: 136 MB > 16 MiB
+    s = hga.make_shape(32, 8, 128, 4160 * 64, 65536, 16, 32)
+    assert hga.hga_workspace_size(s, hga.HGA_OP_ROUTE) > 16 * 2 ** 20
+    st = L.hga_route_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == hga.HGA_ERR_WORKSPACE
+    assert b"static scratch" in L.hga_last_error()
+    s = _shape(top_k_chunks=0)
+    assert L.hga_route_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
