@@ -634,10 +634,14 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // fp32 VALU kernels
 // ---------------------------------------------------------------------------
+// fp32 dQ: one wave per (block, head), one thread per query row; the query
+// and dO rows live in LDS (each thread's own padded row), dQ in registers.
 template <int D>
 __global__ __launch_bounds__(kWave) void attn_bwd_dq_f32_kernel(BwdParams p) {
   __shared__ float Kt[kTile][D + 1];
   __shared__ float Vt[kTile][D + 1];
+  __shared__ float Qs[kWave][D + 1];
+  __shared__ float Gs[kWave][D + 1];
   __shared__ int32_t sel_s[kMaxTopKGroups];
   const int a = threadIdx.x;
   const int n_blocks = p.seg_len / kBlockQ;
@@ -651,12 +655,18 @@ __global__ __launch_bounds__(kWave) void attn_bwd_dq_f32_kernel(BwdParams p) {
   const float* vs_g = static_cast<const float*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
   for (int i = a; i < p.k_g; i += kWave) sel_s[i] = valid_group(sel_bj[i], p.hist_len / kGroup);
-  float qr[D], gr[D], acc[D];
-  for (int e = 0; e < D; ++e) {
-    qr[e] = static_cast<const float*>(p.q)[row * D + e];
-    gr[e] = static_cast<const float*>(p.d_o)[row * D + e];
-    acc[e] = 0.f;
+  {
+    const int64_t row0 = row - a;
+    const float* qb = static_cast<const float*>(p.q) + row0 * D;
+    const float* gb = static_cast<const float*>(p.d_o) + row0 * D;
+    for (int x = a; x < kWave * D; x += kWave) {
+      Qs[x / D][x % D] = qb[x];
+      Gs[x / D][x % D] = gb[x];
+    }
   }
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.f;
   const float lse2 = p.lse[row] * kLog2e;
   const float dr = p.dvec[row];
   const int n_hist_tiles = (p.k_g + 7) / 8;
@@ -696,68 +706,87 @@ __global__ __launch_bounds__(kWave) void attn_bwd_dq_f32_kernel(BwdParams p) {
       if (!valid) continue;
       float s = 0.f, dp = 0.f;
       for (int e = 0; e < D; ++e) {
-        s += qr[e] * Kt[kk][e];
-        dp += gr[e] * Vt[kk][e];
+        s += Qs[a][e] * Kt[kk][e];
+        dp += Gs[a][e] * Vt[kk][e];
       }
       const float pr = exp2f(s * p.scale_log2 - lse2);
       const float ds = pr * (dp - dr);
+#pragma unroll
       for (int e = 0; e < D; ++e) acc[e] += ds * Kt[kk][e];
     }
     __syncthreads();
   }
   float* dq = static_cast<float*>(p.dq) + row * D;
+#pragma unroll
   for (int e = 0; e < D; ++e) dq[e] = acc[e] * p.scale;
 }
 
+// fp32 dK/dV: one workgroup of two waves per (64-key segment tile, KV head),
+// one key per lane; wave h accumulates dimensions [h*D/2, (h+1)*D/2) of dK and
+// dV (both waves form the full scores). The keys' K and V rows live in LDS
+// (each lane's own padded row).
 template <int D>
-__global__ __launch_bounds__(kWave) void attn_bwd_dkdv_f32_kernel(BwdParams p) {
+__global__ __launch_bounds__(2 * kWave) void attn_bwd_dkdv_f32_kernel(BwdParams p) {
+  constexpr int DH = D / 2;
   __shared__ float Qt[kTile][D + 1];
   __shared__ float Gt[kTile][D + 1];
+  __shared__ float Ks[kTile][D + 1];
+  __shared__ float Vs[kTile][D + 1];
   __shared__ float lse_s[kTile];
   __shared__ float dvec_s[kTile];
-  const int a = threadIdx.x;  // key within the tile
+  const int t = threadIdx.x, a = t % kWave, h = t / kWave;  // key within the tile, dimension half
   const int n_blocks = p.seg_len / kBlockQ;
   const int j = blockIdx.x % p.n_kv;
   const int kt_blk = blockIdx.x / p.n_kv;
   const int key_tok = kt_blk * kTile + a;
-  const float* kseg = static_cast<const float*>(p.k_seg) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
-  const float* vseg = static_cast<const float*>(p.v_seg) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
-  float kr[D], vr[D], dk[D], dv[D];
-  for (int e = 0; e < D; ++e) { kr[e] = kseg[e]; vr[e] = vseg[e]; dk[e] = 0.f; dv[e] = 0.f; }
+  {
+    const float* kb = static_cast<const float*>(p.k_seg) + (static_cast<int64_t>(j) * p.seg_len + kt_blk * kTile) * D;
+    const float* vb = static_cast<const float*>(p.v_seg) + (static_cast<int64_t>(j) * p.seg_len + kt_blk * kTile) * D;
+    for (int x = t; x < kTile * D; x += 2 * kWave) {
+      Ks[x / D][x % D] = kb[x];
+      Vs[x / D][x % D] = vb[x];
+    }
+  }
+  float dk[DH], dv[DH];
+#pragma unroll
+  for (int e = 0; e < DH; ++e) { dk[e] = 0.f; dv[e] = 0.f; }
   const int q_last = (kt_blk * kTile + kTile - 2 + p.window) / kBlockQ;
   const int q_end = q_last + 1 < n_blocks ? q_last + 1 : n_blocks;
   for (int qb = kt_blk; qb < q_end; ++qb) {
     for (int hi = 0; hi < p.r; ++hi) {
       const int64_t row0 = static_cast<int64_t>(j * p.r + hi) * p.seg_len + qb * kBlockQ;
       __syncthreads();
-      for (int qq = 0; qq < kTile; ++qq)
-        for (int e = a; e < D; e += kWave) {
-          Qt[qq][e] = static_cast<const float*>(p.q)[(row0 + qq) * D + e];
-          Gt[qq][e] = static_cast<const float*>(p.d_o)[(row0 + qq) * D + e];
-        }
-      lse_s[a] = p.lse[row0 + a] * kLog2e;
-      dvec_s[a] = p.dvec[row0 + a];
+      for (int x = t; x < kTile * D; x += 2 * kWave) {
+        Qt[x / D][x % D] = static_cast<const float*>(p.q)[row0 * D + x];
+        Gt[x / D][x % D] = static_cast<const float*>(p.d_o)[row0 * D + x];
+      }
+      if (h == 0) {
+        lse_s[a] = p.lse[row0 + a] * kLog2e;
+        dvec_s[a] = p.dvec[row0 + a];
+      }
       __syncthreads();
       for (int qq = 0; qq < kTile; ++qq) {
         const int dqk = qb * kBlockQ + qq - key_tok;
         if (dqk < 0 || dqk >= p.window) continue;  // key after the query or out of its window
         float s = 0.f, dp = 0.f;
         for (int e = 0; e < D; ++e) {
-          s += Qt[qq][e] * kr[e];
-          dp += Gt[qq][e] * vr[e];
+          s += Qt[qq][e] * Ks[a][e];
+          dp += Gt[qq][e] * Vs[a][e];
         }
         const float pr = exp2f(s * p.scale_log2 - lse_s[qq]);
         const float ds = pr * (dp - dvec_s[qq]);
-        for (int e = 0; e < D; ++e) {
-          dv[e] += pr * Gt[qq][e];
-          dk[e] += ds * Qt[qq][e];
+#pragma unroll
+        for (int e = 0; e < DH; ++e) {
+          dv[e] += pr * Gt[qq][h * DH + e];
+          dk[e] += ds * Qt[qq][h * DH + e];
         }
       }
     }
   }
-  float* dkp = static_cast<float*>(p.dk) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
-  float* dvp = static_cast<float*>(p.dv) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D;
-  for (int e = 0; e < D; ++e) { dkp[e] = dk[e] * p.scale; dvp[e] = dv[e]; }
+  float* dkp = static_cast<float*>(p.dk) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D + h * DH;
+  float* dvp = static_cast<float*>(p.dv) + (static_cast<int64_t>(j) * p.seg_len + key_tok) * D + h * DH;
+#pragma unroll
+  for (int e = 0; e < DH; ++e) { dkp[e] = dk[e] * p.scale; dvp[e] = dv[e]; }
 }
 
 template <int D>
@@ -773,7 +802,7 @@ hipError_t launch_d(const hga_shape& s, BwdParams& p, hipStream_t st) {
                           static_cast<const float*>(p.o), static_cast<const float*>(p.d_o), p.dvec, n_rows);
     hipExtLaunchKernelGGL((attn_bwd_dq_f32_kernel<D>), dim3(n_blocks * s.n_q_heads), dim3(kWave), 0, st,
                           nullptr, dq1, 0, p);
-    hipExtLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<D>), dim3(n_blocks * s.n_kv_heads), dim3(kWave), 0, st,
+    hipExtLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<D>), dim3(n_blocks * s.n_kv_heads), dim3(2 * kWave), 0, st,
                           kv0, kv1, 0, p);
   } else {
     const int n_pairs = (n_blocks + 1) / 2;

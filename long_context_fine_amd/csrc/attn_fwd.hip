@@ -350,12 +350,17 @@ __global__ __launch_bounds__(256 * HPW) void attn_fwd_bf16_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 VALU kernel: one wave per (block, head), one thread per query row
+// fp32 VALU kernel: one wave per (block, head), one thread per query row.
+// The query rows and the tile's scores live in LDS (each thread's row or
+// column, padded so the wave's accesses fall in distinct banks); only the
+// output accumulator stays in registers.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
   __shared__ float Kt[kTile][D + 1];
   __shared__ float Vt[kTile][D + 1];
+  __shared__ float Qs[kWave][D + 1];        // query row of thread a
+  __shared__ float Ps[kTile][kWave + 1];    // scaled scores of the tile, column a
   __shared__ int32_t sel_s[kMaxTopKGroups];
   const int a = threadIdx.x;  // query row within the block
   int w = blockIdx.x;
@@ -373,11 +378,13 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
   const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
   for (int i = a; i < p.k_g; i += kWave) sel_s[i] = valid_group(sel_bj[i], p.hist_len / kGroup);
 
-  float qr[D], acc[D];
-  for (int e = 0; e < D; ++e) {
-    qr[e] = q[(static_cast<int64_t>(head) * p.seg_len + q_tok) * D + e];
-    acc[e] = 0.f;
+  {
+    const float* qb = q + (static_cast<int64_t>(head) * p.seg_len + b * kBlockQ) * D;
+    for (int x = a; x < kWave * D; x += kWave) Qs[x / D][x % D] = qb[x];
   }
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const int n_hist_tiles = (p.k_g + 7) / 8;
   const int n_sink = p.n_sink_tiles;
@@ -404,7 +411,6 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
       }
     }
     __syncthreads();
-    float sc[kTile];
     float tmax = -INFINITY;
     for (int kk = 0; kk < kTile; ++kk) {
       bool valid;
@@ -418,18 +424,21 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
         valid = key <= q_tok && key > q_tok - p.window;
       }
       float s = 0.f;
-      for (int e = 0; e < D; ++e) s += qr[e] * Kt[kk][e];
-      sc[kk] = valid ? s * p.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sc[kk]);
+      for (int e = 0; e < D; ++e) s += Qs[a][e] * Kt[kk][e];
+      const float sc = valid ? s * p.scale_log2 : -INFINITY;
+      Ps[kk][a] = sc;
+      tmax = fmaxf(tmax, sc);
     }
     const float m_new = fmaxf(m_run, tmax);
     const float m_base = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_base);
     l_run *= alpha;
+#pragma unroll
     for (int e = 0; e < D; ++e) acc[e] *= alpha;
     for (int kk = 0; kk < kTile; ++kk) {
-      const float e_ = exp2f(sc[kk] - m_base);
+      const float e_ = exp2f(Ps[kk][a] - m_base);
       l_run += e_;
+#pragma unroll
       for (int e = 0; e < D; ++e) acc[e] += e_ * Vt[kk][e];
     }
     m_run = m_new;
@@ -437,6 +446,7 @@ __global__ __launch_bounds__(kWave) void attn_fwd_f32_kernel(FwdParams p) {
   }
   float* o = static_cast<float*>(p.o) + (static_cast<int64_t>(head) * p.seg_len + q_tok) * D;
   const float inv = 1.0f / l_run;
+#pragma unroll
   for (int e = 0; e < D; ++e) o[e] = acc[e] * inv;
   p.lse[static_cast<int64_t>(head) * p.seg_len + q_tok] = (m_run + log2f(l_run)) * kLn2;
 }

@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kUpdThreads) void gcache_update_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t x = x0 + u * kUpdThreads;
-      if (x < total) v[u] = src[static_cast<int64_t>(miss[x / V4]) * V4 + x % V4];
+      v[u] = x < total ? src[static_cast<int64_t>(miss[x / V4]) * V4 + x % V4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
