@@ -125,6 +125,30 @@ def host_link_rate(dev, mib=256, reps=5):
     return best
 
 
+def gemm_rate(dev, n=8192, reps=5):
+    """Dense bf16 rate this GPU sustains on random data (TFLOP/s): the best of
+    `reps` timed n x n x n products from the vendor GEMM library, operands drawn
+    uniformly from [-1, 1). The MFMA rate of random operands sits well below
+    the dense spec (the chip holds a lower clock under full matrix load), so
+    this is the practical ceiling an MFMA-bound kernel is compared with, beside
+    the spec peak."""
+    import torch
+    a = torch.empty((n, n), dtype=torch.bfloat16, device=dev).uniform_(-1.0, 1.0)
+    b = torch.empty((n, n), dtype=torch.bfloat16, device=dev).uniform_(-1.0, 1.0)
+    c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.mm(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2.0 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    del a, b, c
+    return best
+
+
 KERNEL_SOURCES = {
     "summaries": ["summaries.hip"], "route": ["route.hip"], "gather": ["gather.hip"],
     "attn_fwd": ["attn_fwd.hip", "attn_tile.hpp"], "bwd_dq": ["attn_bwd.hip", "attn_tile.hpp"],
@@ -570,6 +594,12 @@ def main():
                 "traffic": recorded_traffic(w.name, dom)}
         if dom in executed:
             roof["mfma_util_executed"] = kernels[dom]["mfma_util_executed"]
+        if w.dtype == "bf16":
+            gemm = gemm_rate(dev)
+            roof["measured_gemm_tflops"] = round(gemm, 1)
+            roof["frac_of_measured_gemm"] = round(ach / gemm, 4)
+            if dom in executed:
+                roof["executed_frac_of_measured_gemm"] = round(executed[dom] / (dus * 1e-6) / 1e12 / gemm, 4)
     elif kind == "host":
         # history in page-locked host memory: the routed groups cross the host
         # link, so the link is the roofline (theoretical, and a pinned copy
