@@ -156,6 +156,38 @@ def test_sink_and_local_window_match_oracle(w):
     run_case(w, 3, check_bwd=True)
 
 
+def _random_workloads(n=16, seed=20261203):
+    """Seeded random small shapes, every axis drawn at once: GQA ratio, KV
+    heads, head dim, history and segment lengths, chunk and group budgets
+    (group budgets past the candidate count included), sink, window, dtype."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        r = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        n_kv = int(rng.choice([1, 2, 4]))
+        while n_kv > 1 and n_kv * r > 16:
+            n_kv //= 2
+        d = int(rng.choice([64, 128]))
+        S = 64 * int(rng.integers(1, 9))
+        H = 64 * int(rng.integers(0, 65))
+        kc = int(rng.integers(1, 17))
+        kg = int(rng.integers(1, 8 * kc + 9))
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        sink = int(rng.integers(1, 4)) if rng.random() < 0.4 else 0
+        window = int(rng.integers(1, S + 1)) if rng.random() < 0.5 else 0
+        out.append(_w(f"rand{i}_{dtype}_r{r}_kv{n_kv}_d{d}_H{H}_S{S}_c{kc}_g{kg}_s{sink}_w{window}",
+                      r * n_kv, n_kv, d, H, S, kc, kg, dtype, sink=sink, window=window))
+    return out
+
+
+RANDOM = _random_workloads()
+
+
+@pytest.mark.parametrize("w", RANDOM, ids=[w.name for w in RANDOM])
+def test_random_shapes_match_oracle(w):
+    run_case(w, 5, check_bwd=True)
+
+
 def test_route_with_scores_in_workspace():
     """More than 4,096 chunks per KV head: chunk scores go to the workspace and
     the chunk top-k re-reads them each round instead of holding them in
