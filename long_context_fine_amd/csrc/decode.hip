@@ -383,48 +383,111 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   }
   __syncthreads();
 
-  // ---- P . V: each lane owns DPL dims; a wave takes a quarter of the keys --
-  float acc[QR][DPL];
+  if constexpr (QR <= 8) {
+    // ---- P . V: one V row per LPR lanes (16 bytes each), RPL rows per wave
+    // load, all of a wave's rows requested before any is used; then the RPL
+    // lane groups holding the same dims are summed across lanes. Keys past
+    // the piece load nothing (their P is zero).
+    constexpr int LPR = D / 8;            // lanes per V row
+    constexpr int RPL = kWave / LPR;      // rows per wave load
+    constexpr int KPW = KEYS / NW;        // keys per wave
+    constexpr int NLD = KPW / RPL;        // row loads per lane
+    const int sub = lane % LPR, rsub = lane / LPR;
+    const int kq0 = wave * KPW;
+    uint4 vr[NLD];
 #pragma unroll
-  for (int rq = 0; rq < QR; ++rq)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[rq][e] = 0.f;
-  constexpr int KPI = 16;                       // keys per pass: their row loads in flight together
-  const int kq0 = wave * (KEYS / NW);
-  for (int kk = kq0; kk < kq0 + KEYS / NW && kk < nk; kk += KPI) {
-    float vf[KPI][DPL];
-#pragma unroll
-    for (int u = 0; u < KPI; ++u) {
+    for (int m = 0; m < NLD; ++m) {
+      const int kk = kq0 + m * RPL + rsub;
       bool tail;
       int inf;
-      const int64_t off = resolve(k0 + kk + u, tail, inf);
-      const uint16_t* vp = (tail ? vt : vh) + off + lane * DPL;
-      if (DPL == 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
-        vf[u][0] = __uint_as_float(w << 16);
-        vf[u][DPL - 1] = __uint_as_float(w & 0xffff0000u);
-      } else {
-        vf[u][0] = bf16_to_f32(vp[0]);
-      }
+      const int64_t off = resolve(k0 + kk, tail, inf);
+      vr[m] = kk < nk ? *reinterpret_cast<const uint4*>((tail ? vt : vh) + off + sub * 8) : make_uint4(0, 0, 0, 0);
     }
+    float acc[QR][8];
 #pragma unroll
-    for (int rq = 0; rq < QR; ++rq) {
-      if (rq < R) {
+    for (int rq = 0; rq < QR; ++rq)
 #pragma unroll
-        for (int u4 = 0; u4 < KPI; u4 += 4) {
-          const float4 p4 = *reinterpret_cast<const float4*>(&s_lds[rq][kk + u4]);  // zero past nk
+      for (int e = 0; e < 8; ++e) acc[rq][e] = 0.f;
 #pragma unroll
-          for (int e = 0; e < DPL; ++e)
-            acc[rq][e] += p4.x * vf[u4][e] + p4.y * vf[u4 + 1][e] + p4.z * vf[u4 + 2][e] + p4.w * vf[u4 + 3][e];
+    for (int m = 0; m < NLD; ++m) {
+      const int kk = kq0 + m * RPL + rsub;
+      const uint32_t w4[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
+      float vf[8];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        vf[2 * x] = __uint_as_float(w4[x] << 16);
+        vf[2 * x + 1] = __uint_as_float(w4[x] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int rq = 0; rq < QR; ++rq) {
+        if (rq < R) {
+          const float pr = s_lds[rq][kk];  // zero past nk
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[rq][e] += pr * vf[e];
         }
       }
     }
+#pragma unroll
+    for (int rq = 0; rq < QR; ++rq)
+      if (rq < R)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float x = acc[rq][e];
+#pragma unroll
+          for (int o = LPR; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
+          acc[rq][e] = x;
+        }
+    if (rsub == 0) {
+#pragma unroll
+      for (int rq = 0; rq < QR; ++rq)
+        if (rq < R)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o_lds[wave][rq][sub * 8 + e] = acc[rq][e];
+    }
+  } else {
+    // ---- P . V: each lane owns DPL dims; a wave takes a quarter of the keys --
+    float acc[QR][DPL];
+  #pragma unroll
+    for (int rq = 0; rq < QR; ++rq)
+  #pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[rq][e] = 0.f;
+    constexpr int KPI = 16;                       // keys per pass: their row loads in flight together
+    const int kq0 = wave * (KEYS / NW);
+    for (int kk = kq0; kk < kq0 + KEYS / NW && kk < nk; kk += KPI) {
+      float vf[KPI][DPL];
+  #pragma unroll
+      for (int u = 0; u < KPI; ++u) {
+        bool tail;
+        int inf;
+        const int64_t off = resolve(k0 + kk + u, tail, inf);
+        const uint16_t* vp = (tail ? vt : vh) + off + lane * DPL;
+        if (DPL == 2) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
+          vf[u][0] = __uint_as_float(w << 16);
+          vf[u][DPL - 1] = __uint_as_float(w & 0xffff0000u);
+        } else {
+          vf[u][0] = bf16_to_f32(vp[0]);
+        }
+      }
+  #pragma unroll
+      for (int rq = 0; rq < QR; ++rq) {
+        if (rq < R) {
+  #pragma unroll
+          for (int u4 = 0; u4 < KPI; u4 += 4) {
+            const float4 p4 = *reinterpret_cast<const float4*>(&s_lds[rq][kk + u4]);  // zero past nk
+  #pragma unroll
+            for (int e = 0; e < DPL; ++e)
+              acc[rq][e] += p4.x * vf[u4][e] + p4.y * vf[u4 + 1][e] + p4.z * vf[u4 + 2][e] + p4.w * vf[u4 + 3][e];
+          }
+        }
+      }
+    }
+  #pragma unroll
+    for (int rq = 0; rq < QR; ++rq)
+      if (rq < R)
+  #pragma unroll
+        for (int e = 0; e < DPL; ++e) o_lds[wave][rq][lane * DPL + e] = acc[rq][e];
   }
-#pragma unroll
-  for (int rq = 0; rq < QR; ++rq)
-    if (rq < R)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o_lds[wave][rq][lane * DPL + e] = acc[rq][e];
   __syncthreads();
   for (int x = t; x < R * D; x += kDecThreads) {
     const int rq = x / D, dd = x % D;
