@@ -328,7 +328,7 @@ def decode_step(q_new, k_hist, v_hist, k_tail, v_tail, k_c, k_g, scale, n_sink=0
     position p attends the sink tokens, the tokens of the selected groups and
     the open-segment tokens t with p - W < t <= p (W = window, default the
     whole open segment). sel_groups [n_kv][k_g], if given, replaces the
-    routed selection in the attention (to judge a kernel's outputs with its
+    routed selection in the attention (to check a kernel's outputs against its
     own selection).
 
     Returns (sel_chunks int32 [n_kv][k_c], sel_groups int32 [n_kv][k_g],

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs. Index parity: exact, except near-ties (oracle score gap
-< 1e-5), judged by the oracle's checker. Output parity: max|got-ref| <=
+< 1e-5), as decided by the oracle's checker. Output parity: max|got-ref| <=
 tol * max(1, max|ref|), and ||got-ref||_2 <= tol * ||ref||_2 over the whole
 tensor and over every (head, 64-row block) slice, with tol = 2e-2 (bf16) /
 1e-4 (fp32); LSE element by element within 1e-4 * max(1, |ref|) in every
