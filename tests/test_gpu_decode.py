@@ -200,3 +200,41 @@ def test_decode_retrieves_a_planted_needle():
                                          w.softmax_scale, sel_groups=sg[0].cpu().numpy())
     assert orc.within_tolerance(_f64(o[0]), O_ref, TOL["bf16"])
     assert orc.lse_within(_f64(lse[0]), L_ref)
+
+
+def _random_decode_cases(n=10, seed=20261204):
+    """Seeded random ragged batches, every axis drawn at once: GQA ratio and KV
+    heads, new tokens per sequence (r * n_new <= 16), head dim, capacities,
+    history lengths in whole chunks (0 included), open-segment lengths, budgets,
+    sink, window, dtype."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        r = int(rng.choice([1, 2, 4, 8]))
+        n_kv = int(rng.choice([1, 2, 4]))
+        n_new = int(rng.integers(1, 5))
+        while r * n_new > 16:
+            n_new -= 1
+        d = int(rng.choice([64, 128]))
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        P = 64 * int(rng.integers(1, 48))
+        T = 64 * int(rng.integers(1, 9))
+        B = int(rng.integers(1, 6))
+        hist = [64 * int(rng.integers(0, P // 64 + 1)) for _ in range(B)]
+        tail = [int(rng.integers(n_new, T + 1)) for _ in range(B)]
+        k_c = int(rng.integers(1, 9))
+        k_g = int(rng.integers(1, 8 * k_c + 9))
+        sink = int(rng.integers(1, 3)) if rng.random() < 0.4 else 0
+        window = int(rng.integers(1, T + 1)) if rng.random() < 0.5 else 0
+        out.append((f"rdec{i}", r * n_kv, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new, sink, window))
+    return out
+
+
+RANDOM_DECODE = _random_decode_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_DECODE, ids=[c[0] for c in RANDOM_DECODE])
+def test_decode_random_batches(case):
+    _, n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new, sink, window = case
+    run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new=n_new, seed=7, sink=sink,
+               window=window)

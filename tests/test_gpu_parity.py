@@ -350,6 +350,16 @@ def test_pinned_host_tier_is_bit_identical(w):
     assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
 
 
+RANDOM_HOST = [w.replace(backward=False) for w in _random_workloads(6, seed=20261205)]
+
+
+@pytest.mark.parametrize("w", RANDOM_HOST, ids=[w.name for w in RANDOM_HOST])
+def test_pinned_host_tier_random_shapes(w):
+    """The pinned-host tier on seeded random shapes (sinks, windows, GQA
+    ratios, both head dims and dtypes): bit-identical to the HBM path."""
+    test_pinned_host_tier_is_bit_identical(w)
+
+
 def test_autograd_function_matches_explicit_calls():
     w = _w("bf16_autograd", 8, 2, 128, 1024, 128, 4, 16, "bf16")
     inp = _dev(synth.make_inputs(w, 12, with_grad_out=True))
