@@ -150,3 +150,34 @@ def test_reset_empties_the_cache():
     soc, cos, hand, _ = cache.tables()
     torch.cuda.synchronize()
     assert bool((soc == -1).all()) and bool((cos == -1).all()) and bool((hand == 0).all())
+
+
+def _random_cache_cases(n=6, seed=20261206):
+    """Seeded random shapes for the cached route: GQA ratio, KV heads, head
+    dim, history, segment, budgets, sink, dtype, and a cache between the
+    smallest allowed ((S/64) * k_c slots) and twice that; three calls, the
+    last repeating the first query."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        r = int(rng.choice([1, 2, 4, 8]))
+        n_kv = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        H = 64 * int(rng.integers(2, 65))
+        S = 64 * int(rng.integers(1, 9))
+        k_c = int(rng.integers(1, 9))
+        k_g = int(rng.integers(1, 8 * k_c + 9))
+        n_slots = (S // 64) * k_c + int(rng.integers(0, (S // 64) * k_c + 1))
+        sink = int(rng.integers(1, 3)) if rng.random() < 0.3 else 0
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        out.append((f"rcache{i}", r * n_kv, n_kv, d, H, S, k_c, k_g, n_slots, sink, dtype))
+    return out
+
+
+RANDOM_CACHE = _random_cache_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_CACHE, ids=[c[0] for c in RANDOM_CACHE])
+def test_cache_random_shapes(case):
+    _, n_q, n_kv, d, H, S, k_c, k_g, n_slots, sink, dtype = case
+    _run_sequence(n_q, n_kv, d, H, S, k_c, k_g, n_slots, seeds=[21, 22, 21], sink=sink, dtype=dtype)
