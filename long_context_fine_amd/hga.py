@@ -138,7 +138,9 @@ def _ptr(t: torch.Tensor | None, shape=None, dtype=None, name="", device=True) -
         raise ValueError(f"{name}: must be contiguous")
     if device and not t.is_cuda:
         raise ValueError(f"{name}: must be a GPU tensor")
-    if not device and (t.is_cuda or not t.is_pinned()):
+    # an empty host tensor (no history) is never read; torch does not report
+    # a zero-size allocation as pinned
+    if not device and (t.is_cuda or (t.numel() > 0 and not t.is_pinned())):
         raise ValueError(f"{name}: must be a pinned host tensor")
     return t.data_ptr()
 

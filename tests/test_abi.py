@@ -199,3 +199,12 @@ def test_route_noalloc_rejects_shapes_beyond_its_scratch(L):
     assert b"static scratch" in L.hga_last_error()
     s = _shape(top_k_chunks=0)
     assert L.hga_route_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
+
+
+def test_binding_host_tensors_must_be_pinned_unless_empty():
+    """Host-side history tensors go through the pinned check, except an empty
+    one (a history of zero tokens is never read)."""
+    import torch
+    assert hga._ptr(torch.empty(0, dtype=torch.bfloat16), name="k_hist", device=False) is not None
+    with pytest.raises(ValueError, match="pinned host tensor"):
+        hga._ptr(torch.empty(4, dtype=torch.bfloat16), name="k_hist", device=False)

@@ -271,6 +271,49 @@ def test_gather_groups_is_exact():
             assert torch.equal(vo[b, j].cpu(), want_v)
 
 
+RANDOM_GATHER = [w.replace(backward=False) for w in _random_workloads(6, seed=20261207)]
+
+
+@pytest.mark.parametrize("on_host", [False, True], ids=["hbm", "pinned_host"])
+@pytest.mark.parametrize("w", RANDOM_GATHER, ids=[w.name for w in RANDOM_GATHER])
+def test_gather_groups_random_shapes(w, on_host):
+    """hga_gather_groups on seeded random shapes, from device memory and from
+    page-locked host memory, with every seventh selection slot emptied: the
+    exact rows of each selected group, zeros for empty slots."""
+    _say(f"[case] gather {w.name} {'pinned host' if on_host else 'hbm'}")
+    inp = synth.make_inputs(w, 13)
+    g = _dev(inp)
+    s = _shape(w)
+    C, G = hga.summaries(s, g["k_hist"])
+    _, sel = hga.route(s, g["q"], C, G)
+    sel.view(-1)[::7] = -1
+    n_b, n_kv, kg, d = w.seg_len // 64, w.n_kv_heads, w.top_k_groups, w.head_dim
+    ko = torch.full((n_b, n_kv, kg * 8, d), 7.0, dtype=w.torch_dtype, device="cuda")
+    vo = torch.full((n_b, n_kv, kg * 8, d), 7.0, dtype=w.torch_dtype, device="cuda")
+    if on_host:
+        kh = torch.empty(inp["k_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
+        vh = torch.empty(inp["v_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
+        kh.copy_(inp["k_hist"])
+        vh.copy_(inp["v_hist"])
+        hga.hga_gather_groups(_shape(w.replace(hist_on_host=True)), kh, vh, sel, ko, vo)
+    else:
+        hga.hga_gather_groups(s, g["k_hist"], g["v_hist"], sel, ko, vo)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    for b in range(n_b):
+        for j in range(n_kv):
+            tok = np.array([8 * n + u for n in sel_np[b, j] for u in range(8)])
+            valid = np.repeat(sel_np[b, j] >= 0, 8)
+            want_k = inp["k_hist"][j][np.where(valid, tok, 0)].clone() if w.hist_len else \
+                torch.zeros((kg * 8, d), dtype=w.torch_dtype)
+            want_v = inp["v_hist"][j][np.where(valid, tok, 0)].clone() if w.hist_len else \
+                torch.zeros((kg * 8, d), dtype=w.torch_dtype)
+            want_k[~torch.from_numpy(valid)] = 0
+            want_v[~torch.from_numpy(valid)] = 0
+            assert torch.equal(ko[b, j].cpu(), want_k), (b, j)
+            assert torch.equal(vo[b, j].cpu(), want_v), (b, j)
+
+
 def test_runs_are_bitwise_repeatable():
     w = _w("bf16_repeat", 8, 2, 128, 1024, 256, 4, 16, "bf16")
     inp = _dev(synth.make_inputs(w, 11, with_grad_out=True))
