@@ -238,3 +238,36 @@ def test_decode_random_batches(case):
     _, n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new, sink, window = case
     run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new=n_new, seed=7, sink=sink,
                window=window)
+
+
+def _random_split_cases(n=4, seed=20261208):
+    """Seeded random small batches with long histories (32K-128K capacity), so
+    the chunk scan is split over several workgroups per (sequence, KV head)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        n_kv = int(rng.choice([1, 2, 4]))
+        r = int(rng.choice([1, 2, 4]))
+        n_new = int(rng.integers(1, 3))
+        d = int(rng.choice([64, 128]))
+        P = 64 * int(rng.integers(512, 2049))
+        T = 64 * int(rng.integers(1, 5))
+        B = int(rng.integers(1, 5))
+        hist = [64 * int(rng.integers(P // 128, P // 64 + 1)) for _ in range(B)]
+        tail = [int(rng.integers(n_new, T + 1)) for _ in range(B)]
+        k_c = int(rng.integers(4, 17))
+        k_g = int(rng.integers(8, 8 * k_c + 1))
+        sink = int(rng.integers(1, 3)) if rng.random() < 0.4 else 0
+        window = int(rng.integers(1, T + 1)) if rng.random() < 0.5 else 0
+        out.append((f"rsplit{i}", r * n_kv, n_kv, d, P, T, k_c, k_g, "bf16", hist, tail, n_new, sink, window))
+    return out
+
+
+RANDOM_SPLIT = _random_split_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_SPLIT, ids=[c[0] for c in RANDOM_SPLIT])
+def test_decode_random_long_histories(case):
+    _, n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new, sink, window = case
+    run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new=n_new, seed=8, sink=sink,
+               window=window)
