@@ -269,6 +269,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   // rows padded by 4 floats: the 32 query rows' 16-byte score stores spread over the banks
   __shared__ __attribute__((aligned(16))) float s_lds[QR][KEYS + 4];
   __shared__ int32_t kinfo[KEYS];           // -1 plain, -2 masked, >= 0 open-segment position
+  // element offset of each key's row, one's complement for an open-segment
+  // row: resolved once in the score phase, so that the V loads do not wait
+  // for another read of the routed group ids
+  __shared__ int64_t koff[KEYS];
   __shared__ float o_lds[NW][QR][D];
   const int piece = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t % kWave;
@@ -325,11 +329,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   }
   bf16x8 ka[TPW][NKS];
   int info[TPW];
+  int64_t kcode[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int kk = (wave * TPW + tt) * KT + l32;
     bool tail;
     const int64_t off = resolve(k0 + kk, tail, info[tt]);
+    kcode[tt] = tail ? ~off : off;
     const uint16_t* kp = (tail ? kt : kh) + off + hh * 8;
 #pragma unroll
     for (int ss = 0; ss < NKS; ++ss) ka[tt][ss] = *reinterpret_cast<const bf16x8*>(kp + ss * 16);
@@ -342,7 +348,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
     for (int ss = 0; ss < NKS; ++ss) acc = mfma32(ka[tt][ss], qreg[ss], acc);
-    if (hh == 0) kinfo[tile0 + l32] = info[tt];
+    if (hh == 0) {
+      kinfo[tile0 + l32] = info[tt];
+      koff[tile0 + l32] = kcode[tt];
+    }
     if (l32 < R) {
       // acc[v]: key tile0 + 8*(v/4) + 4*hh + v%4, query row l32
 #pragma unroll
@@ -398,10 +407,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
 #pragma unroll
     for (int m = 0; m < NLD; ++m) {
       const int kk = kq0 + m * RPL + rsub;
-      bool tail;
-      int inf;
-      const int64_t off = resolve(k0 + kk, tail, inf);
-      vr[m] = kk < nk ? *reinterpret_cast<const uint4*>((tail ? vt : vh) + off + sub * 8) : make_uint4(0, 0, 0, 0);
+      const int64_t c = koff[kk];
+      const uint16_t* vp = c < 0 ? vt + ~c : vh + c;
+      vr[m] = kk < nk ? *reinterpret_cast<const uint4*>(vp + sub * 8) : make_uint4(0, 0, 0, 0);
     }
     float acc[QR][8];
 #pragma unroll
@@ -457,10 +465,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
       float vf[KPI][DPL];
   #pragma unroll
       for (int u = 0; u < KPI; ++u) {
-        bool tail;
-        int inf;
-        const int64_t off = resolve(k0 + kk + u, tail, inf);
-        const uint16_t* vp = (tail ? vt : vh) + off + lane * DPL;
+        const int64_t c = koff[kk + u];
+        const uint16_t* vp = (c < 0 ? vt + ~c : vh + c) + lane * DPL;
         if (DPL == 2) {
           const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
           vf[u][0] = __uint_as_float(w << 16);
