@@ -165,12 +165,20 @@ hga_status side_resources(SideResources** out) {
   auto it = g_side.find(dev);
   if (it == g_side.end()) {
     std::unique_ptr<SideResources> r(new SideResources);
+    hipEvent_t* evs[5] = {&r->start, &r->gathered[0], &r->gathered[1], &r->consumed[0], &r->consumed[1]};
+    // on a failed creation, release what was created before reporting it
+    auto release = [&]() {
+      for (hipEvent_t* ev : evs)
+        if (*ev) (void)hipEventDestroy(*ev);
+      if (r->side) (void)hipStreamDestroy(r->side);
+    };
     if ((e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking)) != hipSuccess)
       return hip_fail(e, "hipStreamCreateWithFlags");
-    hipEvent_t* evs[5] = {&r->start, &r->gathered[0], &r->gathered[1], &r->consumed[0], &r->consumed[1]};
     for (hipEvent_t* ev : evs)
-      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
+      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) {
+        release();
         return hip_fail(e, "hipEventCreateWithFlags");
+      }
     it = g_side.emplace(dev, std::move(r)).first;
   }
   *out = it->second.get();
