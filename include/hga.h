@@ -44,7 +44,7 @@
  *
  * Ownership: the caller allocates every buffer and the workspace; the library
  * allocates no device memory and keeps no state between calls except, for the
- * pinned-host history tier, one side stream and five events per device,
+ * pinned-host history tier, one side stream and three events per device,
  * created on first use; host-tier calls on one device from several threads
  * take turns while they enqueue (they share that side stream). Every pointer
  * is a device pointer except k_hist / v_hist under HGA_HIST_HOST_PINNED, which
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 2
+#define HGA_ABI_VERSION 3
 
 typedef enum {
   HGA_OK = 0,
@@ -247,7 +247,10 @@ hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, cons
  * kernels treat any other value as -1, so no entry can make them read outside
  * the history. ws: hga_workspace_size(shape, HGA_OP_ATTN_FWD)
  * bytes (zero for device-resident history; staging for the pinned-host tier,
- * whose gathers run on an internal side stream fenced back to `stream`). */
+ * whose gathers run on an internal side stream fenced back to `stream`). With
+ * pinned-host history and hist_len > 0, ws holds after the call (in stream
+ * order) the routed K/V rows of every query block and the sink rows, which
+ * hga_attn_bwd_staged reads. */
 hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_hist,
                         const void* v_hist, const void* k_seg, const void* v_seg,
                         const int32_t* sel_groups, void* o, float* lse,
@@ -258,14 +261,35 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
  * is detached at the segment boundary). Writes dq for every query, dk_seg and
  * dv_seg for the active segment; history K/V, summaries and selections get no
  * gradient. o and lse are the forward's outputs. Deterministic: no atomics.
- * ws: hga_workspace_size(shape, HGA_OP_ATTN_BWD) bytes. k_hist / v_hist must
- * be in device memory (HGA_HIST_DEVICE). sel_groups as for hga_attn_fwd: ids
- * outside [0, hist_len/8) count as -1. */
+ * ws: hga_workspace_size(shape, HGA_OP_ATTN_BWD) bytes, 256-byte aligned.
+ * k_hist / v_hist live where shape->hist_loc says (gist.science §2.2
+ * "Tiered Memory Hierarchy": history in host RAM, routed exact K/V in VRAM).
+ * With page-locked host history (and hist_len > 0) the call first copies every
+ * query block's routed groups and the sink rows into ws over the host link, in
+ * stream order, then reads only those copies; the result is bit-identical to
+ * the same call on device-resident history. sel_groups as for hga_attn_fwd:
+ * ids outside [0, hist_len/8) count as -1. */
 hga_status hga_attn_bwd(const hga_shape* shape, const void* q, const void* k_hist,
                         const void* v_hist, const void* k_seg, const void* v_seg,
                         const int32_t* sel_groups, const void* o, const float* lse,
                         const void* d_o, void* dq, void* dk_seg, void* dv_seg,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* hga_attn_bwd for pinned-host history (shape->hist_loc ==
+ * HGA_HIST_HOST_PINNED) that reads the history rows hga_attn_fwd left in its
+ * workspace instead of bringing them over the host link again (gist.science
+ * §2.2 "Segment-wise Backward and Tiered Storage": the routed exact K/V of the
+ * active segment stay in VRAM for its backward). fwd_ws / fwd_ws_bytes: the
+ * workspace of an hga_attn_fwd call with the same shape and sel_groups, not
+ * written since (stream order: enqueue this call after that one). ws:
+ * hga_workspace_size(shape, HGA_OP_ATTN_BWD) bytes suffice. Outputs, ids
+ * outside [0, hist_len/8) and determinism as for hga_attn_bwd; the result is
+ * bit-identical to it. */
+hga_status hga_attn_bwd_staged(const hga_shape* shape, const void* q, const void* fwd_ws,
+                               size_t fwd_ws_bytes, const void* k_seg, const void* v_seg,
+                               const int32_t* sel_groups, const void* o, const float* lse,
+                               const void* d_o, void* dq, void* dk_seg, void* dv_seg,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* Exact-token gather on its own (gist.science Technical Summary §2.1 and
  * §2.2 "Tiered Memory Hierarchy": only the selected groups' exact K/V are

@@ -41,6 +41,14 @@ struct BwdParams {
   int seg_len;
   int64_t hist_len;
   int64_t hist_rows;  // rows per KV head in k_hist / v_hist
+  // Staged routed rows (history in host memory): k_hist / v_hist then point
+  // at [n_blocks][n_kv][k_g*8][D] copies of each block's routed groups, with
+  // hist_rows = k_g*8, and the valid group in slot `slot` of block b is read
+  // as group b*n_kv*k_g + slot, which addresses exactly that copy.
+  int staged;
+  const void* k_sink;  // sink rows [n_kv][sink_stride][D] (the history itself when not staged)
+  const void* v_sink;
+  int64_t sink_stride;
   int k_g;
   int n_sink_tiles;   // fixed sink: the first n_sink_tiles*64 history rows
   int window;         // local window W in tokens (<= seg_len)
@@ -48,13 +56,19 @@ struct BwdParams {
   float scale_log2;
 };
 
-__device__ __forceinline__ int64_t hist_offset(const BwdParams& p, const int32_t* sel_s, int j,
+// Group id whose rows hold valid group n of slot `slot` of block b: n itself,
+// or the block's staged copy.
+__device__ __forceinline__ int64_t group_row(const BwdParams& p, int b, int slot, int n) {
+  return p.staged ? static_cast<int64_t>(b) * p.n_kv * p.k_g + slot : static_cast<int64_t>(n);
+}
+
+__device__ __forceinline__ int64_t hist_offset(const BwdParams& p, const int32_t* sel_s, int b, int j,
                                                int ht, int kk, int D) {
   const int slot = ht * 8 + kk / kGroup;
   if (slot >= p.k_g) return -1;
   const int n = sel_s[slot];
   if (n < 0) return -1;
-  return (static_cast<int64_t>(j) * p.hist_rows + static_cast<int64_t>(n) * kGroup + kk % kGroup) * D;
+  return (static_cast<int64_t>(j) * p.hist_rows + group_row(p, b, slot, n) * kGroup + kk % kGroup) * D;
 }
 
 // Dvec = rowsum(dO * O), fp32 accumulation (fp32 path; the bf16 dQ kernel
@@ -129,6 +143,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
 
   const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist) + static_cast<int64_t>(j) * p.hist_rows * D;
   const uint16_t* vh = static_cast<const uint16_t*>(p.v_hist) + static_cast<int64_t>(j) * p.hist_rows * D;
+  const uint16_t* ksk = static_cast<const uint16_t*>(p.k_sink) + static_cast<int64_t>(j) * p.sink_stride * D;
+  const uint16_t* vsk = static_cast<const uint16_t*>(p.v_sink) + static_cast<int64_t>(j) * p.sink_stride * D;
   const uint16_t* ks_g = static_cast<const uint16_t*>(p.k_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const uint16_t* vs_g = static_cast<const uint16_t*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const float c2 = p.scale_log2;
@@ -136,6 +152,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   for (int half = 0; half < 2; ++half) {
     const int b = half == 0 ? b_hi : b_lo;
     if (half == 1 && b_lo >= b_hi) break;
+    // staged rows: slot s of this block is group stage0 + s
+    const int stage0 = p.staged ? b * p.n_kv * p.k_g : -1;
     const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
     __syncthreads();
     for (int i = tid; i < p.k_g; i += NT) sel_s[i] = valid_group(sel_bj[i], p.hist_len / kGroup);
@@ -162,7 +180,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
       const uint16_t* seg = which ? vs_g : ks_g;
       if (t < n_sink) {
         tile_copy_rows_part<D, GT>(smem[buf][grp][which], gwave, lane,
-                                   (which ? vh : kh) + static_cast<int64_t>(t) * kTile * D, part);
+                                   (which ? vsk : ksk) + static_cast<int64_t>(t) * kTile * D, part);
       } else if (t < n_pre) {
         const int ht = __builtin_amdgcn_readfirstlane(hlist[t - n_sink]);
         const uint16_t* base = which ? vh : kh;
@@ -170,7 +188,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
           const uint32_t slot = static_cast<uint32_t>(ht) * 8u + (kq * RPI) / kGroup;
           const int n = slot < static_cast<uint32_t>(p.k_g) ? __builtin_amdgcn_readfirstlane(sel_s[slot]) : -1;
           const uint32_t sub = (kq * RPI) % kGroup;
-          return n >= 0 ? base + (static_cast<int64_t>(n) * kGroup + sub) * D : seg + sub * D;
+          const int64_t g = stage0 >= 0 ? static_cast<int64_t>(stage0) + slot : static_cast<int64_t>(n);
+          return n >= 0 ? base + (g * kGroup + sub) * D : seg + sub * D;
         }, part);
       } else {
         tile_copy_rows_part<D, GT>(smem[buf][grp][which], gwave, lane,
@@ -681,11 +700,11 @@ __global__ __launch_bounds__(kWave) void attn_bwd_dq_f32_kernel(BwdParams p) {
     const int st = seg_t0 + tile - n_sink - n_hist_tiles;
     for (int kk = 0; kk < kTile; ++kk) {
       int64_t off;
-      if (is_sink) off = (static_cast<int64_t>(j) * p.hist_rows + tile * kTile + kk) * D;
-      else if (is_hist) off = hist_offset(p, sel_s, j, ht, kk, D);
+      if (is_sink) off = (static_cast<int64_t>(j) * p.sink_stride + tile * kTile + kk) * D;
+      else if (is_hist) off = hist_offset(p, sel_s, b, j, ht, kk, D);
       else off = static_cast<int64_t>(st * kTile + kk) * D;
-      const float* kb = is_sink || is_hist ? kh : ks_g;
-      const float* vb = is_sink || is_hist ? vh : vs_g;
+      const float* kb = is_sink ? static_cast<const float*>(p.k_sink) : is_hist ? kh : ks_g;
+      const float* vb = is_sink ? static_cast<const float*>(p.v_sink) : is_hist ? vh : vs_g;
       for (int e = a; e < D; e += kWave) {
         Kt[kk][e] = off >= 0 ? kb[off + e] : 0.f;
         Vt[kk][e] = off >= 0 ? vb[off + e] : 0.f;
@@ -855,7 +874,7 @@ hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, const void* o, const float* lse,
                            const void* d_o, void* dq, void* dk_seg, void* dv_seg, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, const StagedHistory* staged) {
   BwdParams p;
   p.q = q; p.k_hist = k_hist; p.v_hist = v_hist; p.k_seg = k_seg; p.v_seg = v_seg;
   p.sel = sel_groups; p.o = o; p.lse = lse; p.d_o = d_o;
@@ -866,6 +885,14 @@ hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist
   p.dkdv_part = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * row);
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads;
   p.seg_len = s.seg_len; p.hist_len = s.hist_len; p.hist_rows = hist_rows(s); p.k_g = s.top_k_groups;
+  p.staged = 0;
+  p.k_sink = k_hist; p.v_sink = v_hist; p.sink_stride = hist_rows(s);
+  if (staged) {
+    p.staged = 1;
+    p.k_hist = staged->k_rows; p.v_hist = staged->v_rows;
+    p.hist_rows = static_cast<int64_t>(s.top_k_groups) * kGroup;
+    p.k_sink = staged->k_sink; p.v_sink = staged->v_sink; p.sink_stride = staged->sink_stride;
+  }
   p.n_sink_tiles = sink_chunks(s);
   p.window = local_window(s);
   p.scale = s.softmax_scale;

@@ -123,12 +123,18 @@ hga_status host_to_device_ptr(const void* host, const void** dev, const char* na
   return HGA_OK;
 }
 
-// Staging for the pinned-host tier: 2 buffers x kPhaseBlocks blocks, K and V.
+// The pinned-host tier gathers routed groups in phases of kPhaseBlocks query
+// blocks, each into its own region of the staging buffers.
 constexpr int kPhaseBlocks = 4;
 
-size_t staging_bytes_per_buffer(const hga_shape& s) {
-  return static_cast<size_t>(kPhaseBlocks) * s.n_kv_heads * s.top_k_groups * hga::kGroup *
-         s.head_dim * elem_bytes(s);
+// Routed rows of one query block, one tensor (K or V): [n_kv][k_g*8][d].
+size_t block_rows_bytes(const hga_shape& s) {
+  return static_cast<size_t>(s.n_kv_heads) * s.top_k_groups * hga::kGroup * s.head_dim * elem_bytes(s);
+}
+
+// Routed rows of every query block, one tensor (K or V): [n_blocks][n_kv][k_g*8][d].
+size_t routed_rows_bytes(const hga_shape& s) {
+  return static_cast<size_t>(s.seg_len / hga::kBlockQ) * block_rows_bytes(s);
 }
 
 // Sink rows staged once per call for the pinned-host tier: [n_kv][sink*64][D].
@@ -136,10 +142,35 @@ size_t sink_bytes(const hga_shape& s) {
   return static_cast<size_t>(s.n_kv_heads) * hga::sink_chunks(s) * hga::kChunk * s.head_dim * elem_bytes(s);
 }
 
+// Forward workspace with pinned-host history: K rows, V rows (every block's
+// routed groups), K sink rows, V sink rows. After the call it still holds
+// them, which hga_attn_bwd_staged reads.
+struct FwdStaging {
+  char* k_rows;
+  char* v_rows;
+  char* k_sink;
+  char* v_sink;
+};
+
+FwdStaging fwd_staging(const hga_shape& s, void* ws) {
+  char* base = static_cast<char*>(ws);
+  const size_t rows = align256(routed_rows_bytes(s));
+  return {base, base + rows, base + 2 * rows, base + 2 * rows + align256(sink_bytes(s))};
+}
+
 size_t fwd_workspace_bytes(const hga_shape& s) {
   if (s.hist_loc != HGA_HIST_HOST_PINNED) return 0;
-  // {K, V} x 2 gather buffers, then the K and V sink rows
-  return 4 * align256(staging_bytes_per_buffer(s)) + 2 * align256(sink_bytes(s));
+  return 2 * align256(routed_rows_bytes(s)) + 2 * align256(sink_bytes(s));
+}
+
+bool bwd_stages_history(const hga_shape& s) { return s.hist_loc == HGA_HIST_HOST_PINNED && s.hist_len > 0; }
+
+// The kernels' workspace, then (history in host memory) the K and V routed
+// rows of every block and the K and V sink rows.
+size_t bwd_total_workspace_bytes(const hga_shape& s) {
+  const size_t base = align256(hga::bwd_workspace_bytes(s));
+  if (!bwd_stages_history(s)) return base;
+  return base + 2 * align256(routed_rows_bytes(s)) + 2 * align256(sink_bytes(s));
 }
 
 // The pinned-host tier's side stream and events, one set per device. A call
@@ -151,7 +182,6 @@ struct SideResources {
   hipStream_t side = nullptr;
   hipEvent_t start = nullptr;
   hipEvent_t gathered[2] = {nullptr, nullptr};
-  hipEvent_t consumed[2] = {nullptr, nullptr};
 };
 
 std::mutex g_side_mu;
@@ -165,7 +195,7 @@ hga_status side_resources(SideResources** out) {
   auto it = g_side.find(dev);
   if (it == g_side.end()) {
     std::unique_ptr<SideResources> r(new SideResources);
-    hipEvent_t* evs[5] = {&r->start, &r->gathered[0], &r->gathered[1], &r->consumed[0], &r->consumed[1]};
+    hipEvent_t* evs[3] = {&r->start, &r->gathered[0], &r->gathered[1]};
     // on a failed creation, release what was created before reporting it
     auto release = [&]() {
       for (hipEvent_t* ev : evs)
@@ -252,7 +282,7 @@ size_t hga_workspace_size(const hga_shape* shape, int32_t op) {
     case HGA_OP_ROUTE: return hga::route_workspace_bytes(*shape);
     case HGA_OP_ROUTE_CACHED: return hga::route_cached_workspace_bytes(*shape);
     case HGA_OP_ATTN_FWD: return fwd_workspace_bytes(*shape);
-    case HGA_OP_ATTN_BWD: return hga::bwd_workspace_bytes(*shape);
+    case HGA_OP_ATTN_BWD: return bwd_total_workspace_bytes(*shape);
   }
   return 0;
 }
@@ -484,8 +514,10 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   }
 
   // Pinned-host history: gather phase p (kPhaseBlocks query blocks) over the
-  // host link on the side stream into staging buffer p % 2, while the main
-  // stream runs attention on phase p-1 from the other buffer.
+  // host link on the side stream into its own region of the staging buffers,
+  // while the main stream runs attention on phase p-1. The regions do not
+  // overlap, so no gather waits for an attention phase, and after the call the
+  // workspace holds every block's routed rows (read by hga_attn_bwd_staged).
   const size_t need = fwd_workspace_bytes(s);
   if (!ws || ws_bytes < need)
     return fail(HGA_ERR_WORKSPACE, "attn_fwd (pinned-host history) needs %zu workspace bytes, got %zu",
@@ -499,13 +531,11 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
   SideResources* r = nullptr;
   HGA_TRY(side_resources(&r));
   std::lock_guard<std::mutex> call_lock(r->mu);
-  const size_t buf = align256(staging_bytes_per_buffer(s));
-  char* base = static_cast<char*>(ws);
-  void* kbuf[2] = {base, base + buf};
-  void* vbuf[2] = {base + 2 * buf, base + 3 * buf};
+  const FwdStaging stg = fwd_staging(s, ws);
+  const size_t block_bytes = block_rows_bytes(s);
   const int n_sink_rows = hga::sink_chunks(s) * hga::kChunk;
-  void* ksink = base + 4 * buf;
-  void* vsink = base + 4 * buf + align256(sink_bytes(s));
+  void* ksink = stg.k_sink;
+  void* vsink = stg.v_sink;
   hipError_t e;
   // the side stream must see everything already enqueued on `stream` (sel_groups)
   if ((e = hipEventRecord(r->start, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -530,20 +560,19 @@ hga_status hga_attn_fwd(const hga_shape* shape, const void* q, const void* k_his
     const int b0 = ph * kPhaseBlocks;
     const int b1 = b0 + kPhaseBlocks < n_blocks ? b0 + kPhaseBlocks : n_blocks;
     const int x = ph % 2;
-    if (ph >= 2 && (e = hipStreamWaitEvent(r->side, r->consumed[x], 0)) != hipSuccess)
-      return hip_fail(e, "hipStreamWaitEvent");
+    void* kbuf = stg.k_rows + b0 * block_bytes;   // phase regions: blocks b0 .. b1-1
+    void* vbuf = stg.v_rows + b0 * block_bytes;
     const bool first = ph == 0, last = ph == n_phases - 1;
-    if ((e = hga::launch_gather(s, kd, vd, sel_groups, kbuf[x], vbuf[x], b0, b1, r->side,
+    if ((e = hga::launch_gather(s, kd, vd, sel_groups, kbuf, vbuf, b0, b1, r->side,
                                 first ? hga::timer_event(HGA_KERNEL_GATHER, 0) : nullptr,
                                 last ? hga::timer_event(HGA_KERNEL_GATHER, 1) : nullptr)) != hipSuccess)
       return hip_fail(e, "gather launch");
     if ((e = hipEventRecord(r->gathered[x], r->side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(st, r->gathered[x], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-    if ((e = hga::launch_attn_fwd(s, q, kd, vd, k_seg, v_seg, sel_groups, o, lse, kbuf[x], vbuf[x],
+    if ((e = hga::launch_attn_fwd(s, q, kd, vd, k_seg, v_seg, sel_groups, o, lse, kbuf, vbuf,
                                   ksink, vsink, n_sink_rows, b0, b1, st, first ? hga::timer_event(HGA_KERNEL_ATTN_FWD, 0) : nullptr,
                                   last ? hga::timer_event(HGA_KERNEL_ATTN_FWD, 1) : nullptr)) != hipSuccess)
       return hip_fail(e, "attn_fwd launch");
-    if ((e = hipEventRecord(r->consumed[x], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   return ok();
 }
@@ -555,18 +584,99 @@ hga_status hga_attn_bwd(const hga_shape* shape, const void* q, const void* k_his
                         void* stream) {
   HGA_TRY(check_shape(shape));
   const hga_shape& s = *shape;
-  if (s.hist_loc != HGA_HIST_DEVICE)
-    return fail(HGA_ERR_UNSUPPORTED, "attn_bwd needs device-resident history (hist_loc = HGA_HIST_DEVICE)");
   HGA_REQUIRE(q && k_seg && v_seg && sel_groups && o && lse && d_o && dq && dk_seg && dv_seg,
               "q, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk_seg and dv_seg must be non-NULL");
   HGA_REQUIRE(s.hist_len == 0 || (k_hist && v_hist), "k_hist and v_hist must be non-NULL");
-  const size_t need = hga::bwd_workspace_bytes(s);
+  const size_t need = bwd_total_workspace_bytes(s);
   if (!ws || ws_bytes < need)
     return fail(HGA_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (reinterpret_cast<uintptr_t>(ws) % 256)
     return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const hipError_t e = hga::launch_attn_bwd(s, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, d_o,
-                                            dq, dk_seg, dv_seg, ws, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!bwd_stages_history(s)) {
+    e = hga::launch_attn_bwd(s, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk_seg,
+                             dv_seg, ws, st, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+    return ok();
+  }
+
+  // History in page-locked host memory: only dQ reads it (the history is
+  // detached, so dK/dV cover segment keys only). Bring every block's routed
+  // groups and the sink rows into the workspace over the host link, in
+  // stream order, then run the kernels on those copies.
+  const void* kd = nullptr;
+  const void* vd = nullptr;
+  HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
+  HGA_TRY(host_to_device_ptr(v_hist, &vd, "v_hist"));
+  char* base = static_cast<char*>(ws) + align256(hga::bwd_workspace_bytes(s));
+  const size_t rows = align256(routed_rows_bytes(s));
+  hga::StagedHistory sh;
+  sh.k_rows = base;
+  sh.v_rows = base + rows;
+  sh.k_sink = base + 2 * rows;
+  sh.v_sink = base + 2 * rows + align256(sink_bytes(s));
+  const int n_sink_rows = hga::sink_chunks(s) * hga::kChunk;
+  sh.sink_stride = n_sink_rows;
+  if ((e = hga::launch_gather(s, kd, vd, sel_groups, const_cast<void*>(sh.k_rows), const_cast<void*>(sh.v_rows),
+                              0, s.seg_len / hga::kBlockQ, st, hga::timer_event(HGA_KERNEL_GATHER, 0),
+                              hga::timer_event(HGA_KERNEL_GATHER, 1))) != hipSuccess)
+    return hip_fail(e, "gather launch");
+  if (n_sink_rows > 0) {
+    const size_t row = static_cast<size_t>(s.head_dim) * elem_bytes(s);
+    const size_t pitch = static_cast<size_t>(hga::hist_rows(s)) * row;
+    if ((e = hipMemcpy2DAsync(const_cast<void*>(sh.k_sink), n_sink_rows * row, k_hist, pitch, n_sink_rows * row,
+                              s.n_kv_heads, hipMemcpyHostToDevice, st)) != hipSuccess)
+      return hip_fail(e, "sink copy");
+    if ((e = hipMemcpy2DAsync(const_cast<void*>(sh.v_sink), n_sink_rows * row, v_hist, pitch, n_sink_rows * row,
+                              s.n_kv_heads, hipMemcpyHostToDevice, st)) != hipSuccess)
+      return hip_fail(e, "sink copy");
+  }
+  e = hga::launch_attn_bwd(s, q, sh.k_rows, sh.v_rows, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk_seg,
+                           dv_seg, ws, st, &sh);
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  return ok();
+}
+
+hga_status hga_attn_bwd_staged(const hga_shape* shape, const void* q, const void* fwd_ws,
+                               size_t fwd_ws_bytes, const void* k_seg, const void* v_seg,
+                               const int32_t* sel_groups, const void* o, const float* lse,
+                               const void* d_o, void* dq, void* dk_seg, void* dv_seg, void* ws,
+                               size_t ws_bytes, void* stream) {
+  HGA_TRY(check_shape(shape));
+  const hga_shape& s = *shape;
+  if (s.hist_loc != HGA_HIST_HOST_PINNED)
+    return fail(HGA_ERR_INVALID_ARG, "attn_bwd_staged reads the staging of a pinned-host forward "
+                                     "(hist_loc = HGA_HIST_HOST_PINNED)");
+  HGA_REQUIRE(q && k_seg && v_seg && sel_groups && o && lse && d_o && dq && dk_seg && dv_seg,
+              "q, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk_seg and dv_seg must be non-NULL");
+  const size_t need_fwd = fwd_workspace_bytes(s);
+  if (!fwd_ws || fwd_ws_bytes < need_fwd)
+    return fail(HGA_ERR_WORKSPACE, "attn_bwd_staged needs the forward's %zu workspace bytes, got %zu", need_fwd,
+                fwd_ws ? fwd_ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(fwd_ws) % 256)
+    return fail(HGA_ERR_WORKSPACE, "the forward's workspace must be 256-byte aligned");
+  const size_t need = align256(hga::bwd_workspace_bytes(s));
+  if (!ws || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "attn_bwd_staged needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (s.hist_len == 0) {  // no history: the forward staged nothing and nothing is read
+    e = hga::launch_attn_bwd(s, q, nullptr, nullptr, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk_seg, dv_seg,
+                             ws, st, nullptr);
+  } else {
+    const FwdStaging stg = fwd_staging(s, const_cast<void*>(fwd_ws));
+    hga::StagedHistory sh;
+    sh.k_rows = stg.k_rows;
+    sh.v_rows = stg.v_rows;
+    sh.k_sink = stg.k_sink;
+    sh.v_sink = stg.v_sink;
+    sh.sink_stride = hga::sink_chunks(s) * hga::kChunk;
+    e = hga::launch_attn_bwd(s, q, sh.k_rows, sh.v_rows, k_seg, v_seg, sel_groups, o, lse, d_o, dq, dk_seg,
+                             dv_seg, ws, st, &sh);
+  }
   if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
   return ok();
 }

@@ -182,10 +182,22 @@ hipError_t launch_attn_fwd(const hga_shape& s, const void* q, const void* k_hist
                            const void* v_sink, int64_t sink_stride, int32_t block_begin,
                            int32_t block_end, hipStream_t stream, hipEvent_t ev_start,
                            hipEvent_t ev_stop);
+// Device copies of the history rows the backward reads, for history kept in
+// host memory: every block's routed groups, [n_blocks][n_kv][top_k_groups*8]
+// [head_dim] (the layout launch_gather writes for blocks 0..n_blocks), and the
+// sink rows, [n_kv][sink_stride][head_dim].
+struct StagedHistory {
+  const void* k_rows;
+  const void* v_rows;
+  const void* k_sink;
+  const void* v_sink;
+  int64_t sink_stride;
+};
+// staged == nullptr: k_hist / v_hist are the device-resident history.
 hipError_t launch_attn_bwd(const hga_shape& s, const void* q, const void* k_hist,
                            const void* v_hist, const void* k_seg, const void* v_seg,
                            const int32_t* sel_groups, const void* o, const float* lse,
                            const void* d_o, void* dq, void* dk_seg, void* dv_seg, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, const StagedHistory* staged);
 
 }  // namespace hga

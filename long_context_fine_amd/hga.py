@@ -24,7 +24,7 @@ EXPORTS = ("hga_build_summaries", "hga_route", "hga_attn_fwd", "hga_attn_bwd",
            "hga_gather_groups", "hga_workspace_size", "hga_status_string",
            "hga_last_error", "hga_abi_version", "hga_set_kernel_events",
            "hga_gcache_bytes", "hga_gcache_reset", "hga_route_cached",
-           "hga_decode_workspace_size", "hga_decode", "hga_route_noalloc")
+           "hga_decode_workspace_size", "hga_decode", "hga_route_noalloc", "hga_attn_bwd_staged")
 
 KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv", "gcache", "decode")
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "hga_route_noalloc": [SP, P, P, P, P, P, P],
         "hga_attn_fwd": [SP, P, P, P, P, P, P, P, P, P, SZ, P],
         "hga_attn_bwd": [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "hga_attn_bwd_staged": [SP, P, P, SZ, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "hga_gather_groups": [SP, P, P, P, P, P, P],
         "hga_gcache_reset": [SP, P, I32, P],
         "hga_route_cached": [SP, P, P, P, P, I32, P, P, P, P, SZ, P],
@@ -235,11 +236,33 @@ def hga_attn_bwd(shape: Shape, q, k_hist, v_hist, k_seg, v_seg, sel_groups, o, l
                  dq, dk_seg, dv_seg, ws=None, stream=None) -> None:
     H, kv, d, S, nq = shape.hist_rows, shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
     dt = shape.torch_dtype
+    host = shape.hist_loc == HGA_HIST_HOST_PINNED
     if ws is None:
         ws = alloc_workspace(shape, HGA_OP_ATTN_BWD, q.device)
     _check(lib().hga_attn_bwd(
         ctypes.byref(shape), _ptr(q, (nq, S, d), dt, "q"),
-        _ptr(k_hist, (kv, H, d), dt, "k_hist"), _ptr(v_hist, (kv, H, d), dt, "v_hist"),
+        _ptr(k_hist, (kv, H, d), dt, "k_hist", not host),
+        _ptr(v_hist, (kv, H, d), dt, "v_hist", not host),
+        _ptr(k_seg, (kv, S, d), dt, "k_seg"), _ptr(v_seg, (kv, S, d), dt, "v_seg"),
+        _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
+        _ptr(o, (nq, S, d), dt, "o"), _ptr(lse, (nq, S), torch.float32, "lse"),
+        _ptr(d_o, (nq, S, d), dt, "d_o"), _ptr(dq, (nq, S, d), dt, "dq"),
+        _ptr(dk_seg, (kv, S, d), dt, "dk_seg"), _ptr(dv_seg, (kv, S, d), dt, "dv_seg"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hga_attn_bwd_staged(shape: Shape, q, fwd_ws, k_seg, v_seg, sel_groups, o, lse, d_o,
+                        dq, dk_seg, dv_seg, ws=None, stream=None) -> None:
+    """hga_attn_bwd for pinned-host history, reading the routed rows that the
+    forward left in its workspace `fwd_ws` (same shape and selections)."""
+    kv, d, S, nq = shape.n_kv_heads, shape.head_dim, shape.seg_len, shape.n_q_heads
+    dt = shape.torch_dtype
+    if ws is None:
+        ws = alloc_workspace(shape, HGA_OP_ATTN_BWD, q.device)
+    _check(lib().hga_attn_bwd_staged(
+        ctypes.byref(shape), _ptr(q, (nq, S, d), dt, "q"),
+        _ptr(fwd_ws, None, None, "fwd_ws"),
+        0 if fwd_ws is None else fwd_ws.numel() * fwd_ws.element_size(),
         _ptr(k_seg, (kv, S, d), dt, "k_seg"), _ptr(v_seg, (kv, S, d), dt, "v_seg"),
         _ptr(sel_groups, (shape.n_blocks, kv, shape.top_k_groups), torch.int32, "sel_groups"),
         _ptr(o, (nq, S, d), dt, "o"), _ptr(lse, (nq, S), torch.float32, "lse"),

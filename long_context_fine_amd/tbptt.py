@@ -25,8 +25,10 @@ summaries in [n_kv][max_hist/64][d] / [n_kv][max_hist/8][d]; the library reads
 them through `hist_stride`, so the history grows in place without repacking.
 Every computation runs in the library's kernels; this module only allocates,
 copies segments into the history and orders the calls. With history in host
-memory the forward gathers routed groups over the host link; the backward
-needs the history on the device and raises otherwise.
+memory the forward gathers routed groups over the host link into its
+workspace, and the backward reads them there (`hga_attn_bwd_staged`), so each
+segment moves its routed groups over the link once. `backward` must therefore
+follow the `forward` of the same segment.
 """
 from __future__ import annotations
 
@@ -76,8 +78,10 @@ class LayerHistory:
         self.ws_route = hga.alloc_workspace(
             full, hga.HGA_OP_ROUTE_CACHED if group_cache_slots else hga.HGA_OP_ROUTE, self.device)
         self.ws_fwd = hga.alloc_workspace(full, hga.HGA_OP_ATTN_FWD, self.device)
-        self.ws_bwd = None if hist_on_host else hga.alloc_workspace(full, hga.HGA_OP_ATTN_BWD,
-                                                                     self.device)
+        # the backward's own workspace (with host history it reads the routed
+        # rows from ws_fwd, so it needs no staging of its own)
+        self.ws_bwd = hga.alloc_workspace(self.shape(max_hist, hist_on_host=False), hga.HGA_OP_ATTN_BWD,
+                                          self.device)
 
     def shape(self, hist_len: int | None = None, hist_on_host: bool | None = None) -> hga.Shape:
         return hga.make_shape(self.n_q, self.n_kv, self.d,
@@ -107,11 +111,15 @@ class LayerHistory:
     def backward(self, q, k_seg, v_seg, o, lse, d_o):
         """Gradients of sum(o * d_o) for the segment: (dq, dk_seg, dv_seg); the
         history is detached and receives none."""
-        if self.on_host:
-            raise NotImplementedError("the backward reads the history from device memory")
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k_seg), torch.empty_like(v_seg)
-        hga.hga_attn_bwd(self.shape(), q, self.k_hist, self.v_hist, k_seg, v_seg, self.sel_groups,
-                         o, lse, d_o, dq, dk, dv, self.ws_bwd)
+        if self.on_host:
+            # the forward of this segment left every block's routed rows in
+            # its workspace: no second trip over the host link
+            hga.hga_attn_bwd_staged(self.shape(), q, self.ws_fwd, k_seg, v_seg, self.sel_groups,
+                                    o, lse, d_o, dq, dk, dv, self.ws_bwd)
+        else:
+            hga.hga_attn_bwd(self.shape(), q, self.k_hist, self.v_hist, k_seg, v_seg, self.sel_groups,
+                             o, lse, d_o, dq, dk, dv, self.ws_bwd)
         return dq, dk, dv
 
     def close_segment(self, k_seg, v_seg) -> None:

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.hga_abi_version() == 2
+    assert L.hga_abi_version() == 3
     assert L.hga_status_string(0) == b"HGA_OK"
     assert L.hga_status_string(3) == b"HGA_ERR_WORKSPACE"
     assert L.hga_status_string(99) == b"HGA_ERR_UNKNOWN"
@@ -125,16 +125,39 @@ def test_workspace_sizes_and_undersized_workspace(L):
     assert st == hga.HGA_ERR_WORKSPACE
     host = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED)
     n_fwd = L.hga_workspace_size(ctypes.byref(host), hga.HGA_OP_ATTN_FWD)
-    assert n_fwd == 4 * (4 * 8 * 32 * 8 * 128 * 2)        # {K,V} x 2 buffers x 4 blocks
+    assert n_fwd == 2 * (32 * 8 * 32 * 8 * 128 * 2)       # {K,V} rows of all 32 blocks
     st = L.hga_attn_fwd(ctypes.byref(host), *([FAKE] * 8), FAKE, n_fwd - 1, None)
     assert st == hga.HGA_ERR_WORKSPACE
-    assert L.hga_attn_bwd(ctypes.byref(host), *([FAKE] * 13), 1 << 30, None) == hga.HGA_ERR_UNSUPPORTED
+    # backward over host history: + {K, V} routed rows of all 32 blocks,
+    # [32][8][32*8][128] bf16 each, copied over the host link before dQ
+    n_bwd_dev = L.hga_workspace_size(ctypes.byref(s), hga.HGA_OP_ATTN_BWD)
+    n_bwd_host = L.hga_workspace_size(ctypes.byref(host), hga.HGA_OP_ATTN_BWD)
+    assert n_bwd_host == n_bwd_dev + 2 * (32 * 8 * 256 * 128 * 2)
+    st = L.hga_attn_bwd(ctypes.byref(host), *([FAKE] * 13), n_bwd_host - 1, None)
+    assert st == hga.HGA_ERR_WORKSPACE
+    # the staged backward reads the forward's workspace: it needs a pinned-host
+    # shape, the forward's full workspace and only the kernels' own workspace
+    staged = lambda sh, fwd_bytes, bwd_bytes: L.hga_attn_bwd_staged(  # noqa: E731
+        ctypes.byref(sh), FAKE, FAKE, fwd_bytes, *([FAKE] * 9), FAKE, bwd_bytes, None)
+    assert staged(s, n_fwd, n_bwd_dev) == hga.HGA_ERR_INVALID_ARG          # device history
+    assert staged(host, n_fwd - 1, n_bwd_dev) == hga.HGA_ERR_WORKSPACE
+    assert staged(host, n_fwd, n_bwd_dev - 1) == hga.HGA_ERR_WORKSPACE
+    assert L.hga_attn_bwd_staged(ctypes.byref(host), FAKE, None, n_fwd, *([FAKE] * 9), FAKE, n_bwd_dev,
+                                 None) == hga.HGA_ERR_WORKSPACE
+    assert L.hga_attn_bwd_staged(ctypes.byref(host), FAKE, FAKE + 8, n_fwd, *([FAKE] * 9), FAKE, n_bwd_dev,
+                                 None) == hga.HGA_ERR_WORKSPACE            # misaligned
+    assert L.hga_attn_bwd_staged(ctypes.byref(host), FAKE, FAKE, n_fwd, *([FAKE] * 8), None, FAKE, n_bwd_dev,
+                                 None) == hga.HGA_ERR_INVALID_ARG          # dv_seg NULL
     # sink rows staged per call: + {K, V} x [8][2*64][128] bf16; the sink is
     # clamped to the history (224 chunks)
     sink = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED, n_sink_chunks=2, local_window=1024)
     assert L.hga_workspace_size(ctypes.byref(sink), hga.HGA_OP_ATTN_FWD) == n_fwd + 2 * (8 * 128 * 128 * 2)
     huge = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED, n_sink_chunks=1000)
     assert L.hga_workspace_size(ctypes.byref(huge), hga.HGA_OP_ATTN_FWD) == n_fwd + 2 * (8 * 14336 * 128 * 2)
+    assert L.hga_workspace_size(ctypes.byref(sink), hga.HGA_OP_ATTN_BWD) == n_bwd_host + 2 * (8 * 128 * 128 * 2)
+    # no history: nothing to copy
+    empty = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED, hist_len=0)
+    assert L.hga_workspace_size(ctypes.byref(empty), hga.HGA_OP_ATTN_BWD) == n_bwd_dev
     # a device-resident sink or a window needs no workspace of its own
     dev = _shape(n_sink_chunks=4, local_window=512)
     for op in (hga.HGA_OP_ROUTE, hga.HGA_OP_ATTN_FWD, hga.HGA_OP_ATTN_BWD):

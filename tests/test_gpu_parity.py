@@ -339,7 +339,10 @@ def test_qwen3_8b_16k_forward():
 
 
 def test_qwen3_8b_16k_forward_backward():
-    run_case(synth.WORKLOADS["qwen3_8b_16k_fwdbwd"], 1, check_bwd=True)
+    r = run_case(synth.WORKLOADS["qwen3_8b_16k_fwdbwd"], 1, check_bwd=True)
+    # the backward with the history in page-locked host memory (all routed
+    # groups copied over the host link first) is bit-identical
+    _pinned_host_backward_matches(synth.WORKLOADS["qwen3_8b_16k_fwdbwd"], r)
 
 
 def test_qwen3_8b_16k_forward_backward_with_sink_and_window():
@@ -369,31 +372,64 @@ def test_qwen3_8b_131k_forward_and_pinned_host_tier():
     assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
 
 
+def _pinned_copy(t, dtype):
+    h = torch.empty(t.shape, dtype=dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+def _pinned_host_backward_matches(w, r):
+    """With the history in page-locked host memory, both backwards give the
+    device-history backward of run_case `r` bit for bit: hga_attn_bwd, which
+    copies the routed rows over the host link itself, and hga_attn_bwd_staged,
+    which reads the rows the forward left in its workspace."""
+    sh = _shape(w.replace(hist_on_host=True))
+    kh = _pinned_copy(r["inp"]["k_hist"], w.torch_dtype)
+    vh = _pinned_copy(r["inp"]["v_hist"], w.torch_dtype)
+    g = r["g"]
+    _say(f"[case] {w.name}: backward with history in pinned host memory")
+    ws_f = hga.alloc_workspace(sh, hga.HGA_OP_ATTN_FWD, g["q"].device)
+    o2, lse2 = hga.attn_fwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"], ws_f)
+    dq2, dk2, dv2 = hga.attn_bwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"], r["o"], r["lse"],
+                                 g["d_o"])
+    torch.cuda.synchronize()
+    assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
+    assert torch.equal(dq2, r["dq"]) and torch.equal(dk2, r["dk"]) and torch.equal(dv2, r["dv"])
+    _say(f"[case] {w.name}: backward from the forward's staged rows")
+    dq3, dk3, dv3 = torch.empty_like(dq2), torch.empty_like(dk2), torch.empty_like(dv2)
+    hga.hga_attn_bwd_staged(sh, g["q"], ws_f, g["k_seg"], g["v_seg"], r["sel_g"], o2, lse2, g["d_o"],
+                            dq3, dk3, dv3)
+    torch.cuda.synchronize()
+    assert torch.equal(dq3, r["dq"]) and torch.equal(dk3, r["dk"]) and torch.equal(dv3, r["dv"])
+
+
 HOST_TIER = [
     # sink rows are staged from host memory once per call; routed groups are
     # gathered per phase (6 query blocks: two phases, the second partial)
-    _w("bf16_host_sink2_w96", 8, 2, 128, 1536, 384, 5, 13, "bf16", bwd=False, sink=2, window=96),
-    _w("bf16_host_d64", 8, 2, 64, 1024, 320, 4, 16, "bf16", bwd=False),   # d = 64, 5 blocks
-    _w("f32_host_d64", 4, 2, 64, 512, 256, 3, 10, "f32", bwd=False),      # fp32 rows over the link
+    _w("bf16_host_sink2_w96", 8, 2, 128, 1536, 384, 5, 13, "bf16", sink=2, window=96),
+    _w("bf16_host_d64", 8, 2, 64, 1024, 320, 4, 16, "bf16"),   # d = 64, 5 blocks
+    _w("f32_host_d64", 4, 2, 64, 512, 256, 3, 10, "f32"),      # fp32 rows over the link
 ]
 
 
 @pytest.mark.parametrize("w", HOST_TIER, ids=[w.name for w in HOST_TIER])
 def test_pinned_host_tier_is_bit_identical(w):
-    r = run_case(w, 4, check_bwd=False)
+    """Forward (and backward, for workloads that have one) with the history in
+    page-locked host memory: bit-identical to the oracle-checked HBM path."""
+    r = run_case(w, 4, check_bwd=w.backward)
     sh = _shape(w.replace(hist_on_host=True))
-    kh = torch.empty(r["inp"]["k_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
-    vh = torch.empty(r["inp"]["v_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
-    kh.copy_(r["inp"]["k_hist"])
-    vh.copy_(r["inp"]["v_hist"])
+    kh = _pinned_copy(r["inp"]["k_hist"], w.torch_dtype)
+    vh = _pinned_copy(r["inp"]["v_hist"], w.torch_dtype)
     _say(f"[case] {w.name}: the same call with history in pinned host memory")
     g = r["g"]
     o2, lse2 = hga.attn_fwd(sh, g["q"], kh, vh, g["k_seg"], g["v_seg"], r["sel_g"])
     torch.cuda.synchronize()
     assert torch.equal(o2, r["o"]) and torch.equal(lse2, r["lse"])
+    if w.backward:
+        _pinned_host_backward_matches(w, r)
 
 
-RANDOM_HOST = [w.replace(backward=False) for w in _random_workloads(6, seed=20261205)]
+RANDOM_HOST = _random_workloads(6, seed=20261205)
 
 
 @pytest.mark.parametrize("w", RANDOM_HOST, ids=[w.name for w in RANDOM_HOST])

@@ -117,22 +117,29 @@ def test_group_summary_cache_gives_identical_segments():
     assert torch.equal(dev.group_sum.cpu(), cached.group_sum)
 
 
-def test_pinned_host_history_forward_is_bit_identical():
+@pytest.mark.parametrize("sink,window", [(0, 0), (1, 96)])
+def test_pinned_host_history_is_bit_identical(sink, window):
+    """Segment by segment, forward and backward with the history in
+    page-locked host memory equal the device-history driver bit for bit (which
+    the test above checks against the oracle)."""
     segs, _, _ = _sequence(6)
-    dev = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, top_k_chunks=K_C, top_k_groups=K_G)
-    host = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, top_k_chunks=K_C, top_k_groups=K_G,
-                              hist_on_host=True)
+    kw = dict(top_k_chunks=K_C, top_k_groups=K_G, n_sink_chunks=sink, local_window=window)
+    dev = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, **kw)
+    host = tbptt.LayerHistory(N_Q, N_KV, D, S, max_hist=4 * S, hist_on_host=True, **kw)
     for i, sg in enumerate(segs):
-        print(f"[case] tbptt pinned-host segment {i}", flush=True)
+        print(f"[case] tbptt pinned-host segment {i} sink {sink} window {window}", flush=True)
         g = {k: v.cuda() for k, v in sg.items()}
         o1, l1 = dev.forward(g["q"], g["k"], g["v"])
         o2, l2 = host.forward(g["q"], g["k"], g["v"])
         torch.cuda.synchronize()
         assert torch.equal(dev.sel_groups, host.sel_groups)
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        g1 = dev.backward(g["q"], g["k"], g["v"], o1, l1, g["d_o"])
+        g2 = host.backward(g["q"], g["k"], g["v"], o2, l2, g["d_o"])
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
         dev.close_segment(g["k"], g["v"])
         host.close_segment(g["k"], g["v"])
     torch.cuda.synchronize()
     assert torch.equal(dev.chunk_sum, host.chunk_sum) and torch.equal(dev.group_sum, host.group_sum)
-    with pytest.raises(NotImplementedError):
-        host.backward(g["q"], g["k"], g["v"], o2, l2, g["d_o"])
