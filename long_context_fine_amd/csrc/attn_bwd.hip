@@ -43,8 +43,9 @@ struct BwdParams {
   int64_t hist_rows;  // rows per KV head in k_hist / v_hist
   // Staged routed rows (history in host memory): k_hist / v_hist then point
   // at [n_blocks][n_kv][k_g*8][D] copies of each block's routed groups, with
-  // hist_rows = k_g*8, and the valid group in slot `slot` of block b is read
-  // as group b*n_kv*k_g + slot, which addresses exactly that copy.
+  // hist_rows = k_g*8, and the kernels keep group b*n_kv*k_g + slot in place
+  // of the valid group of slot `slot` of block b (see staged_group), which
+  // addresses exactly that copy.
   int staged;
   const void* k_sink;  // sink rows [n_kv][sink_stride][D] (the history itself when not staged)
   const void* v_sink;
@@ -56,19 +57,20 @@ struct BwdParams {
   float scale_log2;
 };
 
-// Group id whose rows hold valid group n of slot `slot` of block b: n itself,
-// or the block's staged copy.
-__device__ __forceinline__ int64_t group_row(const BwdParams& p, int b, int slot, int n) {
-  return p.staged ? static_cast<int64_t>(b) * p.n_kv * p.k_g + slot : static_cast<int64_t>(n);
+// Group whose rows the kernels read for slot `slot` of block b: the validated
+// id (-1 for an empty slot), or with staged rows the block's copy of it.
+__device__ __forceinline__ int32_t staged_group(const BwdParams& p, int b, int slot, int32_t id) {
+  const int32_t n = valid_group(id, p.hist_len / kGroup);
+  return n >= 0 && p.staged ? b * p.n_kv * p.k_g + slot : n;
 }
 
-__device__ __forceinline__ int64_t hist_offset(const BwdParams& p, const int32_t* sel_s, int b, int j,
+__device__ __forceinline__ int64_t hist_offset(const BwdParams& p, const int32_t* sel_s, int j,
                                                int ht, int kk, int D) {
   const int slot = ht * 8 + kk / kGroup;
   if (slot >= p.k_g) return -1;
   const int n = sel_s[slot];
   if (n < 0) return -1;
-  return (static_cast<int64_t>(j) * p.hist_rows + group_row(p, b, slot, n) * kGroup + kk % kGroup) * D;
+  return (static_cast<int64_t>(j) * p.hist_rows + static_cast<int64_t>(n) * kGroup + kk % kGroup) * D;
 }
 
 // Dvec = rowsum(dO * O), fp32 accumulation (fp32 path; the bf16 dQ kernel
@@ -152,11 +154,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
   for (int half = 0; half < 2; ++half) {
     const int b = half == 0 ? b_hi : b_lo;
     if (half == 1 && b_lo >= b_hi) break;
-    // staged rows: slot s of this block is group stage0 + s
-    const int stage0 = p.staged ? b * p.n_kv * p.k_g : -1;
     const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
     __syncthreads();
-    for (int i = tid; i < p.k_g; i += NT) sel_s[i] = valid_group(sel_bj[i], p.hist_len / kGroup);
+    for (int i = tid; i < p.k_g; i += NT) sel_s[i] = staged_group(p, b, i, sel_bj[i]);
     __syncthreads();
     build_hist_tile_list(sel_s, p.k_g, hlist, &n_hist_s);
     __syncthreads();
@@ -188,8 +188,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_bwd_dq_bf16_kernel(BwdParams p
           const uint32_t slot = static_cast<uint32_t>(ht) * 8u + (kq * RPI) / kGroup;
           const int n = slot < static_cast<uint32_t>(p.k_g) ? __builtin_amdgcn_readfirstlane(sel_s[slot]) : -1;
           const uint32_t sub = (kq * RPI) % kGroup;
-          const int64_t g = stage0 >= 0 ? static_cast<int64_t>(stage0) + slot : static_cast<int64_t>(n);
-          return n >= 0 ? base + (g * kGroup + sub) * D : seg + sub * D;
+          return n >= 0 ? base + (static_cast<int64_t>(n) * kGroup + sub) * D : seg + sub * D;
         }, part);
       } else {
         tile_copy_rows_part<D, GT>(smem[buf][grp][which], gwave, lane,
@@ -673,7 +672,7 @@ __global__ __launch_bounds__(kWave) void attn_bwd_dq_f32_kernel(BwdParams p) {
   const float* ks_g = static_cast<const float*>(p.k_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const float* vs_g = static_cast<const float*>(p.v_seg) + static_cast<int64_t>(j) * p.seg_len * D;
   const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
-  for (int i = a; i < p.k_g; i += kWave) sel_s[i] = valid_group(sel_bj[i], p.hist_len / kGroup);
+  for (int i = a; i < p.k_g; i += kWave) sel_s[i] = staged_group(p, b, i, sel_bj[i]);
   {
     const int64_t row0 = row - a;
     const float* qb = static_cast<const float*>(p.q) + row0 * D;
@@ -701,7 +700,7 @@ __global__ __launch_bounds__(kWave) void attn_bwd_dq_f32_kernel(BwdParams p) {
     for (int kk = 0; kk < kTile; ++kk) {
       int64_t off;
       if (is_sink) off = (static_cast<int64_t>(j) * p.sink_stride + tile * kTile + kk) * D;
-      else if (is_hist) off = hist_offset(p, sel_s, b, j, ht, kk, D);
+      else if (is_hist) off = hist_offset(p, sel_s, j, ht, kk, D);
       else off = static_cast<int64_t>(st * kTile + kk) * D;
       const float* kb = is_sink ? static_cast<const float*>(p.k_sink) : is_hist ? kh : ks_g;
       const float* vb = is_sink ? static_cast<const float*>(p.v_sink) : is_hist ? vh : vs_g;
