@@ -430,14 +430,25 @@ class HGAAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, shape, q, k_seg, v_seg, k_hist, v_hist, chunk_sum, group_sum):
         _, sel_g = route(shape, q, chunk_sum, group_sum)
-        o, lse = attn_fwd(shape, q, k_hist, v_hist, k_seg, v_seg, sel_g)
+        ws_f = None
+        if shape.hist_loc == HGA_HIST_HOST_PINNED and shape.hist_len > 0:
+            # kept for the backward: it holds the routed rows the forward
+            # brought over the host link
+            ws_f = alloc_workspace(shape, HGA_OP_ATTN_FWD, q.device)
+        o, lse = attn_fwd(shape, q, k_hist, v_hist, k_seg, v_seg, sel_g, ws_f)
         ctx.shape = shape
+        ctx.ws_f = ws_f
         ctx.save_for_backward(q, k_seg, v_seg, k_hist, v_hist, sel_g, o, lse)
         return o
 
     @staticmethod
     def backward(ctx, d_o):
         q, k_seg, v_seg, k_hist, v_hist, sel_g, o, lse = ctx.saved_tensors
-        dq, dk, dv = attn_bwd(ctx.shape, q, k_hist, v_hist, k_seg, v_seg, sel_g, o, lse,
-                              d_o.contiguous())
+        d_o = d_o.contiguous()
+        if ctx.ws_f is not None:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k_seg), torch.empty_like(v_seg)
+            hga_attn_bwd_staged(ctx.shape, q, ctx.ws_f, k_seg, v_seg, sel_g, o, lse, d_o, dq, dk, dv)
+            ctx.ws_f = None
+        else:
+            dq, dk, dv = attn_bwd(ctx.shape, q, k_hist, v_hist, k_seg, v_seg, sel_g, o, lse, d_o)
         return None, dq, dk, dv, None, None, None, None

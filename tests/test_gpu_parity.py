@@ -439,15 +439,25 @@ def test_pinned_host_tier_random_shapes(w):
     test_pinned_host_tier_is_bit_identical(w)
 
 
-def test_autograd_function_matches_explicit_calls():
+@pytest.mark.parametrize("on_host", [False, True], ids=["hbm", "pinned_host"])
+def test_autograd_function_matches_explicit_calls(on_host):
+    """The autograd op equals explicit calls on device-resident history bit for
+    bit, also with the history in pinned host memory (its backward then reads
+    the rows its forward staged)."""
     w = _w("bf16_autograd", 8, 2, 128, 1024, 128, 4, 16, "bf16")
-    inp = _dev(synth.make_inputs(w, 12, with_grad_out=True))
+    _say(f"[case] autograd op, history {'pinned host' if on_host else 'hbm'}")
+    host_in = synth.make_inputs(w, 12, with_grad_out=True)
+    inp = _dev(host_in)
     s = _shape(w)
     C, G = hga.summaries(s, inp["k_hist"])
     q = inp["q"].clone().requires_grad_(True)
     ks = inp["k_seg"].clone().requires_grad_(True)
     vs = inp["v_seg"].clone().requires_grad_(True)
-    o = hga.HGAAttention.apply(s, q, ks, vs, inp["k_hist"], inp["v_hist"], C, G)
+    if on_host:
+        kh, vh = _pinned_copy(host_in["k_hist"], w.torch_dtype), _pinned_copy(host_in["v_hist"], w.torch_dtype)
+        o = hga.HGAAttention.apply(_shape(w.replace(hist_on_host=True)), q, ks, vs, kh, vh, C, G)
+    else:
+        o = hga.HGAAttention.apply(s, q, ks, vs, inp["k_hist"], inp["v_hist"], C, G)
     o.backward(inp["d_o"])
     _, sg = hga.route(s, inp["q"], C, G)
     o_ref, lse = hga.attn_fwd(s, inp["q"], inp["k_hist"], inp["v_hist"], inp["k_seg"], inp["v_seg"], sg)
