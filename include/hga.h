@@ -332,8 +332,10 @@ hga_status hga_set_kernel_events(int32_t kernel, void* ev_start, void* ev_stop);
  * invalid or the op needs none. */
 size_t hga_workspace_size(const hga_shape* shape, int32_t op);
 
-/* Static string for a status code. */
-const char* hga_status_string(hga_status status);
+/* Static string for a status code (an hga_status value); any other value
+ * gives "HGA_ERR_UNKNOWN". Taken as a plain integer so that every value the
+ * caller passes is well-defined. */
+const char* hga_status_string(int32_t status);
 
 /* Detail of the last non-OK status returned on the calling thread ("" if
  * none). The pointer stays valid until the next call on that thread. */

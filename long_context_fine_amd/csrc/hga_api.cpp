@@ -260,7 +260,7 @@ hga_status hga_set_kernel_events(int32_t kernel, void* ev_start, void* ev_stop) 
 
 int32_t hga_abi_version(void) { return HGA_ABI_VERSION; }
 
-const char* hga_status_string(hga_status status) {
+const char* hga_status_string(int32_t status) {
   switch (status) {
     case HGA_OK: return "HGA_OK";
     case HGA_ERR_INVALID_ARG: return "HGA_ERR_INVALID_ARG";

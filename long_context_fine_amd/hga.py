@@ -97,7 +97,7 @@ def lib() -> ctypes.CDLL:
     L.hga_gcache_bytes.restype = SZ
     L.hga_decode_workspace_size.argtypes = [SP, I32, I32]
     L.hga_decode_workspace_size.restype = SZ
-    L.hga_status_string.argtypes = [ctypes.c_int]
+    L.hga_status_string.argtypes = [I32]
     L.hga_status_string.restype = ctypes.c_char_p
     L.hga_last_error.argtypes = []
     L.hga_last_error.restype = ctypes.c_char_p
