@@ -702,8 +702,11 @@ hipError_t launch_route_cached(const hga_shape& s, const void* q, const float* c
 int decode_route_parts(const hga_shape& s, int batch) {
   const int64_t rows = hist_rows(s) / kChunk;
   const int64_t wgs = static_cast<int64_t>(batch) * s.n_kv_heads;
-  if (wgs > 32 || rows < 2 * kThreads) return 1;
-  const int64_t want = (2 * kThreads + wgs - 1) / wgs;
+  if (wgs > 64 || rows < 2 * kThreads) return 1;
+  // up to 32 pairs: about two workgroups per CU; 33 to 64 pairs: about one per
+  // CU (four to seven parts). Fewer parts over more pairs measured slower
+  // than one workgroup per pair.
+  const int64_t want = wgs <= 32 ? (2 * kThreads + wgs - 1) / wgs : kThreads / wgs;
   int P = static_cast<int>(want < 8 ? want : 8);
   while (P > 1 && P * s.top_k_chunks >= kMaxTopKChunks * (kChunk / kGroup)) --P;
   if (P <= 1 || (rows + P - 1) / P > kLdsScores) return 1;

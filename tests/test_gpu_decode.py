@@ -121,7 +121,7 @@ def test_decode_lengths_are_clamped_to_the_buffers():
 
 
 # Small batches split the chunk scan of each (sequence, KV head) over several
-# workgroups (history capacity of 32,768+ tokens and fewer than 256
+# workgroups (history capacity of 32,768+ tokens and at most 64
 # (sequence, KV head) pairs): ragged histories from full to empty, some with
 # fewer chunks than parts, against the oracle.
 @pytest.mark.parametrize("n_new,sink,window", [(1, 0, 0), (2, 1, 40)])
@@ -131,10 +131,11 @@ def test_decode_split_route_ragged(n_new, sink, window):
 
 
 def test_decode_split_route_matches_unsplit():
-    # the same four sequences alone (32 (sequence, KV head) pairs: split
-    # route) and tiled to a batch of 32 (256 pairs: one workgroup each) give
-    # bit-identical selections; the attention splits the keys into pieces of
-    # 128 (small batch) or 256, so its outputs agree to rounding
+    # the same four sequences alone (32 (sequence, KV head) pairs: the chunk
+    # scan split in 8 parts), tiled to a batch of 8 (64 pairs: 4 parts) and to
+    # a batch of 32 (256 pairs: one workgroup each) give bit-identical
+    # selections; the attention splits the keys into pieces of 128 (small
+    # batch) or 256, so its outputs agree to rounding
     n_q, n_kv, d, P, T = 32, 8, 128, 32768, 256
     hist, tail = [32768, 26624, 4096, 64], [256, 33, 128, 1]
     w = synth.Workload("decode", n_q, n_kv, d, P, T, 16, 32, "bf16", 1.0 / math.sqrt(d))
@@ -153,8 +154,13 @@ def test_decode_split_route_matches_unsplit():
     o32, lse32, sc32, sg32 = hga.decode(s, rep(g["q"]), rep(g["k_hist"]), rep(g["v_hist"]), rep(C), rep(G),
                                         rep(g["k_tail"]), rep(g["v_tail"]), rep(g["hist_lens"]),
                                         rep(g["tail_lens"]))
+    rep2 = lambda x: x.repeat((2,) + (1,) * (x.dim() - 1))
+    o8, lse8, sc8, sg8 = hga.decode(s, rep2(g["q"]), rep2(g["k_hist"]), rep2(g["v_hist"]), rep2(C), rep2(G),
+                                    rep2(g["k_tail"]), rep2(g["v_tail"]), rep2(g["hist_lens"]),
+                                    rep2(g["tail_lens"]))
     torch.cuda.synchronize()
     assert torch.equal(sc32[:4], sc4) and torch.equal(sg32[:4], sg4)
+    assert torch.equal(sc32[:8], sc8) and torch.equal(sg32[:8], sg8)
     o_ref = o4.float()
     assert (o32[:4].float() - o_ref).abs().max() <= 1e-2 * o_ref.abs().max()
     assert (lse32[:4] - lse4).abs().max() <= 1e-5 * lse4.abs().max()
