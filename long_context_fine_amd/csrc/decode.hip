@@ -266,6 +266,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   constexpr int KT = 32;                        // keys per MFMA tile
   constexpr int TPW = KEYS / (NW * KT);     // tiles per wave
   constexpr int DPL = D / kWave;                // output dims per lane in P.V
+  // 16 query rows: P.V on MFMA from a V tile staged in LDS (128-key pieces
+  // keep the workgroup's LDS near 50 KiB); fewer rows: P.V on the VALU
+  constexpr bool kMfmaPV = QR > 8;
+  static_assert(!kMfmaPV || KEYS == 128, "the MFMA P.V path stages 128-key pieces");
+  constexpr int NO = kMfmaPV ? 1 : NW;          // partial-O slots the epilogue sums
   // rows padded by 4 floats: the 32 query rows' 16-byte score stores spread over the banks
   __shared__ __attribute__((aligned(16))) float s_lds[QR][KEYS + 4];
   __shared__ int32_t kinfo[KEYS];           // -1 plain, -2 masked, >= 0 open-segment position
@@ -273,7 +278,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   // row: resolved once in the score phase, so that the V loads do not wait
   // for another read of the routed group ids
   __shared__ int64_t koff[KEYS];
-  __shared__ float o_lds[NW][QR][D];
+  __shared__ float o_lds[NO][QR][D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kMfmaPV ? KEYS * D : 8];
   const int piece = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -339,6 +345,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
     const uint16_t* kp = (tail ? kt : kh) + off + hh * 8;
 #pragma unroll
     for (int ss = 0; ss < NKS; ++ss) ka[tt][ss] = *reinterpret_cast<const bf16x8*>(kp + ss * 16);
+  }
+  // 16 query rows: this lane's half of its key's V row (16-byte chunks
+  // 2i + hh), requested now so that the score MFMAs and the softmax hide its
+  // latency; it goes to the LDS tile after them. A key past the piece reads
+  // the finite filler row; its probability is zero.
+  constexpr int NVE = kMfmaPV ? D / 16 : 1;
+  bf16x8 vpre[NVE];
+  if constexpr (kMfmaPV) {
+    static_assert(TPW == 1, "one 32-key tile per wave");
+    const uint16_t* vp = kcode[0] < 0 ? vt + ~kcode[0] : vh + kcode[0];
+#pragma unroll
+    for (int i = 0; i < NVE; ++i) vpre[i] = *reinterpret_cast<const bf16x8*>(vp + (2 * i + hh) * 8);
   }
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
@@ -453,53 +471,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
           for (int e = 0; e < 8; ++e) o_lds[wave][rq][sub * 8 + e] = acc[rq][e];
     }
   } else {
-    // ---- P . V: each lane owns DPL dims; a wave takes a quarter of the keys --
-    float acc[QR][DPL];
-  #pragma unroll
-    for (int rq = 0; rq < QR; ++rq)
-  #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[rq][e] = 0.f;
-    constexpr int KPI = 16;                       // keys per pass: their row loads in flight together
-    const int kq0 = wave * (KEYS / NW);
-    for (int kk = kq0; kk < kq0 + KEYS / NW && kk < nk; kk += KPI) {
-      float vf[KPI][DPL];
-  #pragma unroll
-      for (int u = 0; u < KPI; ++u) {
-        const int64_t c = koff[kk + u];
-        const uint16_t* vp = (c < 0 ? vt + ~c : vh + c) + lane * DPL;
-        if (DPL == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
-          vf[u][0] = __uint_as_float(w << 16);
-          vf[u][DPL - 1] = __uint_as_float(w & 0xffff0000u);
-        } else {
-          vf[u][0] = bf16_to_f32(vp[0]);
+    // ---- P . V on MFMA: O^T = V^T . P^T in 32 x 32 x 16 tiles. The piece's V
+    // rows (requested in the score phase) go to a swizzled LDS tile; wave w
+    // owns output dims [32w, 32w + 32) over all keys. V^T comes from transposed
+    // LDS reads, whose contraction slots are keys k0 + 8*(i/4) + 4*hh + i%4;
+    // the P^T operand takes the same keys from this lane's score row (query
+    // row l32; rows R..31 are zero). P is rounded to bf16 for the MFMA, as in
+    // the training forward.
+    {
+      const uint32_t kk = static_cast<uint32_t>(wave * KT + l32);   // this lane's key
+#pragma unroll
+      for (int i = 0; i < NVE; ++i)
+        *reinterpret_cast<bf16x8*>(&v_lds[Swz<D>::off(kk, static_cast<uint32_t>((2 * i + hh) * 8))]) = vpre[i];
+    }
+    __syncthreads();
+    if (wave < D / 32) {
+      f32x16 acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+      const bool live = l32 < R;
+#pragma unroll
+      for (int k0 = 0; k0 < KEYS; k0 += 16) {
+        const bf16x8 a = lds_a_tr_swz<D>(v_lds, k0, wave * 32, lane);
+        uint4 bu = make_uint4(0, 0, 0, 0);
+        if (live) {
+          const float4 p0 = *reinterpret_cast<const float4*>(&s_lds[l32][k0 + 4 * hh]);
+          const float4 p1 = *reinterpret_cast<const float4*>(&s_lds[l32][k0 + 8 + 4 * hh]);
+          bu = make_uint4(cvt_pk_bf16(p0.x, p0.y), cvt_pk_bf16(p0.z, p0.w), cvt_pk_bf16(p1.x, p1.y),
+                          cvt_pk_bf16(p1.z, p1.w));
         }
+        acc = mfma32(a, __builtin_bit_cast(bf16x8, bu), acc);
       }
-  #pragma unroll
-      for (int rq = 0; rq < QR; ++rq) {
-        if (rq < R) {
-  #pragma unroll
-          for (int u4 = 0; u4 < KPI; u4 += 4) {
-            const float4 p4 = *reinterpret_cast<const float4*>(&s_lds[rq][kk + u4]);  // zero past nk
-  #pragma unroll
-            for (int e = 0; e < DPL; ++e)
-              acc[rq][e] += p4.x * vf[u4][e] + p4.y * vf[u4 + 1][e] + p4.z * vf[u4 + 2][e] + p4.w * vf[u4 + 3][e];
-          }
-        }
+      // acc[v]: O^T[dim 32*wave + 8*(v/4) + 4*hh + v%4][query row l32]
+      if (live) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o_lds[0][l32][wave * 32 + 8 * (v / 4) + 4 * hh + v % 4] = acc[v];
       }
     }
-  #pragma unroll
-    for (int rq = 0; rq < QR; ++rq)
-      if (rq < R)
-  #pragma unroll
-        for (int e = 0; e < DPL; ++e) o_lds[wave][rq][lane * DPL + e] = acc[rq][e];
   }
   __syncthreads();
   for (int x = t; x < R * D; x += kDecThreads) {
     const int rq = x / D, dd = x % D;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += o_lds[w][rq][dd];
+    for (int w = 0; w < NO; ++w) v += o_lds[w][rq][dd];
     const int64_t row = (static_cast<int64_t>(b) * p.n_q + j * p.r) * p.n_new + rq;
     p.part[(row * p.n_piece + piece) * D + dd] = v;
   }
@@ -533,20 +548,18 @@ hipError_t launch_td(const hga_shape& s, DecodeParams& p, int batch, hipStream_t
   const int R = p.r * p.n_new;
   hipEvent_t e0 = timer_event(HGA_KERNEL_DECODE, 0), e1 = timer_event(HGA_KERNEL_DECODE, 1);
   if constexpr (sizeof(T) == 2) {
-    if (p.piece_keys == 128) {
+    if (R > 8) {  // decode_piece_keys gives 128-key pieces here
+      hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 16, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+    } else if (p.piece_keys == 128) {
       if (R <= 4)
         hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 4, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
-      else if (R <= 8)
-        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
       else
-        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 16, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8, 128>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
     } else {
       if (R <= 4)
         hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 4, kDecKeys>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
-      else if (R <= 8)
-        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8, kDecKeys>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
       else
-        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 16, kDecKeys>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
+        hipExtLaunchKernelGGL((decode_attn_bf16_kernel<D, 8, kDecKeys>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
     }
   } else if (R <= 4)
     hipExtLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, st, e0, nullptr, 0, p);
@@ -571,21 +584,23 @@ int64_t decode_max_keys(const hga_shape& s) {
 }  // namespace
 
 // Keys per piece: kDecKeys, or 128 for bf16 when 256-key pieces would give
-// the attention launch fewer than 512 workgroups.
-int decode_piece_keys(const hga_shape& s, int batch) {
+// the attention launch fewer than 512 workgroups or the query rows per KV head
+// (r * n_new) exceed 8 (the MFMA P.V path stages 128-key V tiles).
+int decode_piece_keys(const hga_shape& s, int batch, int n_new) {
   if (s.dtype != HGA_BF16) return kDecKeys;
+  if ((s.n_q_heads / s.n_kv_heads) * n_new > 8) return 128;
   const int64_t wgs = static_cast<int64_t>(batch) * s.n_kv_heads * ((decode_max_keys(s) + kDecKeys - 1) / kDecKeys);
   return wgs < 512 ? 128 : kDecKeys;
 }
 
-int decode_pieces(const hga_shape& s, int batch) {
-  const int pk = decode_piece_keys(s, batch);
+int decode_pieces(const hga_shape& s, int batch, int n_new) {
+  const int pk = decode_piece_keys(s, batch, n_new);
   return static_cast<int>((decode_max_keys(s) + pk - 1) / pk);
 }
 
 size_t decode_attn_workspace_bytes(const hga_shape& s, int batch, int n_new) {
   const size_t rows = static_cast<size_t>(batch) * s.n_q_heads * n_new;
-  const size_t n = decode_pieces(s, batch);
+  const size_t n = decode_pieces(s, batch, n_new);
   return ((rows * n * s.head_dim * sizeof(float) + 255) & ~size_t(255)) + rows * n * 2 * sizeof(float);
 }
 
@@ -598,7 +613,7 @@ hipError_t launch_decode_attn(const hga_shape& s, int batch, int n_new, const vo
   p.sel = sel_groups; p.hist_lens = hist_lens; p.tail_lens = tail_lens; p.o = o; p.lse = lse;
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads; p.n_new = n_new;
   p.P = hist_rows(s); p.T = s.seg_len; p.k_g = s.top_k_groups; p.n_sink = s.n_sink_chunks;
-  p.window = local_window(s); p.n_piece = decode_pieces(s, batch); p.piece_keys = decode_piece_keys(s, batch);
+  p.window = local_window(s); p.n_piece = decode_pieces(s, batch, n_new); p.piece_keys = decode_piece_keys(s, batch, n_new);
   p.scale_log2 = s.softmax_scale * 1.4426950408889634f;
   const size_t rows = static_cast<size_t>(batch) * s.n_q_heads * n_new;
   p.part = static_cast<float*>(ws);
