@@ -173,6 +173,20 @@ def test_decode_qwen3_8b_131k():
                seed=6)
 
 
+def test_decode_qwen3_8b_131k_four_new_tokens():
+    # the same shapes with four new tokens: 16 query rows per KV head, whose
+    # P.V runs on MFMA over 128-key pieces
+    run_decode(32, 8, 128, 129024, 2048, 16, 32, "bf16", [129024, 64064], [2048, 1029], n_new=4,
+               seed=8)
+
+
+def test_decode_gqa8_two_new_tokens_with_sink_and_window():
+    # GQA ratio 8 x 2 new tokens: 16 query rows (MFMA P.V) at d = 128, with a
+    # sink and a window that cuts into the open segment
+    run_decode(16, 2, 128, 2048, 256, 6, 24, "bf16", [2048, 704, 64], [256, 31, 2], n_new=2, seed=9,
+               sink=2, window=100)
+
+
 def test_decode_retrieves_a_planted_needle():
     # retrieval: one history chunk of sequence 0, far back, gets keys aligned
     # with the new token's query; routing must select it and most attention
