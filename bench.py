@@ -51,6 +51,9 @@ def parse():
                     help="run the decode step instead: this many sequences of the workload's "
                          "history length, ragged, one JSON line")
     ap.add_argument("--decode-new", type=int, default=1, help="new tokens per sequence and step")
+    ap.add_argument("--decode-host", action="store_true",
+                    help="decode with the history in page-locked host memory: each step copies the "
+                         "sink rows and routed groups over the host link before the attention")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB (one plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -340,6 +343,17 @@ def decode_bench(args):
             sb = hga.make_shape(nq, kv, d, hist_lens[b], S, w.top_k_chunks, w.top_k_groups,
                                 w.torch_dtype, hist_stride=H)
             hga.hga_build_summaries(sb, k_hist[b], C[b], G[b])
+    if args.decode_host:
+        # the summaries stay on the device; the history moves to page-locked memory
+        kh_dev, vh_dev = k_hist, v_hist
+        k_hist = torch.empty(kh_dev.shape, dtype=w.torch_dtype, pin_memory=True)
+        v_hist = torch.empty(vh_dev.shape, dtype=w.torch_dtype, pin_memory=True)
+        k_hist.copy_(kh_dev)
+        v_hist.copy_(vh_dev)
+        del kh_dev, vh_dev
+        s = hga.make_shape(nq, kv, d, H, S, w.top_k_chunks, w.top_k_groups, w.torch_dtype,
+                           w.softmax_scale, True, n_sink_chunks=args.sink_chunks,
+                           local_window=args.local_window)
     hl = torch.tensor(hist_lens, dtype=torch.int32, device=dev)
     tl = torch.tensor(tail_lens, dtype=torch.int32, device=dev)
     sc = torch.empty((B, kv, w.top_k_chunks), dtype=torch.int32, device=dev)
@@ -360,7 +374,7 @@ def decode_bench(args):
     # K and V rows of every attended key once (plus queries and outputs)
     W = S if args.local_window <= 0 else min(args.local_window, S)
     sel = None
-    route_b = attn_b = 0
+    route_b = attn_b = link_b = 0
     step()
     torch.cuda.synchronize()
     sel = sg.cpu()
@@ -371,12 +385,17 @@ def decode_bench(args):
         route_b += kv * (r * n_new * d * e + (n_c - sink) * d * 4 + 8 * kc * d * 4
                          + (w.top_k_chunks + w.top_k_groups) * 4)
         t_lo = max(0, tail_lens[b] - n_new - W + 1)
+        sink_rows = min(64 * args.sink_chunks, H)
         for j in range(kv):
             n_keys = 64 * sink + 8 * int((sel[b, j] >= 0).sum()) + tail_lens[b] - t_lo
             attn_b += n_keys * d * e * 2 + 2 * r * n_new * d * e
+            # host tier: the staging copy's K and V rows over the link
+            link_b += (sink_rows + 8 * int((sel[b, j] >= 0).sum())) * d * e * 2
 
     names = list(hga.KERNELS)
     ids = {"route": names.index("route"), "decode": names.index("decode")}
+    if args.decode_host:
+        ids["stage"] = names.index("gather")
 
     def new_events(n):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -406,7 +425,23 @@ def decode_bench(args):
     elapsed = time.perf_counter() - t0
     ms = 1e3 * elapsed / args.steps
     gbs = {"route": route_b / (us["route"] * 1e-6) / 1e9, "decode": attn_b / (us["decode"] * 1e-6) / 1e9}
-    dom = max(us, key=us.get)
+    dom = max(gbs, key=lambda k: us[k])
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(gbs[dom], 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs[dom] / PEAK_HBM_GBS, 4), "traffic": None}
+    kernels = {"route": {"avg_us": round(us["route"], 3), "gbs": round(gbs["route"], 1),
+                         "mib_per_launch": round(route_b / 2 ** 20, 3)},
+               "decode_attn+merge": {"avg_us": round(us["decode"], 3), "gbs": round(gbs["decode"], 1),
+                                     "mib_per_launch": round(attn_b / 2 ** 20, 3)}}
+    if args.decode_host:
+        link = link_b / (us["stage"] * 1e-6) / 1e9
+        kernels["stage"] = {"avg_us": round(us["stage"], 3), "gbs": round(link, 1),
+                            "mib_per_launch": round(link_b / 2 ** 20, 3)}
+        measured = host_link_rate(dev)
+        # the staging copy over the host link bounds the step
+        roof = {"kernel": "stage", "bound": "host_link", "achieved": round(link, 1),
+                "peak": PEAK_HOST_LINK_GBS, "unit": "GB/s", "frac": round(link / PEAK_HOST_LINK_GBS, 4),
+                "measured_link_gbs": round(measured, 1), "frac_of_measured": round(link / measured, 4),
+                "traffic": None}
     print(json.dumps({
         "mode": "decode", "metric": "decode tokens/s (HGA route + attention, one layer)",
         "value": round(B * n_new * args.steps / elapsed, 1), "unit": "tokens/s",
@@ -417,12 +452,9 @@ def decode_bench(args):
                    "tail_lens": [min(tail_lens), max(tail_lens)], "n_sink_chunks": args.sink_chunks,
                    "local_window": args.local_window, "top_k_chunks": w.top_k_chunks,
                    "top_k_groups": w.top_k_groups},
-        "kernels": {"route": {"avg_us": round(us["route"], 3), "gbs": round(gbs["route"], 1),
-                              "mib_per_launch": round(route_b / 2 ** 20, 3)},
-                    "decode_attn+merge": {"avg_us": round(us["decode"], 3), "gbs": round(gbs["decode"], 1),
-                                          "mib_per_launch": round(attn_b / 2 ** 20, 3)}},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(gbs[dom], 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs[dom] / PEAK_HBM_GBS, 4), "traffic": None},
+        "history": "pinned host" if args.decode_host else "hbm",
+        "kernels": kernels,
+        "roofline": roof,
     }))
 
 

@@ -210,7 +210,8 @@ hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* 
  * open-segment tokens t with p - W < t <= p (W = local_window, default the
  * whole open segment):
  *   o[b][h][i] = sum_t softmax_t(scale * q[b][h][i] . k_t) v_t, lse likewise.
- * Layouts (device memory; P = hist_stride or hist_len is the history
+ * Layouts (device memory, except k_hist / v_hist, which live where
+ * shape->hist_loc says; P = hist_stride or hist_len is the history
  * capacity, T = seg_len the open-segment capacity):
  *   q, o           [batch][n_q][n_new][head_dim]        (dtype)
  *   k_hist, v_hist [batch][n_kv][P][head_dim]           (dtype)
@@ -222,7 +223,11 @@ hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* 
  *                  [n_new, T]
  *   sel_chunks [batch][n_kv][top_k_chunks], sel_groups [batch][n_kv][top_k_groups]
  *   lse            fp32 [batch][n_q][n_new]
- * Requires hist_loc = HGA_HIST_DEVICE, 1 <= n_new <= seg_len and
+ * With hist_loc = HGA_HIST_HOST_PINNED (gist.science §2.2 "Tiered Memory
+ * Hierarchy": history in host RAM, summaries in VRAM) each call copies every
+ * (sequence, KV head)'s sink rows and routed groups over the host link into
+ * ws after routing, then attends to those copies; results are bit-identical
+ * to device-resident history. Requires 1 <= n_new <= seg_len and
  * r * n_new <= 16 (r = n_q_heads / n_kv_heads). ws:
  * hga_decode_workspace_size(shape, batch, n_new) bytes, 256-byte aligned. */
 size_t hga_decode_workspace_size(const hga_shape* shape, int32_t batch, int32_t n_new);

@@ -40,6 +40,12 @@ struct DecodeParams {
   int n_q, n_kv, r, n_new;
   int64_t P;           // history rows per (sequence, KV head)
   int T;               // open-segment rows per (sequence, KV head)
+  // rows per (sequence, KV head) of k_hist / v_hist as read by the attention:
+  // P, or with staged copies (history in host memory) sink_rows + k_g*8, the
+  // sink rows first and then the routed groups' rows slot by slot
+  int64_t hrows;
+  int staged;
+  int sink_rows;
   int k_g, n_sink, window, n_piece;
   int piece_keys;      // keys per piece (kDecKeys, or 128 for small bf16 batches)
   float scale_log2;
@@ -63,6 +69,12 @@ __device__ __forceinline__ SeqKeys seq_keys(const DecodeParams& p, int b) {
   s.t_lo = max(0, s.tb - p.n_new - p.window + 1);
   s.n_keys = s.sink + p.k_g * kGroup + (s.tb - s.t_lo);
   return s;
+}
+
+// Row, within its (sequence, KV head), of routed key u (slot u/8, valid group
+// g): the group's own row in the history, or its slot's row in the copies.
+__device__ __forceinline__ int64_t routed_row(const DecodeParams& p, int g, int u) {
+  return p.staged ? static_cast<int64_t>(p.sink_rows) + u : static_cast<int64_t>(g) * kGroup + u % kGroup;
 }
 
 // Sum over the LPK lanes of a key row (in-row DPP adds).
@@ -92,7 +104,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
   const int nk = min(kDecKeys, sk.n_keys - k0);
   const int R = p.r * p.n_new;            // query rows, <= NQ (checked on the host)
   const int n_routed = p.k_g * kGroup;
-  const int64_t hrow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.P;
+  const int64_t hrow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.hrows;
   const int64_t trow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.T;
   const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
 
@@ -104,7 +116,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecodeParams p
     v -= sk.sink;
     if (v < n_routed) {
       const int g = sel_bj[v / kGroup];
-      return g >= 0 ? hist + (hrow0 + static_cast<int64_t>(g) * kGroup + v % kGroup) * D : nullptr;
+      return g >= 0 ? hist + (hrow0 + routed_row(p, g, v)) * D : nullptr;
     }
     tpos = sk.t_lo + v - n_routed;
     return tail + (trow0 + tpos) * D;
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
   const int nk = min(KEYS, sk.n_keys - k0);
   const int R = p.r * p.n_new;
   const int n_routed = p.k_g * kGroup;
-  const int64_t hrow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.P;
+  const int64_t hrow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.hrows;
   const int64_t trow0 = (static_cast<int64_t>(b) * p.n_kv + j) * p.T;
   const int32_t* sel_bj = p.sel + (static_cast<int64_t>(b) * p.n_kv + j) * p.k_g;
   const uint16_t* kh = static_cast<const uint16_t*>(p.k_hist);
@@ -308,7 +320,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecodePar
       const int u = v - sk.sink;
       if (u < n_routed) {
         const int g = sel_bj[u / kGroup];
-        if (g >= 0) { tail = false; info = -1; return (hrow0 + static_cast<int64_t>(g) * kGroup + u % kGroup) * D; }
+        if (g >= 0) { tail = false; info = -1; return (hrow0 + routed_row(p, g, u)) * D; }
       } else {
         tail = true;
         info = sk.t_lo + u - n_routed;
@@ -542,6 +554,54 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   if (threadIdx.x == 0) p.lse[row] = (m + log2f(l)) * kLn2;
 }
 
+// History in host memory: one workgroup per 64 staged rows of a (sequence,
+// KV head) copies its sink rows and the rows of its routed groups, 16 bytes
+// per lane, every load of a thread in flight before its stores. Rows of empty
+// slots are not written; the attention never reads them.
+constexpr int kStageRows = 64;
+
+template <int CPR>  // 16-byte chunks per row
+__global__ __launch_bounds__(256) void decode_stage_kernel(const uint4* __restrict__ k_hist,
+                                                           const uint4* __restrict__ v_hist,
+                                                           const int32_t* __restrict__ sel, int64_t P, int k_g,
+                                                           int sink_rows, int64_t stage_rows,
+                                                           uint4* __restrict__ k_st, uint4* __restrict__ v_st) {
+  constexpr int PER = kStageRows * CPR / 256;  // chunks per thread
+  static_assert(PER * 256 == kStageRows * CPR, "whole rows per workgroup");
+  const int64_t bj = blockIdx.y;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kStageRows;
+  uint4 kv[PER], vv[PER];
+  int64_t dst[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int x = static_cast<int>(threadIdx.x) + i * 256;
+    const int64_t row = r0 + x / CPR;
+    const int ch = x % CPR;
+    int64_t src = -1;
+    if (row < sink_rows) {
+      src = row;
+    } else if (row < stage_rows) {
+      const int64_t u = row - sink_rows;
+      const int g = sel[bj * k_g + u / kGroup];
+      if (g >= 0) src = static_cast<int64_t>(g) * kGroup + u % kGroup;
+    }
+    dst[i] = -1;
+    if (src >= 0) {
+      const int64_t o = (bj * P + src) * CPR + ch;
+      kv[i] = k_hist[o];
+      vv[i] = v_hist[o];
+      dst[i] = (bj * stage_rows + row) * CPR + ch;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (dst[i] >= 0) {
+      k_st[dst[i]] = kv[i];
+      v_st[dst[i]] = vv[i];
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_td(const hga_shape& s, DecodeParams& p, int batch, hipStream_t st) {
   const dim3 grid(p.n_piece, s.n_kv_heads, batch);
@@ -598,6 +658,41 @@ int decode_pieces(const hga_shape& s, int batch, int n_new) {
   return static_cast<int>((decode_max_keys(s) + pk - 1) / pk);
 }
 
+int64_t decode_stage_sink_rows(const hga_shape& s) {
+  const int64_t P = hist_rows(s);
+  const int64_t sink = static_cast<int64_t>(s.n_sink_chunks) * kChunk;
+  return sink < P ? sink : P;
+}
+
+int64_t decode_stage_rows(const hga_shape& s) {
+  return decode_stage_sink_rows(s) + static_cast<int64_t>(s.top_k_groups) * kGroup;
+}
+
+hipError_t launch_decode_stage(const hga_shape& s, int batch, const void* k_hist, const void* v_hist,
+                               const int32_t* sel_groups, void* k_stage, void* v_stage, hipStream_t stream) {
+  const int64_t rows = decode_stage_rows(s);
+  const int cpr = s.head_dim * (s.dtype == HGA_BF16 ? 2 : 4) / 16;
+  const dim3 grid(static_cast<unsigned>((rows + kStageRows - 1) / kStageRows),
+                  static_cast<unsigned>(batch * s.n_kv_heads));
+  const uint4* kh = static_cast<const uint4*>(k_hist);
+  const uint4* vh = static_cast<const uint4*>(v_hist);
+  uint4* ko = static_cast<uint4*>(k_stage);
+  uint4* vo = static_cast<uint4*>(v_stage);
+  const int64_t P = hist_rows(s);
+  const int sink = static_cast<int>(decode_stage_sink_rows(s));
+  hipEvent_t e0 = timer_event(HGA_KERNEL_GATHER, 0), e1 = timer_event(HGA_KERNEL_GATHER, 1);
+  if (cpr == 8)
+    hipExtLaunchKernelGGL((decode_stage_kernel<8>), grid, dim3(256), 0, stream, e0, e1, 0, kh, vh, sel_groups, P,
+                          s.top_k_groups, sink, rows, ko, vo);
+  else if (cpr == 16)
+    hipExtLaunchKernelGGL((decode_stage_kernel<16>), grid, dim3(256), 0, stream, e0, e1, 0, kh, vh, sel_groups, P,
+                          s.top_k_groups, sink, rows, ko, vo);
+  else
+    hipExtLaunchKernelGGL((decode_stage_kernel<32>), grid, dim3(256), 0, stream, e0, e1, 0, kh, vh, sel_groups, P,
+                          s.top_k_groups, sink, rows, ko, vo);
+  return hipGetLastError();
+}
+
 size_t decode_attn_workspace_bytes(const hga_shape& s, int batch, int n_new) {
   const size_t rows = static_cast<size_t>(batch) * s.n_q_heads * n_new;
   const size_t n = decode_pieces(s, batch, n_new);
@@ -607,12 +702,15 @@ size_t decode_attn_workspace_bytes(const hga_shape& s, int batch, int n_new) {
 hipError_t launch_decode_attn(const hga_shape& s, int batch, int n_new, const void* q, const void* k_hist,
                               const void* v_hist, const void* k_tail, const void* v_tail,
                               const int32_t* sel_groups, const int32_t* hist_lens, const int32_t* tail_lens,
-                              void* o, float* lse, void* ws, hipStream_t stream) {
+                              void* o, float* lse, void* ws, hipStream_t stream, bool staged) {
   DecodeParams p;
   p.q = q; p.k_hist = k_hist; p.v_hist = v_hist; p.k_tail = k_tail; p.v_tail = v_tail;
   p.sel = sel_groups; p.hist_lens = hist_lens; p.tail_lens = tail_lens; p.o = o; p.lse = lse;
   p.n_q = s.n_q_heads; p.n_kv = s.n_kv_heads; p.r = s.n_q_heads / s.n_kv_heads; p.n_new = n_new;
   p.P = hist_rows(s); p.T = s.seg_len; p.k_g = s.top_k_groups; p.n_sink = s.n_sink_chunks;
+  p.staged = staged ? 1 : 0;
+  p.hrows = staged ? decode_stage_rows(s) : p.P;
+  p.sink_rows = static_cast<int>(decode_stage_sink_rows(s));
   p.window = local_window(s); p.n_piece = decode_pieces(s, batch, n_new); p.piece_keys = decode_piece_keys(s, batch, n_new);
   p.scale_log2 = s.softmax_scale * 1.4426950408889634f;
   const size_t rows = static_cast<size_t>(batch) * s.n_q_heads * n_new;

@@ -423,8 +423,6 @@ hga_status hga_route_cached(const hga_shape* shape, const void* q, const float* 
 
 // Decode validation; 0 bytes (with the error recorded) when invalid.
 hga_status decode_check(const hga_shape& s, int32_t batch, int32_t n_new) {
-  if (s.hist_loc != HGA_HIST_DEVICE)
-    return fail(HGA_ERR_UNSUPPORTED, "decode needs device-resident history (hist_loc = HGA_HIST_DEVICE)");
   if (batch < 1) return fail(HGA_ERR_INVALID_ARG, "batch %d must be >= 1", batch);
   if (n_new < 1 || n_new > s.seg_len)
     return fail(HGA_ERR_INVALID_ARG, "n_new %d outside [1, seg_len = %d]", n_new, s.seg_len);
@@ -434,9 +432,21 @@ hga_status decode_check(const hga_shape& s, int32_t batch, int32_t n_new) {
   return HGA_OK;
 }
 
+bool decode_stages_history(const hga_shape& s) {
+  return s.hist_loc == HGA_HIST_HOST_PINNED && hga::hist_rows(s) > 0;
+}
+
+// Route part, attention part, then (history in host memory) the K and V
+// copies of every (sequence, KV head)'s sink rows and routed groups.
+size_t decode_stage_bytes(const hga_shape& s, int32_t batch) {
+  return align256(static_cast<size_t>(batch) * s.n_kv_heads * hga::decode_stage_rows(s) * s.head_dim *
+                  elem_bytes(s));
+}
+
 size_t decode_ws_parts(const hga_shape& s, int32_t batch, int32_t n_new, size_t* route_part) {
-  *route_part = hga::decode_route_workspace_bytes(s, batch);
-  return *route_part + hga::decode_attn_workspace_bytes(s, batch, n_new);
+  *route_part = align256(hga::decode_route_workspace_bytes(s, batch));
+  const size_t attn = align256(hga::decode_attn_workspace_bytes(s, batch, n_new));
+  return *route_part + attn + (decode_stages_history(s) ? 2 * decode_stage_bytes(s, batch) : 0);
 }
 
 size_t hga_decode_workspace_size(const hga_shape* shape, int32_t batch, int32_t n_new) {
@@ -463,11 +473,30 @@ hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, cons
     return fail(HGA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(HGA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool staged = decode_stages_history(s);
+  const void* kd = k_hist;
+  const void* vd = v_hist;
+  if (staged) {
+    HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
+    HGA_TRY(host_to_device_ptr(v_hist, &vd, "v_hist"));
+  }
   hipError_t e = hga::launch_decode_route(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks,
                                           sel_groups, ws, st);
   if (e != hipSuccess) return hip_fail(e, "decode route launch");
-  e = hga::launch_decode_attn(s, batch, n_new, q, k_hist, v_hist, k_tail, v_tail, sel_groups, hist_lens,
-                              tail_lens, o, lse, static_cast<char*>(ws) + route_part, st);
+  char* attn_ws = static_cast<char*>(ws) + route_part;
+  if (staged) {
+    // history in page-locked host memory: bring each (sequence, KV head)'s
+    // sink rows and routed groups over the host link, then attend to those
+    char* stage = attn_ws + align256(hga::decode_attn_workspace_bytes(s, batch, n_new));
+    void* ks = stage;
+    void* vs = stage + decode_stage_bytes(s, batch);
+    e = hga::launch_decode_stage(s, batch, kd, vd, sel_groups, ks, vs, st);
+    if (e != hipSuccess) return hip_fail(e, "decode staging launch");
+    kd = ks;
+    vd = vs;
+  }
+  e = hga::launch_decode_attn(s, batch, n_new, q, kd, vd, k_tail, v_tail, sel_groups, hist_lens, tail_lens, o,
+                              lse, attn_ws, st, staged);
   if (e != hipSuccess) return hip_fail(e, "decode attention launch");
   return ok();
 }

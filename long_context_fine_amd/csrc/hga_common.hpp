@@ -160,10 +160,21 @@ hipError_t launch_decode_route(const hga_shape& s, int batch, int n_new, const v
                                int32_t* sel_chunks, int32_t* sel_groups, void* ws, hipStream_t stream);
 size_t decode_route_workspace_bytes(const hga_shape& s, int batch);
 size_t decode_attn_workspace_bytes(const hga_shape& s, int batch, int n_new);
+// History kept in host memory: rows per (sequence, KV head) of the device
+// copies the decode attention reads instead, [batch][n_kv][sink rows + k_g*8]
+// (the sink rows, then the 8 rows of each routed group slot by slot).
+int64_t decode_stage_sink_rows(const hga_shape& s);
+int64_t decode_stage_rows(const hga_shape& s);
+// Copies every (sequence, KV head)'s sink rows and routed groups from the
+// history (k_hist / v_hist, device addresses of page-locked host memory) into
+// k_stage / v_stage.
+hipError_t launch_decode_stage(const hga_shape& s, int batch, const void* k_hist, const void* v_hist,
+                               const int32_t* sel_groups, void* k_stage, void* v_stage, hipStream_t stream);
+// staged: k_hist / v_hist are the copies launch_decode_stage wrote.
 hipError_t launch_decode_attn(const hga_shape& s, int batch, int n_new, const void* q, const void* k_hist,
                               const void* v_hist, const void* k_tail, const void* v_tail,
                               const int32_t* sel_groups, const int32_t* hist_lens, const int32_t* tail_lens,
-                              void* o, float* lse, void* ws, hipStream_t stream);
+                              void* o, float* lse, void* ws, hipStream_t stream, bool staged);
 hipError_t launch_route_cached(const hga_shape& s, const void* q, const float* chunk_sum,
                                const GcacheLayout& L, const float* group_sum_dev, int32_t* sel_chunks,
                                int32_t* sel_groups, int32_t* stats, void* ws, hipStream_t stream);

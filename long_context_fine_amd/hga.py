@@ -323,7 +323,8 @@ def hga_decode(shape: Shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_
         ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
     _check(lib().hga_decode(
         ctypes.byref(shape), B, n_new, _ptr(q, (B, shape.n_q_heads, n_new, d), dt, "q"),
-        _ptr(k_hist, (B, kv, P, d), dt, "k_hist"), _ptr(v_hist, (B, kv, P, d), dt, "v_hist"),
+        _ptr(k_hist, (B, kv, P, d), dt, "k_hist", shape.hist_loc != HGA_HIST_HOST_PINNED),
+        _ptr(v_hist, (B, kv, P, d), dt, "v_hist", shape.hist_loc != HGA_HIST_HOST_PINNED),
         _ptr(chunk_sum, (B, kv, P // 64, d), torch.float32, "chunk_sum"),
         _ptr(group_sum, (B, kv, P // 8, d), torch.float32, "group_sum"),
         _ptr(k_tail, (B, kv, T, d), dt, "k_tail"), _ptr(v_tail, (B, kv, T, d), dt, "v_tail"),

@@ -231,3 +231,33 @@ def test_binding_host_tensors_must_be_pinned_unless_empty():
     assert hga._ptr(torch.empty(0, dtype=torch.bfloat16), name="k_hist", device=False) is not None
     with pytest.raises(ValueError, match="pinned host tensor"):
         hga._ptr(torch.empty(4, dtype=torch.bfloat16), name="k_hist", device=False)
+
+
+def test_decode_arguments_and_workspace(L):
+    """hga_decode's host checks: batch and n_new ranges, at most 16 query rows
+    per KV head, workspace size (history in host memory adds the K and V
+    copies of every (sequence, KV head)'s sink rows and routed groups)."""
+    s = _shape()                                 # capacity 14,336, open segment 2,048
+    n = L.hga_decode_workspace_size(ctypes.byref(s), 4, 1)
+    assert n > 0 and n % 256 == 0
+    assert L.hga_decode_workspace_size(ctypes.byref(s), 0, 1) == 0       # batch < 1
+    assert L.hga_decode_workspace_size(ctypes.byref(s), 4, 0) == 0       # n_new < 1
+    assert L.hga_decode_workspace_size(ctypes.byref(s), 4, 5) == 0       # 4 x 5 rows > 16
+    host = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED)
+    # + {K, V} x [4 sequences][8 KV heads][32 groups x 8][128] bf16
+    assert L.hga_decode_workspace_size(ctypes.byref(host), 4, 1) == n + 2 * (4 * 8 * 256 * 128 * 2)
+    # with a 2-chunk sink the attention also has more keys; the copies add the
+    # sink's 128 rows per (sequence, KV head)
+    ns = L.hga_decode_workspace_size(ctypes.byref(_shape(n_sink_chunks=2)), 4, 1)
+    sink = _shape(hist_loc=hga.HGA_HIST_HOST_PINNED, n_sink_chunks=2)
+    assert L.hga_decode_workspace_size(ctypes.byref(sink), 4, 1) == ns + 2 * (4 * 8 * (128 + 256) * 128 * 2)
+    dec = lambda sh, batch, n_new, ws, nbytes: L.hga_decode(  # noqa: E731
+        ctypes.byref(sh), batch, n_new, *([FAKE] * 13), ws, nbytes, None)
+    assert dec(s, 0, 1, FAKE, n) == hga.HGA_ERR_INVALID_ARG
+    assert dec(s, 4, 2049, FAKE, n) == hga.HGA_ERR_INVALID_ARG            # n_new > seg_len
+    assert dec(s, 4, 5, FAKE, n) == hga.HGA_ERR_UNSUPPORTED
+    assert dec(s, 4, 1, FAKE, n - 1) == hga.HGA_ERR_WORKSPACE
+    assert dec(s, 4, 1, FAKE + 8, n) == hga.HGA_ERR_WORKSPACE              # misaligned
+    assert dec(s, 4, 1, None, n) == hga.HGA_ERR_WORKSPACE
+    nh = L.hga_decode_workspace_size(ctypes.byref(host), 4, 1)
+    assert dec(host, 4, 1, FAKE, nh - 1) == hga.HGA_ERR_WORKSPACE

@@ -28,7 +28,10 @@ def _f64(t):
 
 
 def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new, seed, sink=0,
-               window=0, check_outputs=True):
+               window=0, check_outputs=True, pinned_host=False):
+    """Decode one ragged batch, check it against the oracle sequence by
+    sequence; with pinned_host, run it again with the history in page-locked
+    host memory and require bit-identical results."""
     print(f"[case] decode nq={n_q} nkv={n_kv} d={d} P={P} T={T} kc={k_c} kg={k_g} {dtype} "
           f"hist={list(hist_lens)} tail={list(tail_lens)} n_new={n_new} sink={sink} W={window}",
           flush=True)
@@ -49,6 +52,19 @@ def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new,
     o, lse, sc, sg = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
                                 g["hist_lens"], g["tail_lens"])
     torch.cuda.synchronize()
+    if pinned_host:
+        print("  the same batch with the history in pinned host memory", flush=True)
+        kh_p = torch.empty(inp["k_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
+        vh_p = torch.empty(inp["v_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
+        kh_p.copy_(inp["k_hist"])
+        vh_p.copy_(inp["v_hist"])
+        sh = hga.make_shape(n_q, n_kv, d, P, T, k_c, k_g, w.torch_dtype, w.softmax_scale, True,
+                            n_sink_chunks=sink, local_window=window)
+        o2, lse2, sc2, sg2 = hga.decode(sh, g["q"], kh_p, vh_p, C, G, g["k_tail"], g["v_tail"],
+                                        g["hist_lens"], g["tail_lens"])
+        torch.cuda.synchronize()
+        assert torch.equal(sc2, sc) and torch.equal(sg2, sg)
+        assert torch.equal(o2, o) and torch.equal(lse2, lse)
     tol = TOL[dtype]
     for b in range(B):
         H, Tb = hist_lens[b], tail_lens[b]
@@ -168,9 +184,22 @@ def test_decode_split_route_matches_unsplit():
 
 def test_decode_qwen3_8b_131k():
     # Qwen3-8B layer shapes, 129,024-token history capacity, 2,048-token open
-    # segment, one new token per sequence, ragged lengths
+    # segment, one new token per sequence, ragged lengths; again with the
+    # history in pinned host memory
     run_decode(32, 8, 128, 129024, 2048, 16, 32, "bf16", [129024, 100032], [2048, 517], n_new=1,
-               seed=6)
+               seed=6, pinned_host=True)
+
+
+# History in page-locked host memory: each (sequence, KV head)'s sink rows and
+# routed groups are copied over the host link before the attention; the
+# results equal the device-history decode bit for bit. One and four new
+# tokens (VALU and MFMA P.V), a sink and window, ragged lengths down to empty,
+# fp32 at d = 64.
+@pytest.mark.parametrize("n_q,d,n_new,sink,window,dtype", [
+    (8, 128, 1, 0, 0, "bf16"), (8, 128, 4, 1, 40, "bf16"), (4, 64, 2, 2, 0, "f32")])
+def test_decode_pinned_host_history(n_q, d, n_new, sink, window, dtype):
+    run_decode(n_q, 2, d, 2048, 256, 5, 13, dtype, [2048, 704, 0, 128], [256, 31, 9, 64], n_new=n_new,
+               seed=30 + n_new, sink=sink, window=window, pinned_host=True)
 
 
 def test_decode_qwen3_8b_131k_four_new_tokens():
