@@ -51,6 +51,10 @@ def parse():
                     help="run the decode step instead: this many sequences of the workload's "
                          "history length, ragged, one JSON line")
     ap.add_argument("--decode-new", type=int, default=1, help="new tokens per sequence and step")
+    ap.add_argument("--decode-twopass", action="store_true",
+                    help="decode through hga_decode_twopass: chunk scores from bf16 copies of the "
+                         "chunk summaries bound the fp32 ones; only chunks that can reach the top k "
+                         "are re-scored in fp32 (same selections, half the bytes)")
     ap.add_argument("--decode-host", action="store_true",
                     help="decode with the history in page-locked host memory: each step copies the "
                          "sink rows and routed groups over the host link before the attention")
@@ -361,17 +365,25 @@ def decode_bench(args):
     o = torch.empty_like(q)
     lse = torch.empty((B, nq, n_new), dtype=torch.float32, device=dev)
     ws = torch.empty(hga.hga_decode_workspace_size(s, B, n_new), dtype=torch.uint8, device=dev)
+    # the bf16 copies are kept beside the summaries, like them outside the step
+    C_lo = hga.summaries_to_bf16(C) if args.decode_twopass else None
 
     def step():
-        hga.hga_decode(s, q, k_hist, v_hist, C, G, k_tail, v_tail, hl, tl, sc, sg, o, lse, ws)
+        if C_lo is None:
+            hga.hga_decode(s, q, k_hist, v_hist, C, G, k_tail, v_tail, hl, tl, sc, sg, o, lse, ws)
+        else:
+            hga.hga_decode_twopass(s, q, k_hist, v_hist, C, C_lo, G, k_tail, v_tail, hl, tl, sc, sg, o,
+                                   lse, ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # algorithmic bytes: route reads the new queries, every ranked chunk
-    # summary and the 8 * k_c candidate group summaries; attention reads the
-    # K and V rows of every attended key once (plus queries and outputs)
+    # summary (two-pass: its bf16 copy, plus the k_c kept chunks' fp32 rows,
+    # the least any exact re-score reads) and the 8 * k_c candidate group
+    # summaries; attention reads the K and V rows of every attended key once
+    # (plus queries and outputs)
     W = S if args.local_window <= 0 else min(args.local_window, S)
     sel = None
     route_b = attn_b = link_b = 0
@@ -382,8 +394,8 @@ def decode_bench(args):
         n_c = hist_lens[b] // 64
         sink = min(args.sink_chunks, n_c)
         kc = min(w.top_k_chunks, n_c - sink)
-        route_b += kv * (r * n_new * d * e + (n_c - sink) * d * 4 + 8 * kc * d * 4
-                         + (w.top_k_chunks + w.top_k_groups) * 4)
+        scan_b = (n_c - sink) * d * 2 + kc * d * 4 if args.decode_twopass else (n_c - sink) * d * 4
+        route_b += kv * (r * n_new * d * e + scan_b + 8 * kc * d * 4 + (w.top_k_chunks + w.top_k_groups) * 4)
         t_lo = max(0, tail_lens[b] - n_new - W + 1)
         sink_rows = min(64 * args.sink_chunks, H)
         for j in range(kv):
@@ -451,7 +463,8 @@ def decode_bench(args):
                    "hist_lens": [min(hist_lens), max(hist_lens)],
                    "tail_lens": [min(tail_lens), max(tail_lens)], "n_sink_chunks": args.sink_chunks,
                    "local_window": args.local_window, "top_k_chunks": w.top_k_chunks,
-                   "top_k_groups": w.top_k_groups},
+                   "top_k_groups": w.top_k_groups,
+                   "chunk_route": "two-pass (bf16 bound, fp32 re-score)" if args.decode_twopass else "fp32"},
         "history": "pinned host" if args.decode_host else "hbm",
         "kernels": kernels,
         "roofline": roof,

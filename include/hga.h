@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 3
+#define HGA_ABI_VERSION 4
 
 typedef enum {
   HGA_OK = 0,
@@ -238,6 +238,37 @@ hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, cons
                       const int32_t* hist_lens, const int32_t* tail_lens,
                       int32_t* sel_chunks, int32_t* sel_groups, void* o, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* hga_decode with a two-pass chunk route (gist.science §2.1 "Chunk Selection":
+ * the same top-k_c chunks, lowest index on ties). chunk_sum_bf16 holds bf16
+ * copies of chunk_sum, same layout [batch][n_kv][P/64][head_dim], rounded to
+ * nearest even (hga_summaries_to_bf16), device memory, 16-byte aligned, kept
+ * by the caller beside chunk_sum. Each (sequence, KV head) scores its chunks
+ * from the copies, which read half the bytes; a chunk whose copy score is
+ * more than twice the rounding bound below the k_c-th largest cannot be in
+ * the fp32 top k_c, and the rest are re-scored from chunk_sum. Outputs are
+ * bit-identical to hga_decode on the same inputs provided the copies are
+ * those of chunk_sum: a stale copy can change the selection (never a memory
+ * access). Batches whose chunk scan is split over several workgroups per
+ * (sequence, KV head) (at most 64 pairs) read no copies: their short scans
+ * are latency bound. Non-finite or huge summaries, and routes where too many
+ * chunks stay candidates, fall back to the fp32 scan inside the kernel. Same
+ * arguments, requirements, workspace (hga_decode_workspace_size) and errors
+ * as hga_decode, plus HGA_ERR_INVALID_ARG for a NULL or misaligned
+ * chunk_sum_bf16 when the history capacity is > 0. */
+hga_status hga_decode_twopass(const hga_shape* shape, int32_t batch, int32_t n_new, const void* q,
+                              const void* k_hist, const void* v_hist, const float* chunk_sum,
+                              const uint16_t* chunk_sum_bf16, const float* group_sum, const void* k_tail,
+                              const void* v_tail, const int32_t* hist_lens, const int32_t* tail_lens,
+                              int32_t* sel_chunks, int32_t* sel_groups, void* o, float* lse, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* dst[i] = src[i] rounded to bf16 (nearest even; NaN stays NaN, values
+ * beyond the bf16 range become infinite) for i < n, on `stream`: the copies
+ * hga_decode_twopass reads. n must be a multiple of 8 (0: nothing to do);
+ * src and dst are device memory, 16-byte aligned, not overlapping.
+ * HGA_ERR_INVALID_ARG otherwise. */
+hga_status hga_summaries_to_bf16(const float* src, uint16_t* dst, int64_t n, void* stream);
 
 /* Exact-token attention forward (gist.science Technical Summary §2.1,
  * "Exact-Token Attention"; pith.science review, Figure 1: summaries select

@@ -455,11 +455,13 @@ size_t hga_decode_workspace_size(const hga_shape* shape, int32_t batch, int32_t 
   return decode_ws_parts(*shape, batch, n_new, &route_part);
 }
 
-hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, const void* q,
-                      const void* k_hist, const void* v_hist, const float* chunk_sum,
-                      const float* group_sum, const void* k_tail, const void* v_tail,
-                      const int32_t* hist_lens, const int32_t* tail_lens, int32_t* sel_chunks,
-                      int32_t* sel_groups, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+// hga_decode and hga_decode_twopass: chunk_sum_lo null for the one-pass route.
+hga_status decode_impl(const hga_shape* shape, int32_t batch, int32_t n_new, const void* q,
+                       const void* k_hist, const void* v_hist, const float* chunk_sum,
+                       const uint16_t* chunk_sum_lo, const float* group_sum, const void* k_tail,
+                       const void* v_tail, const int32_t* hist_lens, const int32_t* tail_lens,
+                       int32_t* sel_chunks, int32_t* sel_groups, void* o, float* lse, void* ws,
+                       size_t ws_bytes, void* stream) {
   HGA_TRY(check_shape(shape));
   const hga_shape& s = *shape;
   HGA_TRY(decode_check(s, batch, n_new));
@@ -480,8 +482,8 @@ hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, cons
     HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
     HGA_TRY(host_to_device_ptr(v_hist, &vd, "v_hist"));
   }
-  hipError_t e = hga::launch_decode_route(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks,
-                                          sel_groups, ws, st);
+  hipError_t e = hga::launch_decode_route(s, batch, n_new, q, chunk_sum, chunk_sum_lo, group_sum, hist_lens,
+                                          sel_chunks, sel_groups, ws, st);
   if (e != hipSuccess) return hip_fail(e, "decode route launch");
   char* attn_ws = static_cast<char*>(ws) + route_part;
   if (staged) {
@@ -498,6 +500,43 @@ hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, cons
   e = hga::launch_decode_attn(s, batch, n_new, q, kd, vd, k_tail, v_tail, sel_groups, hist_lens, tail_lens, o,
                               lse, attn_ws, st, staged);
   if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  return ok();
+}
+
+hga_status hga_decode(const hga_shape* shape, int32_t batch, int32_t n_new, const void* q,
+                      const void* k_hist, const void* v_hist, const float* chunk_sum,
+                      const float* group_sum, const void* k_tail, const void* v_tail,
+                      const int32_t* hist_lens, const int32_t* tail_lens, int32_t* sel_chunks,
+                      int32_t* sel_groups, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(shape, batch, n_new, q, k_hist, v_hist, chunk_sum, nullptr, group_sum, k_tail, v_tail,
+                     hist_lens, tail_lens, sel_chunks, sel_groups, o, lse, ws, ws_bytes, stream);
+}
+
+hga_status hga_decode_twopass(const hga_shape* shape, int32_t batch, int32_t n_new, const void* q,
+                              const void* k_hist, const void* v_hist, const float* chunk_sum,
+                              const uint16_t* chunk_sum_bf16, const float* group_sum, const void* k_tail,
+                              const void* v_tail, const int32_t* hist_lens, const int32_t* tail_lens,
+                              int32_t* sel_chunks, int32_t* sel_groups, void* o, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
+  HGA_TRY(check_shape(shape));
+  if (hga::hist_rows(*shape) > 0) {
+    HGA_REQUIRE(chunk_sum_bf16, "chunk_sum_bf16 must be non-NULL when the history capacity is > 0");
+    if (reinterpret_cast<uintptr_t>(chunk_sum_bf16) % 16)
+      return fail(HGA_ERR_INVALID_ARG, "chunk_sum_bf16 must be 16-byte aligned");
+  }
+  return decode_impl(shape, batch, n_new, q, k_hist, v_hist, chunk_sum, chunk_sum_bf16, group_sum, k_tail,
+                     v_tail, hist_lens, tail_lens, sel_chunks, sel_groups, o, lse, ws, ws_bytes, stream);
+}
+
+hga_status hga_summaries_to_bf16(const float* src, uint16_t* dst, int64_t n, void* stream) {
+  if (n < 0 || n % 8) return fail(HGA_ERR_INVALID_ARG, "n = %lld must be a non-negative multiple of 8",
+                                  static_cast<long long>(n));
+  if (n == 0) return ok();
+  HGA_REQUIRE(src && dst, "src and dst must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16)
+    return fail(HGA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  const hipError_t e = hga::launch_round_bf16(src, dst, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bf16 rounding launch");
   return ok();
 }
 

@@ -155,9 +155,13 @@ GcacheLayout gcache_layout(const hga_shape& s, void* cache, int n_slots);
 size_t route_workspace_bytes(const hga_shape& s);
 size_t route_cached_workspace_bytes(const hga_shape& s);
 hipError_t launch_gcache_reset(const hga_shape& s, const GcacheLayout& L, hipStream_t stream);
+// chunk_sum_lo: bf16 copies of chunk_sum for the two-pass chunk route, or null
 hipError_t launch_decode_route(const hga_shape& s, int batch, int n_new, const void* q,
-                               const float* chunk_sum, const float* group_sum, const int32_t* hist_lens,
-                               int32_t* sel_chunks, int32_t* sel_groups, void* ws, hipStream_t stream);
+                               const float* chunk_sum, const uint16_t* chunk_sum_lo, const float* group_sum,
+                               const int32_t* hist_lens, int32_t* sel_chunks, int32_t* sel_groups, void* ws,
+                               hipStream_t stream);
+// n fp32 values (n % 8 == 0, 16-byte aligned) to bf16, round to nearest even
+hipError_t launch_round_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
 size_t decode_route_workspace_bytes(const hga_shape& s, int batch);
 size_t decode_attn_workspace_bytes(const hga_shape& s, int batch, int n_new);
 // History kept in host memory: rows per (sequence, KV head) of the device

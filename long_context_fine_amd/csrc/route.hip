@@ -123,6 +123,168 @@ __device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
   return r;
 }
 
+// Radix select of the need-th largest order-preserving key among sc[0, n)
+// (1 <= need <= n; need = 0 selects nothing): 8-bit digits, most significant
+// first, one LDS histogram (256 bins, one per thread) per pass. Histograms and
+// selections alternate between two buffers by pass, so a pass needs four
+// barriers: counts done, two in the scan, selection. Every thread returns the
+// same result:
+//   exact:  the need-th largest key equals prefix (all 32 bits fixed) and
+//           `need` of the keys equal to prefix are still to be taken;
+//   !exact: the keys k with (k & pmask) >= prefix are exactly the need
+//           largest (the threshold bin is taken whole).
+struct RadixSel {
+  uint32_t prefix, pmask;
+  int need;
+  bool exact;
+};
+
+__device__ RadixSel radix_select(const float* sc, int n, int need, int32_t (*hist_s)[kThreads],
+                                 int32_t (*rsel)[3], int32_t* scan_ws) {
+  static_assert(kThreads == 256, "one histogram bin per thread");
+  const int t = threadIdx.x;
+  RadixSel rs{0u, 0u, need, false};
+  hist_s[0][t] = 0;
+  __syncthreads();
+  int hb = 0;
+  for (int shift = 24; shift >= 0 && need > 0; shift -= 8, hb ^= 1) {
+    for (int m = t; m < n; m += kThreads) {
+      const uint32_t k = score_key(sc[m]);
+      if ((k & rs.pmask) == rs.prefix) atomicAdd(&hist_s[hb][(k >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    const int bin = kThreads - 1 - t;           // thread order = bins descending
+    const int h = hist_s[hb][bin];
+    hist_s[hb ^ 1][t] = 0;                      // the next pass's histogram
+    int total;
+    const int at_or_above = block_scan_excl<kThreads, false>(h, &total, scan_ws) + h;
+    if (at_or_above >= rs.need && at_or_above - h < rs.need) {
+      rsel[hb][0] = bin;
+      rsel[hb][1] = at_or_above - h;
+      rsel[hb][2] = h;
+    }
+    __syncthreads();
+    rs.prefix |= static_cast<uint32_t>(rsel[hb][0]) << shift;
+    rs.pmask |= 255u << shift;
+    rs.need -= rsel[hb][1];
+    if (rsel[hb][2] == rs.need) break;          // the whole bin is kept
+    if (shift == 0) rs.exact = true;
+  }
+  return rs;
+}
+
+// Top-k of n 64-bit rank keys gkey[0, n) by rank counting (0 marks an empty
+// slot; gkey[n] must be readable and 0): candidate c is taken when fewer than
+// k keys exceed its own. One ballot word per 64 candidates into wmask, so the
+// taken candidates keep their order (ordered_pos). Every thread must call it;
+// the caller passes a barrier before reading wmask.
+__device__ __forceinline__ void rank_take_mask(const uint64_t* gkey, int n, int k, uint64_t* wmask) {
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(gkey);
+  for (int cb = 0; cb < n; cb += kThreads) {
+    const int c = cb + t;
+    bool take = false;
+    if (c < n) {
+      const uint64_t mine = gkey[c];
+      if (mine != 0ull) {
+        int beaten = 0;
+#pragma unroll 4
+        for (int o2 = 0; o2 < (n + 1) / 2; ++o2) {
+          const ulonglong2 x = k2[o2];
+          beaten += (x.x > mine) + (x.y > mine);
+        }
+        take = beaten < k;
+      }
+    }
+    const uint64_t m = __ballot(take);
+    if (lane == 0) wmask[cb / kWave + wave] = m;
+  }
+}
+
+__device__ __forceinline__ bool mask_taken(const uint64_t* wmask, int c) {
+  return (wmask[c / kWave] >> (c % kWave)) & 1ull;
+}
+// Output position of taken candidate c: the taken candidates before it.
+__device__ __forceinline__ int ordered_pos(const uint64_t* wmask, int c) {
+  int pos = __popcll(wmask[c / kWave] & ((1ull << (c % kWave)) - 1ull));
+  for (int w2 = 0; w2 < c / kWave; ++w2) pos += __popcll(wmask[w2]);
+  return pos;
+}
+
+// score_rows for rows of D bf16 values (row_ptr(i): the row's first element),
+// loads of 16 bytes (lane sub reads elements [8(8c + sub), 8(8c + sub) + 8)),
+// 8*UNROLL rows per wave in flight. Also returns, per thread, the largest
+// sum over a row of |qv[e]| * |row[e]| among the rows it reduced, as raw bits
+// with the sign cleared (a NaN compares above every number).
+template <int D, int UNROLL, class RowPtr>
+__device__ __forceinline__ uint32_t score_rows_bf16(const float* qv, int n, RowPtr row_ptr, float* out) {
+  constexpr int LPR = 8;                 // lanes per row
+  constexpr int EPL = D / LPR;           // elements per lane (16 or 8)
+  constexpr int VPL = EPL / 8;           // 16-byte loads per lane and row
+  constexpr int RPP = kWave / LPR;       // rows per wave pass
+  constexpr int NW = kThreads / kWave;
+  constexpr int STEP = NW * RPP * UNROLL;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int sub = lane % LPR;
+  float qr[EPL];
+#pragma unroll
+  for (int c = 0; c < VPL; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qr[8 * c + e] = qv[(c * LPR + sub) * 8 + e];
+  using Buf = uint4[UNROLL][VPL];
+  auto load = [&](int r0, Buf& v) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int row = min(r0 + u * NW * RPP + lane / LPR, n - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(row_ptr(row));
+#pragma unroll
+      for (int c = 0; c < VPL; ++c) v[u][c] = src[c * LPR + sub];
+    }
+  };
+  uint32_t amax = 0u;
+  auto reduce = [&](int r0, const Buf& v) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      float s = 0.f, a = 0.f;
+#pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const uint32_t w[4] = {v[u][c].x, v[u][c].y, v[u][c].z, v[u][c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+          s += lo * qr[8 * c + 2 * i] + hi * qr[8 * c + 2 * i + 1];
+          a += fabsf(lo) * fabsf(qr[8 * c + 2 * i]) + fabsf(hi) * fabsf(qr[8 * c + 2 * i + 1]);
+        }
+      }
+      s = sum8_f32(s);
+      a = sum8_f32(a);
+      const int row = r0 + u * NW * RPP + lane / LPR;
+      if (row < n && sub == 0) {
+        out[row] = s;
+        amax = max(amax, __float_as_uint(a) & 0x7fffffffu);
+      }
+    }
+  };
+  Buf va, vb;
+  int r0 = wave * RPP;
+  if (r0 < n) load(r0, va);
+  while (r0 < n) {
+    if (r0 + STEP < n) load(r0 + STEP, vb);
+    reduce(r0, va);
+    r0 += STEP;
+    if (r0 >= n) break;
+    if (r0 + STEP < n) load(r0 + STEP, va);
+    reduce(r0, vb);
+    r0 += STEP;
+  }
+  return amax;
+}
+
+// Inverse of score_key for the keys of finite scores.
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 enum RouteMode {
   kRouteFull = 0, kRouteChunks = 1, kRouteGroups = 2, kRouteDecode = 3,
   // decode with the chunk scan split over n_part workgroups per (sequence,
@@ -145,6 +307,11 @@ struct DecodeView {
   int n_part = 1;              // split decode: parts per (sequence, KV head)
   int32_t* cand_id = nullptr;  // [batch][n_kv][n_part][k_c] kept chunk ids (-1: none)
   float* cand_sc = nullptr;    // their scores
+  // bf16 copies of the chunk summaries (layout of csum) for the two-pass
+  // chunk route of the unsplit decode mode, or null: scores from these bound
+  // the fp32 scores, and only the chunks that can reach the top k_c are
+  // re-scored from csum
+  const uint16_t* csum_lo = nullptr;
 };
 
 // Group rows of the cache: [n_kv][n_slots][8][D] fp32, slot of each chunk in
@@ -180,6 +347,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ uint64_t wmask[kMaxCand / kWave];
   __shared__ int32_t cnt_s[kThreads / 2];
   __shared__ int32_t slot_s[kMaxTopKChunks];
+  constexpr bool kTwoPass = MODE == kRouteDecode;
+  __shared__ int32_t cidx_s[kTwoPass ? kMaxCand : 1];      // two-pass candidates (ascending)
+  __shared__ uint32_t red_s[2];                             // two-pass: max |q||C~| bits, threshold key
+  __shared__ float thr_s;
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   // KV head fastest: with 8 KV heads all workgroups of head j run on one XCD
@@ -195,6 +366,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     n_chunks = nc - chunk0;
     csum += static_cast<int64_t>(b) * n_kv * chunk_rows * D;
     gsum += static_cast<int64_t>(b) * n_kv * chunk_rows * (kChunk / kGroup) * D;
+    if (dec.csum_lo != nullptr) dec.csum_lo += static_cast<int64_t>(b) * n_kv * chunk_rows * D;
     if constexpr (MODE == kRouteDecodePart) {  // this workgroup's part of the ranked chunks
       const int per = (n_chunks + dec.n_part - 1) / dec.n_part;
       const int lo = min(n_chunks, static_cast<int>(blockIdx.z) * per);
@@ -260,88 +432,114 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       gkey[c] = id >= 0 ? rank_key(dec.cand_sc[c0 + c], static_cast<uint32_t>(id)) : 0ull;
     }
     __syncthreads();
-    const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(gkey);
-    for (int cb = 0; cb < ncc; cb += kThreads) {
-      const int c = cb + t;
-      bool take = false;
-      if (c < ncc) {
-        const uint64_t mine = gkey[c];
-        if (mine != 0ull) {
-          int beaten = 0;
-#pragma unroll 4
-          for (int o2 = 0; o2 < (ncc + 1) / 2; ++o2) {
-            const ulonglong2 x = k2[o2];
-            beaten += (x.x > mine) + (x.y > mine);
-          }
-          take = beaten < k_c;
-        }
-      }
-      const uint64_t m = __ballot(take);
-      if (lane == 0) wmask[cb / kWave + wave] = m;
-    }
+    rank_take_mask(gkey, ncc, k_c, wmask);
     __syncthreads();
     int total = 0;
     for (int w2 = 0; w2 < (ncc + kWave - 1) / kWave; ++w2) total += __popcll(wmask[w2]);
     kc_eff = total;
-    for (int c = t; c < ncc; c += kThreads) {
-      const uint64_t m = wmask[c / kWave];
-      if ((m >> (c % kWave)) & 1ull) {
-        int pos = __popcll(m & ((1ull << (c % kWave)) - 1ull));
-        for (int w2 = 0; w2 < c / kWave; ++w2) pos += __popcll(wmask[w2]);
-        sorted[pos] = dec.cand_id[c0 + c];
-      }
-    }
+    for (int c = t; c < ncc; c += kThreads)
+      if (mask_taken(wmask, c)) sorted[ordered_pos(wmask, c)] = dec.cand_id[c0 + c];
     __syncthreads();
     if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
   } else {
-    // ---- 2. chunk scores ----------------------------------------------------
     float* sc = n_chunks <= kLdsScores ? sc_lds
                                        : ws_scores + bj * (kDec ? chunk_rows : n_chunks);
     // ranked chunks are chunk0 .. chunk0 + n_chunks - 1 (the sink is attended in full)
     const float* cbase = csum + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
-    score_rows<D, 4>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
-    __syncthreads();
-
-    // ---- 3. chunk top-k: exact radix select over the order-preserving score
-    // keys (8-bit digits, most significant first, LDS histograms) until the
-    // threshold bin is taken whole or the key is fixed in all 32 bits; equal
-    // keys at the threshold go to the lowest indices. The kept chunks are then
-    // written in ascending index order by one ordered compaction.
-    kc_eff = min(k_c, n_chunks);
-    static_assert(kThreads == 256, "one histogram bin per thread");
-    {
-      uint32_t prefix = 0u, pmask = 0u;
-      int need = kc_eff;        // keys still to take among those equal to prefix under pmask
-      bool exact = false;       // threshold fixed in all 32 bits: ties resolved by index
-      // histograms and selections alternate between two buffers by pass, so
-      // a pass needs four barriers: counts done, two in the scan, selection
-      hist_s[0][t] = 0;
-      __syncthreads();
-      int hb = 0;
-      for (int shift = 24; shift >= 0 && kc_eff > 0; shift -= 8, hb ^= 1) {
-        for (int m = t; m < n_chunks; m += kThreads) {
-          const uint32_t k = score_key(sc[m]);
-          if ((k & pmask) == prefix) atomicAdd(&hist_s[hb][(k >> shift) & 255u], 1);
+    bool done = false;
+    if constexpr (kTwoPass) {
+      // ---- 2-3 in two passes. Scores s~ from the bf16 copies C~ differ from
+      // the fp32 scores s by at most e = 0.0045 * max_m sum|qbar||C~_m| (plus
+      // 1e-30 * (1 + sum|qbar|) for subnormals): 2^-8 relative rounding of C~,
+      // 128 * 2^-24 for either fp32 dot product, with room to spare. Every
+      // chunk of the fp32 top k_c then has s~ >= tau - 2e, tau the k_c-th
+      // largest s~; those candidates are re-scored from the fp32 summaries
+      // (the same arithmetic as the one-pass scan) and their top k_c under
+      // (score, lower index) is the one-pass selection. Non-finite or huge
+      // values, or more candidates than fit, fall back to the one-pass scan.
+      if (dec.csum_lo != nullptr && n_chunks > k_c) {
+        if (t == 0) {
+          red_s[0] = 0u;
+          red_s[1] = 0xffffffffu;
         }
         __syncthreads();
-        const int bin = kThreads - 1 - t;           // thread order = bins descending
-        const int h = hist_s[hb][bin];
-        hist_s[hb ^ 1][t] = 0;                      // the next pass's histogram
-        int total;
-        const int at_or_above = block_scan_excl<kThreads, false>(h, &total, scan_ws) + h;
-        if (at_or_above >= need && at_or_above - h < need) {
-          rsel[hb][0] = bin;
-          rsel[hb][1] = at_or_above - h;
-          rsel[hb][2] = h;
-        }
+        const uint16_t* lbase = dec.csum_lo + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
+        uint32_t am = score_rows_bf16<D, 4>(
+            qv, n_chunks, [&](int m) { return lbase + static_cast<int64_t>(m) * D; }, sc);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1)
+          am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), o, kWave)));
+        if (lane == 0) atomicMax(&red_s[0], am);
         __syncthreads();
-        prefix |= static_cast<uint32_t>(rsel[hb][0]) << shift;
-        pmask |= 255u << shift;
-        need -= rsel[hb][1];
-        if (rsel[hb][2] == need) break;             // the whole bin is kept
-        if (shift == 0) exact = true;
+        const float amax = __uint_as_float(red_s[0]);
+        if (amax <= 1e30f) {                    // the same for every thread; false for NaN
+          const RadixSel rs = radix_select(sc, n_chunks, k_c, hist_s, rsel, scan_ws);
+          if (!rs.exact) {
+            // the threshold bin was taken whole: tau is its smallest key
+            uint32_t kmin = 0xffffffffu;
+            for (int m = t; m < n_chunks; m += kThreads) {
+              const uint32_t k = score_key(sc[m]);
+              if ((k & rs.pmask) == rs.prefix) kmin = min(kmin, k);
+            }
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1)
+              kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, kWave)));
+            if (lane == 0) atomicMin(&red_s[1], kmin);
+          }
+          __syncthreads();
+          if (t == 0) {
+            float q1 = 0.f;
+            for (int e = 0; e < D; ++e) q1 += fabsf(qv[e]);
+            const float bound = 0.0045f * amax + 1e-30f * (1.f + q1);
+            thr_s = key_score(rs.exact ? rs.prefix : red_s[1]) - 2.f * bound;
+          }
+          __syncthreads();
+          const float thr = thr_s;
+          // candidates in ascending chunk order: thread t owns [t*E, t*E + E)
+          const int E = (n_chunks + kThreads - 1) / kThreads;
+          const int m0 = min(t * E, n_chunks), m1 = min(m0 + E, n_chunks);
+          int n_here = 0;
+          for (int m = m0; m < m1; ++m) n_here += sc[m] >= thr;
+          int n_cand;
+          int pos = block_scan_excl<kThreads>(n_here, &n_cand, scan_ws);
+          if (n_cand < kMaxCand) {              // the same for every thread
+            for (int m = m0; m < m1; ++m)
+              if (sc[m] >= thr) cidx_s[pos++] = m;
+            __syncthreads();
+            score_rows<D, 4>(qv, n_cand, [&](int c) { return cbase + static_cast<int64_t>(cidx_s[c]) * D; }, gsc);
+            __syncthreads();
+            for (int c = t; c <= n_cand; c += kThreads)
+              gkey[c] = c < n_cand ? rank_key(gsc[c], static_cast<uint32_t>(chunk0 + cidx_s[c])) : 0ull;
+            __syncthreads();
+            rank_take_mask(gkey, n_cand, k_c, wmask);
+            __syncthreads();
+            for (int c = t; c < n_cand; c += kThreads)
+              if (mask_taken(wmask, c)) sorted[ordered_pos(wmask, c)] = chunk0 + cidx_s[c];
+            // k_c taken (n_cand >= k_c: the k_c largest s~ are candidates), counted anyway
+            int taken = 0;
+            for (int w2 = 0; w2 < (n_cand + kWave - 1) / kWave; ++w2) taken += __popcll(wmask[w2]);
+            __syncthreads();
+            kc_eff = taken;
+            done = true;
+            if (t < k_c) sel_chunks[bj * k_c + t] = t < kc_eff ? sorted[t] : -1;
+          }
+        }
       }
-      if (!exact) {
+    }
+    if (!done) {
+      // ---- 2. chunk scores --------------------------------------------------
+      score_rows<D, 4>(qv, n_chunks, [&](int m) { return cbase + static_cast<int64_t>(m) * D; }, sc);
+      __syncthreads();
+
+      // ---- 3. chunk top-k: exact radix select over the order-preserving
+      // score keys until the threshold bin is taken whole or the key is fixed
+      // in all 32 bits; equal keys at the threshold go to the lowest indices.
+      // The kept chunks are then written in ascending index order.
+      kc_eff = min(k_c, n_chunks);
+      const RadixSel rs = radix_select(sc, n_chunks, kc_eff, hist_s, rsel, scan_ws);
+      const uint32_t prefix = rs.prefix, pmask = rs.pmask;
+      const int need = rs.need;
+      if (!rs.exact) {
         // every key with the prefix under the mask, or above it, is kept: the
         // kc_eff chunk ids are appended in any order, then placed by rank
         // (ids are unique, so the result is fixed)
@@ -738,17 +936,19 @@ DecodeRouteWs decode_route_ws(const hga_shape& s, int batch) {
 
 template <typename T, int D>
 hipError_t launch_decode_t(const hga_shape& s, int batch, int n_new, const void* q, const float* cs,
-                           const float* gs, const int32_t* hist_lens, int32_t* sc_out, int32_t* sg_out,
-                           void* ws, hipStream_t st) {
+                           const uint16_t* cs_lo, const float* gs, const int32_t* hist_lens, int32_t* sc_out,
+                           int32_t* sg_out, void* ws, hipStream_t st) {
   const int r = s.n_q_heads / s.n_kv_heads;
   const int chunk_rows = static_cast<int>(hist_rows(s) / kChunk);
   const int P = decode_route_parts(s, batch);
   if (P == 1) {
+    DecodeView dv{hist_lens, s.n_sink_chunks, s.n_q_heads};
+    dv.csum_lo = cs_lo;
     hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecode>), dim3(s.n_kv_heads, batch), dim3(kThreads), 0, st,
                           timer_event(HGA_KERNEL_ROUTE, 0), timer_event(HGA_KERNEL_ROUTE, 1), 0,
                           static_cast<const T*>(q), cs, gs, n_new, s.n_kv_heads, r, 0, 0, chunk_rows,
                           s.top_k_chunks, s.top_k_groups, static_cast<float*>(ws), sc_out, sg_out, nullptr,
-                          CacheView{}, DecodeView{hist_lens, s.n_sink_chunks, s.n_q_heads});
+                          CacheView{}, dv);
     return hipGetLastError();
   }
   const DecodeRouteWs w = decode_route_ws(s, batch);
@@ -756,7 +956,7 @@ hipError_t launch_decode_t(const hga_shape& s, int batch, int n_new, const void*
   float* qbar = reinterpret_cast<float*>(base + w.qbar);
   const size_t nc = static_cast<size_t>(batch) * s.n_kv_heads * P * s.top_k_chunks;
   DecodeView dv{hist_lens, s.n_sink_chunks, s.n_q_heads};
-  dv.n_part = P;
+  dv.n_part = P;  // parts of a split scan are short and latency bound: fp32 scan
   dv.cand_id = reinterpret_cast<int32_t*>(base + w.cand);
   dv.cand_sc = reinterpret_cast<float*>(base + w.cand + align256(sizeof(int32_t) * nc));
   hipExtLaunchKernelGGL((route_kernel<T, D, kRouteDecodePart>), dim3(s.n_kv_heads, batch, P), dim3(kThreads), 0,
@@ -775,14 +975,16 @@ hipError_t launch_decode_t(const hga_shape& s, int batch, int n_new, const void*
 size_t decode_route_workspace_bytes(const hga_shape& s, int batch) { return decode_route_ws(s, batch).bytes; }
 
 hipError_t launch_decode_route(const hga_shape& s, int batch, int n_new, const void* q,
-                               const float* chunk_sum, const float* group_sum, const int32_t* hist_lens,
-                               int32_t* sel_chunks, int32_t* sel_groups, void* ws, hipStream_t stream) {
+                               const float* chunk_sum, const uint16_t* chunk_sum_lo, const float* group_sum,
+                               const int32_t* hist_lens, int32_t* sel_chunks, int32_t* sel_groups, void* ws,
+                               hipStream_t stream) {
   const bool bf = s.dtype == HGA_BF16;
-  if (s.head_dim == 128)
-    return bf ? launch_decode_t<uint16_t, 128>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream)
-              : launch_decode_t<float, 128>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream);
-  return bf ? launch_decode_t<uint16_t, 64>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream)
-            : launch_decode_t<float, 64>(s, batch, n_new, q, chunk_sum, group_sum, hist_lens, sel_chunks, sel_groups, ws, stream);
+#define HGA_DECODE_ROUTE(T, D)                                                                              \
+  launch_decode_t<T, D>(s, batch, n_new, q, chunk_sum, chunk_sum_lo, group_sum, hist_lens, sel_chunks, \
+                        sel_groups, ws, stream)
+  if (s.head_dim == 128) return bf ? HGA_DECODE_ROUTE(uint16_t, 128) : HGA_DECODE_ROUTE(float, 128);
+  return bf ? HGA_DECODE_ROUTE(uint16_t, 64) : HGA_DECODE_ROUTE(float, 64);
+#undef HGA_DECODE_ROUTE
 }
 
 hipError_t launch_route(const hga_shape& s, const void* q, const float* chunk_sum,

@@ -72,7 +72,39 @@ hipError_t launch_t(const hga_shape& s, const void* k, int64_t c0, int64_t c1, f
   return hipGetLastError();
 }
 
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet), overflow goes
+// to infinity. Eight elements per thread: two 16-byte loads, one 16-byte store.
+__device__ __forceinline__ uint32_t round_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(kThreads) void round_bf16_kernel(const float* __restrict__ src,
+                                                              uint16_t* __restrict__ dst, int64_t n8) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n8; i += stride) {
+    const float4 a = reinterpret_cast<const float4*>(src)[2 * i];
+    const float4 b = reinterpret_cast<const float4*>(src)[2 * i + 1];
+    uint4 o;
+    o.x = round_bf16(a.x) | (round_bf16(a.y) << 16);
+    o.y = round_bf16(a.z) | (round_bf16(a.w) << 16);
+    o.z = round_bf16(b.x) | (round_bf16(b.y) << 16);
+    o.w = round_bf16(b.z) | (round_bf16(b.w) << 16);
+    reinterpret_cast<uint4*>(dst)[i] = o;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_round_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  const int64_t wgs = (n8 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(round_bf16_kernel, dim3(static_cast<unsigned>(wgs < (1 << 20) ? wgs : (1 << 20))),
+                     dim3(kThreads), 0, stream, src, dst, n8);
+  return hipGetLastError();
+}
 
 hipError_t launch_build_summaries(const hga_shape& s, const void* k_hist, int64_t tok_begin,
                                   int64_t tok_end, float* chunk_sum, float* group_sum,

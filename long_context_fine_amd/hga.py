@@ -24,7 +24,8 @@ EXPORTS = ("hga_build_summaries", "hga_route", "hga_attn_fwd", "hga_attn_bwd",
            "hga_gather_groups", "hga_workspace_size", "hga_status_string",
            "hga_last_error", "hga_abi_version", "hga_set_kernel_events",
            "hga_gcache_bytes", "hga_gcache_reset", "hga_route_cached",
-           "hga_decode_workspace_size", "hga_decode", "hga_route_noalloc", "hga_attn_bwd_staged")
+           "hga_decode_workspace_size", "hga_decode", "hga_route_noalloc", "hga_attn_bwd_staged",
+           "hga_decode_twopass", "hga_summaries_to_bf16")
 
 KERNELS = ("summaries", "route", "gather", "attn_fwd", "bwd_dq", "bwd_dkdv", "gcache", "decode")
 
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         "hga_gcache_reset": [SP, P, I32, P],
         "hga_route_cached": [SP, P, P, P, P, I32, P, P, P, P, SZ, P],
         "hga_decode": [SP, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "hga_decode_twopass": [SP, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "hga_summaries_to_bf16": [P, P, ctypes.c_int64, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -312,20 +315,20 @@ def hga_decode_workspace_size(shape: Shape, batch: int, n_new: int) -> int:
     return int(lib().hga_decode_workspace_size(ctypes.byref(shape), batch, n_new))
 
 
-def hga_decode(shape: Shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens,
-               tail_lens, sel_chunks, sel_groups, o, lse, ws=None, stream=None) -> None:
-    """One decode step for a batch (layouts of include/hga.h: q [B][n_q][n_new][d],
-    history [B][n_kv][P][d], open segment [B][n_kv][T][d], lengths int32 [B] on the GPU)."""
+def _decode_call(entry, shape: Shape, q, k_hist, v_hist, chunk_sum, chunk_sum_bf16, group_sum, k_tail,
+                 v_tail, hist_lens, tail_lens, sel_chunks, sel_groups, o, lse, ws, stream) -> None:
     B, nq, n_new, d = q.shape
     kv, P, T, dt = shape.n_kv_heads, shape.hist_rows, shape.seg_len, shape.torch_dtype
     if ws is None:
         n = hga_decode_workspace_size(shape, B, n_new)
         ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().hga_decode(
+    lo = () if chunk_sum_bf16 is False else (
+        _ptr(chunk_sum_bf16, (B, kv, P // 64, d), torch.bfloat16, "chunk_sum_bf16"),)
+    _check(entry(
         ctypes.byref(shape), B, n_new, _ptr(q, (B, shape.n_q_heads, n_new, d), dt, "q"),
         _ptr(k_hist, (B, kv, P, d), dt, "k_hist", shape.hist_loc != HGA_HIST_HOST_PINNED),
         _ptr(v_hist, (B, kv, P, d), dt, "v_hist", shape.hist_loc != HGA_HIST_HOST_PINNED),
-        _ptr(chunk_sum, (B, kv, P // 64, d), torch.float32, "chunk_sum"),
+        _ptr(chunk_sum, (B, kv, P // 64, d), torch.float32, "chunk_sum"), *lo,
         _ptr(group_sum, (B, kv, P // 8, d), torch.float32, "group_sum"),
         _ptr(k_tail, (B, kv, T, d), dt, "k_tail"), _ptr(v_tail, (B, kv, T, d), dt, "v_tail"),
         _ptr(hist_lens, (B,), torch.int32, "hist_lens"), _ptr(tail_lens, (B,), torch.int32, "tail_lens"),
@@ -335,17 +338,53 @@ def hga_decode(shape: Shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def hga_decode(shape: Shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens,
+               tail_lens, sel_chunks, sel_groups, o, lse, ws=None, stream=None) -> None:
+    """One decode step for a batch (layouts of include/hga.h: q [B][n_q][n_new][d],
+    history [B][n_kv][P][d], open segment [B][n_kv][T][d], lengths int32 [B] on the GPU)."""
+    _decode_call(lib().hga_decode, shape, q, k_hist, v_hist, chunk_sum, False, group_sum, k_tail, v_tail,
+                 hist_lens, tail_lens, sel_chunks, sel_groups, o, lse, ws, stream)
+
+
+def hga_decode_twopass(shape: Shape, q, k_hist, v_hist, chunk_sum, chunk_sum_bf16, group_sum, k_tail,
+                       v_tail, hist_lens, tail_lens, sel_chunks, sel_groups, o, lse, ws=None,
+                       stream=None) -> None:
+    """hga_decode with the two-pass chunk route; chunk_sum_bf16 (torch.bfloat16, the
+    layout of chunk_sum) holds hga_summaries_to_bf16 of chunk_sum."""
+    _decode_call(lib().hga_decode_twopass, shape, q, k_hist, v_hist, chunk_sum, chunk_sum_bf16, group_sum,
+                 k_tail, v_tail, hist_lens, tail_lens, sel_chunks, sel_groups, o, lse, ws, stream)
+
+
+def hga_summaries_to_bf16(src, dst, stream=None) -> None:
+    """dst (torch.bfloat16) = src (torch.float32, same shape) rounded to nearest even."""
+    _check(lib().hga_summaries_to_bf16(_ptr(src, tuple(src.shape), torch.float32, "src"),
+                                       _ptr(dst, tuple(src.shape), torch.bfloat16, "dst"),
+                                       src.numel(), _stream(stream)))
+
+
+def summaries_to_bf16(src):
+    """Allocate and fill the bf16 copies of fp32 summaries."""
+    dst = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    hga_summaries_to_bf16(src, dst)
+    return dst
+
+
 def decode(shape: Shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens, tail_lens,
-           ws=None):
-    """Allocate the outputs and run hga_decode: (o, lse, sel_chunks, sel_groups)."""
+           ws=None, chunk_sum_bf16=None):
+    """Allocate the outputs and run hga_decode, or hga_decode_twopass when
+    chunk_sum_bf16 is given: (o, lse, sel_chunks, sel_groups)."""
     B, nq, n_new, _ = q.shape
     dev = q.device
     sc = torch.empty((B, shape.n_kv_heads, shape.top_k_chunks), dtype=torch.int32, device=dev)
     sg = torch.empty((B, shape.n_kv_heads, shape.top_k_groups), dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, nq, n_new), dtype=torch.float32, device=dev)
-    hga_decode(shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens, tail_lens,
-               sc, sg, o, lse, ws)
+    if chunk_sum_bf16 is None:
+        hga_decode(shape, q, k_hist, v_hist, chunk_sum, group_sum, k_tail, v_tail, hist_lens, tail_lens,
+                   sc, sg, o, lse, ws)
+    else:
+        hga_decode_twopass(shape, q, k_hist, v_hist, chunk_sum, chunk_sum_bf16, group_sum, k_tail, v_tail,
+                           hist_lens, tail_lens, sc, sg, o, lse, ws)
     return o, lse, sc, sg
 
 

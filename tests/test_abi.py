@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "hga.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hga_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hga_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.hga_abi_version() == 3
+    assert L.hga_abi_version() == 4
     assert L.hga_status_string(0) == b"HGA_OK"
     assert L.hga_status_string(3) == b"HGA_ERR_WORKSPACE"
     assert L.hga_status_string(99) == b"HGA_ERR_UNKNOWN"
@@ -261,3 +261,24 @@ def test_decode_arguments_and_workspace(L):
     assert dec(s, 4, 1, None, n) == hga.HGA_ERR_WORKSPACE
     nh = L.hga_decode_workspace_size(ctypes.byref(host), 4, 1)
     assert dec(host, 4, 1, FAKE, nh - 1) == hga.HGA_ERR_WORKSPACE
+
+
+def test_decode_twopass_and_bf16_copy_arguments(L):
+    """hga_decode_twopass: hga_decode's checks plus a non-NULL, 16-byte aligned
+    bf16 copy of the chunk summaries; hga_summaries_to_bf16: n a multiple of 8,
+    aligned pointers. All rejected on the host before any launch."""
+    s = _shape()
+    n = L.hga_decode_workspace_size(ctypes.byref(s), 4, 1)
+    dec2 = lambda sh, batch, n_new, lo, ws, nbytes: L.hga_decode_twopass(  # noqa: E731
+        ctypes.byref(sh), batch, n_new, *([FAKE] * 4), lo, *([FAKE] * 9), ws, nbytes, None)
+    assert dec2(s, 4, 1, None, FAKE, n) == hga.HGA_ERR_INVALID_ARG          # no bf16 copy
+    assert dec2(s, 4, 1, FAKE + 2, FAKE, n) == hga.HGA_ERR_INVALID_ARG      # misaligned copy
+    assert b"chunk_sum_bf16" in L.hga_last_error()
+    assert dec2(s, 0, 1, FAKE, FAKE, n) == hga.HGA_ERR_INVALID_ARG          # the hga_decode checks follow
+    assert dec2(s, 4, 5, FAKE, FAKE, n) == hga.HGA_ERR_UNSUPPORTED
+    assert dec2(s, 4, 1, FAKE, FAKE, n - 1) == hga.HGA_ERR_WORKSPACE
+    assert L.hga_summaries_to_bf16(None, None, 0, None) == hga.HGA_OK       # nothing to do
+    assert L.hga_summaries_to_bf16(FAKE, FAKE, 12, None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_summaries_to_bf16(FAKE, FAKE, -8, None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_summaries_to_bf16(None, FAKE, 16, None) == hga.HGA_ERR_INVALID_ARG
+    assert L.hga_summaries_to_bf16(FAKE, FAKE + 4, 16, None) == hga.HGA_ERR_INVALID_ARG

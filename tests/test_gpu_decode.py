@@ -28,10 +28,12 @@ def _f64(t):
 
 
 def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new, seed, sink=0,
-               window=0, check_outputs=True, pinned_host=False):
+               window=0, check_outputs=True, pinned_host=False, twopass=True):
     """Decode one ragged batch, check it against the oracle sequence by
     sequence; with pinned_host, run it again with the history in page-locked
-    host memory and require bit-identical results."""
+    host memory and require bit-identical results; with twopass, run it again
+    through hga_decode_twopass (bf16 copies of the chunk summaries) and
+    require bit-identical results."""
     print(f"[case] decode nq={n_q} nkv={n_kv} d={d} P={P} T={T} kc={k_c} kg={k_g} {dtype} "
           f"hist={list(hist_lens)} tail={list(tail_lens)} n_new={n_new} sink={sink} W={window}",
           flush=True)
@@ -52,6 +54,8 @@ def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new,
     o, lse, sc, sg = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
                                 g["hist_lens"], g["tail_lens"])
     torch.cuda.synchronize()
+    if twopass:
+        _assert_twopass_identical(s, g, C, G, (o, lse, sc, sg))
     if pinned_host:
         print("  the same batch with the history in pinned host memory", flush=True)
         kh_p = torch.empty(inp["k_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
@@ -91,6 +95,21 @@ def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new,
             ok = orc.lse_within(got, ref) if name == "LSE" else orc.within_tolerance(got, ref, tol)
             assert ok, (b, name, err, rel)
     return o, lse, sc, sg
+
+
+def _assert_twopass_identical(s, g, C, G, ref):
+    """hga_decode_twopass on bf16 copies of C gives hga_decode's outputs bit for
+    bit; the copies themselves are torch's round-to-nearest-even of C."""
+    print("  two-pass chunk route on bf16 copies", flush=True)
+    lo = hga.summaries_to_bf16(C)
+    fin = torch.isfinite(C)
+    assert torch.equal(lo[fin], C[fin].to(torch.bfloat16))
+    assert torch.isnan(lo[torch.isnan(C)].float()).all()
+    out = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
+                     g["hist_lens"], g["tail_lens"], chunk_sum_bf16=lo)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("o", "lse", "sel_chunks", "sel_groups"), out, ref):
+        assert torch.equal(a, b), name
 
 
 def test_decode_ragged_batch_one_new_token():
@@ -320,3 +339,56 @@ def test_decode_random_long_histories(case):
     _, n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new, sink, window = case
     run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist, tail, n_new=n_new, seed=8, sink=sink,
                window=window)
+
+
+def _twopass_variants(C, seed):
+    """Chunk summaries built to stress the two-pass bound: the real ones,
+    identical rows (every chunk ties), rows equal in bf16 but apart in fp32
+    (the order is decided by fp32 alone), zeros, huge and subnormal scales
+    (fallback and absolute-bound paths), a NaN and an infinite row."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    B, kv, R, d = C.shape
+    base = C[:, :, :1].clone()
+    yield "real", C
+    yield "identical", base.expand(-1, -1, R, -1).contiguous()
+    tie = base.expand(-1, -1, R, -1).clone()
+    # chunks differ in one coordinate by less than a quarter of a bf16 ulp
+    # (relative 2^-9), in shuffled order: their copies mostly coincide
+    perm = torch.randperm(R, generator=gen).to(C.device).view(1, 1, R).float()
+    tie[..., 0] = tie[..., 0] * (1 + perm * 2.0 ** -20)
+    yield "bf16-ties", tie.contiguous()
+    yield "zeros", torch.zeros_like(C)
+    yield "huge", (C * 1e35).contiguous()
+    yield "subnormal", (C * 1e-39).contiguous()
+    bad = C.clone()
+    bad[0, 0, R // 3, 5] = float("nan")
+    bad[-1, -1, R // 2, 7] = float("inf")
+    yield "nan-inf", bad
+
+
+@pytest.mark.parametrize("B,P", [(4, 16384), (4, 32768), (9, 32768)],
+                         ids=["unsplit-256", "split-8x64", "unsplit-512"])
+def test_decode_twopass_adversarial_summaries(B, P):
+    """hga_decode_twopass equals hga_decode bit for bit on chunk summaries made
+    to defeat the bf16 bound: 256 chunks in one workgroup, 512 chunks split in
+    8 parts of 64 (a split scan reads no copies: both run the fp32 scan), and
+    512 chunks in one workgroup (every chunk a candidate: the fp32 scan)."""
+    n_q, n_kv, d, T = 8, 8, 64, 64
+    hist = [P - 64 * b for b in range(B)]
+    tail = [64 - b for b in range(B)]
+    w = synth.Workload("decode", n_q, n_kv, d, P, T, 16, 32, "bf16", 1.0 / math.sqrt(d))
+    print(f"[case] decode two-pass adversarial B={B} P={P}", flush=True)
+    inp = synth.make_decode_inputs(w, hist, tail, 1, 31 + B)
+    g = {k: v.cuda() for k, v in inp.items()}
+    s = hga.make_shape(n_q, n_kv, d, P, T, 16, 32, torch.bfloat16, w.softmax_scale)
+    C = torch.zeros((B, n_kv, P // 64, d), dtype=torch.float32, device="cuda")
+    G = torch.zeros((B, n_kv, P // 8, d), dtype=torch.float32, device="cuda")
+    for b in range(B):
+        sb = hga.make_shape(n_q, n_kv, d, hist[b], T, 16, 32, torch.bfloat16, hist_stride=P)
+        hga.hga_build_summaries(sb, g["k_hist"][b], C[b], G[b])
+    for name, Cv in _twopass_variants(C, 7 + B):
+        print(f"  summaries: {name}", flush=True)
+        ref = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], Cv, G, g["k_tail"], g["v_tail"],
+                         g["hist_lens"], g["tail_lens"])
+        torch.cuda.synchronize()
+        _assert_twopass_identical(s, g, Cv, G, ref)

@@ -221,6 +221,34 @@ def test_exact_arithmetic_route_is_bit_exact():
     assert np.array_equal(sel_g.cpu().numpy(), ref_g)
 
 
+@pytest.mark.parametrize("n_tied", [300, 600])
+def test_route_mass_ties_are_bit_exact(n_tied):
+    """600 history chunks, 3 planted above the rest and n_tied whole-chunk ties
+    just below them (integer inputs: every score exact). The chunk top-k takes
+    the planted chunks and then the lowest-index tied ones, with the radix
+    select's threshold key shared by hundreds of chunks."""
+    H, S, kc, kg = 600 * 64, 256, 6, 12
+    w = _w(f"bf16_mass_ties_{n_tied}", 8, 2, 128, H, S, kc, kg, "bf16", bwd=False)
+    _say(f"[case] {w.name}")
+    rng = np.random.default_rng(11)
+    q = torch.from_numpy(rng.integers(0, 2, (8, S, 128)).astype(np.float32)).bfloat16()
+    pat = rng.integers(1, 4, (2, 64, 128)).astype(np.float32)      # one chunk's keys
+    k = np.tile(pat, (1, 600, 1)) - (np.arange(H) >= 64 * n_tied)[None, :, None]
+    for c in (5, 77, 410):                                         # planted chunks
+        k[:, 64 * c:64 * (c + 1)] += 1.0
+    k = torch.from_numpy(k.astype(np.float32)).bfloat16()
+    s = _shape(w)
+    C, G = hga.summaries(s, k.cuda())
+    sel_c, sel_g = hga.route(s, q.cuda(), C, G)
+    torch.cuda.synchronize()
+    ref_c, ref_g, _ = orc.route(q.float().numpy(), k.float().numpy(), 2, kc, kg)
+    assert np.array_equal(sel_c.cpu().numpy(), ref_c)
+    assert np.array_equal(sel_g.cpu().numpy(), ref_g)
+    planted = [5, 77, 410] if n_tied > 410 else [5, 77]
+    ties = [c for c in range(n_tied) if c not in planted][:kc - len(planted)]
+    assert (ref_c == np.array(sorted(planted + ties))).all()
+
+
 def test_arbitrary_selection_with_holes():
     """Selections with -1 holes anywhere (not only at the end) are masked."""
     w = _w("bf16_holes", 8, 2, 128, 1024, 192, 4, 24, "bf16")
