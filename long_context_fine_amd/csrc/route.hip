@@ -127,27 +127,29 @@ __device__ int block_scan_excl(int v, int* total, int32_t* wsum) {
 // (1 <= need <= n; need = 0 selects nothing): 8-bit digits, most significant
 // first, one LDS histogram (256 bins, one per thread) per pass. Histograms and
 // selections alternate between two buffers by pass, so a pass needs four
-// barriers: counts done, two in the scan, selection. Every thread returns the
-// same result:
+// barriers: counts done, two in the scan, selection. The digits below bit
+// last_shift are left open. Every thread returns the same result:
+//   whole:  the keys k with (k & pmask) >= prefix are exactly the need
+//           largest (the threshold bin is taken whole);
 //   exact:  the need-th largest key equals prefix (all 32 bits fixed) and
 //           `need` of the keys equal to prefix are still to be taken;
-//   !exact: the keys k with (k & pmask) >= prefix are exactly the need
-//           largest (the threshold bin is taken whole).
+//   neither (last_shift > 0): the need-th largest key has prefix under pmask,
+//           so it lies in [prefix, prefix | ~pmask].
 struct RadixSel {
   uint32_t prefix, pmask;
   int need;
-  bool exact;
+  bool exact, whole;
 };
 
 __device__ RadixSel radix_select(const float* sc, int n, int need, int32_t (*hist_s)[kThreads],
-                                 int32_t (*rsel)[3], int32_t* scan_ws) {
+                                 int32_t (*rsel)[3], int32_t* scan_ws, int last_shift = 0) {
   static_assert(kThreads == 256, "one histogram bin per thread");
   const int t = threadIdx.x;
-  RadixSel rs{0u, 0u, need, false};
+  RadixSel rs{0u, 0u, need, false, false};
   hist_s[0][t] = 0;
   __syncthreads();
   int hb = 0;
-  for (int shift = 24; shift >= 0 && need > 0; shift -= 8, hb ^= 1) {
+  for (int shift = 24; shift >= last_shift && need > 0; shift -= 8, hb ^= 1) {
     for (int m = t; m < n; m += kThreads) {
       const uint32_t k = score_key(sc[m]);
       if ((k & rs.pmask) == rs.prefix) atomicAdd(&hist_s[hb][(k >> shift) & 255u], 1);
@@ -167,7 +169,10 @@ __device__ RadixSel radix_select(const float* sc, int n, int need, int32_t (*his
     rs.prefix |= static_cast<uint32_t>(rsel[hb][0]) << shift;
     rs.pmask |= 255u << shift;
     rs.need -= rsel[hb][1];
-    if (rsel[hb][2] == rs.need) break;          // the whole bin is kept
+    if (rsel[hb][2] == rs.need) {               // the whole bin is kept
+      rs.whole = true;
+      break;
+    }
     if (shift == 0) rs.exact = true;
   }
   return rs;
@@ -215,9 +220,11 @@ __device__ __forceinline__ int ordered_pos(const uint64_t* wmask, int c) {
 // loads of 16 bytes (lane sub reads elements [8(8c + sub), 8(8c + sub) + 8)),
 // 8*UNROLL rows per wave in flight. Also returns, per thread, the largest
 // sum over a row of |qv[e]| * |row[e]| among the rows it reduced, as raw bits
-// with the sign cleared (a NaN compares above every number).
+// with the sign cleared (a NaN compares above every number), and in *q1 the
+// sum of |qv[e]| (the same bits in every lane).
 template <int D, int UNROLL, class RowPtr>
-__device__ __forceinline__ uint32_t score_rows_bf16(const float* qv, int n, RowPtr row_ptr, float* out) {
+__device__ __forceinline__ uint32_t score_rows_bf16(const float* qv, int n, RowPtr row_ptr, float* out,
+                                                    float* q1) {
   constexpr int LPR = 8;                 // lanes per row
   constexpr int EPL = D / LPR;           // elements per lane (16 or 8)
   constexpr int VPL = EPL / 8;           // 16-byte loads per lane and row
@@ -231,6 +238,12 @@ __device__ __forceinline__ uint32_t score_rows_bf16(const float* qv, int n, RowP
   for (int c = 0; c < VPL; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) qr[8 * c + e] = qv[(c * LPR + sub) * 8 + e];
+  {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a += fabsf(qr[e]);
+    *q1 = sum8_f32(a);               // the 8 lanes of a row hold all of qv
+  }
   using Buf = uint4[UNROLL][VPL];
   auto load = [&](int r0, Buf& v) {
 #pragma unroll
@@ -350,7 +363,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   constexpr bool kTwoPass = MODE == kRouteDecode;
   __shared__ int32_t cidx_s[kTwoPass ? kMaxCand : 1];      // two-pass candidates (ascending)
   __shared__ uint32_t red_s[2];                             // two-pass: max |q||C~| bits, threshold key
-  __shared__ float thr_s;
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   // KV head fastest: with 8 KV heads all workgroups of head j run on one XCD
@@ -464,8 +476,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         }
         __syncthreads();
         const uint16_t* lbase = dec.csum_lo + (static_cast<int64_t>(j) * chunk_rows + chunk0) * D;
+        float q1;
         uint32_t am = score_rows_bf16<D, 4>(
-            qv, n_chunks, [&](int m) { return lbase + static_cast<int64_t>(m) * D; }, sc);
+            qv, n_chunks, [&](int m) { return lbase + static_cast<int64_t>(m) * D; }, sc, &q1);
 #pragma unroll
         for (int o = kWave / 2; o > 0; o >>= 1)
           am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), o, kWave)));
@@ -473,8 +486,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         __syncthreads();
         const float amax = __uint_as_float(red_s[0]);
         if (amax <= 1e30f) {                    // the same for every thread; false for NaN
-          const RadixSel rs = radix_select(sc, n_chunks, k_c, hist_s, rsel, scan_ws);
-          if (!rs.exact) {
+          // tau only bounds the candidates from below: two digits (sign,
+          // exponent, 7 mantissa bits) leave it within 2^-7 of the k_c-th
+          // largest s~, well inside the 2e band
+          const RadixSel rs = radix_select(sc, n_chunks, k_c, hist_s, rsel, scan_ws, 16);
+          if (rs.whole) {
             // the threshold bin was taken whole: tau is its smallest key
             uint32_t kmin = 0xffffffffu;
             for (int m = t; m < n_chunks; m += kThreads) {
@@ -487,14 +503,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
             if (lane == 0) atomicMin(&red_s[1], kmin);
           }
           __syncthreads();
-          if (t == 0) {
-            float q1 = 0.f;
-            for (int e = 0; e < D; ++e) q1 += fabsf(qv[e]);
-            const float bound = 0.0045f * amax + 1e-30f * (1.f + q1);
-            thr_s = key_score(rs.exact ? rs.prefix : red_s[1]) - 2.f * bound;
-          }
-          __syncthreads();
-          const float thr = thr_s;
+          // the same value in every thread: tau is the bin's smallest key, or
+          // the k_c-th largest key's lower bound with the open digits 0
+          const float bound = 0.0045f * amax + 1e-30f * (1.f + q1);
+          const float thr = key_score(rs.whole ? red_s[1] : rs.prefix) - 2.f * bound;
           // candidates in ascending chunk order: thread t owns [t*E, t*E + E)
           const int E = (n_chunks + kThreads - 1) / kThreads;
           const int m0 = min(t * E, n_chunks), m1 = min(m0 + E, n_chunks);
