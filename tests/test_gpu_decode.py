@@ -54,8 +54,7 @@ def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new,
     o, lse, sc, sg = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
                                 g["hist_lens"], g["tail_lens"])
     torch.cuda.synchronize()
-    if twopass:
-        _assert_twopass_identical(s, g, C, G, (o, lse, sc, sg))
+    lo = _assert_twopass_identical(s, g, C, G, (o, lse, sc, sg)) if twopass else None
     if pinned_host:
         print("  the same batch with the history in pinned host memory", flush=True)
         kh_p = torch.empty(inp["k_hist"].shape, dtype=w.torch_dtype, pin_memory=True)
@@ -69,6 +68,13 @@ def run_decode(n_q, n_kv, d, P, T, k_c, k_g, dtype, hist_lens, tail_lens, n_new,
         torch.cuda.synchronize()
         assert torch.equal(sc2, sc) and torch.equal(sg2, sg)
         assert torch.equal(o2, o) and torch.equal(lse2, lse)
+        if lo is not None:
+            print("  pinned host memory with the two-pass route", flush=True)
+            out = hga.decode(sh, g["q"], kh_p, vh_p, C, G, g["k_tail"], g["v_tail"], g["hist_lens"],
+                             g["tail_lens"], chunk_sum_bf16=lo)
+            torch.cuda.synchronize()
+            for name, a, b in zip(("o", "lse", "sel_chunks", "sel_groups"), out, (o, lse, sc, sg)):
+                assert torch.equal(a, b), name
     tol = TOL[dtype]
     for b in range(B):
         H, Tb = hist_lens[b], tail_lens[b]
@@ -110,6 +116,7 @@ def _assert_twopass_identical(s, g, C, G, ref):
     torch.cuda.synchronize()
     for name, a, b in zip(("o", "lse", "sel_chunks", "sel_groups"), out, ref):
         assert torch.equal(a, b), name
+    return lo
 
 
 def test_decode_ragged_batch_one_new_token():
