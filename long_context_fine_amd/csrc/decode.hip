@@ -570,7 +570,10 @@ __global__ __launch_bounds__(256) void decode_stage_kernel(const uint4* __restri
   static_assert(PER * 256 == kStageRows * CPR, "whole rows per workgroup");
   const int64_t bj = blockIdx.y;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kStageRows;
-  uint4 kv[PER], vv[PER];
+  // a native vector type: arrays of the HIP vector struct, loaded under a
+  // branch, went to scratch, each store then waiting for its load
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 kv[PER], vv[PER];
   int64_t dst[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -588,16 +591,16 @@ __global__ __launch_bounds__(256) void decode_stage_kernel(const uint4* __restri
     dst[i] = -1;
     if (src >= 0) {
       const int64_t o = (bj * P + src) * CPR + ch;
-      kv[i] = k_hist[o];
-      vv[i] = v_hist[o];
+      kv[i] = reinterpret_cast<const u32x4*>(k_hist)[o];
+      vv[i] = reinterpret_cast<const u32x4*>(v_hist)[o];
       dst[i] = (bj * stage_rows + row) * CPR + ch;
     }
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (dst[i] >= 0) {
-      k_st[dst[i]] = kv[i];
-      v_st[dst[i]] = vv[i];
+      reinterpret_cast<u32x4*>(k_st)[dst[i]] = kv[i];
+      reinterpret_cast<u32x4*>(v_st)[dst[i]] = vv[i];
     }
   }
 }
