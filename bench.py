@@ -307,6 +307,17 @@ def tbptt_sweep(args):
                               "(append K/V, summaries) runs outside the timing"}), flush=True)
 
 
+def calibration_copy(mib, dev):
+    """A plain device copy of known size: what a profiler's HBM byte counters
+    read for it scales theirs for the kernels of the same run."""
+    import torch
+    src = torch.ones(mib * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def decode_bench(args):
     """Decode step (hga_decode) for a ragged batch: sequence b holds a history
     of H - 64 * ((13 b) % 32) tokens (H = the workload's history length) and
@@ -454,6 +465,8 @@ def decode_bench(args):
                 "peak": PEAK_HOST_LINK_GBS, "unit": "GB/s", "frac": round(link / PEAK_HOST_LINK_GBS, 4),
                 "measured_link_gbs": round(measured, 1), "frac_of_measured": round(link / measured, 4),
                 "traffic": None}
+    if args.copy_calibration_mib > 0:
+        calibration_copy(args.copy_calibration_mib, dev)
     print(json.dumps({
         "mode": "decode", "metric": "decode tokens/s (HGA route + attention, one layer)",
         "value": round(B * n_new * args.steps / elapsed, 1), "unit": "tokens/s",
@@ -808,12 +821,7 @@ def main():
                      "host_gbs": round(moved / (upd_us * 1e-6) / 1e9, 1)},
         }
     if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * 2 ** 20 // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        calibration_copy(args.copy_calibration_mib, dev)
         out["copy_calibration_mib"] = args.copy_calibration_mib
     if args.cpu_baseline == "on":
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
