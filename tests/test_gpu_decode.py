@@ -399,3 +399,27 @@ def test_decode_twopass_adversarial_summaries(B, P):
                          g["hist_lens"], g["tail_lens"])
         torch.cuda.synchronize()
         _assert_twopass_identical(s, g, Cv, G, ref)
+
+
+def test_summaries_to_bf16_special_values_and_ragged_length():
+    """hga_summaries_to_bf16 rounds to nearest even like torch: zeros of both
+    signs, subnormals, halfway cases, values that overflow to infinity,
+    infinities and NaN; a length of 8 * 1001 elements leaves a ragged last
+    workgroup, and an empty call does nothing."""
+    print("[case] bf16 copies: special values, 8008 elements", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    x = torch.randn(8 * 1001, generator=gen)
+    special = torch.tensor([0.0, -0.0, 1e-40, -1e-40, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 3.39e38, 3.4e38,
+                            -3.4e38, float("inf"), float("-inf"), float("nan")])
+    x[: special.numel()] = special
+    x[100:200] *= 1e-39
+    src = x.cuda()
+    dst = torch.full(src.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    hga.hga_summaries_to_bf16(src, dst)
+    hga.hga_summaries_to_bf16(src[:0], dst[:0])
+    torch.cuda.synchronize()
+    want = x.to(torch.bfloat16)
+    got = dst.cpu()
+    nan = torch.isnan(x)
+    assert torch.isnan(got[nan].float()).all()
+    assert torch.equal(got[~nan].view(torch.int16), want[~nan].view(torch.int16))
