@@ -423,3 +423,50 @@ def test_summaries_to_bf16_special_values_and_ragged_length():
     nan = torch.isnan(x)
     assert torch.isnan(got[nan].float()).all()
     assert torch.equal(got[~nan].view(torch.int16), want[~nan].view(torch.int16))
+
+
+def test_decode_twopass_over_a_growing_history():
+    """A decode loop whose history grows: at every step some sequences close a
+    chunk, whose summaries are built on their own and whose sequence's bf16
+    copies are refreshed; hga_decode_twopass equals hga_decode bit for bit at
+    every step, and the incrementally built summaries equal a full build."""
+    n_q, n_kv, d, P, T, B = 8, 8, 64, 32768, 64, 9
+    hist = [P - 64 * (4 + b) for b in range(B)]
+    tail = [64 - 3 * b for b in range(B)]
+    w = synth.Workload("decode", n_q, n_kv, d, P, T, 16, 32, "bf16", 1.0 / math.sqrt(d))
+    print(f"[case] decode two-pass, growing history B={B} P={P}", flush=True)
+    inp = synth.make_decode_inputs(w, hist, tail, 1, 41)
+    g = {k: v.cuda() for k, v in inp.items()}
+    s = hga.make_shape(n_q, n_kv, d, P, T, 16, 32, torch.bfloat16, w.softmax_scale)
+    C = torch.zeros((B, n_kv, P // 64, d), dtype=torch.float32, device="cuda")
+    G = torch.zeros((B, n_kv, P // 8, d), dtype=torch.float32, device="cuda")
+
+    def close(b, t0, t1):
+        sb = hga.make_shape(n_q, n_kv, d, t1, T, 16, 32, torch.bfloat16, hist_stride=P)
+        hga.hga_build_summaries(sb, g["k_hist"][b], C[b], G[b], t0, t1)
+
+    for b in range(B):
+        close(b, 0, hist[b])
+    lo = hga.summaries_to_bf16(C)
+    for step in range(4):
+        for b in range(B):
+            if (b + step) % 2 == 0:
+                hist[b] += 64
+                close(b, hist[b] - 64, hist[b])
+                hga.hga_summaries_to_bf16(C[b], lo[b])
+        g["hist_lens"] = torch.tensor(hist, dtype=torch.int32, device="cuda")
+        print(f"  step {step}: hist={hist}", flush=True)
+        ref = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
+                         g["hist_lens"], g["tail_lens"])
+        out = hga.decode(s, g["q"], g["k_hist"], g["v_hist"], C, G, g["k_tail"], g["v_tail"],
+                         g["hist_lens"], g["tail_lens"], chunk_sum_bf16=lo)
+        torch.cuda.synchronize()
+        for name, a, b_ in zip(("o", "lse", "sel_chunks", "sel_groups"), out, ref):
+            assert torch.equal(a, b_), (step, name)
+    C2 = torch.zeros_like(C)
+    G2 = torch.zeros_like(G)
+    for b in range(B):
+        sb = hga.make_shape(n_q, n_kv, d, hist[b], T, 16, 32, torch.bfloat16, hist_stride=P)
+        hga.hga_build_summaries(sb, g["k_hist"][b], C2[b], G2[b])
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2) and torch.equal(G, G2)
