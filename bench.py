@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--decode-host", action="store_true",
                     help="decode with the history in page-locked host memory: each step copies the "
                          "sink rows and routed groups over the host link before the attention")
+    ap.add_argument("--also", default="auto",
+                    help="comma-separated workloads also timed, each in a child process, and "
+                         "summarised under other_configs; 'auto': the other Qwen3-8B "
+                         "workloads when the default one runs, 'none': nothing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB (one plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -484,6 +488,48 @@ def decode_bench(args):
     }))
 
 
+ALSO_DEFAULT = ("qwen3_8b_16k_fwd", "qwen3_8b_131k_fwd", "qwen3_8b_131k_fwd_host")
+
+
+def other_configs(args):
+    """Time further workloads, each in a child process of this script (its
+    own JSON line, no CPU baseline), and keep the figures that compare them:
+    throughput, step time, the dominant kernel's roofline, the route and the
+    per-kernel durations. Called before this process initialises the GPU."""
+    import subprocess
+    if args.also == "none":
+        return None
+    if args.also == "auto":
+        if args.workload != "qwen3_8b_16k_fwdbwd":
+            return None
+        names = ALSO_DEFAULT
+    else:
+        names = [n for n in args.also.split(",") if n]
+    res = {}
+    for name in names:
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--also", "none",
+               "--cpu-baseline", "off", "--steps", str(args.steps), "--warmup", str(args.warmup),
+               "--seed", str(args.seed)]
+        print(f"bench.py: timing {name} in a child process", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=600)
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            res[name] = {"error": f"exit {r.returncode}", "stderr_tail": r.stderr[-400:]}
+            continue
+        d = json.loads(lines[-1])
+        ent = {k: d[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "roofline",
+                                 "route") if k in d}
+        ent["config"] = {k: d["config"][k] for k in ("context_tokens", "hist_len", "pass", "history")}
+        ent["kernels_avg_us"] = {k: v["avg_us"] for k, v in d.get("kernels", {}).items()}
+        if "gather_device" in d:
+            ent["gather_device"] = {k: d["gather_device"][k] for k in ("avg_us", "gbs", "frac_hbm", "cold")
+                                    if k in d["gather_device"]}
+        ent["child_wall_s"] = round(time.perf_counter() - t0, 1)
+        res[name] = ent
+    return res
+
+
 def main():
     args = parse()
     if args.tbptt_max_hist:
@@ -496,6 +542,8 @@ def main():
               f"WORLD_SIZE {world}); the path would shard by KV head across GPUs, which is "
               "not implemented here.", file=sys.stderr)
         sys.exit(2)
+    # the children run before this process touches the GPU
+    others = other_configs(args)
 
     import torch
     from long_context_fine_amd import hga, synth
@@ -825,6 +873,8 @@ def main():
         out["copy_calibration_mib"] = args.copy_calibration_mib
     if args.cpu_baseline == "on":
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    if others:
+        out["other_configs"] = others
     print(json.dumps(out), flush=True)
 
 

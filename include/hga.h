@@ -126,8 +126,9 @@ typedef struct {
  * k_hist lives where shape->hist_loc says (device or pinned host); chunk_sum
  * is device memory; group_sum is device memory or page-locked host memory
  * (hipHostMalloc; recognised by its pointer attributes, written over the host
- * link) for use with hga_route_cached. Summaries outside the range are
- * untouched. */
+ * link) for use with hga_route_cached. Both are 16-byte aligned (rows are
+ * written 16 bytes at a time), else HGA_ERR_INVALID_ARG. Summaries outside the
+ * range are untouched. */
 hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist,
                                int64_t tok_begin, int64_t tok_end,
                                float* chunk_sum, float* group_sum, void* stream);

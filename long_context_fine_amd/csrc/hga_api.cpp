@@ -298,6 +298,8 @@ hga_status hga_build_summaries(const hga_shape* shape, const void* k_hist, int64
               "token range bounds must be multiples of 64");
   if (tok_end == tok_begin) return ok();
   HGA_REQUIRE(k_hist && chunk_sum && group_sum, "k_hist, chunk_sum and group_sum must be non-NULL");
+  HGA_REQUIRE(reinterpret_cast<uintptr_t>(chunk_sum) % 16 == 0 && reinterpret_cast<uintptr_t>(group_sum) % 16 == 0,
+              "chunk_sum and group_sum must be 16-byte aligned");
   const void* kd = k_hist;
   if (s.hist_loc == HGA_HIST_HOST_PINNED) HGA_TRY(host_to_device_ptr(k_hist, &kd, "k_hist"));
   float* gd = group_sum;

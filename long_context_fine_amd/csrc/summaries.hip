@@ -1,64 +1,66 @@
 // Chunk and group summaries: segmented means of the history keys.
 //
-// One workgroup summarises one 64-token chunk of one KV head: it streams the
-// chunk's keys once (coalesced 16-byte loads, 256 B per token row), forms the
-// eight 8-token group sums in LDS, and derives the chunk sum from them. HBM
+// One workgroup summarises one 64-token chunk of one KV head with D threads:
+// thread (g, c) owns group g (8 tokens) and the 8 dims c*8..c*8+7, loads its
+// eight 16-byte (bf16) pieces at once, sums them in registers and writes its
+// part of the group mean straight to memory; the chunk sum then adds the
+// eight group sums through LDS after one barrier. Every load of the chunk is
+// in flight before any add, and only the chunk sums pass through LDS. HBM
 // bound: per chunk it reads 64*d elements and writes 9*d floats.
+// Summation order (bitwise the same for every launch shape): a group sum is
+// (k0+k1+k2+k3) + (k4+k5+k6+k7); a chunk sum adds the group sums in order,
+// each sum starting from +0.
 #include "hga_common.hpp"
 
 namespace hga {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;   // round_bf16_kernel
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void build_summaries_kernel(
+__global__ __launch_bounds__(D) void build_summaries_kernel(
     const T* __restrict__ k_hist, int64_t hist_rows, int64_t chunk_begin,
     float* __restrict__ chunk_sum, float* __restrict__ group_sum) {
-  constexpr int TPR = D / 8;                  // threads per token row
-  constexpr int RG = kThreads / TPR;          // row groups
-  constexpr int TOK_PER_RG = kChunk / RG;     // consecutive tokens per row group
-  constexpr int RG_PER_GROUP = kGroup / TOK_PER_RG;
-  static_assert(TOK_PER_RG * RG == kChunk && RG_PER_GROUP * TOK_PER_RG == kGroup, "tiling");
-
-  __shared__ float part[RG][D + 1];
-  __shared__ float gsum[kChunk / kGroup][D + 1];
+  constexpr int TPG = D / 8;                   // threads per group row
+  constexpr int NG = kChunk / kGroup;          // groups per chunk
+  static_assert(TPG * NG == D, "one thread per (group, 8 dims)");
+  __shared__ __attribute__((aligned(16))) float gsum[NG][D];
 
   const int t = threadIdx.x;
-  const int dc = t % TPR;
-  const int rg = t / TPR;
+  const int c = t % TPG;                       // 8-dim column
+  const int g = t / TPG;                       // group within the chunk
   const int64_t m = chunk_begin + blockIdx.x;  // chunk index
   const int j = blockIdx.y;                    // KV head
 
-  const T* src = k_hist + (static_cast<int64_t>(j) * hist_rows + m * kChunk + rg * TOK_PER_RG) * D + dc * 8;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const T* src = k_hist + (static_cast<int64_t>(j) * hist_rows + m * kChunk + g * kGroup) * D + c * 8;
+  float v[kGroup][8];
 #pragma unroll
-  for (int u = 0; u < TOK_PER_RG; ++u) {
-    float v[8];
-    Elem<T>::load8(src + static_cast<int64_t>(u) * D, v);
+  for (int u = 0; u < kGroup; ++u) Elem<T>::load8(src + static_cast<int64_t>(u) * D, v[u]);
+  float s[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  for (int e = 0; e < 8; ++e) {
+    const float lo = (((0.f + v[0][e]) + v[1][e]) + v[2][e]) + v[3][e];
+    const float hi = (((0.f + v[4][e]) + v[5][e]) + v[6][e]) + v[7][e];
+    s[e] = (0.f + lo) + hi;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg][dc * 8 + e] = acc[e];
-  __syncthreads();
-
+  *reinterpret_cast<float4*>(&gsum[g][c * 8]) = make_float4(s[0], s[1], s[2], s[3]);
+  *reinterpret_cast<float4*>(&gsum[g][c * 8 + 4]) = make_float4(s[4], s[5], s[6], s[7]);
   const int64_t n_groups_total = hist_rows / kGroup;   // group rows per KV head
-  for (int idx = t; idx < (kChunk / kGroup) * D; idx += kThreads) {
-    const int g = idx / D, e = idx % D;
-    float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < RG_PER_GROUP; ++q) s += part[g * RG_PER_GROUP + q][e];
-    gsum[g][e] = s;
-    group_sum[(static_cast<int64_t>(j) * n_groups_total + m * (kChunk / kGroup) + g) * D + e] =
-        s * (1.0f / kGroup);
-  }
+  float* gdst = group_sum + (static_cast<int64_t>(j) * n_groups_total + m * NG + g) * D + c * 8;
+  constexpr float kInvG = 1.0f / kGroup;
+  *reinterpret_cast<float4*>(gdst) = make_float4(s[0] * kInvG, s[1] * kInvG, s[2] * kInvG, s[3] * kInvG);
+  *reinterpret_cast<float4*>(gdst + 4) = make_float4(s[4] * kInvG, s[5] * kInvG, s[6] * kInvG, s[7] * kInvG);
   __syncthreads();
-  if (t < D) {
-    float s = 0.f;
+  if (t < D / 4) {                             // 4 chunk dims per thread
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int g = 0; g < kChunk / kGroup; ++g) s += gsum[g][t];
-    chunk_sum[(static_cast<int64_t>(j) * (hist_rows / kChunk) + m) * D + t] = s * (1.0f / kChunk);
+    for (int q = 0; q < NG; ++q) {
+      const float4 b = *reinterpret_cast<const float4*>(&gsum[q][t * 4]);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    constexpr float kInvC = 1.0f / kChunk;
+    *reinterpret_cast<float4*>(chunk_sum + (static_cast<int64_t>(j) * (hist_rows / kChunk) + m) * D + t * 4) =
+        make_float4(a.x * kInvC, a.y * kInvC, a.z * kInvC, a.w * kInvC);
   }
 }
 
@@ -66,7 +68,7 @@ template <typename T, int D>
 hipError_t launch_t(const hga_shape& s, const void* k, int64_t c0, int64_t c1, float* cs,
                     float* gs, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(c1 - c0), static_cast<unsigned>(s.n_kv_heads));
-  hipExtLaunchKernelGGL((build_summaries_kernel<T, D>), grid, dim3(kThreads), 0, st,
+  hipExtLaunchKernelGGL((build_summaries_kernel<T, D>), grid, dim3(D), 0, st,
                         timer_event(HGA_KERNEL_SUMMARIES, 0), timer_event(HGA_KERNEL_SUMMARIES, 1), 0,
                         static_cast<const T*>(k), hist_rows(s), c0, cs, gs);
   return hipGetLastError();

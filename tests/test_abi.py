@@ -201,6 +201,10 @@ def test_summary_range_checks(L):
     assert L.hga_build_summaries(ctypes.byref(s), FAKE, 64, 32, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
     assert L.hga_build_summaries(ctypes.byref(s), FAKE, 0, 14336 + 64, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
     assert L.hga_build_summaries(ctypes.byref(s), FAKE, 0, 100, FAKE, FAKE, None) == hga.HGA_ERR_INVALID_ARG
+    # summaries are written 16 bytes at a time: misaligned outputs are refused
+    assert L.hga_build_summaries(ctypes.byref(s), FAKE, 0, 64, FAKE + 4, FAKE, None) == hga.HGA_ERR_INVALID_ARG
+    assert b"16-byte aligned" in L.hga_last_error()
+    assert L.hga_build_summaries(ctypes.byref(s), FAKE, 0, 64, FAKE, FAKE + 8, None) == hga.HGA_ERR_INVALID_ARG
     # an empty range is a no-op that touches nothing
     assert L.hga_build_summaries(ctypes.byref(s), None, 128, 128, None, None, None) == hga.HGA_OK
     assert L.hga_last_error() == b""
