@@ -499,6 +499,10 @@ def other_configs(args):
     import subprocess
     if args.also == "none":
         return None
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        # under rocprofv3 the profiler's preloaded library has set up the GPU
+        # in this process already: start no other program from it
+        return {"skipped": "running under rocprofv3"}
     if args.also == "auto":
         if args.workload != "qwen3_8b_16k_fwdbwd":
             return None
@@ -512,7 +516,11 @@ def other_configs(args):
                "--seed", str(args.seed)]
         print(f"bench.py: timing {name} in a child process", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
-        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=600)
+        try:
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=600)
+        except (OSError, subprocess.SubprocessError) as e:
+            res[name] = {"error": f"{type(e).__name__}: {e}"}
+            continue
         lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
         if r.returncode != 0 or not lines:
             res[name] = {"error": f"exit {r.returncode}", "stderr_tail": r.stderr[-400:]}
