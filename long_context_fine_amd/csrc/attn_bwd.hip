@@ -630,23 +630,34 @@ __global__ __launch_bounds__(128 * HPW) void attn_bwd_dkdv_bf16_kernel(BwdParams
 }
 
 // dK = scale * sum_h partial_h, dV = sum_h partial_h, summed in head-group order.
+// Eight elements per thread: every partial's two 16-byte loads are issued
+// before the adds.
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part, int n_hg,
                                                           int64_t n_elem, float scale,
                                                           uint16_t* __restrict__ dk,
                                                           uint16_t* __restrict__ dv) {
-  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
   if (i >= n_elem) return;
-  float4 sk = *reinterpret_cast<const float4*>(part + i);
-  float4 sv = *reinterpret_cast<const float4*>(part + n_elem + i);
+  float4 sk0 = *reinterpret_cast<const float4*>(part + i);
+  float4 sk1 = *reinterpret_cast<const float4*>(part + i + 4);
+  float4 sv0 = *reinterpret_cast<const float4*>(part + n_elem + i);
+  float4 sv1 = *reinterpret_cast<const float4*>(part + n_elem + i + 4);
   for (int h = 1; h < n_hg; ++h) {
-    const float4 a = *reinterpret_cast<const float4*>(part + (2 * h) * n_elem + i);
-    const float4 b = *reinterpret_cast<const float4*>(part + (2 * h + 1) * n_elem + i);
-    sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
-    sv.x += b.x; sv.y += b.y; sv.z += b.z; sv.w += b.w;
+    const float* pk = part + (2 * h) * n_elem + i;
+    const float* pv = part + (2 * h + 1) * n_elem + i;
+    const float4 a0 = *reinterpret_cast<const float4*>(pk), a1 = *reinterpret_cast<const float4*>(pk + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(pv), b1 = *reinterpret_cast<const float4*>(pv + 4);
+    sk0.x += a0.x; sk0.y += a0.y; sk0.z += a0.z; sk0.w += a0.w;
+    sk1.x += a1.x; sk1.y += a1.y; sk1.z += a1.z; sk1.w += a1.w;
+    sv0.x += b0.x; sv0.y += b0.y; sv0.z += b0.z; sv0.w += b0.w;
+    sv1.x += b1.x; sv1.y += b1.y; sv1.z += b1.z; sv1.w += b1.w;
   }
-  *reinterpret_cast<uint2*>(dk + i) = make_uint2(cvt_pk_bf16(sk.x * scale, sk.y * scale),
-                                                 cvt_pk_bf16(sk.z * scale, sk.w * scale));
-  *reinterpret_cast<uint2*>(dv + i) = make_uint2(cvt_pk_bf16(sv.x, sv.y), cvt_pk_bf16(sv.z, sv.w));
+  uint2* ok = reinterpret_cast<uint2*>(dk + i);   // 8-byte stores: dK/dV need 8-byte alignment only
+  uint2* ov = reinterpret_cast<uint2*>(dv + i);
+  ok[0] = make_uint2(cvt_pk_bf16(sk0.x * scale, sk0.y * scale), cvt_pk_bf16(sk0.z * scale, sk0.w * scale));
+  ok[1] = make_uint2(cvt_pk_bf16(sk1.x * scale, sk1.y * scale), cvt_pk_bf16(sk1.z * scale, sk1.w * scale));
+  ov[0] = make_uint2(cvt_pk_bf16(sv0.x, sv0.y), cvt_pk_bf16(sv0.z, sv0.w));
+  ov[1] = make_uint2(cvt_pk_bf16(sv1.x, sv1.y), cvt_pk_bf16(sv1.z, sv1.w));
 }
 
 // ---------------------------------------------------------------------------
@@ -849,7 +860,7 @@ hipError_t launch_d(const hga_shape& s, BwdParams& p, hipStream_t st) {
     }
     if (n_hg > 1) {
       const int64_t n_elem = static_cast<int64_t>(s.n_kv_heads) * s.seg_len * D;
-      hipExtLaunchKernelGGL(dkdv_reduce_kernel, dim3(static_cast<unsigned>((n_elem / 4 + 255) / 256)),
+      hipExtLaunchKernelGGL(dkdv_reduce_kernel, dim3(static_cast<unsigned>((n_elem / 8 + 255) / 256)),
                             dim3(256), 0, st, nullptr, kv1, 0, p.dkdv_part, n_hg, n_elem, p.scale,
                             static_cast<uint16_t*>(p.dk), static_cast<uint16_t*>(p.dv));
     }
